@@ -1,0 +1,98 @@
+"""float64 CPU oracle for the row-wise log-sum-exp.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg are the only callers. The HIP library never
+imports, links or runs anything here, and this package imports nothing from
+it.
+
+``lse(x, dtype)`` returns, for each row of a 2-D array, log(sum_j exp(x_ij))
+in float64, computed by ``lse_oracle.c`` (plain two-pass max-subtract with
+libm ``exp``/``log``; its header states the definition and the special
+cases). bf16 inputs are passed as uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+HERE = Path(__file__).resolve().parent
+SOURCE = HERE / "lse_oracle.c"
+LIBRARY = HERE / "liblse_oracle.so"
+
+DTYPES = {"f32": 0, "bf16": 1}
+
+
+def build(source: Path = SOURCE, output: Path = LIBRARY) -> Path:
+    """Compile the oracle with gcc: -O2, IEEE semantics (no fast-math)."""
+    tmp = output.with_name(output.name + f".tmp{os.getpid()}")
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", "-Wall", "-Werror", "-pthread",
+           "-o", str(tmp), str(source), "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, output)
+    return output
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library (the real one, or a test mutant)."""
+
+    def __init__(self, path: Path = LIBRARY):
+        path = Path(path)
+        if not path.exists():
+            build(output=path)
+        self.path = path
+        self._lib = ctypes.CDLL(str(path))
+        fn = self._lib.lse_oracle_f64
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_int]
+        self._fn = fn
+
+    def lse(self, x: np.ndarray, dtype: str | None = None, threads: int = 1) -> np.ndarray:
+        """Row-wise LSE of a 2-D array in float64.
+
+        ``x`` is float32 (dtype "f32") or uint16 bf16 bits (dtype "bf16"). Any
+        row stride is accepted as long as the last axis is contiguous.
+        """
+        x = np.asarray(x)
+        if dtype is None:
+            dtype = "bf16" if x.dtype == np.uint16 else "f32"
+        want = np.uint16 if dtype == "bf16" else np.float32
+        if x.dtype != want:
+            raise TypeError(f"dtype {dtype} needs a {np.dtype(want)} array, got {x.dtype}")
+        if x.ndim != 2:
+            raise ValueError("x must be 2-D")
+        rows, cols = x.shape
+        if (cols > 1 and x.strides[1] != x.itemsize) or \
+                (rows > 1 and (x.strides[0] < cols * x.itemsize or x.strides[0] % x.itemsize)):
+            x = np.ascontiguousarray(x)
+        stride = x.strides[0] // x.itemsize if rows > 1 else cols
+        out = np.full(rows, np.nan, dtype=np.float64)  # rows left unwritten stay NaN
+        rc = self._fn(x.ctypes.data if x.size else None, DTYPES[dtype], rows, cols,
+                      stride, out.ctypes.data, int(threads))
+        if rc != 0:
+            raise ValueError("lse_oracle_f64 rejected its arguments")
+        return out
+
+    def raw(self, ptr, dtype_code: int, rows: int, cols: int, stride: int, out_ptr,
+            threads: int = 1) -> int:
+        """Direct call with raw pointers, for argument-checking tests."""
+        return self._fn(ptr, dtype_code, rows, cols, stride, out_ptr, threads)
+
+
+_default: Oracle | None = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def lse(x: np.ndarray, dtype: str | None = None, threads: int = 1) -> np.ndarray:
+    return default().lse(x, dtype, threads)

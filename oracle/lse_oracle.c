@@ -1,0 +1,167 @@
+/*
+ * lse_oracle.c - float64 reference for the row-wise log-sum-exp.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link
+ * or call this file: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it. It shares no code with the HIP library.
+ *
+ * What it computes. For every row r of a row-major matrix x with `cols`
+ * elements per row and `row_stride` elements between row starts,
+ *
+ *     out[r] = LSE(x[r, :]) = log( sum_j exp(x[r, j]) ),
+ *
+ * the natural-log log-sum-exp that the paper "Speeding up Log-Sum-Exp:
+ * Kernel Fusion at the Memory Wall, Integer Arithmetic at the Compute Wall"
+ * names as its primitive (title, abstract, §1) and reduces over the last
+ * axis of a (B, N) tensor, one scalar per row (§2.1, §3.1). The output is in
+ * base e, as the paper's integer variant converts its result back to base-e
+ * float32 (§3.2).
+ *
+ * How. The plain max-subtract definition, the recipe of the PyTorch baseline
+ * that the paper profiles (§2.1, Figure 1), in float64 as the paper's
+ * accuracy reference is FP64 (§4):
+ *     m = max_j x_j,   s = sum_j exp(x_j - m)  (in ascending j),
+ *     out = m + log(s).
+ * Elements are widened exactly to double: fp32 directly, bf16 by placing its
+ * 16 bits in the high half of an fp32 word. Nothing is flushed to zero.
+ *
+ * Special cases (the paper lists edge-case handling in its Table 3 without
+ * the cells; these follow torch.logsumexp, which it replaces as a drop-in):
+ *     any NaN in the row            -> NaN
+ *     cols == 0, or every x = -inf  -> -inf
+ *     otherwise a +inf in the row   -> +inf
+ *
+ * The rows are split over `nthreads` POSIX threads; a row's arithmetic does
+ * not depend on the thread count.
+ *
+ * Parity pins: every function here is pinned by tests against closed forms,
+ * brute force and a library routine; see tests/test_oracle.py.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <string.h>
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Exact widening of the element at `index` (in elements from x) to double. */
+static double load_elem(const void *x, int dtype, int64_t index)
+{
+    if (dtype == ORACLE_F32) {
+        float f;
+        memcpy(&f, (const char *)x + 4 * index, 4);
+        return (double)f;
+    } else {
+        uint16_t h;
+        uint32_t w;
+        float f;
+        memcpy(&h, (const char *)x + 2 * index, 2);
+        w = (uint32_t)h << 16;
+        memcpy(&f, &w, 4);
+        return (double)f;
+    }
+}
+
+/* The log-sum-exp of one row in float64: max, then the shifted exp-sum. */
+static double lse_one_row(const void *x, int dtype, int64_t start, int64_t cols)
+{
+    double m = -INFINITY;
+    double s = 0.0;
+    int64_t j;
+
+    if (cols == 0)
+        return -INFINITY;
+
+    /* First pass: the row maximum; a NaN anywhere makes the result NaN. */
+    for (j = 0; j < cols; ++j) {
+        double v = load_elem(x, dtype, start + j);
+        if (isnan(v))
+            return NAN;
+        if (v > m)
+            m = v;
+    }
+    if (m == -INFINITY)
+        return -INFINITY;
+    if (m == INFINITY)
+        return INFINITY;
+
+    /* Second pass: sum of exp(x_j - m); a -inf entry contributes exp(-inf) = 0. */
+    for (j = 0; j < cols; ++j)
+        s += exp(load_elem(x, dtype, start + j) - m);
+
+    return m + log(s);
+}
+
+struct job {
+    const void *x;
+    int dtype;
+    int64_t row_begin, row_end, cols, row_stride;
+    double *out;
+};
+
+static void *run_rows(void *arg)
+{
+    const struct job *jb = (const struct job *)arg;
+    int64_t r;
+    for (r = jb->row_begin; r < jb->row_end; ++r)
+        jb->out[r] = lse_one_row(jb->x, jb->dtype, r * jb->row_stride, jb->cols);
+    return NULL;
+}
+
+#define ORACLE_MAX_THREADS 256
+
+/*
+ * out[r] = LSE of row r, r in [0, rows). `x` is a host pointer to the first
+ * element; row r starts `r * row_stride` elements after it. Returns 0, or -1
+ * for an invalid argument (unknown dtype, negative size, row_stride < cols
+ * with more than one row, null pointer with work to do).
+ */
+int lse_oracle_f64(const void *x, int dtype, int64_t rows, int64_t cols,
+                   int64_t row_stride, double *out, int nthreads)
+{
+    pthread_t tid[ORACLE_MAX_THREADS];
+    struct job jobs[ORACLE_MAX_THREADS];
+    int64_t per;
+    int t, started = 0;
+
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16)
+        return -1;
+    if (rows < 0 || cols < 0 || (rows > 1 && row_stride < cols))
+        return -1;
+    if (rows == 0)
+        return 0;
+    if (out == NULL || (cols > 0 && x == NULL))
+        return -1;
+
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > ORACLE_MAX_THREADS)
+        nthreads = ORACLE_MAX_THREADS;
+    if ((int64_t)nthreads > rows)
+        nthreads = (int)rows;
+
+    per = (rows + nthreads - 1) / nthreads;
+    for (t = 0; t < nthreads; ++t) {
+        jobs[t].x = x;
+        jobs[t].dtype = dtype;
+        jobs[t].row_begin = (int64_t)t * per;
+        jobs[t].row_end = jobs[t].row_begin + per < rows ? jobs[t].row_begin + per : rows;
+        jobs[t].cols = cols;
+        jobs[t].row_stride = row_stride;
+        jobs[t].out = out;
+    }
+    if (nthreads == 1) {
+        run_rows(&jobs[0]);
+        return 0;
+    }
+    for (t = 0; t < nthreads; ++t) {
+        if (pthread_create(&tid[t], NULL, run_rows, &jobs[t]) != 0)
+            break;
+        ++started;
+    }
+    for (t = started; t < nthreads; ++t)   /* thread creation failed: finish here */
+        run_rows(&jobs[t]);
+    for (t = 0; t < started; ++t)
+        pthread_join(tid[t], NULL);
+    return 0;
+}

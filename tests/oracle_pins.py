@@ -1,0 +1,234 @@
+"""Checks that pin the float64 oracle to facts outside itself.
+
+Each check takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with a closed form, a brute-force sum, a library routine or
+an invariant of log-sum-exp. ``test_oracle.py`` runs them on the real oracle;
+``test_oracle_mutants.py`` runs them on copies of the oracle with planted
+mistakes and expects each copy to fail at least one.
+
+The expected values here never come from the oracle itself (nor from the HIP
+library): they are written from the mathematics, in Python's own float64
+arithmetic (``math.fsum``, ``math.log1p``, ``struct`` for bit decoding) or by
+SciPy.
+"""
+from __future__ import annotations
+
+import math
+import struct
+
+import numpy as np
+
+LN2 = math.log(2.0)
+LOG2E = 1.0 / LN2
+
+
+def _close(got, want, rel=1e-14, what=""):
+    got = float(got)
+    want = float(want)
+    if math.isnan(want):
+        assert math.isnan(got), f"{what}: want NaN, got {got!r}"
+        return
+    if math.isinf(want):
+        assert got == want, f"{what}: want {want!r}, got {got!r}"
+        return
+    tol = rel * max(1.0, abs(want))
+    assert abs(got - want) <= tol, f"{what}: |{got!r} - {want!r}| > {tol:.3g}"
+
+
+def _bf16_value(bits: int) -> float:
+    """Decode a bf16 bit pattern with struct: high half of an fp32 word."""
+    return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+def brute_lse(values) -> float:
+    """log(sum exp(v)) by exact summation; only for |v| small enough not to overflow."""
+    vals = [float(v) for v in values]
+    if any(math.isnan(v) for v in vals):
+        return math.nan
+    if not vals or all(v == -math.inf for v in vals):
+        return -math.inf
+    if any(v == math.inf for v in vals):
+        return math.inf
+    return math.log(math.fsum(math.exp(v) for v in vals if v != -math.inf))
+
+
+def pair_lse(a: float, b: float) -> float:
+    """The pairwise operator in the base-2 form f(z) = log2(1 + 2^z), z <= 0.
+
+    The paper's IntLSE error analysis (§A.1) takes f(z) = log2(1 + 2^z) as the
+    exact pairwise correction: lse(a, b) = ln 2 * (max' + f(min' - max')) with
+    a' = a * log2(e). Written here with log1p/exp2 in float64.
+    """
+    hi, lo = max(a, b), min(a, b)
+    if hi == -math.inf:
+        return -math.inf
+    z = (lo - hi) * LOG2E          # z <= 0, in base-2 units
+    # ln 2 * f(z) = ln 2 * log2(1 + 2^z) = log1p(2^z)
+    return hi + math.log1p(2.0 ** z)
+
+
+# --- closed forms --------------------------------------------------------
+
+def pin_constant_rows(orc):
+    """A row of N copies of c gives c + ln N (sum of N ones, exactly N)."""
+    for c in (0.0, 1.5, -7.25, 100.0, 800.0, -800.0, -29952.0):
+        for n in (1, 2, 3, 7, 1000, 32000):
+            x = np.full((2, n), c, dtype=np.float32)
+            got = orc.lse(x, "f32")
+            _close(got[0], c + math.log(n), 4e-16, f"f32 const c={c} N={n}")
+            _close(got[1], c + math.log(n), 4e-16, f"f32 const c={c} N={n} (row 1)")
+            # the same constant as bf16 (every c above is a bf16 value)
+            bits = np.full((1, n), struct.unpack("<I", struct.pack("<f", c))[0] >> 16,
+                           dtype=np.uint16)
+            _close(orc.lse(bits, "bf16")[0], c + math.log(n), 4e-16, f"bf16 const c={c} N={n}")
+
+
+def pin_two_element_closed_form(orc):
+    """Two-element rows against the base-2 pairwise form f(z) (§A.1)."""
+    rng = np.random.default_rng(11)
+    pairs = [(0.0, 0.0), (1.0, 0.0), (0.0, 1.0), (800.0, 0.0), (0.0, -800.0),
+             (-1000.0, 1000.0), (3.5, -2.25), (-60.0, -61.0), (30.0, -60.0)]
+    pairs += [tuple(v) for v in rng.uniform(-40, 40, size=(40, 2)).astype(np.float32)]
+    x = np.array(pairs, dtype=np.float32)
+    got = orc.lse(x, "f32")
+    for (a, b), g in zip(x.astype(np.float64), got):
+        _close(g, pair_lse(a, b), 1e-14, f"pair ({a}, {b})")
+
+
+def pin_brute_force_tiny(orc):
+    """Rows of <= 64 elements with |x| <= 50 against log(fsum(exp(x))), strided."""
+    rng = np.random.default_rng(5)
+    for cols in (1, 2, 3, 5, 8, 16, 17, 33, 64):
+        for stride in (cols, cols + 3):
+            buf = rng.uniform(-50, 50, size=(6, stride)).astype(np.float32)
+            view = buf[:, :cols]
+            got = orc.lse(view, "f32")
+            for r in range(view.shape[0]):
+                _close(got[r], brute_lse(view[r]), 1e-14, f"f32 brute cols={cols} r={r}")
+            bits = (rng.integers(0, 1 << 16, size=(5, stride), dtype=np.uint32)).astype(np.uint16)
+            # keep finite values with |x| <= 50: clear exponents above 2^5
+            vals = [[_bf16_value(b) for b in row] for row in bits]
+            for r in range(bits.shape[0]):
+                for j in range(stride):
+                    if not math.isfinite(vals[r][j]) or abs(vals[r][j]) > 50:
+                        bits[r, j] = 0x3F80 if j % 2 else 0xC1A0  # 1.0 or -20.0
+            bview = bits[:, :cols]
+            got = orc.lse(bview, "bf16")
+            for r in range(bview.shape[0]):
+                want = brute_lse([_bf16_value(b) for b in bview[r]])
+                _close(got[r], want, 1e-14, f"bf16 brute cols={cols} r={r}")
+
+
+def pin_special_values(orc):
+    """NaN, +-inf, empty and subnormal rows (semantics of torch.logsumexp)."""
+    inf, nan = math.inf, math.nan
+    cases = [
+        ([-inf, -inf, -inf], -inf),
+        ([-inf], -inf),
+        ([1.0, nan, 2.0], nan),
+        ([nan, 1.0], nan),
+        ([inf, 1.0, -inf], inf),
+        ([1.0, inf], inf),
+        ([inf, nan], nan),
+        ([nan, inf], nan),
+        ([-inf, nan], nan),
+        ([-inf, 0.0], 0.0),
+        ([0.0, -inf, -inf, 0.0], LN2),
+        ([1e-45, -inf], 1e-45),
+        ([3.0e38, 3.0e38], None),
+        ([-3.0e38, -3.0e38, -3.0e38], None),
+    ]
+    for row, want in cases:
+        x = np.array([row], dtype=np.float32)
+        if want is None:  # huge magnitudes: m + ln(count)
+            v = float(x[0, 0])
+            want = v + math.log(len(row))
+        elif want == 1e-45:
+            want = float(np.float32(1e-45))
+        _close(orc.lse(x, "f32")[0], want, 1e-15, f"special {row}")
+    # empty rows: the empty sum gives -inf
+    got = orc.lse(np.zeros((3, 0), dtype=np.float32), "f32")
+    assert np.all(got == -np.inf), f"cols=0 gave {got}"
+    # bf16 specials: 0x7F80 = +inf, 0xFF80 = -inf, 0x7FC1 = NaN
+    b = np.array([[0xFF80, 0xFF80], [0x7F80, 0x3F80], [0x7FC1, 0x3F80], [0x3F80, 0x3F80]],
+                 dtype=np.uint16)
+    got = orc.lse(b, "bf16")
+    assert got[0] == -np.inf and got[1] == np.inf and np.isnan(got[2]), f"bf16 specials {got}"
+    _close(got[3], 1.0 + LN2, 1e-15, "bf16 [1, 1]")
+
+
+# --- invariants --------------------------------------------------------------
+
+def pin_shift_invariance(orc):
+    """LSE(x + c) = LSE(x) + c, with x on a 1/64 grid so x + c is exact in fp32."""
+    rng = np.random.default_rng(7)
+    x = (rng.integers(-640, 640, size=(8, 300)) / 64.0).astype(np.float32)
+    base = orc.lse(x, "f32")
+    for k in (-3, 0, 4, 7):
+        c = np.float32(2.0 ** k)
+        shifted = orc.lse(x + c, "f32")
+        for r in range(x.shape[0]):
+            _close(shifted[r], base[r] + float(c), 1e-14, f"shift 2^{k} r={r}")
+
+
+def pin_permutation_invariance(orc):
+    """The pairwise operator is commutative (§3.1): any column order, same value."""
+    rng = np.random.default_rng(8)
+    x = rng.normal(0, 5, size=(6, 513)).astype(np.float32)
+    base = orc.lse(x, "f32")
+    for _ in range(3):
+        perm = rng.permutation(x.shape[1])
+        _close_all(orc.lse(np.ascontiguousarray(x[:, perm]), "f32"), base, 1e-14, "permutation")
+
+
+def pin_concat_merge(orc):
+    """Associativity (§3.1): LSE(a ++ b) = lse(LSE(a), LSE(b)) via the pairwise form."""
+    rng = np.random.default_rng(9)
+    a = rng.normal(0, 4, size=(5, 200)).astype(np.float32)
+    b = (rng.normal(0, 4, size=(5, 77)) + 9).astype(np.float32)
+    whole = orc.lse(np.concatenate([a, b], axis=1), "f32")
+    la, lb = orc.lse(a, "f32"), orc.lse(b, "f32")
+    for r in range(a.shape[0]):
+        _close(whole[r], pair_lse(la[r], lb[r]), 1e-14, f"concat r={r}")
+
+
+def pin_thread_count_invariance(orc):
+    """The row split over threads changes nothing, bit for bit."""
+    rng = np.random.default_rng(10)
+    for rows in (1, 2, 7, 10, 33):
+        x = rng.normal(0, 3, size=(rows, 45)).astype(np.float32)
+        one = orc.lse(x, "f32", threads=1)
+        for t in (2, 3, 7, 64):
+            assert np.array_equal(orc.lse(x, "f32", threads=t), one), f"threads={t} rows={rows}"
+        for r in range(rows):
+            _close(one[r], brute_lse(x[r]), 1e-14, f"threads brute r={r}")
+
+
+def pin_argument_checks(orc):
+    out = np.empty(4)
+    x = np.zeros((4, 4), np.float32)
+    assert orc.raw(x.ctypes.data, 2, 4, 4, 4, out.ctypes.data) == -1, "bad dtype accepted"
+    assert orc.raw(x.ctypes.data, 0, -1, 4, 4, out.ctypes.data) == -1, "rows < 0 accepted"
+    assert orc.raw(x.ctypes.data, 0, 4, -1, 4, out.ctypes.data) == -1, "cols < 0 accepted"
+    assert orc.raw(x.ctypes.data, 0, 4, 4, 3, out.ctypes.data) == -1, "stride < cols accepted"
+    assert orc.raw(None, 0, 0, 4, 4, None) == 0, "rows = 0 must be a no-op"
+    assert orc.raw(None, 0, 4, 4, 4, out.ctypes.data) == -1, "null x accepted"
+
+
+def _close_all(got, want, rel, what):
+    assert got.shape == want.shape, f"{what}: shape"
+    for i, (g, w) in enumerate(zip(got, want)):
+        _close(g, w, rel, f"{what}[{i}]")
+
+
+CHEAP_PINS = [
+    pin_argument_checks,
+    pin_constant_rows,
+    pin_two_element_closed_form,
+    pin_special_values,
+    pin_brute_force_tiny,
+    pin_shift_invariance,
+    pin_permutation_invariance,
+    pin_concat_merge,
+    pin_thread_count_invariance,
+]

@@ -1,0 +1,153 @@
+"""Pins of the float64 oracle (CPU only).
+
+The closed-form, brute-force and invariant checks live in ``oracle_pins.py``
+so that the mutation test can run them on planted-mistake copies too. The
+checks below add the library cross-check (SciPy) and closed forms taken from
+the generators' own draws on prefixes of the five workloads.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle_pins
+import workloads
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+# Prefix sizes: each spans several of the GPU kernels' tiles and runs in well
+# under a second through the oracle.
+PREFIX = {1: 64, 2: 16, 3: 8, 4: 256, 5: 1 << 16}
+
+
+@pytest.fixture(scope="module")
+def prefixes():
+    return {c: workloads.make(c, rows=n, aux=True) for c, n in PREFIX.items()}
+
+
+@pytest.mark.parametrize("pin", oracle_pins.CHEAP_PINS, ids=lambda f: f.__name__)
+def test_pin(oracle, pin):
+    pin(oracle)
+
+
+def _as_f64(w):
+    if w.dtype == "bf16":
+        return workloads.bf16_bits_to_f32(w.x).astype(np.float64)
+    return w.x.astype(np.float64)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_scipy_logsumexp(oracle, prefixes, cfg):
+    """A library routine: scipy.special.logsumexp in float64 on the same rows."""
+    w = prefixes[cfg]
+    got = oracle.lse(w.x, w.dtype, threads=4)
+    want = scipy.special.logsumexp(_as_f64(w), axis=1)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.all(got[~fin] == want[~fin])
+    err = np.abs(got[fin] - want[fin]) / np.maximum(1.0, np.abs(want[fin]))
+    assert err.max(initial=0.0) <= 1e-13
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_max_bounds(oracle, prefixes, cfg):
+    """max_j x_j <= LSE <= max_j x_j + ln(#entries > -inf), on every row."""
+    w = prefixes[cfg]
+    got = oracle.lse(w.x, w.dtype, threads=4)
+    x = _as_f64(w)
+    mx = x.max(axis=1)
+    count = np.isfinite(x).sum(axis=1)
+    live = count > 0
+    assert np.all(got[~live] == -np.inf)
+    slack = 1e-12 * np.maximum(1.0, np.abs(mx[live]))
+    assert np.all(got[live] >= mx[live] - slack)
+    assert np.all(got[live] <= mx[live] + np.log(count[live]) + slack)
+
+
+def test_config5_dirichlet_closed_form(oracle, prefixes):
+    """x = fp32(ln p) with p a Dirichlet draw: LSE(x) = ln(sum of kept p_j).
+
+    LSE is 1-Lipschitz in the max norm, so |LSE(x) - ln sum_kept p| is at most
+    max_j |x_j - ln p_j| (the fp32 rounding of ln p), plus double rounding.
+    Rows that keep every entry have sum p = 1, so their LSE is ~0.
+    """
+    w = prefixes[5]
+    p, keep, allneg = w.aux["p"], w.aux["keep"].copy(), w.aux["allneg"]
+    keep[allneg] = False
+    got = oracle.lse(w.x, "f32", threads=4)
+    mass = np.where(keep, p, 0.0).sum(axis=1)
+    dead = ~keep.any(axis=1)
+    assert np.all(got[dead] == -np.inf)
+    assert dead.sum() >= len(allneg)
+    lnp = np.log(p)
+    delta = np.where(keep, np.abs(w.x.astype(np.float64) - lnp), 0.0).max(axis=1)
+    live = ~dead
+    err = np.abs(got[live] - np.log(mass[live]))
+    assert np.all(err <= delta[live] + 4e-16 * np.maximum(1.0, np.abs(got[live])) + 1e-15)
+    full = keep.all(axis=1)
+    assert full.sum() > 1000
+    assert np.all(np.abs(got[full]) <= delta[full] + 1e-15)
+
+
+def test_config4_particle_rows_brute(oracle, prefixes):
+    """Particle-filter rows: exact fsum brute force, and the closed-form mean.
+
+    E[exp(-z^2/(2 s^2))] = s / sqrt(1 + s^2) for z ~ N(0, 1), so
+    sum_j exp(x_ij) ~ 4096 / sqrt(1 + s_i^2) and LSE_i ~ ln 4096 - ln(1 + s_i^2)/2.
+    """
+    w = prefixes[4]
+    got = oracle.lse(w.x, "f32", threads=4)
+    for r in range(0, w.rows, 37):
+        assert abs(got[r] - oracle_pins.brute_lse(w.x[r])) <= 1e-14 * max(1, abs(got[r]))
+    sigma = w.aux["sigma"]
+    pred = math.log(4096) - 0.5 * np.log1p(sigma * sigma)
+    assert abs(np.mean(got - pred)) < 0.01
+    assert np.percentile(np.abs(got - pred), 90) < 0.2
+
+
+def test_config2_spike_bound(oracle, prefixes):
+    """Eight spike columns equal to bf16(o_i + 15) are the row maximum, so
+    LSE_i >= spike + ln 8 and LSE_i <= spike + ln 8 + ln(1 + (N - 8) e^(next - spike) / 8)."""
+    w = prefixes[2]
+    got = oracle.lse(w.x, "bf16")
+    x = _as_f64(w)
+    spikes = w.aux["spikes"]
+    for r in range(w.rows):
+        sv = x[r, spikes[r]]
+        assert np.all(sv == sv[0])
+        rest = np.delete(x[r], spikes[r])
+        assert rest.max() < sv[0]
+        lo = sv[0] + math.log(8)
+        hi = lo + math.log1p((x.shape[1] - 8) * math.exp(rest.max() - sv[0]) / 8)
+        assert lo - 1e-12 <= got[r] <= hi + 1e-12
+
+
+def test_prefix_rows_match_full_rows(oracle):
+    """A prefix of a workload equals the same rows of a longer draw, bit for bit."""
+    a = workloads.make(4, rows=1500)
+    b = workloads.make(4, rows=1100)
+    assert np.array_equal(a.x[:1100], b.x)
+
+
+def test_golden_edge_cases(oracle):
+    """The stored edge cases: the oracle reproduces them bit for bit, and every
+    stored value agrees with brute-force summation where that cannot overflow."""
+    import golden_cases
+    cases = golden_cases.load()
+    assert len(cases) >= 20
+    for c in cases:
+        got = oracle.lse(c["x"], c["dtype"])
+        want = c["out"]
+        assert np.array_equal(np.isnan(got), np.isnan(want)), c["name"]
+        ok = ~np.isnan(want)
+        assert np.array_equal(got[ok], want[ok]), c["name"]
+        vals = c["x"] if c["dtype"] == "f32" else workloads.bf16_bits_to_f32(c["x"])
+        for r in range(vals.shape[0]):
+            row = vals[r].astype(np.float64)
+            if np.all(np.abs(row[np.isfinite(row)]) < 700):
+                w = oracle_pins.brute_lse(row)
+                if np.isnan(w):
+                    assert np.isnan(want[r]), c["name"]
+                else:
+                    assert abs(want[r] - w) <= 1e-14 * max(1.0, abs(w)) or want[r] == w, c["name"]

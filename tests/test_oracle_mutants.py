@@ -1,0 +1,57 @@
+"""Plant mistakes in copies of the oracle and check that the pins catch each.
+
+Every mutant is a text edit of ``oracle/lse_oracle.c`` compiled into a
+temporary directory; the real oracle is never touched. A mutant that passes
+every pin would mean the pins could not tell that mistake from the truth.
+"""
+import shutil
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "no_max_shift": ("s += exp(load_elem(x, dtype, start + j) - m);",
+                     "s += exp(load_elem(x, dtype, start + j));"),
+    "minus_log": ("return m + log(s);", "return m - log(s);"),
+    "dropped_max": ("return m + log(s);", "return log(s);"),
+    "dropped_first_term": ("for (j = 0; j < cols; ++j)\n        s +=",
+                           "for (j = 1; j < cols; ++j)\n        s +="),
+    "dropped_last_term": ("for (j = 0; j < cols; ++j)\n        s +=",
+                          "for (j = 0; j + 1 < cols; ++j)\n        s +="),
+    "max_skips_first": ("for (j = 0; j < cols; ++j) {", "for (j = 1; j < cols; ++j) {"),
+    "min_not_max": ("if (v > m)", "if (v < m)"),
+    "bf16_shift_15": ("w = (uint32_t)h << 16;", "w = (uint32_t)h << 15;"),
+    "bf16_low_half": ("w = (uint32_t)h << 16;", "w = (uint32_t)h;"),
+    "f32_wrong_width": ("(const char *)x + 4 * index", "(const char *)x + 2 * index"),
+    "row_start_uses_cols": ("r * jb->row_stride", "r * jb->cols"),
+    "nan_not_checked_with_inf": ("if (m == INFINITY)\n        return INFINITY;",
+                                 "if (m == INFINITY && 0)\n        return INFINITY;"),
+    "nan_check_removed": ("if (isnan(v))\n            return NAN;", ""),
+    "neg_inf_guard_removed": ("if (m == -INFINITY)\n        return -INFINITY;", ""),
+    "rows_per_thread_floor": ("per = (rows + nthreads - 1) / nthreads;",
+                              "per = rows / nthreads;"),
+    "log2_not_ln": ("return m + log(s);", "return m + log2(s);"),
+    "exp2_not_exp": ("s += exp(load_elem", "s += exp2(load_elem"),
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = oracle.SOURCE.read_text()
+    assert src.count(old) == 1, f"mutation site for {name} not unique in the oracle source"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle.build(mutant_src, tmp_path / "libmutant.so")
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.CHEAP_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError) as e:
+            caught.append(f"{pin.__name__}: {str(e)[:80]}")
+            break
+    assert caught, f"mutant {name} passed every pin"
