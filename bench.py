@@ -1,0 +1,258 @@
+"""Benchmark of the row-wise log-sum-exp on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--all]
+
+One step is one lse_forward call over the whole workload: every row's
+log-sum-exp in one pass. The headline workload is bf16 [512, 128256] (the
+(B, N) shape the LSE paper profiles), with inputs already resident in device
+memory. To measure HBM rather than the 256 MiB Infinity Cache, consecutive
+steps read different copies of the input (enough copies to exceed twice the
+cache), so every step streams its input from HBM.
+
+Prints ONE JSON line with the metric, the per-launch roofline of the kernel
+(algorithmic bytes / mean launch time from HIP events on the launch stream,
+against the 8 TB/s HBM peak) and the float64 CPU oracle's rate on the same
+workload as a baseline. --all also times the other four workloads and writes
+their lines to --all-out.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+import workloads  # noqa: E402
+
+METRIC = "LSE input GB/s (% of HBM peak) at [512,128256] bf16; µs/call small shapes"
+HBM_PEAK_GBS = 8000.0
+CACHE_BYTES = 256 << 20
+TRAFFIC_FILE = ROOT / "profiles" / "traffic.txt"
+KERNEL_SOURCES = [ROOT / "row_wise_log_amd" / "csrc" / n
+                  for n in ("lse_kernels.hip", "lse_device.h")]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(cfg: int) -> float | None:
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; None otherwise."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    fields = {}
+    for line in TRAFFIC_FILE.read_text().splitlines():
+        if ":" in line and not line.startswith("#"):
+            k, _, v = line.partition(":")
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    v = fields.get(f"config{cfg}_bytes_per_launch")
+    return float(v) if v else None
+
+
+def plan_name(plan: dict) -> str:
+    names = {1: "rows_per_wave", 2: "row_per_wg", 3: "split_row"}
+    s = names.get(plan["schedule"], "none")
+    if plan["schedule"] == 1:
+        return (f"{s}(G={plan['lanes_per_row']},loads={plan['loads_per_lane']},"
+                f"vec={plan['vector_loads']},grid={plan['grid']})")
+    return f"{s}(block={plan['block']},unroll={plan['unroll']},parts={plan['parts']},grid={plan['grid']})"
+
+
+def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int | None):
+    w = workloads.make(cfg)
+    rows, cols = w.rows, w.cols
+    esize = 2 if w.dtype == "bf16" else 4
+    in_bytes = rows * cols * esize
+    out_bytes = rows * 4
+    dtype_code = B.LSE_DTYPE_BF16 if w.dtype == "bf16" else B.LSE_DTYPE_F32
+    if rotate is None:
+        rotate = max(1, -(-2 * CACHE_BYTES // in_bytes) + 1)
+    host = torch.from_numpy(w.x.view(np.int16) if w.dtype == "bf16" else w.x)
+    bufs = [host.to("cuda") for _ in range(rotate)]
+    out = torch.empty(rows, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    plan = B.lse_plan(dtype_code, rows, cols, cols, bufs[0].data_ptr(), 256, 0)
+
+    def step(i):
+        B.lse_forward(handle, bufs[i % rotate].data_ptr(), dtype_code, rows, cols, cols,
+                      out.data_ptr(), sh)
+
+    for i in range(warmup):
+        step(i)
+    # The timed region: K back-to-back launches between a synchronize on each
+    # side, with one HIP event pair on the launch stream around them. The
+    # wall clock gives the whole-job rate; the events give the mean launch
+    # duration on the GPU (the launches are queued ahead, so host overhead
+    # is hidden and the event interval is the kernels' own time plus the
+    # hardware's inter-dispatch gaps).
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_launch = e0.elapsed_time(e1) / steps
+
+    ms_step = wall / steps * 1e3
+    return {
+        "w": w, "plan": plan, "rotate": rotate, "in_bytes": in_bytes, "out_bytes": out_bytes,
+        "ms_per_step": ms_step, "launch_ms_mean": mean_launch,
+        "value_gbs": in_bytes / (ms_step * 1e-3) / 1e9,
+        "achieved_gbs": (in_bytes + out_bytes) / (mean_launch * 1e-3) / 1e9,
+        "out": out,
+    }
+
+
+def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0) -> dict:
+    """The float64 oracle on the host cores over the same input; its first
+    pass also checks the GPU output of the timed steps."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    orc = oracle.default()
+    nbytes = w.x.nbytes
+    passes = 0
+    t0 = time.perf_counter()
+    ref = None
+    while True:
+        r = orc.lse(w.x, w.dtype, threads=threads)
+        if ref is None:
+            ref = r
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or passes >= 1000:
+            break
+    tol = 1e-5 if w.dtype == "bf16" else 2e-6
+    fin = np.isfinite(ref)
+    exact = np.array_equal(gpu_out[~fin], ref[~fin].astype(np.float32), equal_nan=True)
+    err = np.abs(gpu_out[fin] - ref[fin]) / (tol * np.maximum(1.0, np.abs(ref[fin])))
+    log(f"GPU output vs oracle: max |err|/tol = {err.max(initial=0):.3f}, non-finite match {exact}")
+    return {"value": round(nbytes * passes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"the whole {w.rows}x{w.cols} {w.dtype} input, {passes} passes in "
+                       f"{el:.1f} s wall on {threads} threads (float64 two-pass max-subtract, "
+                       "libm exp/log)")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--rotate", type=int, default=None,
+                    help="input copies cycled through (default: enough to exceed 2x the 256 MiB cache)")
+    ap.add_argument("--all", action="store_true", help="also time the other four workloads")
+    ap.add_argument("--all-out", default="gpurun_out/bench_all.jsonl")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the row-wise LSE "
+                                   "shards by rows with no communication, so --gpus N > 1 is "
+                                   "not measured here"}))
+        return 2
+
+    import torch
+
+    from row_wise_log_amd import binding as B
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    B.load()
+    handle = B.lse_create(0)
+    try:
+        log(f"timing config {args.config}: {args.steps} steps after {args.warmup} warmup")
+        r = time_config(torch, B, handle, args.config, args.steps, args.warmup, args.rotate)
+        w = r["w"]
+        traffic = recorded_traffic(args.config)
+        line = {
+            "metric": METRIC,
+            "value": round(r["value_gbs"], 1),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(r["ms_per_step"], 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "f32",
+            "data": "synthetic",
+            "config": {
+                "workload": f"config{args.config} {w.spec.name}: {w.spec.recipe}",
+                "rows": w.rows, "cols": w.cols, "input_dtype": w.dtype,
+                "input_bytes": r["in_bytes"], "output_bytes": r["out_bytes"],
+                "rotating_copies": r["rotate"], "plan": plan_name(r["plan"]),
+                "pct_of_hbm_peak": round(100 * r["value_gbs"] / HBM_PEAK_GBS, 2),
+                "us_per_call": round(r["ms_per_step"] * 1e3, 2),
+                "rows_per_s": round(w.rows / (r["ms_per_step"] * 1e-3), 1),
+            },
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(r["achieved_gbs"], 1),
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": round(r["achieved_gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "launch_us_mean": round(r["launch_ms_mean"] * 1e3, 2),
+                "algorithmic_bytes_per_launch": r["in_bytes"] + r["out_bytes"],
+            },
+        }
+        if args.all:
+            Path(args.all_out).parent.mkdir(parents=True, exist_ok=True)
+            with open(args.all_out, "w") as f:
+                for cfg in [1, 2, 3, 4, 5]:
+                    log(f"timing config {cfg}")
+                    rc = r if cfg == args.config else time_config(
+                        torch, B, handle, cfg, args.steps, args.warmup, None)
+                    rec = {"config": cfg, "workload": rc["w"].spec.name,
+                           "plan": plan_name(rc["plan"]),
+                           "input_GBs": round(rc["value_gbs"], 1),
+                           "pct_hbm_peak": round(100 * rc["value_gbs"] / HBM_PEAK_GBS, 2),
+                           "us_per_call": round(rc["ms_per_step"] * 1e3, 2),
+                           "launch_us_mean": round(rc["launch_ms_mean"] * 1e3, 2),
+                           "achieved_GBs_per_launch": round(rc["achieved_gbs"], 1),
+                           "rows_per_s": round(rc["w"].rows / (rc["ms_per_step"] * 1e-3), 1)}
+                    log(json.dumps(rec))
+                    f.write(json.dumps(rec) + "\n")
+                    if cfg != args.config:
+                        del rc
+        if not args.no_cpu_baseline:
+            log("timing the float64 oracle on the host cores")
+            gpu_out = r["out"].cpu().numpy().astype(np.float64)
+            line["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds)
+        else:
+            line["cpu_baseline"] = None
+        print(json.dumps(line), flush=True)
+    finally:
+        torch.cuda.synchronize()
+        B.lse_destroy(handle)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

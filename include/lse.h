@@ -1,0 +1,161 @@
+/*
+ * lse.h - C ABI of the MI355X (gfx950) row-wise log-sum-exp library.
+ *
+ * The operation. For a row-major matrix x with `rows` rows of `cols`
+ * elements, row r starting `r * row_stride` elements after x, the library
+ * writes one fp32 scalar per row,
+ *
+ *     out[r] = log( sum_j exp(x[r, j]) )        (natural log),
+ *
+ * the log-sum-exp (LSE) that the paper "Speeding up Log-Sum-Exp: Kernel
+ * Fusion at the Memory Wall, Integer Arithmetic at the Compute Wall" defines
+ * as its primitive (title, abstract, §1) and reduces over the last axis of a
+ * (B, N) tensor (§2.1, Figure 1). As in its single-pass fused kernel
+ * (§3.1), every input element is read from device memory once, each lane
+ * folds its elements into a running (max, exp-sum) pair, the pairs are
+ * merged with the associative, commutative pairwise LSE, and one scalar per
+ * row is written. The output is base e, as the paper's integer variant also
+ * returns base-e float32 (§3.2). Accumulation is fp32 for both input types.
+ *
+ * Special values follow torch.logsumexp, which the paper's kernels replace
+ * as a drop-in (abstract, §6): a NaN anywhere in a row gives NaN; a row of
+ * only -inf, or an empty row (cols == 0), gives -inf; otherwise a +inf in the
+ * row gives +inf.
+ *
+ * Streams and ownership. All device work is enqueued on the caller's
+ * `stream` and returns without synchronising. `x` and `out` are device
+ * pointers owned by the caller and must stay valid until the stream reaches
+ * the call. A handle owns a small device workspace for the split-row
+ * schedule; calls that share one handle must not run concurrently (use one
+ * handle per stream).
+ *
+ * Errors. Every entry point returns an lse_status_t; nothing aborts. The
+ * arguments of lse_forward are checked on the host before any HIP call, in
+ * this order: dtype, sizes, pointers and alignment, then the handle.
+ */
+#ifndef ROW_WISE_LOG_AMD_LSE_H
+#define ROW_WISE_LOG_AMD_LSE_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lse_handle_s *lse_handle_t;
+
+/* Element type of x. bf16 is decoded exactly (its 16 bits become the high
+ * half of an fp32 word) and accumulated in fp32, like fp32 input. */
+typedef enum {
+    LSE_DTYPE_F32 = 0,
+    LSE_DTYPE_BF16 = 1
+} lse_dtype_t;
+
+typedef enum {
+    LSE_OK = 0,
+    LSE_ERR_INVALID_ARG = 1,       /* a size, pointer, alignment or handle is invalid */
+    LSE_ERR_UNSUPPORTED_DTYPE = 2, /* dtype is not one of lse_dtype_t */
+    LSE_ERR_NO_DEVICE = 3,         /* no HIP device, or the device is not gfx950 */
+    LSE_ERR_ALLOC = 4,             /* device memory for the workspace could not be allocated */
+    LSE_ERR_HIP = 5                /* a HIP runtime call or kernel launch failed */
+} lse_status_t;
+
+/* Schedules. AUTO picks by shape; the others force one schedule, which the
+ * tests and the benchmark use to compare them. Every schedule computes every
+ * shape: ROWS_PER_WAVE holds a row in registers and passes rows longer than
+ * 64 x 16 loads (16 KiB when rows are 16-byte aligned, else 1024 elements) to
+ * ROW_PER_WG; SPLIT_ROW processes at most LSE_SPLIT_MAX_ROWS rows per launch
+ * and issues more launches for more rows. */
+typedef enum {
+    LSE_SCHED_AUTO = 0,
+    LSE_SCHED_ROWS_PER_WAVE = 1, /* short rows held in registers, 64/G rows per wavefront */
+    LSE_SCHED_ROW_PER_WG = 2,    /* one workgroup streams one row */
+    LSE_SCHED_SPLIT_ROW = 3      /* S workgroups per row, partial (max, sum) pairs merged by the last */
+} lse_schedule_t;
+
+/*
+ * Create a handle on HIP device `device` (an index as for hipSetDevice).
+ * Queries the compute-unit count, allocates and zeroes the split-row
+ * workspace (LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS (max, sum) pairs plus
+ * one counter per row, about 0.5 MiB), and synchronises once. On success
+ * *out receives the handle; on failure *out is set to NULL.
+ * Errors: INVALID_ARG (out NULL, device out of range), NO_DEVICE (no device
+ * or not gfx950), ALLOC, HIP.
+ */
+lse_status_t lse_create(lse_handle_t *out, int device);
+
+/*
+ * out[r] = LSE(x[r, 0:cols]) for r in [0, rows), enqueued on `stream`
+ * (NULL means the null stream of the handle's device).
+ *   x          device pointer to element (0, 0); aligned to its element size.
+ *   dtype      LSE_DTYPE_F32 or LSE_DTYPE_BF16.
+ *   rows       >= 0; rows == 0 is a no-op (x and out may be NULL).
+ *   cols       >= 0, < 2^31; cols == 0 writes -inf to every out[r].
+ *   row_stride elements between consecutive row starts; >= cols when
+ *              rows > 1 (ignored when rows == 1). Rows may be padded.
+ *   out        device pointer to rows fp32 values, 4-byte aligned; must not
+ *              overlap x.
+ * No allocation, no synchronisation. Only bytes inside the rows
+ * [x + r*row_stride, x + r*row_stride + cols) are read.
+ * Errors: UNSUPPORTED_DTYPE; INVALID_ARG (negative or too large sizes,
+ * row_stride < cols, NULL pointer with work to do, misaligned x or out, NULL
+ * handle); HIP (launch failure, from hipGetLastError).
+ */
+lse_status_t lse_forward(lse_handle_t h, const void *x, lse_dtype_t dtype,
+                         int64_t rows, int64_t cols, int64_t row_stride,
+                         float *out, hipStream_t stream);
+
+/* Release the handle and its workspace. NULL is allowed and returns LSE_OK.
+ * The caller must ensure no work using the handle is still pending. */
+lse_status_t lse_destroy(lse_handle_t h);
+
+/* A static, human-readable name for a status code. */
+const char *lse_status_string(lse_status_t s);
+
+/* Force a schedule for later lse_forward calls on this handle (AUTO resets).
+ * Errors: INVALID_ARG (NULL handle or unknown schedule). */
+lse_status_t lse_set_schedule(lse_handle_t h, lse_schedule_t s);
+
+/* Tuning overrides for the streaming schedules, for measurement: threads per
+ * workgroup `block` (256, 512 or 1024), 16-byte loads per lane per batch
+ * `unroll` (4 or 8), and SPLIT_ROW workgroups per row `parts` (1..64). 0
+ * restores the planner's choice. Errors: INVALID_ARG (NULL handle or a value
+ * outside those sets). */
+lse_status_t lse_set_tuning(lse_handle_t h, int32_t block, int32_t unroll, int32_t parts);
+
+/* Launch plan chosen for one call: which kernel runs, with what grid. */
+typedef struct {
+    int32_t schedule;        /* an lse_schedule_t other than AUTO; 0 when rows == 0 */
+    int32_t block;           /* threads per workgroup */
+    int64_t grid;            /* workgroups launched */
+    int32_t vector_loads;    /* 1: 16-byte loads, 0: one element per load */
+    int32_t lanes_per_row;   /* ROWS_PER_WAVE: lanes G sharing one row */
+    int32_t loads_per_lane;  /* ROWS_PER_WAVE: loads each lane holds for a row */
+    int32_t rows_per_wave;   /* ROWS_PER_WAVE: rows a wavefront holds at once */
+    int32_t parts;           /* SPLIT_ROW: workgroups per row (1 otherwise) */
+    int32_t unroll;          /* ROW_PER_WG / SPLIT_ROW: 16-byte loads per lane per batch */
+    int64_t workspace_bytes; /* SPLIT_ROW: workspace bytes the call uses */
+} lse_plan_t;
+
+/* Capacity of a handle's split-row workspace. */
+#define LSE_SPLIT_MAX_ROWS 1024
+#define LSE_SPLIT_MAX_PARTS 64
+
+/*
+ * The launch plan lse_forward would use, computed on the host with no HIP
+ * call: for tests and profiling. `x_addr` is the device address of x (only
+ * its alignment matters), `n_cu` the compute-unit count, `schedule` an
+ * lse_schedule_t (AUTO for the shape-based choice). Arguments are checked as
+ * in lse_forward, minus the handle and the pointers' nullness.
+ * Errors: UNSUPPORTED_DTYPE, INVALID_ARG (also plan NULL or n_cu < 1).
+ */
+lse_status_t lse_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t row_stride,
+                      uint64_t x_addr, int32_t n_cu, lse_schedule_t schedule,
+                      lse_plan_t *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROW_WISE_LOG_AMD_LSE_H */

@@ -1,0 +1,50 @@
+"""Row-wise log-sum-exp on MI355X (gfx950): a C-ABI HIP library and its binding.
+
+``logsumexp(x)`` returns log(sum(exp(x), dim=-1)) in fp32 for a 2-D fp32 or
+bf16 CUDA/HIP tensor whose last axis is contiguous. PyTorch only provides the
+device memory and the current stream; the computation is the HIP library's
+``lse_forward`` (see include/lse.h). The library is loaded on first use and a
+missing library is an error, never a fallback.
+"""
+from __future__ import annotations
+
+from .binding import (LseError, lse_create, lse_destroy, lse_forward, lse_plan,  # noqa: F401
+                      lse_set_schedule, lse_set_tuning, lse_status_string, load)
+
+_handles: dict[int, int] = {}
+
+
+def handle(device: int) -> int:
+    """A library handle for `device`, created once per process."""
+    h = _handles.get(device)
+    if h is None:
+        h = lse_create(device)
+        _handles[device] = h
+    return h
+
+
+def logsumexp(x, out=None, handle_=None):
+    """LSE over the last axis of a 2-D fp32/bf16 GPU tensor, as fp32[rows]."""
+    import torch
+
+    from .binding import LSE_DTYPE_BF16, LSE_DTYPE_F32
+
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows, cols)")
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    codes = {torch.float32: LSE_DTYPE_F32, torch.bfloat16: LSE_DTYPE_BF16}
+    if x.dtype not in codes:
+        raise TypeError(f"unsupported dtype {x.dtype}: fp32 or bf16")
+    rows, cols = x.shape
+    if cols > 1 and x.stride(1) != 1:
+        raise ValueError("the last axis must be contiguous")
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=x.device)
+    elif out.dtype != torch.float32 or out.shape != (rows,) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor of shape (rows,)")
+    h = handle_ if handle_ is not None else handle(x.device.index or 0)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    lse_forward(h, x.data_ptr(), codes[x.dtype], rows, cols, x.stride(0) if rows > 1 else cols,
+                out.data_ptr(), stream)
+    return out

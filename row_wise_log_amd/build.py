@@ -1,0 +1,58 @@
+"""Compile the HIP library (csrc/) for gfx950 into row_wise_log_amd/liblse_amd.so.
+
+    python -m row_wise_log_amd.build
+
+hipcc cross-compiles for gfx950 without a GPU. Packed-fp32 VALU forms are
+disabled for the device code (-packed-fp32-ops): the kernels are written with
+scalar fp32 arithmetic and must compile to scalar fp32 instructions.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+INCLUDE = ROOT / "include"
+LIBRARY = PKG / "liblse_amd.so"
+SOURCES = [CSRC / "lse_kernels.hip", CSRC / "lse_api.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not Path(path).exists():
+        raise RuntimeError("hipcc not found: the ROCm toolchain is required to build the library")
+    return path
+
+
+def command(output: Path, extra: list[str] | None = None) -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-Wall", "-Wno-unused-command-line-argument",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            f"-I{INCLUDE}", f"-I{CSRC}", *(extra or []),
+            "-x", "hip", *map(str, SOURCES), "-o", str(output)]
+
+
+def build(output: Path = LIBRARY, extra: list[str] | None = None, quiet: bool = True) -> Path:
+    tmp = output.with_name(output.name + f".tmp{os.getpid()}")
+    proc = subprocess.run(command(tmp, extra), capture_output=True, text=True)
+    if proc.returncode != 0:
+        sys.stderr.write(proc.stdout + proc.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+    if not quiet:
+        # hipcc's host pass reports the device-only feature flag as unknown
+        noise = "not a recognized feature for this target"
+        msg = "\n".join(l for l in (proc.stdout + proc.stderr).splitlines() if noise not in l)
+        if msg.strip():
+            sys.stderr.write(msg + "\n")
+    os.replace(tmp, output)
+    return output
+
+
+if __name__ == "__main__":
+    print(build(quiet=False))

@@ -1,0 +1,299 @@
+// lse_api.cpp - the C ABI declared in include/lse.h: argument checks, the
+// shape-based launch planner, the handle and its split-row workspace.
+//
+// The planner is a pure host function (lse_plan) so that its choices can be
+// tested without a GPU. lse_forward checks its arguments, plans, and launches
+// on the caller's stream; it never allocates and never synchronises.
+#include "lse.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "lse_launch.h"
+
+struct lse_handle_s {
+    int device;
+    int n_cu;
+    unsigned* ws_pairs;  // LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS (max, sum) pairs
+    unsigned* counters;  // LSE_SPLIT_MAX_ROWS arrival counters, zero between calls
+    int schedule;        // lse_schedule_t forced for later calls (AUTO = by shape)
+    int block, unroll, parts;  // tuning overrides, 0 = planner default
+};
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+constexpr int kRegsMaxUnits = 1024;   // schedule A holds up to 64 lanes x 16 loads of a row
+constexpr int kWavesPerCU = 32;       // schedule A grid cap (the loop covers the rest)
+constexpr int64_t kSplitMinRowBytes = 256 << 10;  // shorter rows stream faster unsplit
+constexpr int64_t kSplitPartBytes = 128 << 10;    // target bytes per split part
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int pow2_at_least(int64_t v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+struct Tuning {
+    int block, unroll, parts;
+};
+
+lse_status_t check_sizes(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t row_stride,
+                         uint64_t x_addr) {
+    if (dtype != LSE_DTYPE_F32 && dtype != LSE_DTYPE_BF16) return LSE_ERR_UNSUPPORTED_DTYPE;
+    if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return LSE_ERR_INVALID_ARG;
+    if (rows > 1 && (row_stride < cols || row_stride > (INT64_MAX / 4) / rows))
+        return LSE_ERR_INVALID_ARG;
+    const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
+    if (rows > 0 && cols > 0 && x_addr % esize != 0) return LSE_ERR_INVALID_ARG;
+    return LSE_OK;
+}
+
+lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t row_stride,
+                       uint64_t x_addr, int n_cu, int schedule, Tuning tune, lse_plan_t* p) {
+    std::memset(p, 0, sizeof(*p));
+    if (rows == 0) return LSE_OK;
+
+    const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
+    const int k = 16 / esize;
+    const int64_t stride_bytes = (rows > 1 ? row_stride : cols) * esize;
+    const bool aligned16 = x_addr % 16 == 0 && (rows == 1 || stride_bytes % 16 == 0);
+    const int64_t vec_units = cols / k;
+    const int64_t vec_tail = cols - vec_units * k;
+    const bool regs_vec = aligned16 && vec_units <= kRegsMaxUnits;
+    const bool regs_scalar = cols <= kRegsMaxUnits;
+
+    int sched = schedule;
+    if (sched == LSE_SCHED_AUTO) {
+        const int64_t row_bytes = cols * esize;
+        if (regs_vec || (regs_scalar && !aligned16))
+            sched = LSE_SCHED_ROWS_PER_WAVE;
+        else if (rows < n_cu && row_bytes >= kSplitMinRowBytes)
+            sched = LSE_SCHED_SPLIT_ROW;  // few long rows: one workgroup per row would idle CUs
+        else
+            sched = LSE_SCHED_ROW_PER_WG;
+    }
+    // Rows longer than registers hold go to the streaming schedule.
+    if (sched == LSE_SCHED_ROWS_PER_WAVE && !regs_vec && !regs_scalar) sched = LSE_SCHED_ROW_PER_WG;
+
+    p->schedule = sched;
+    if (sched == LSE_SCHED_ROWS_PER_WAVE) {
+        const bool vec = regs_vec;
+        const int64_t units = vec ? vec_units : cols;
+        const int64_t tail = vec ? vec_tail : 0;
+        // every tail element needs its own lane: G >= tail
+        int g = pow2_at_least(std::max<int64_t>({units, tail, 1}));
+        if (g > 64) g = 64;
+        const int vpl = pow2_at_least(ceil_div(units > 0 ? units : 1, g));
+        const int rounds = vpl == 1 ? 4 : (vpl == 2 ? 2 : 1);
+        p->block = 256;
+        p->vector_loads = vec ? 1 : 0;
+        p->lanes_per_row = g;
+        p->loads_per_lane = vpl;
+        p->rows_per_wave = (64 / g) * rounds;
+        const int64_t iters = ceil_div(rows, p->rows_per_wave);
+        int64_t waves = iters;
+        if (waves > static_cast<int64_t>(n_cu) * kWavesPerCU) waves = static_cast<int64_t>(n_cu) * kWavesPerCU;
+        p->grid = ceil_div(waves, 4);
+        p->parts = 1;
+        return LSE_OK;
+    }
+
+    p->vector_loads = 1;
+    if (sched == LSE_SCHED_ROW_PER_WG) {
+        p->block = tune.block ? tune.block : 512;
+        p->unroll = tune.unroll ? tune.unroll : (dtype == LSE_DTYPE_BF16 ? 4 : 8);
+        p->parts = 1;
+        p->grid = rows;
+        return LSE_OK;
+    }
+    // LSE_SCHED_SPLIT_ROW: parts of about kSplitPartBytes, at least 2, at most
+    // LSE_SPLIT_MAX_PARTS, and no more than ~8 workgroups per CU in total.
+    p->block = tune.block ? tune.block : 512;
+    p->unroll = tune.unroll ? tune.unroll : (dtype == LSE_DTYPE_BF16 ? 4 : 8);
+    int64_t parts = tune.parts;
+    if (!parts) {
+        const int64_t r = rows < LSE_SPLIT_MAX_ROWS ? rows : LSE_SPLIT_MAX_ROWS;
+        parts = ceil_div(cols * esize, kSplitPartBytes);
+        const int64_t cap = ceil_div(8 * static_cast<int64_t>(n_cu), r);
+        if (parts > cap) parts = cap;
+        if (parts < 2) parts = 2;
+    }
+    if (parts > LSE_SPLIT_MAX_PARTS) parts = LSE_SPLIT_MAX_PARTS;
+    p->parts = static_cast<int32_t>(parts);
+    const int64_t batch_rows = rows < LSE_SPLIT_MAX_ROWS ? rows : LSE_SPLIT_MAX_ROWS;
+    p->grid = batch_rows * parts;  // per launch; rows beyond LSE_SPLIT_MAX_ROWS take more launches
+    p->workspace_bytes = batch_rows * parts * 8 + batch_rows * 4;
+    return LSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lse_status_string(lse_status_t s) {
+    switch (s) {
+        case LSE_OK: return "LSE_OK";
+        case LSE_ERR_INVALID_ARG: return "LSE_ERR_INVALID_ARG";
+        case LSE_ERR_UNSUPPORTED_DTYPE: return "LSE_ERR_UNSUPPORTED_DTYPE";
+        case LSE_ERR_NO_DEVICE: return "LSE_ERR_NO_DEVICE";
+        case LSE_ERR_ALLOC: return "LSE_ERR_ALLOC";
+        case LSE_ERR_HIP: return "LSE_ERR_HIP";
+    }
+    return "LSE_ERR_UNKNOWN";
+}
+
+lse_status_t lse_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t row_stride,
+                      uint64_t x_addr, int32_t n_cu, lse_schedule_t schedule, lse_plan_t* plan) {
+    if (plan == nullptr || n_cu < 1) return LSE_ERR_INVALID_ARG;
+    lse_status_t st = check_sizes(dtype, rows, cols, row_stride, x_addr);
+    if (st != LSE_OK) return st;
+    if (schedule < LSE_SCHED_AUTO || schedule > LSE_SCHED_SPLIT_ROW) return LSE_ERR_INVALID_ARG;
+    return make_plan(dtype, rows, cols, row_stride, x_addr, n_cu, schedule, Tuning{0, 0, 0}, plan);
+}
+
+lse_status_t lse_create(lse_handle_t* out, int device) {
+    if (out == nullptr) return LSE_ERR_INVALID_ARG;
+    *out = nullptr;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
+        (void)hipGetLastError();
+        return LSE_ERR_NO_DEVICE;
+    }
+    if (device < 0 || device >= count) return LSE_ERR_INVALID_ARG;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return LSE_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return LSE_ERR_NO_DEVICE;
+
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) return LSE_ERR_HIP;
+    if (hipSetDevice(device) != hipSuccess) return LSE_ERR_HIP;
+
+    lse_handle_s* h = new (std::nothrow) lse_handle_s{};
+    lse_status_t st = LSE_OK;
+    if (h == nullptr) {
+        st = LSE_ERR_ALLOC;
+    } else {
+        h->device = device;
+        h->n_cu = prop.multiProcessorCount;
+        const size_t pair_bytes = size_t{LSE_SPLIT_MAX_ROWS} * LSE_SPLIT_MAX_PARTS * 8;
+        const size_t count_bytes = size_t{LSE_SPLIT_MAX_ROWS} * 4;
+        void* mem = nullptr;
+        if (hipMalloc(&mem, pair_bytes + count_bytes) != hipSuccess) {
+            st = LSE_ERR_ALLOC;
+        } else {
+            h->ws_pairs = static_cast<unsigned*>(mem);
+            h->counters = reinterpret_cast<unsigned*>(static_cast<char*>(mem) + pair_bytes);
+            if (hipMemset(h->counters, 0, count_bytes) != hipSuccess ||
+                hipDeviceSynchronize() != hipSuccess)
+                st = LSE_ERR_HIP;
+        }
+    }
+    if (st != LSE_OK && h != nullptr) {
+        if (h->ws_pairs) (void)hipFree(h->ws_pairs);
+        delete h;
+        h = nullptr;
+    }
+    (void)hipSetDevice(prev);
+    *out = h;
+    return st;
+}
+
+lse_status_t lse_destroy(lse_handle_t h) {
+    if (h == nullptr) return LSE_OK;
+    lse_status_t st = LSE_OK;
+    int prev = 0;
+    if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(h->device) == hipSuccess) {
+        if (h->ws_pairs && hipFree(h->ws_pairs) != hipSuccess) st = LSE_ERR_HIP;
+        (void)hipSetDevice(prev);
+    } else {
+        st = LSE_ERR_HIP;
+    }
+    delete h;
+    return st;
+}
+
+lse_status_t lse_set_schedule(lse_handle_t h, lse_schedule_t s) {
+    if (h == nullptr || s < LSE_SCHED_AUTO || s > LSE_SCHED_SPLIT_ROW) return LSE_ERR_INVALID_ARG;
+    h->schedule = s;
+    return LSE_OK;
+}
+
+lse_status_t lse_set_tuning(lse_handle_t h, int32_t block, int32_t unroll, int32_t parts) {
+    if (h == nullptr) return LSE_ERR_INVALID_ARG;
+    if (block != 0 && block != 256 && block != 512 && block != 1024) return LSE_ERR_INVALID_ARG;
+    if (unroll != 0 && unroll != 4 && unroll != 8) return LSE_ERR_INVALID_ARG;
+    if (parts < 0 || parts > LSE_SPLIT_MAX_PARTS) return LSE_ERR_INVALID_ARG;
+    h->block = block;
+    h->unroll = unroll;
+    h->parts = parts;
+    return LSE_OK;
+}
+
+lse_status_t lse_forward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,
+                         int64_t cols, int64_t row_stride, float* out, hipStream_t stream) {
+    const uint64_t x_addr = reinterpret_cast<uint64_t>(x);
+    lse_status_t st = check_sizes(dtype, rows, cols, row_stride, x_addr);
+    if (st != LSE_OK) return st;
+    if (rows == 0) return h == nullptr ? LSE_ERR_INVALID_ARG : LSE_OK;
+    if (out == nullptr || (cols > 0 && x == nullptr)) return LSE_ERR_INVALID_ARG;
+    if (reinterpret_cast<uint64_t>(out) % 4 != 0) return LSE_ERR_INVALID_ARG;
+    if (h == nullptr) return LSE_ERR_INVALID_ARG;
+
+    lse_plan_t p;
+    st = make_plan(dtype, rows, cols, row_stride, x_addr, h->n_cu, h->schedule,
+                   Tuning{h->block, h->unroll, h->parts}, &p);
+    if (st != LSE_OK) return st;
+
+    const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
+    lse::LaunchArgs a{};
+    a.schedule = p.schedule;
+    a.bf16 = dtype == LSE_DTYPE_BF16;
+    a.block = p.block;
+    a.grid = p.grid;
+    a.vector_loads = p.vector_loads != 0;
+    a.lanes_per_row = p.lanes_per_row;
+    a.loads_per_lane = p.loads_per_lane;
+    a.rows_per_wave = p.rows_per_wave;
+    a.parts = p.parts;
+    a.unroll = p.unroll;
+    a.x = static_cast<const char*>(x);
+    a.rows = rows;
+    a.cols = cols;
+    a.stride_bytes = (rows > 1 ? row_stride : cols) * esize;
+    a.out = out;
+    a.ws_pairs = h->ws_pairs;
+    a.counters = h->counters;
+    a.stream = stream;
+
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return LSE_ERR_HIP;
+    if (prev != h->device && hipSetDevice(h->device) != hipSuccess) return LSE_ERR_HIP;
+
+    hipError_t err = hipSuccess;
+    if (p.schedule == LSE_SCHED_SPLIT_ROW) {
+        // The workspace holds LSE_SPLIT_MAX_ROWS rows; larger inputs go in
+        // row batches on the same stream (each launch resets its counters).
+        for (int64_t r0 = 0; r0 < rows && err == hipSuccess; r0 += LSE_SPLIT_MAX_ROWS) {
+            const int64_t n = rows - r0 < LSE_SPLIT_MAX_ROWS ? rows - r0 : LSE_SPLIT_MAX_ROWS;
+            lse::LaunchArgs b = a;
+            b.x = a.x + r0 * a.stride_bytes;
+            b.out = a.out + r0;
+            b.rows = n;
+            b.grid = n * p.parts;
+            err = lse::launch(b);
+        }
+    } else {
+        err = lse::launch(a);
+    }
+    if (prev != h->device) (void)hipSetDevice(prev);
+    return err == hipSuccess ? LSE_OK : LSE_ERR_HIP;
+}
+
+}  // extern "C"

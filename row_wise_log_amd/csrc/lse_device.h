@@ -1,0 +1,291 @@
+// lse_device.h - device-side building blocks of the row-wise log-sum-exp
+// kernels for gfx950 (CDNA4, wave64).
+//
+// The accumulator. The paper "Speeding up Log-Sum-Exp: Kernel Fusion at the
+// Memory Wall, Integer Arithmetic at the Compute Wall" computes LSE in one
+// pass by folding elements with the associative, commutative pairwise LSE,
+// each thread keeping a register accumulator (§3.1): a running maximum and a
+// sum of exponentials, the online form its §2.2 describes. Here a lane keeps
+//
+//     m  the largest element folded so far (natural units, exact),
+//     c  = fl(clamp(m, -2^126, 2^126) * log2(e)), the base-2 reference,
+//     s  = sum over folded x of 2^(x*log2(e) - c),
+//
+// so the value it represents is ln2 * (c + log2 s). The exponentials run on
+// the hardware exp2 (v_exp_f32): each term costs one fused multiply-add
+// x*log2(e) - c and one v_exp_f32. A new maximum rescales s by 2^(c_old -
+// c_new) <= 1. The pairwise merge of (m1, c1, s1) and (m2, c2, s2) is
+// (max m, max c, s1*2^(c1 - C) + s2*2^(c2 - C)); the kernels apply it once
+// per batch of elements, across lanes and across workgroups.
+//
+// Why the clamp: c = fl(m*log2e) misses m*log2e by up to half an ulp, and a
+// term x = m contributes 2^(m*log2e - c). For |m| <= 2^30, m*log2e < 2^31,
+// so that residual is at most 2^6 and every term is at most 2^64: no sum can
+// overflow. Clamping m to +-2^30 before taking c keeps c finite for every m,
+// including +-inf, so no inf - inf or 0 * inf arises in the recursion. Rows
+// whose maximum lies beyond +-2^30 are recomputed by a natural-units pass,
+// sum 2^((x - m)*log2e), which has no such limit.
+//
+// Special values: a NaN element makes its own term NaN, so s becomes NaN and
+// stays NaN whatever the max does; +inf gives s = +inf with m = +inf; a row
+// of -inf (or no elements) keeps s = 0 and m = -inf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lse {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 0x1.715476p+0f;  // log2(e) rounded to fp32
+constexpr float kLn2 = 0x1.62e430p-1f;    // ln(2) rounded to fp32
+constexpr float kClamp = 0x1p30f;         // |m| beyond this takes the slow pass
+constexpr float kInf = __builtin_inff();
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+template <DType D> struct Elem;
+template <> struct Elem<DType::F32> {
+    static constexpr int kBytes = 4;
+    static constexpr int kPerVec = 4;            // elements in one 16-byte load
+    static constexpr unsigned kNegInfWord = 0xFF800000u;
+};
+template <> struct Elem<DType::BF16> {
+    static constexpr int kBytes = 2;
+    static constexpr int kPerVec = 8;
+    static constexpr unsigned kNegInfWord = 0xFF80FF80u;  // two bf16 -inf
+};
+
+// ---- arithmetic primitives -------------------------------------------------
+
+// max of three floats in one v_max3_f32. Written as asm so that the compiler
+// does not wrap each input in a canonicalising max (IEEE maxNum lowering);
+// NaN handling does not rely on the max (see the header comment).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// c(m): the base-2 reference of a running maximum; finite for every m.
+__device__ __forceinline__ float base2_ref(float m) {
+    return __builtin_amdgcn_fmed3f(m, -kClamp, kClamp) * kLog2e;
+}
+
+__device__ __forceinline__ bool is_nan(float v) {
+    return (__float_as_uint(v) & 0x7FFFFFFFu) > 0x7F800000u;
+}
+
+// ---- element decoding ------------------------------------------------------
+
+// One 16-byte word vector to fp32 values, in memory order. bf16 is exact: its
+// 16 bits become the high half of an fp32 word.
+template <DType D>
+__device__ __forceinline__ void decode(const u32x4 w, float* f) {
+    if constexpr (D == DType::F32) {
+        f[0] = __uint_as_float(w.x);
+        f[1] = __uint_as_float(w.y);
+        f[2] = __uint_as_float(w.z);
+        f[3] = __uint_as_float(w.w);
+    } else {
+        f[0] = __uint_as_float(w.x << 16);
+        f[1] = __uint_as_float(w.x & 0xFFFF0000u);
+        f[2] = __uint_as_float(w.y << 16);
+        f[3] = __uint_as_float(w.y & 0xFFFF0000u);
+        f[4] = __uint_as_float(w.z << 16);
+        f[5] = __uint_as_float(w.z & 0xFFFF0000u);
+        f[6] = __uint_as_float(w.w << 16);
+        f[7] = __uint_as_float(w.w & 0xFFFF0000u);
+    }
+}
+
+template <DType D>
+__device__ __forceinline__ float load_scalar(const char* p) {
+    if constexpr (D == DType::F32) {
+        return __builtin_nontemporal_load(reinterpret_cast<const float*>(p));
+    } else {
+        unsigned short h = __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p));
+        return __uint_as_float(static_cast<unsigned>(h) << 16);
+    }
+}
+
+__device__ __forceinline__ u32x4 load_vec(const u32x4* p) {
+    return __builtin_nontemporal_load(p);
+}
+
+template <DType D>
+__device__ __forceinline__ u32x4 neg_inf_vec() {
+    const unsigned w = Elem<D>::kNegInfWord;
+    return u32x4{w, w, w, w};
+}
+
+// ---- the accumulator -------------------------------------------------------
+
+struct Acc {
+    float m;  // running max
+    float c;  // base2_ref(m)
+    float s;  // sum of 2^(x*log2e - c) ...
+    float e;  // ... plus this compensation term (rounding errors of the sum)
+};
+
+__device__ __forceinline__ Acc acc_empty() { return Acc{-kInf, base2_ref(-kInf), 0.0f, 0.0f}; }
+
+// The lane's sum, compensation included. Once s is +inf or NaN (a +inf or NaN
+// element, or a maximum beyond 2^126), TwoSum's inf - inf has made e NaN:
+// s alone is then the answer.
+__device__ __forceinline__ float acc_sum(const Acc& a) {
+    return (__float_as_uint(a.s) & 0x7FFFFFFFu) >= 0x7F800000u ? a.s : a.s + a.e;
+}
+
+// Maximum of the N values v[0..N) by a chain of v_max3_f32, each taking two
+// new values: (N - 1) / 2 instructions, rounded up.
+template <int N>
+__device__ __forceinline__ float max_chain(const float* v) {
+    float r = v[0];
+    int j = 1;
+#pragma unroll
+    for (; j + 1 < N; j += 2) r = max3f(r, v[j], v[j + 1]);
+    if (j < N) r = max3f(r, v[j], v[j]);
+    return r;
+}
+
+// Maximum of m0 and f[0..N): three independent chains of odd length (no
+// wasted max3 operand when N + 1 splits evenly) joined by one more max3.
+template <int N>
+__device__ __forceinline__ float max_of(float m0, const float* f) {
+    constexpr int V = N + 1;
+    float v[V];
+    v[0] = m0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j + 1] = f[j];
+    if constexpr (V <= 7) {
+        return max_chain<V>(v);
+    } else {
+        constexpr int A = (V / 3) | 1;
+        constexpr int B = ((V - A) / 2) | 1;
+        return max3f(max_chain<A>(v), max_chain<B>(v + A), max_chain<V - A - B>(v + A + B));
+    }
+}
+
+// Pairwise (tree) sum of 2^(f[j]*log2e - c), j < N.
+template <int N>
+__device__ __forceinline__ float sum_exp_of(const float* f, float c) {
+    if constexpr (N == 1) {
+        return exp2_hw(__builtin_fmaf(f[0], kLog2e, -c));
+    } else {
+        constexpr int H = N / 2;
+        return sum_exp_of<H>(f, c) + sum_exp_of<N - H>(f + H, c);
+    }
+}
+
+// Fold N values into the accumulator: one max, one rescale, N exponentials
+// summed as a tree, and one compensated add of that batch sum. The add is
+// Knuth's TwoSum, whose rounding error goes to `e`: without it, a long row
+// of near-constant batch sums (each smaller than the running sum's ulp
+// allows to add exactly) drifts by up to 1e-4 relative over 10^5 batches.
+template <int N>
+__device__ __forceinline__ void fold(Acc& a, const float* f) {
+    const float m = max_of<N>(a.m, f);
+    const float c = base2_ref(m);
+    const float t = sum_exp_of<N>(f, c);
+    const float r = exp2_hw(a.c - c);  // rescale of the old sum, <= 1
+    const float s = a.s * r;
+    const float sum = s + t;
+    const float bp = sum - s;
+    const float err = (s - (sum - bp)) + (t - bp);
+    a.e = __builtin_fmaf(a.e, r, err);
+    a.s = sum;
+    a.m = m;
+    a.c = c;
+}
+
+// The finished value ln(sum exp) = m + ln2 * (log2 s - (m*log2e - c)) for a
+// reduced (m, c, s); `slow` is set when |m| > 2^30 and the row must be
+// recomputed in natural units.
+__device__ __forceinline__ float finish(float m, float c, float s, bool& slow) {
+    slow = false;
+    if (is_nan(s)) return __builtin_nanf("");
+    if (m == kInf) return kInf;
+    if (m == -kInf) return -kInf;
+    if (__builtin_fabsf(m) > kClamp) {
+        slow = true;
+        return 0.0f;
+    }
+    const float e = __builtin_fmaf(m, kLog2e, -c);  // exact residual of c = fl(m*log2e)
+    return __builtin_fmaf(log2_hw(s) - e, kLn2, m);
+}
+
+// ---- cross-lane reductions (wave64) ---------------------------------------
+//
+// DPP row patterns combine lanes within a row of 16: quad_perm [1,0,3,2]
+// pairs lanes i^1, [2,3,0,1] pairs i^2, row_half_mirror pairs i and 7-i in
+// each half-row, row_mirror pairs i and 15-i. Applied in that order they give
+// every lane of a group of 2, 4, 8 or 16 the group total (the pairs are
+// symmetric, and a+b == b+a exactly, so all lanes agree bit for bit).
+// ds_swizzle's xor-16 pattern joins two rows within 32 lanes; readlane joins
+// the two halves of the wave.
+
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+constexpr int kSwizzleXor16 = 0x401F;  // bit mode: and 0x1f, or 0, xor 0x10
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float swizzle_xor16(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+struct OpMax {
+    __device__ __forceinline__ float operator()(float a, float b) const { return max3f(a, b, b); }
+};
+struct OpSum {
+    __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+
+// Every lane of each aligned group of G lanes (G a power of two <= 64) gets
+// the group's reduction. All lanes of a group must be active.
+template <int G, typename Op>
+__device__ __forceinline__ float group_reduce(float v, Op op) {
+    if constexpr (G >= 2) v = op(v, dpp<kDppXor1>(v));
+    if constexpr (G >= 4) v = op(v, dpp<kDppXor2>(v));
+    if constexpr (G >= 8) v = op(v, dpp<kDppHalfMirror>(v));
+    if constexpr (G >= 16) v = op(v, dpp<kDppMirror>(v));
+    if constexpr (G >= 32) v = op(v, swizzle_xor16(v));
+    if constexpr (G >= 64) v = op(readlane(v, 0), readlane(v, 32));
+    return v;
+}
+
+// Workgroup-wide reduction; the result is uniform. `scratch` holds one float
+// per wavefront. Contains barriers: every thread of the block must call it.
+template <int BLOCK, typename Op>
+__device__ __forceinline__ float block_reduce(float v, Op op, float* scratch) {
+    constexpr int NW = BLOCK / 64;
+    v = group_reduce<64>(v, op);
+    if constexpr (NW == 1) {
+        return v;
+    } else {
+        const int wave = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) scratch[wave] = v;
+        __syncthreads();
+        float r = scratch[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) r = op(r, scratch[w]);
+        __syncthreads();
+        return r;
+    }
+}
+
+}  // namespace lse

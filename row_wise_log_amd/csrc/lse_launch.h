@@ -1,0 +1,38 @@
+// lse_launch.h - the interface between the host planner (lse_api.cpp) and the
+// kernel dispatch (lse_kernels.hip). Host-only types; no device code.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace lse {
+
+enum : int { kSchedRowsPerWave = 1, kSchedRowPerWG = 2, kSchedSplitRow = 3 };
+
+struct LaunchArgs {
+    // what to run
+    int schedule;
+    bool bf16;
+    int block;
+    int64_t grid;
+    bool vector_loads;
+    int lanes_per_row;
+    int loads_per_lane;
+    int rows_per_wave;
+    int parts;
+    int unroll;
+    // operands
+    const char* x;
+    int64_t rows;
+    int64_t cols;
+    int64_t stride_bytes;
+    float* out;
+    unsigned* ws_pairs;  // split-row (max, sum) pairs, 2 words each
+    unsigned* counters;  // split-row arrival counters, one per row, zero between calls
+    hipStream_t stream;
+};
+
+// Launches the kernel the plan names; returns hipGetLastError() after it.
+hipError_t launch(const LaunchArgs& a);
+
+}  // namespace lse

@@ -1,0 +1,85 @@
+"""Helpers for the GPU parity tests: upload, call through the C ABI, compare.
+
+The comparison rule: for a finite oracle value r, |g - r| <= tol * max(1, |r|)
+with tol = 2e-6 for fp32 input and 1e-5 for bf16 input; an infinite r must be
+matched exactly and a NaN r by a NaN.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from row_wise_log_amd import binding as B
+
+TOL = {"f32": 2e-6, "bf16": 1e-5}
+DTYPE_CODE = {"f32": B.LSE_DTYPE_F32, "bf16": B.LSE_DTYPE_BF16}
+ESIZE = {"f32": 4, "bf16": 2}
+SCHEDULES = ["auto", "rows_per_wave", "row_per_wg", "split_row"]
+
+
+def note(msg: str) -> None:
+    """Name the case on stderr before a GPU step, so a failure can be traced."""
+    print(msg, file=sys.stderr, flush=True)
+
+
+def upload(torch, x: np.ndarray, pad_front: int = 0):
+    """Copy a 2-D host array to the GPU; return (tensor, device address of x[0, 0]).
+
+    The array keeps its row stride (a padded view uploads its padding too).
+    pad_front elements of zeros precede x, to give a misaligned base address.
+    """
+    itemsize = x.itemsize
+    rows, cols = x.shape
+    stride = x.strides[0] // itemsize if rows > 1 else cols
+    n = (rows - 1) * stride + cols if rows > 0 else 0
+    flat = np.zeros(pad_front + n, dtype=x.dtype)
+    if n:
+        base = np.lib.stride_tricks.as_strided(x, shape=(n,), strides=(itemsize,))
+        flat[pad_front:] = base
+    view = flat.view(np.int16 if itemsize == 2 else np.int32)
+    t = torch.from_numpy(view).to("cuda")
+    return t, t.data_ptr() + pad_front * itemsize, stride
+
+
+def gpu_lse(torch, handle, x: np.ndarray, dtype: str, schedule: str = "auto",
+            pad_front: int = 0, tuning=(0, 0, 0)) -> np.ndarray:
+    """Run lse_forward on a host array; returns the fp32 outputs on the host."""
+    rows, cols = x.shape
+    t, ptr, stride = upload(torch, x, pad_front)
+    out = torch.full((max(rows, 1),), float("nan"), dtype=torch.float32, device="cuda")
+    B.lse_set_schedule(handle, schedule)
+    B.lse_set_tuning(handle, *tuning)
+    try:
+        B.lse_forward(handle, ptr if x.size else 0, DTYPE_CODE[dtype], rows, cols, stride,
+                      out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    finally:
+        B.lse_set_schedule(handle, "auto")
+        B.lse_set_tuning(handle, 0, 0, 0)
+    del t
+    return out.cpu().numpy()[:rows]
+
+
+def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, rows=None) -> float:
+    """Assert the tolerance rule; return the worst |g - r| / (tol * max(1, |r|))."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, what
+    tol = TOL[dtype]
+    idx = np.arange(len(ref)) if rows is None else np.asarray(rows)
+    nan = np.isnan(ref)
+    bad = nan & ~np.isnan(got)
+    assert not bad.any(), f"{what}: rows {idx[bad][:8]} want NaN, got {got[bad][:8]}"
+    inf = np.isinf(ref)
+    bad = inf & (got != ref)
+    assert not bad.any(), f"{what}: rows {idx[bad][:8]} want {ref[bad][:8]}, got {got[bad][:8]}"
+    fin = ~nan & ~inf
+    if not fin.any():
+        return 0.0
+    assert np.all(np.isfinite(got[fin])), f"{what}: non-finite output for finite reference"
+    ratio = np.abs(got[fin] - ref[fin]) / (tol * np.maximum(1.0, np.abs(ref[fin])))
+    worst = int(np.argmax(ratio))
+    assert ratio[worst] <= 1.0, (f"{what}: row {idx[fin][worst]} got {got[fin][worst]!r} "
+                                 f"want {ref[fin][worst]!r} ({ratio[worst]:.2f} x tol)")
+    return float(ratio.max())

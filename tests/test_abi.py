@@ -1,0 +1,192 @@
+"""The C ABI on the host: symbols, argument checks and the launch planner.
+
+These run without a GPU. lse_forward checks its arguments before any HIP
+call (handle last), so a NULL handle with one bad argument reports that
+argument's error; lse_plan is the planner lse_forward uses, exported as a
+pure host function.
+"""
+import re
+import shutil
+import subprocess
+from pathlib import Path
+
+import pytest
+
+from row_wise_log_amd import binding as B
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "lse.h"
+F32, BF16 = B.LSE_DTYPE_F32, B.LSE_DTYPE_BF16
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|lse_status_t)\s*(lse_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert {"lse_create", "lse_forward", "lse_destroy", "lse_status_string"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", str(B.LIBRARY)], capture_output=True,
+                             text=True, check=True).stdout
+        exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+        assert set(names) <= exported
+        assert set(B.EXPORTS) == set(names)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_header_is_valid_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "lse.h"\nint main(void) { lse_plan_t p; (void)p; '
+                   'return (int)sizeof(lse_status_t) - 4 + (int)LSE_OK; }\n')
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    f"-I{ROOT / 'include'}", "-I/opt/rocm/include", "-c", str(src),
+                    "-o", str(tmp_path / "use.o")], check=True)
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "LSE_OK"), (1, "LSE_ERR_INVALID_ARG"), (2, "LSE_ERR_UNSUPPORTED_DTYPE"),
+                       (3, "LSE_ERR_NO_DEVICE"), (4, "LSE_ERR_ALLOC"), (5, "LSE_ERR_HIP")]:
+        assert B.status_string(code) == name
+    assert B.status_string(99) == "LSE_ERR_UNKNOWN"
+
+
+def test_create_without_device_reports_no_device(lib):
+    try:
+        h = B.lse_create(0)
+    except B.LseError as e:
+        assert e.status == B.LSE_ERR_NO_DEVICE
+    else:
+        B.lse_destroy(h)
+        pytest.skip("a GPU is present")
+    assert B.load().lse_create(None, 0) == B.LSE_ERR_INVALID_ARG
+
+
+def test_destroy_null_is_ok(lib):
+    B.lse_destroy(None)
+
+
+@pytest.mark.parametrize("args, status", [
+    # (x, dtype, rows, cols, row_stride, out) with a NULL handle
+    ((16, 7, 4, 4, 4, 16), B.LSE_ERR_UNSUPPORTED_DTYPE),
+    ((16, -1, 4, 4, 4, 16), B.LSE_ERR_UNSUPPORTED_DTYPE),
+    ((16, F32, -1, 4, 4, 16), B.LSE_ERR_INVALID_ARG),
+    ((16, F32, 4, -1, 4, 16), B.LSE_ERR_INVALID_ARG),
+    ((16, F32, 1 << 31, 4, 4, 16), B.LSE_ERR_INVALID_ARG),
+    ((16, F32, 4, 1 << 31, 1 << 31, 16), B.LSE_ERR_INVALID_ARG),
+    ((16, F32, 4, 8, 7, 16), B.LSE_ERR_INVALID_ARG),           # stride < cols
+    ((16, F32, 4, 8, 1 << 62, 16), B.LSE_ERR_INVALID_ARG),     # byte offsets overflow
+    ((18, F32, 4, 4, 4, 16), B.LSE_ERR_INVALID_ARG),           # x not 4-byte aligned
+    ((17, BF16, 4, 4, 4, 16), B.LSE_ERR_INVALID_ARG),          # x not 2-byte aligned
+    ((None, F32, 4, 4, 4, 16), B.LSE_ERR_INVALID_ARG),         # NULL x with work
+    ((16, F32, 4, 4, 4, None), B.LSE_ERR_INVALID_ARG),         # NULL out
+    ((16, F32, 4, 4, 4, 18), B.LSE_ERR_INVALID_ARG),           # out not 4-byte aligned
+    ((16, F32, 4, 4, 4, 16), B.LSE_ERR_INVALID_ARG),           # all fine but the handle
+    ((None, F32, 0, 4, 4, None), B.LSE_ERR_INVALID_ARG),       # rows = 0 still needs a handle
+])
+def test_forward_argument_checks(lib, args, status):
+    x, dtype, rows, cols, stride, out = args
+    assert B.lse_forward_status(None, x, dtype, rows, cols, stride, out) == status
+
+
+def test_forward_accepts_stride_below_cols_for_one_row(lib):
+    # one row: row_stride is ignored, so only the handle is wrong
+    assert B.lse_forward_status(None, 16, F32, 1, 8, 0, 16) == B.LSE_ERR_INVALID_ARG
+    assert B.lse_forward_status(None, 16, BF16, 1, 8, 3, 16) == B.LSE_ERR_INVALID_ARG
+
+
+def test_setters_reject_bad_values(lib):
+    assert lib.lse_set_schedule(None, 1) == B.LSE_ERR_INVALID_ARG
+    assert lib.lse_set_tuning(None, 0, 0, 0) == B.LSE_ERR_INVALID_ARG
+
+
+# ---- the planner ------------------------------------------------------------
+
+def plan(dtype, rows, cols, stride=None, addr=0, n_cu=256, schedule=0):
+    return B.lse_plan(dtype, rows, cols, cols if stride is None else stride, addr, n_cu, schedule)
+
+
+def test_plan_for_the_five_workloads():
+    p1 = plan(F32, 64, 32000)
+    assert p1["schedule"] == B.LSE_SCHED_ROW_PER_WG and p1["grid"] == 64 and p1["unroll"] == 8
+    p2 = plan(BF16, 512, 128256)
+    assert p2["schedule"] == B.LSE_SCHED_ROW_PER_WG and p2["grid"] == 512
+    p3 = plan(BF16, 4096, 262144)
+    assert p3["schedule"] == B.LSE_SCHED_ROW_PER_WG and p3["grid"] == 4096
+    p4 = plan(F32, 65536, 4096)
+    assert p4["schedule"] == B.LSE_SCHED_ROWS_PER_WAVE
+    assert (p4["lanes_per_row"], p4["loads_per_lane"], p4["vector_loads"]) == (64, 16, 1)
+    p5 = plan(F32, 1 << 24, 16)
+    assert p5["schedule"] == B.LSE_SCHED_ROWS_PER_WAVE
+    assert (p5["lanes_per_row"], p5["loads_per_lane"], p5["rows_per_wave"]) == (4, 1, 64)
+    assert p5["grid"] == 256 * 32 // 4
+
+
+def test_plan_rows_zero():
+    assert plan(F32, 0, 100)["schedule"] == 0 and plan(F32, 0, 100)["grid"] == 0
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_plan_register_rows_cover_every_element(dtype):
+    k = 4 if dtype == F32 else 8
+    for cols in list(range(0, 80)) + [127, 128, 129, 255, 256, 257, 1023, 1024, 1025, 4095, 4096,
+                                      4097, 8191, 8192, 8193]:
+        for stride_pad, addr in [(0, 0), (k, 0), (1, 0), (0, 4 if dtype == F32 else 2)]:
+            stride = cols + stride_pad
+            p = plan(dtype, 100, cols, stride, addr)
+            if p["schedule"] != B.LSE_SCHED_ROWS_PER_WAVE:
+                continue
+            g, vpl = p["lanes_per_row"], p["loads_per_lane"]
+            assert g in (1, 2, 4, 8, 16, 32, 64) and vpl in (1, 2, 4, 8, 16)
+            assert vpl == 1 or g == 64
+            if p["vector_loads"]:
+                esize = 16 // k
+                assert addr % 16 == 0 and (stride * esize) % 16 == 0
+                assert g * vpl * k + (cols % k) >= cols and g >= cols % k
+            else:
+                assert g * vpl >= cols
+            assert p["rows_per_wave"] == (64 // g) * (4 if vpl == 1 else 2 if vpl == 2 else 1)
+
+
+def test_plan_long_rows_and_few_rows():
+    # few long rows split into ~128 KiB parts; otherwise one workgroup per row
+    p = plan(F32, 8, 1 << 20)
+    assert p["schedule"] == B.LSE_SCHED_SPLIT_ROW and p["parts"] == 32 and p["grid"] == 256
+    assert p["workspace_bytes"] == 8 * 32 * 8 + 8 * 4
+    assert plan(F32, 1, 1 << 28)["parts"] == B.LSE_SPLIT_MAX_PARTS
+    assert plan(F32, 255, 1 << 16)["schedule"] == B.LSE_SCHED_SPLIT_ROW
+    assert plan(F32, 255, 1 << 16)["parts"] == 2
+    assert plan(F32, 256, 1 << 16)["schedule"] == B.LSE_SCHED_ROW_PER_WG
+    assert plan(F32, 8, (1 << 16) - 4)["schedule"] == B.LSE_SCHED_ROW_PER_WG
+    # unaligned long rows stream with a head peel
+    assert plan(BF16, 4, 5001, 5001)["schedule"] == B.LSE_SCHED_ROW_PER_WG
+    assert plan(BF16, 4, 500001, 500001)["schedule"] == B.LSE_SCHED_SPLIT_ROW
+    assert plan(BF16, 4000, 500001, 500001)["schedule"] == B.LSE_SCHED_ROW_PER_WG
+
+
+def test_plan_forced_schedules():
+    assert plan(F32, 1 << 24, 16, schedule=2)["schedule"] == B.LSE_SCHED_ROW_PER_WG
+    p = plan(F32, 1 << 24, 16, schedule=3)
+    assert p["schedule"] == B.LSE_SCHED_SPLIT_ROW and p["grid"] == B.LSE_SPLIT_MAX_ROWS * 2
+    # rows longer than registers hold cannot stay on ROWS_PER_WAVE
+    assert plan(F32, 4, 1 << 20, schedule=1)["schedule"] == B.LSE_SCHED_ROW_PER_WG
+    assert plan(F32, 4, 1024, 1025, schedule=1)["schedule"] == B.LSE_SCHED_ROWS_PER_WAVE
+
+
+def test_plan_rejects_bad_args():
+    with pytest.raises(B.LseError):
+        B.lse_plan(F32, 4, 8, 8, 0, 0, 0)
+    with pytest.raises(B.LseError):
+        B.lse_plan(F32, 4, 8, 8, 0, 256, 9)
+    with pytest.raises(B.LseError):
+        B.lse_plan(5, 4, 8, 8, 0, 256, 0)
