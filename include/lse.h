@@ -64,9 +64,10 @@ typedef enum {
 /* Schedules. AUTO picks by shape; the others force one schedule, which the
  * tests and the benchmark use to compare them. Every schedule computes every
  * shape: ROWS_PER_WAVE holds a row in registers and passes rows longer than
- * 64 x 16 loads (16 KiB when rows are 16-byte aligned, else 1024 elements) to
+ * it holds (4 KiB when rows are 16-byte aligned, else 1024 elements) to
  * ROW_PER_WG; SPLIT_ROW processes at most LSE_SPLIT_MAX_ROWS rows per launch
- * and issues more launches for more rows. */
+ * and issues more launches for more rows; an empty row (cols == 0) needs no
+ * loads and always runs as ROWS_PER_WAVE. */
 typedef enum {
     LSE_SCHED_AUTO = 0,
     LSE_SCHED_ROWS_PER_WAVE = 1, /* short rows held in registers, 64/G rows per wavefront */
@@ -117,12 +118,16 @@ const char *lse_status_string(lse_status_t s);
  * Errors: INVALID_ARG (NULL handle or unknown schedule). */
 lse_status_t lse_set_schedule(lse_handle_t h, lse_schedule_t s);
 
-/* Tuning overrides for the streaming schedules, for measurement: threads per
- * workgroup `block` (256, 512 or 1024), 16-byte loads per lane per batch
- * `unroll` (4 or 8), and SPLIT_ROW workgroups per row `parts` (1..64). 0
- * restores the planner's choice. Errors: INVALID_ARG (NULL handle or a value
- * outside those sets). */
-lse_status_t lse_set_tuning(lse_handle_t h, int32_t block, int32_t unroll, int32_t parts);
+/* Tuning overrides, for measurement. Streaming schedules: threads per
+ * workgroup `block` (64, 128, 256, 512 or 1024), 16-byte loads per lane per
+ * batch `unroll` (4 or 8), SPLIT_ROW workgroups per row `parts` (1..64).
+ * ROWS_PER_WAVE: at most `waves_per_cu` wavefronts per compute unit in the
+ * grid (1..1024; the wavefronts loop over the rest) and `lanes_per_row` lanes
+ * sharing a row (a power of two up to 64; ignored where no kernel instance
+ * fits the shape). 0 restores the planner's choice.
+ * Errors: INVALID_ARG (NULL handle or a value outside those sets). */
+lse_status_t lse_set_tuning(lse_handle_t h, int32_t block, int32_t unroll, int32_t parts,
+                            int32_t waves_per_cu, int32_t lanes_per_row);
 
 /* Launch plan chosen for one call: which kernel runs, with what grid. */
 typedef struct {

@@ -72,7 +72,7 @@ def load(path: Path | str = LIBRARY) -> ctypes.CDLL:
         "lse_destroy": (i32, [vp]),
         "lse_status_string": (ctypes.c_char_p, [i32]),
         "lse_set_schedule": (i32, [vp, i32]),
-        "lse_set_tuning": (i32, [vp, i32, i32, i32]),
+        "lse_set_tuning": (i32, [vp, i32, i32, i32, i32, i32]),
         "lse_plan": (i32, [i32, i64, i64, i64, ctypes.c_uint64, i32, i32,
                            ctypes.POINTER(lse_plan_t)]),
     }
@@ -123,8 +123,10 @@ def lse_set_schedule(handle: int, schedule: int | str) -> None:
     _check(load().lse_set_schedule(handle, schedule), "lse_set_schedule")
 
 
-def lse_set_tuning(handle: int, block: int = 0, unroll: int = 0, parts: int = 0) -> None:
-    _check(load().lse_set_tuning(handle, block, unroll, parts), "lse_set_tuning")
+def lse_set_tuning(handle: int, block: int = 0, unroll: int = 0, parts: int = 0,
+                   waves_per_cu: int = 0, lanes_per_row: int = 0) -> None:
+    _check(load().lse_set_tuning(handle, block, unroll, parts, waves_per_cu, lanes_per_row),
+           "lse_set_tuning")
 
 
 def lse_plan(dtype: int, rows: int, cols: int, row_stride: int, x_addr: int = 0,

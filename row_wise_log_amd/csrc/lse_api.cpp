@@ -21,14 +21,15 @@ struct lse_handle_s {
     unsigned* ws_pairs;  // LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS (max, sum) pairs
     unsigned* counters;  // LSE_SPLIT_MAX_ROWS arrival counters, zero between calls
     int schedule;        // lse_schedule_t forced for later calls (AUTO = by shape)
-    int block, unroll, parts;  // tuning overrides, 0 = planner default
+    int block, unroll, parts, waves_per_cu, lanes_per_row;  // tuning overrides, 0 = planner default
 };
 
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
-constexpr int kRegsMaxUnits = 1024;   // schedule A holds up to 64 lanes x 16 loads of a row
-constexpr int kWavesPerCU = 32;       // schedule A grid cap (the loop covers the rest)
+constexpr int kRegsMaxVecUnits = 256;  // schedule A: rows of up to 4 KiB in 16-byte loads...
+constexpr int kRegsMaxElems = 1024;    // ...or up to 1024 single elements (unaligned rows)
+constexpr int kWavesPerCU = 64;       // schedule A grid cap (the loop covers the rest)
 constexpr int64_t kSplitMinRowBytes = 256 << 10;  // shorter rows stream faster unsplit
 constexpr int64_t kSplitPartBytes = 128 << 10;    // target bytes per split part
 
@@ -41,8 +42,16 @@ int pow2_at_least(int64_t v) {
 }
 
 struct Tuning {
-    int block, unroll, parts;
+    int block, unroll, parts, waves_per_cu, lanes_per_row;
 };
+
+// Register-rows instances (lse_kernels.hip): VPL 1, 2, 4 for G in {1, 2, 4,
+// 64}; VPL 1 for G in {8, 16, 32}; scalar rows also VPL 8, 16 for G = 64.
+bool regs_instance(int g, int vpl, bool vec) {
+    if (vpl == 1) return true;
+    if (vpl == 2 || vpl == 4) return g <= 4 || g == 64;
+    return !vec && g == 64 && (vpl == 8 || vpl == 16);
+}
 
 lse_status_t check_sizes(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t row_stride,
                          uint64_t x_addr) {
@@ -66,13 +75,13 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
     const bool aligned16 = x_addr % 16 == 0 && (rows == 1 || stride_bytes % 16 == 0);
     const int64_t vec_units = cols / k;
     const int64_t vec_tail = cols - vec_units * k;
-    const bool regs_vec = aligned16 && vec_units <= kRegsMaxUnits;
-    const bool regs_scalar = cols <= kRegsMaxUnits;
+    const bool regs_vec = aligned16 && vec_units >= 1 && vec_units <= kRegsMaxVecUnits;
+    const bool regs_scalar = cols <= kRegsMaxElems;
 
     int sched = schedule;
     if (sched == LSE_SCHED_AUTO) {
         const int64_t row_bytes = cols * esize;
-        if (regs_vec || (regs_scalar && !aligned16))
+        if (regs_vec || (regs_scalar && (!aligned16 || vec_units == 0)))
             sched = LSE_SCHED_ROWS_PER_WAVE;
         else if (rows < n_cu && row_bytes >= kSplitMinRowBytes)
             sched = LSE_SCHED_SPLIT_ROW;  // few long rows: one workgroup per row would idle CUs
@@ -81,16 +90,26 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
     }
     // Rows longer than registers hold go to the streaming schedule.
     if (sched == LSE_SCHED_ROWS_PER_WAVE && !regs_vec && !regs_scalar) sched = LSE_SCHED_ROW_PER_WG;
+    if (sched != LSE_SCHED_ROWS_PER_WAVE && cols == 0) sched = LSE_SCHED_ROWS_PER_WAVE;  // no loads
 
     p->schedule = sched;
     if (sched == LSE_SCHED_ROWS_PER_WAVE) {
         const bool vec = regs_vec;
         const int64_t units = vec ? vec_units : cols;
         const int64_t tail = vec ? vec_tail : 0;
-        // every tail element needs its own lane: G >= tail
+        // G lanes cover the row's units (every tail element needs its own lane:
+        // G >= tail); VPL loads per lane cover the rest.
         int g = pow2_at_least(std::max<int64_t>({units, tail, 1}));
         if (g > 64) g = 64;
-        const int vpl = pow2_at_least(ceil_div(units > 0 ? units : 1, g));
+        int vpl = pow2_at_least(ceil_div(units > 0 ? units : 1, g));
+        if (tune.lanes_per_row) {
+            const int tg = tune.lanes_per_row;
+            const int tv = pow2_at_least(ceil_div(units > 0 ? units : 1, tg));
+            if (tg >= tail && regs_instance(tg, tv, vec)) {
+                g = tg;
+                vpl = tv;
+            }
+        }
         const int rounds = vpl == 1 ? 4 : (vpl == 2 ? 2 : 1);
         p->block = 256;
         p->vector_loads = vec ? 1 : 0;
@@ -99,16 +118,29 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
         p->rows_per_wave = (64 / g) * rounds;
         const int64_t iters = ceil_div(rows, p->rows_per_wave);
         int64_t waves = iters;
-        if (waves > static_cast<int64_t>(n_cu) * kWavesPerCU) waves = static_cast<int64_t>(n_cu) * kWavesPerCU;
+        const int64_t cap = static_cast<int64_t>(n_cu) * (tune.waves_per_cu ? tune.waves_per_cu : kWavesPerCU);
+        if (waves > cap) waves = cap;
         p->grid = ceil_div(waves, 4);
         p->parts = 1;
         return LSE_OK;
     }
 
+    const int64_t nvec = cols / k;  // 16-byte vectors in a row (one fewer if unaligned)
     p->vector_loads = 1;
     if (sched == LSE_SCHED_ROW_PER_WG) {
-        p->block = tune.block ? tune.block : 512;
-        p->unroll = tune.unroll ? tune.unroll : (dtype == LSE_DTYPE_BF16 ? 4 : 8);
+        // About 32 fp32 or 64 bf16 elements per lane (one or two batches of
+        // four 16-byte loads), 64 to 256 threads; 512 threads when there are
+        // too few rows for every CU to hold one.
+        int block = 256;
+        if (rows < n_cu) {
+            block = 512;
+        } else {
+            const int64_t per = nvec / (dtype == LSE_DTYPE_BF16 ? 8 : 4);
+            block = 64;
+            while (block < 256 && 2 * block <= per) block *= 2;
+        }
+        p->block = tune.block ? tune.block : block;
+        p->unroll = tune.unroll ? tune.unroll : 4;
         p->parts = 1;
         p->grid = rows;
         return LSE_OK;
@@ -116,7 +148,7 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
     // LSE_SCHED_SPLIT_ROW: parts of about kSplitPartBytes, at least 2, at most
     // LSE_SPLIT_MAX_PARTS, and no more than ~8 workgroups per CU in total.
     p->block = tune.block ? tune.block : 512;
-    p->unroll = tune.unroll ? tune.unroll : (dtype == LSE_DTYPE_BF16 ? 4 : 8);
+    p->unroll = tune.unroll ? tune.unroll : 4;
     int64_t parts = tune.parts;
     if (!parts) {
         const int64_t r = rows < LSE_SPLIT_MAX_ROWS ? rows : LSE_SPLIT_MAX_ROWS;
@@ -155,7 +187,7 @@ lse_status_t lse_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t row
     lse_status_t st = check_sizes(dtype, rows, cols, row_stride, x_addr);
     if (st != LSE_OK) return st;
     if (schedule < LSE_SCHED_AUTO || schedule > LSE_SCHED_SPLIT_ROW) return LSE_ERR_INVALID_ARG;
-    return make_plan(dtype, rows, cols, row_stride, x_addr, n_cu, schedule, Tuning{0, 0, 0}, plan);
+    return make_plan(dtype, rows, cols, row_stride, x_addr, n_cu, schedule, Tuning{0, 0, 0, 0, 0}, plan);
 }
 
 lse_status_t lse_create(lse_handle_t* out, int device) {
@@ -225,14 +257,21 @@ lse_status_t lse_set_schedule(lse_handle_t h, lse_schedule_t s) {
     return LSE_OK;
 }
 
-lse_status_t lse_set_tuning(lse_handle_t h, int32_t block, int32_t unroll, int32_t parts) {
+lse_status_t lse_set_tuning(lse_handle_t h, int32_t block, int32_t unroll, int32_t parts,
+                            int32_t waves_per_cu, int32_t lanes_per_row) {
     if (h == nullptr) return LSE_ERR_INVALID_ARG;
-    if (block != 0 && block != 256 && block != 512 && block != 1024) return LSE_ERR_INVALID_ARG;
+    if (block != 0 && block != 64 && block != 128 && block != 256 && block != 512 && block != 1024)
+        return LSE_ERR_INVALID_ARG;
     if (unroll != 0 && unroll != 4 && unroll != 8) return LSE_ERR_INVALID_ARG;
     if (parts < 0 || parts > LSE_SPLIT_MAX_PARTS) return LSE_ERR_INVALID_ARG;
+    if (waves_per_cu < 0 || waves_per_cu > 1024) return LSE_ERR_INVALID_ARG;
+    if (lanes_per_row < 0 || lanes_per_row > 64 || (lanes_per_row & (lanes_per_row - 1)))
+        return LSE_ERR_INVALID_ARG;
     h->block = block;
     h->unroll = unroll;
     h->parts = parts;
+    h->waves_per_cu = waves_per_cu;
+    h->lanes_per_row = lanes_per_row;
     return LSE_OK;
 }
 
@@ -248,7 +287,7 @@ lse_status_t lse_forward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64
 
     lse_plan_t p;
     st = make_plan(dtype, rows, cols, row_stride, x_addr, h->n_cu, h->schedule,
-                   Tuning{h->block, h->unroll, h->parts}, &p);
+                   Tuning{h->block, h->unroll, h->parts, h->waves_per_cu, h->lanes_per_row}, &p);
     if (st != LSE_OK) return st;
 
     const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;

@@ -203,18 +203,24 @@ __device__ __forceinline__ void fold(Acc& a, const float* f) {
     a.c = c;
 }
 
-// The finished value ln(sum exp) = m + ln2 * (log2 s - (m*log2e - c)) for a
-// reduced (m, c, s); `slow` is set when |m| > 2^30 and the row must be
-// recomputed in natural units.
-__device__ __forceinline__ float finish(float m, float c, float s, bool& slow) {
-    slow = false;
+// True when |m| is finite and beyond 2^30: one unsigned range test on the bits.
+__device__ __forceinline__ bool beyond_clamp(float m) {
+    return (__float_as_uint(m) & 0x7FFFFFFFu) - 0x4E800001u < 0x7F800000u - 0x4E800001u;
+}
+
+// True when a reduced row must be recomputed in natural units: its maximum is
+// finite but beyond +-2^30 (and no NaN made the answer NaN already).
+__device__ __forceinline__ bool needs_natural_units(float m, float s) {
+    return !is_nan(s) && __builtin_fabsf(m) > kClamp && __builtin_fabsf(m) != kInf;
+}
+
+// The finished value ln(sum exp) = m + ln2 * (log2 s - (m*log2e - c)) of a
+// reduced (m, c, s) with |m| <= 2^30 or m = +-inf: NaN if s is NaN, +inf if
+// m = +inf, -inf if m = -inf (s = 0: no element above -inf).
+__device__ __forceinline__ float finish(float m, float c, float s) {
     if (is_nan(s)) return __builtin_nanf("");
     if (m == kInf) return kInf;
     if (m == -kInf) return -kInf;
-    if (__builtin_fabsf(m) > kClamp) {
-        slow = true;
-        return 0.0f;
-    }
     const float e = __builtin_fmaf(m, kLog2e, -c);  // exact residual of c = fl(m*log2e)
     return __builtin_fmaf(log2_hw(s) - e, kLn2, m);
 }
@@ -226,18 +232,28 @@ __device__ __forceinline__ float finish(float m, float c, float s, bool& slow) {
 // each half-row, row_mirror pairs i and 15-i. Applied in that order they give
 // every lane of a group of 2, 4, 8 or 16 the group total (the pairs are
 // symmetric, and a+b == b+a exactly, so all lanes agree bit for bit).
-// ds_swizzle's xor-16 pattern joins two rows within 32 lanes; readlane joins
-// the two halves of the wave.
+// ds_swizzle's xor-16 pattern joins two rows within 32 lanes. For the whole
+// wavefront, row_bcast15 (row r's lane 15 into row r+1, rows 1 and 3) and
+// row_bcast31 (lane 31 into rows 2 and 3) carry the row totals into lane 63,
+// which readlane makes uniform: all DPP, no LDS-unit latency.
 
 constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
 constexpr int kDppMirror = 0x140;      // row_mirror
+constexpr int kDppBcast15 = 0x142;     // row_bcast:15
+constexpr int kDppBcast31 = 0x143;     // row_bcast:31
 constexpr int kSwizzleXor16 = 0x401F;  // bit mode: and 0x1f, or 0, xor 0x10
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
     return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+
+// DPP move restricted to the rows in ROW_MASK; other rows keep `old`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_rows(float old, float v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
 }
 
 __device__ __forceinline__ float swizzle_xor16(float v) {
@@ -250,26 +266,42 @@ __device__ __forceinline__ float readlane(float v, int lane) {
 
 struct OpMax {
     __device__ __forceinline__ float operator()(float a, float b) const { return max3f(a, b, b); }
+    static constexpr float kIdentity = -__builtin_inff();
 };
 struct OpSum {
     __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+    static constexpr float kIdentity = 0.0f;
 };
+
+// A DPP move with no old value (every lane reads an in-bounds lane for the
+// quad and mirror patterns), so that the compiler can fold it into the
+// consuming add as a DPP operand.
+template <int CTRL>
+__device__ __forceinline__ float dpp_free(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 
 // Every lane of each aligned group of G lanes (G a power of two <= 64) gets
 // the group's reduction. All lanes of a group must be active.
 template <int G, typename Op>
 __device__ __forceinline__ float group_reduce(float v, Op op) {
-    if constexpr (G >= 2) v = op(v, dpp<kDppXor1>(v));
-    if constexpr (G >= 4) v = op(v, dpp<kDppXor2>(v));
-    if constexpr (G >= 8) v = op(v, dpp<kDppHalfMirror>(v));
-    if constexpr (G >= 16) v = op(v, dpp<kDppMirror>(v));
-    if constexpr (G >= 32) v = op(v, swizzle_xor16(v));
-    if constexpr (G >= 64) v = op(readlane(v, 0), readlane(v, 32));
+    if constexpr (G >= 2) v = op(v, dpp_free<kDppXor1>(v));
+    if constexpr (G >= 4) v = op(v, dpp_free<kDppXor2>(v));
+    if constexpr (G >= 8) v = op(v, dpp_free<kDppHalfMirror>(v));
+    if constexpr (G >= 16) v = op(v, dpp_free<kDppMirror>(v));
+    if constexpr (G == 32) v = op(v, swizzle_xor16(v));
+    if constexpr (G == 64) {
+        // rows 1, 3 += row 0, 2 (via lane 15, 47); rows 2, 3 += lane 31
+        v = op(v, dpp_rows<kDppBcast15, 0xA>(Op::kIdentity, v));
+        v = op(v, dpp_rows<kDppBcast31, 0xC>(Op::kIdentity, v));
+        v = readlane(v, 63);
+    }
     return v;
 }
 
 // Workgroup-wide reduction; the result is uniform. `scratch` holds one float
 // per wavefront. Contains barriers: every thread of the block must call it.
+// Used only off the hot path (the natural-units pass).
 template <int BLOCK, typename Op>
 __device__ __forceinline__ float block_reduce(float v, Op op, float* scratch) {
     constexpr int NW = BLOCK / 64;
@@ -285,6 +317,45 @@ __device__ __forceinline__ float block_reduce(float v, Op op, float* scratch) {
         for (int w = 1; w < NW; ++w) r = op(r, scratch[w]);
         __syncthreads();
         return r;
+    }
+}
+
+// The block's merged accumulator, uniform in every thread.
+struct Merged {
+    float m, c, s;
+};
+
+// Merge every lane's (m, c, s) into the workgroup's: each wavefront takes its
+// lanes' max and then the sum of their sums rescaled to it (DPP, no LDS);
+// lane 0 posts the wavefront's (max, sum) to `pairs` (2 floats per
+// wavefront); after one barrier every thread folds the pairs in wavefront
+// order, so the result is uniform and the same on every run. Every thread of
+// the block must call it; `pairs` must not be rewritten before all threads
+// have returned (a barrier separates two calls).
+template <int BLOCK>
+__device__ __forceinline__ Merged block_merge(float m, float c, float s, float* pairs) {
+    constexpr int NW = BLOCK / 64;
+    const float wm = group_reduce<64>(m, OpMax{});
+    const float wc = base2_ref(wm);
+    const float ws = group_reduce<64>(s * exp2_hw(c - wc), OpSum{});
+    if constexpr (NW == 1) {
+        return Merged{wm, wc, ws};
+    } else {
+        const int wave = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) {
+            pairs[2 * wave] = wm;
+            pairs[2 * wave + 1] = ws;
+        }
+        __syncthreads();
+        float bm = pairs[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) bm = max3f(bm, pairs[2 * w], pairs[2 * w]);
+        const float bc = base2_ref(bm);
+        float bs = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            bs = __builtin_fmaf(pairs[2 * w + 1], exp2_hw(base2_ref(pairs[2 * w]) - bc), bs);
+        return Merged{bm, bc, bs};
     }
 }
 

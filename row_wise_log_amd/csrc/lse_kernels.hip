@@ -50,72 +50,216 @@ __device__ float natural_units_sum(const char* rp, int64_t cols, float m, int64_
 // Schedule A: rows held in registers.
 //
 // Lane l of a wavefront belongs to group l / G and is member g = l % G. In
-// round q, group r of wavefront w holds row (w * ROUNDS + q) * (64/G) + r.
-// Member g loads the row's units g, g + G, ..., g + (VPL-1) * G, where a unit
-// is 16 bytes (VEC) or one element (rows not 16-byte aligned); members
-// g < tail also load the tail element units*K + g (a row's last cols % K
-// elements). Loads outside the row are replaced by -inf, which changes
-// neither the max nor the sum.
-template <DType D, int G, int VPL, bool VEC, int ROUNDS>
+// round q of iteration i, group r of the wavefront holds row
+// i * RW + q * (64/G) + r, RW = (64/G) * ROUNDS rows per iteration. Member g
+// loads the row's units g, g + G, ..., g + (VPL-1) * G, where a unit is 16
+// bytes (VEC) or one element (rows not 16-byte aligned); with TAIL, members
+// g < tail also load the element units*K + g (the row's last cols % K
+// elements). A wavefront handles iterations wave, wave + nwaves, ... and loads
+// its next iteration while it folds the current one.
+//
+// Loads never branch. FAST launches (every row has exactly G * VPL units and
+// the rows fill whole iterations) need no index checks at all; otherwise a
+// unit index past the row, or a row past the last, is clamped to one in
+// bounds and its value replaced by -inf, which changes neither the max nor
+// the sum. The prefetch of an iteration past the last reloads the last one.
+// The planner guarantees units >= 1 for VEC and cols >= 1 (cols == 0 is
+// written directly).
+template <DType D, int VPL, bool VEC, int ROUNDS>
+struct RegTile {
+    u32x4 w[ROUNDS][VEC ? VPL : 1];  // 16-byte units (VEC)
+    float e[ROUNDS][VEC ? 1 : VPL];  // single elements (not VEC)
+    float tv[ROUNDS];                // tail element (TAIL)
+};
+
+// What every iteration of one wavefront shares.
+struct RegRows {
+    const char* x;     // element (0, 0)
+    int64_t rows;
+    int64_t units;     // whole units per row
+    int64_t stride;    // bytes between row starts
+    int64_t last_it;   // index of the last iteration
+    int64_t lane_off;  // sub * stride + g * (bytes per unit): this lane's first unit in round 0
+    int g, sub, tail;
+};
+
+template <DType D, int G, int VPL, bool VEC, bool TAIL, bool FAST, int ROUNDS>
+__device__ __forceinline__ void load_tile(RegTile<D, VPL, VEC, ROUNDS>& t, const RegRows& rr,
+                                          int64_t it) {
+    constexpr int EB = Elem<D>::kBytes;
+    constexpr int K = VEC ? Elem<D>::kPerVec : 1;
+    constexpr int UB = VEC ? 16 : EB;  // bytes per unit
+    constexpr int R = 64 / G;
+    constexpr int RW = R * ROUNDS;
+    const char* base = rr.x + it * RW * rr.stride;  // uniform
+#pragma unroll
+    for (int q = 0; q < ROUNDS; ++q) {
+        const char* row_start;
+        if constexpr (FAST) {
+            row_start = base + q * R * rr.stride + rr.lane_off - rr.g * UB;
+        } else {
+            int64_t row = it * RW + q * R + rr.sub;
+            row = row < rr.rows ? row : rr.rows - 1;
+            row_start = rr.x + row * rr.stride;
+        }
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) {
+            int64_t unit = rr.g + static_cast<int64_t>(u) * G;
+            if constexpr (!FAST) unit = unit < rr.units ? unit : rr.units - 1;
+            const char* p = row_start + unit * UB;
+            if constexpr (VEC)
+                t.w[q][u] = load_vec(reinterpret_cast<const u32x4*>(p));
+            else
+                t.e[q][u] = load_scalar<D>(p);
+        }
+        if constexpr (TAIL)
+            t.tv[q] = load_scalar<D>(row_start + (rr.units * K + (rr.g < rr.tail ? rr.g : 0)) * EB);
+    }
+}
+
+// Fold one tile: every round's row max and rescaled sum, then the finish, and
+// store the iteration's RW results.
+template <DType D, int G, int VPL, bool VEC, bool TAIL, bool FAST, int ROUNDS>
+__device__ __forceinline__ void fold_tile(const RegTile<D, VPL, VEC, ROUNDS>& t,
+                                          const RegRows& rr, int64_t it, float* out,
+                                          float* stage) {
+    constexpr int K = VEC ? Elem<D>::kPerVec : 1;
+    constexpr int R = 64 / G;
+    constexpr int RW = R * ROUNDS;
+    constexpr int NV = VPL * K;
+    const int g = rr.g;
+    // Decode, with -inf in place of every clamped unit.
+    float v[ROUNDS][NV];
+    float tv[ROUNDS];
+#pragma unroll
+    for (int q = 0; q < ROUNDS; ++q) {
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) {
+            const bool ok = FAST || g + static_cast<int64_t>(u) * G < rr.units;
+            if constexpr (VEC) {
+                float f[K];
+                decode<D>(t.w[q][u], f);
+#pragma unroll
+                for (int k = 0; k < K; ++k) v[q][u * K + k] = ok ? f[k] : -kInf;
+            } else {
+                v[q][u] = ok ? t.e[q][u] : -kInf;
+            }
+        }
+        tv[q] = -kInf;
+        if constexpr (TAIL) tv[q] = g < rr.tail ? t.tv[q] : -kInf;
+    }
+    // Per round: the group's max, then the group's sum rescaled to it.
+    float mx[ROUNDS], sq[ROUNDS];
+    bool any_slow = false;
+#pragma unroll
+    for (int q = 0; q < ROUNDS; ++q) {
+        mx[q] = group_reduce<G>(TAIL ? max_of<NV>(tv[q], v[q]) : max_of<NV - 1>(v[q][0], v[q] + 1),
+                                OpMax{});
+        const float c = base2_ref(mx[q]);
+        float sum = sum_exp_of<NV>(v[q], c);
+        if constexpr (TAIL) sum += exp2_hw(__builtin_fmaf(tv[q], kLog2e, -c));
+        sq[q] = group_reduce<G>(sum, OpSum{});
+        any_slow |= beyond_clamp(mx[q]);
+    }
+    if (any_slow) {  // rare: a row's max is finite and beyond +-2^30
+#pragma unroll
+        for (int q = 0; q < ROUNDS; ++q) {
+            if (needs_natural_units(mx[q], sq[q])) {  // uniform within the group
+                float s2 = exp2_hw((tv[q] - mx[q]) * kLog2e);
+#pragma unroll
+                for (int j = 0; j < NV; ++j) s2 += exp2_hw((v[q][j] - mx[q]) * kLog2e);
+                s2 = group_reduce<G>(s2, OpSum{});
+                // The result is then m + ln2 * log2(s2), s2 >= 1; a sum is never
+                // negative otherwise, so -s2 marks the round for the finish.
+                sq[q] = -s2;
+            }
+        }
+    }
+    // Every lane of a group holds every round's result; member g finishes
+    // rounds g, g + G, ..., so the log and the special-value checks run once
+    // per row. The results go through this wavefront's LDS slots in row order
+    // so that lane l stores row it*RW + l: consecutive lanes write
+    // consecutive words.
+#pragma unroll
+    for (int j = 0; j < (ROUNDS + G - 1) / G; ++j) {
+        const int q = g + j * G;
+        float m = mx[0], sum = sq[0];
+#pragma unroll
+        for (int k = 1; k < ROUNDS; ++k) {
+            m = q == k ? mx[k] : m;
+            sum = q == k ? sq[k] : sum;
+        }
+        if (G <= ROUNDS || q < ROUNDS)
+            stage[q * R + rr.sub] = sum < 0.0f ? __builtin_fmaf(log2_hw(-sum), kLn2, m)
+                                               : finish(m, base2_ref(m), sum);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < (RW + 63) / 64; ++i) {
+        const int slot = lane + 64 * i;
+        const int64_t r = it * RW + slot;
+        if ((RW % 64 == 0 || slot < RW) && (FAST || r < rr.rows)) out[r] = stage[slot];
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// The wavefront's loop over iterations wave, wave + nwaves, ...: the next
+// iteration's tile is loaded (into the other buffer) before this one is folded.
+template <DType D, int G, int VPL, bool VEC, bool TAIL, bool FAST, int ROUNDS>
+__device__ __forceinline__ void fold_rows(const RegRows& rr, float* out, int64_t wave,
+                                          int64_t nwaves) {
+    constexpr int RW = (64 / G) * ROUNDS;
+    __shared__ float stage_all[4][RW];  // per-wavefront output staging (4 per block)
+    float* stage = stage_all[threadIdx.x >> 6];
+    RegTile<D, VPL, VEC, ROUNDS> ta, tb;
+    int64_t it = wave;
+    if (it > rr.last_it) return;
+    load_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS>(ta, rr, it);
+    while (true) {
+        int64_t next = it + nwaves;
+        load_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS>(tb, rr, next < rr.last_it ? next : rr.last_it);
+        fold_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS>(ta, rr, it, out, stage);
+        it = next;
+        if (it > rr.last_it) break;
+        next = it + nwaves;
+        load_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS>(ta, rr, next < rr.last_it ? next : rr.last_it);
+        fold_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS>(tb, rr, it, out, stage);
+        it = next;
+        if (it > rr.last_it) break;
+    }
+}
+
+template <DType D, int G, int VPL, bool VEC, bool TAIL, int ROUNDS>
 __global__ __launch_bounds__(256) void rows_in_registers(const char* __restrict__ x,
                                                          int64_t rows, int64_t cols,
                                                          int64_t stride_bytes,
                                                          float* __restrict__ out) {
-    constexpr int EB = Elem<D>::kBytes;
-    constexpr int K = VEC ? Elem<D>::kPerVec : 1;  // elements per unit
-    constexpr int R = 64 / G;                      // rows per wavefront per round
-    constexpr int NV = VPL * K;                    // values per lane per round
-
+    constexpr int K = VEC ? Elem<D>::kPerVec : 1;
+    constexpr int UB = VEC ? 16 : Elem<D>::kBytes;
+    constexpr int RW = (64 / G) * ROUNDS;
     const int lane = threadIdx.x & 63;
-    const int g = lane & (G - 1);
-    const int sub = lane / G;
     const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
     const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
-    const int64_t units = cols / K;
-    const int tail = static_cast<int>(cols - units * K);
 
-    for (int64_t it = wave; it * (R * ROUNDS) < rows; it += nwaves) {
-        float v[ROUNDS][NV];
-        float tv[ROUNDS];
-        int64_t row[ROUNDS];
-#pragma unroll
-        for (int q = 0; q < ROUNDS; ++q) {
-            row[q] = (it * ROUNDS + q) * R + sub;
-            const bool live = row[q] < rows;
-            const char* rp = x + (live ? row[q] : 0) * stride_bytes;
-#pragma unroll
-            for (int u = 0; u < VPL; ++u) {
-                const int64_t unit = g + static_cast<int64_t>(u) * G;
-                if constexpr (VEC) {
-                    u32x4 w = neg_inf_vec<D>();
-                    if (live && unit < units)
-                        w = load_vec(reinterpret_cast<const u32x4*>(rp + unit * 16));
-                    decode<D>(w, &v[q][u * K]);
-                } else {
-                    v[q][u] = (live && unit < units) ? load_scalar<D>(rp + unit * EB) : -kInf;
-                }
-            }
-            tv[q] = (live && g < tail) ? load_scalar<D>(rp + (units * K + g) * EB) : -kInf;
-        }
-#pragma unroll
-        for (int q = 0; q < ROUNDS; ++q) {
-            float mx = max_of<NV>(tv[q], v[q]);
-            mx = group_reduce<G>(mx, OpMax{});
-            const float c = base2_ref(mx);
-            float s = sum_exp_of<NV>(v[q], c) + exp2_hw(__builtin_fmaf(tv[q], kLog2e, -c));
-            s = group_reduce<G>(s, OpSum{});
-            bool slow;
-            float r = finish(mx, c, s, slow);
-            if (slow) {  // uniform within the group: mx and s are group-reduced
-                float s2 = exp2_hw((tv[q] - mx) * kLog2e);
-#pragma unroll
-                for (int j = 0; j < NV; ++j) s2 += exp2_hw((v[q][j] - mx) * kLog2e);
-                s2 = group_reduce<G>(s2, OpSum{});
-                r = __builtin_fmaf(log2_hw(s2), kLn2, mx);
-            }
-            if (g == 0 && row[q] < rows) out[row[q]] = r;
-        }
+    if (cols == 0) {  // the empty sum: every row is -inf
+        for (int64_t r = wave * 64 + lane; r < rows; r += nwaves * 64) out[r] = -kInf;
+        return;
     }
+    RegRows rr;
+    rr.x = x;
+    rr.rows = rows;
+    rr.units = cols / K;
+    rr.stride = stride_bytes;
+    rr.last_it = (rows + RW - 1) / RW - 1;
+    rr.g = lane & (G - 1);
+    rr.sub = lane / G;
+    rr.tail = static_cast<int>(cols - rr.units * K);
+    rr.lane_off = rr.sub * stride_bytes + rr.g * UB;
+    if (rr.units == G * VPL && rows % RW == 0)
+        fold_rows<D, G, VPL, VEC, TAIL, true, ROUNDS>(rr, out, wave, nwaves);
+    else
+        fold_rows<D, G, VPL, VEC, TAIL, false, ROUNDS>(rr, out, wave, nwaves);
 }
 
 // ---------------------------------------------------------------------------
@@ -136,7 +280,7 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
                                                      unsigned* __restrict__ counters) {
     constexpr int EB = Elem<D>::kBytes;
     constexpr int K = Elem<D>::kPerVec;
-    __shared__ float scratch[BLOCK / 64];
+    __shared__ float pairs[2 * (BLOCK / 64)];
     __shared__ int is_last;
 
     const int tid = threadIdx.x;
@@ -229,10 +373,8 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
         }
     }
 
-    // Merge the lanes: common maximum first, then each lane's sum rescaled to it.
-    float m = block_reduce<BLOCK>(a.m, OpMax{}, scratch);
-    float c = base2_ref(m);
-    float s = block_reduce<BLOCK>(acc_sum(a) * exp2_hw(a.c - c), OpSum{}, scratch);
+    // Merge the lanes (one barrier), then across parts for a split row.
+    Merged b = block_merge<BLOCK>(a.m, a.c, acc_sum(a), pairs);
 
     if constexpr (SPLIT) {
         // Publish this part's pair, then count the part in. The pair is
@@ -243,9 +385,9 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
         // or invalidate is needed, as every access involved is agent-scope.
         if (tid == 0) {
             unsigned* slot = ws_pairs + 2 * (row * nparts + part);
-            __hip_atomic_store(slot, __float_as_uint(m), __ATOMIC_RELAXED,
+            __hip_atomic_store(slot, __float_as_uint(b.m), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(slot + 1, __float_as_uint(s), __ATOMIC_RELAXED,
+            __hip_atomic_store(slot + 1, __float_as_uint(b.s), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -263,20 +405,19 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
             ps = __uint_as_float(
                 __hip_atomic_load(slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         }
-        const float pc = base2_ref(pm);
-        m = block_reduce<BLOCK>(pm, OpMax{}, scratch);
-        c = base2_ref(m);
-        s = block_reduce<BLOCK>(ps * exp2_hw(pc - c), OpSum{}, scratch);
+        b = block_merge<BLOCK>(pm, base2_ref(pm), ps, pairs);
         if (tid == 0)
             __hip_atomic_store(counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    bool slow;
-    float r = finish(m, c, s, slow);
-    if (slow) {  // uniform: m and s are block-reduced
-        float s2 = natural_units_sum<D>(rp, cols, m, tid, BLOCK);
-        s2 = block_reduce<BLOCK>(s2, OpSum{}, scratch);
-        r = __builtin_fmaf(log2_hw(s2), kLn2, m);
+    float r;
+    if (needs_natural_units(b.m, b.s)) {  // uniform: b is the same in every thread
+        __syncthreads();                    // `pairs` readers are done before scratch reuse
+        float s2 = natural_units_sum<D>(rp, cols, b.m, tid, BLOCK);
+        s2 = block_reduce<BLOCK>(s2, OpSum{}, pairs);
+        r = __builtin_fmaf(log2_hw(s2), kLn2, b.m);
+    } else {
+        r = finish(b.m, b.c, b.s);
     }
     if (tid == 0) out[row] = r;
 }
@@ -291,19 +432,28 @@ hipError_t launch_regs(const LaunchArgs& a) {
     // More rounds in flight when each lane's share of a row is small.
     constexpr int ROUNDS = VPL == 1 ? 4 : (VPL == 2 ? 2 : 1);
     if (a.rows_per_wave != (64 / G) * ROUNDS) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((rows_in_registers<D, G, VPL, VEC, ROUNDS>), dim3(a.grid), dim3(256), 0,
-                       a.stream, a.x, a.rows, a.cols, a.stride_bytes, a.out);
+    const int k = VEC ? (a.bf16 ? 8 : 4) : 1;
+    const bool tail = a.cols % k != 0;
+    if (tail)
+        hipLaunchKernelGGL((rows_in_registers<D, G, VPL, VEC, VEC, ROUNDS>), dim3(a.grid),
+                           dim3(256), 0, a.stream, a.x, a.rows, a.cols, a.stride_bytes, a.out);
+    else
+        hipLaunchKernelGGL((rows_in_registers<D, G, VPL, VEC, false, ROUNDS>), dim3(a.grid),
+                           dim3(256), 0, a.stream, a.x, a.rows, a.cols, a.stride_bytes, a.out);
     return hipGetLastError();
 }
 
+// Instances: VPL 1, 2, 4 for G = 1, 2, 4 and 64 (G = 64 also holds scalar rows
+// of up to 1024 elements with VPL 8 and 16), VPL 1 for G = 8, 16, 32.
 template <DType D, int G, bool VEC>
 hipError_t launch_regs_vpl(const LaunchArgs& a) {
+    constexpr bool kWide = G <= 4 || G == 64;
     switch (a.loads_per_lane) {
         case 1: return launch_regs<D, G, 1, VEC>(a);
-        case 2: if constexpr (G == 64) return launch_regs<D, G, 2, VEC>(a); break;
-        case 4: if constexpr (G == 64) return launch_regs<D, G, 4, VEC>(a); break;
-        case 8: if constexpr (G == 64) return launch_regs<D, G, 8, VEC>(a); break;
-        case 16: if constexpr (G == 64) return launch_regs<D, G, 16, VEC>(a); break;
+        case 2: if constexpr (kWide) return launch_regs<D, G, 2, VEC>(a); break;
+        case 4: if constexpr (kWide) return launch_regs<D, G, 4, VEC>(a); break;
+        case 8: if constexpr (G == 64 && !VEC) return launch_regs<D, G, 8, VEC>(a); break;
+        case 16: if constexpr (G == 64 && !VEC) return launch_regs<D, G, 16, VEC>(a); break;
     }
     return hipErrorInvalidConfiguration;
 }
@@ -334,6 +484,10 @@ template <DType D, bool SPLIT>
 hipError_t launch_stream_cfg(const LaunchArgs& a) {
     const int key = a.block * 100 + a.unroll;
     switch (key) {
+        case 6404: return launch_stream<D, 64, 4, SPLIT>(a);
+        case 6408: return launch_stream<D, 64, 8, SPLIT>(a);
+        case 12804: return launch_stream<D, 128, 4, SPLIT>(a);
+        case 12808: return launch_stream<D, 128, 8, SPLIT>(a);
         case 25604: return launch_stream<D, 256, 4, SPLIT>(a);
         case 25608: return launch_stream<D, 256, 8, SPLIT>(a);
         case 51204: return launch_stream<D, 512, 4, SPLIT>(a);

@@ -43,7 +43,7 @@ def upload(torch, x: np.ndarray, pad_front: int = 0):
 
 
 def gpu_lse(torch, handle, x: np.ndarray, dtype: str, schedule: str = "auto",
-            pad_front: int = 0, tuning=(0, 0, 0)) -> np.ndarray:
+            pad_front: int = 0, tuning=(0, 0, 0, 0, 0)) -> np.ndarray:
     """Run lse_forward on a host array; returns the fp32 outputs on the host."""
     rows, cols = x.shape
     t, ptr, stride = upload(torch, x, pad_front)
@@ -56,7 +56,7 @@ def gpu_lse(torch, handle, x: np.ndarray, dtype: str, schedule: str = "auto",
         torch.cuda.synchronize()
     finally:
         B.lse_set_schedule(handle, "auto")
-        B.lse_set_tuning(handle, 0, 0, 0)
+        B.lse_set_tuning(handle, 0, 0, 0, 0, 0)
     del t
     return out.cpu().numpy()[:rows]
 

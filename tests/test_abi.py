@@ -107,7 +107,7 @@ def test_forward_accepts_stride_below_cols_for_one_row(lib):
 
 def test_setters_reject_bad_values(lib):
     assert lib.lse_set_schedule(None, 1) == B.LSE_ERR_INVALID_ARG
-    assert lib.lse_set_tuning(None, 0, 0, 0) == B.LSE_ERR_INVALID_ARG
+    assert lib.lse_set_tuning(None, 0, 0, 0, 0, 0) == B.LSE_ERR_INVALID_ARG
 
 
 # ---- the planner ------------------------------------------------------------
@@ -118,44 +118,68 @@ def plan(dtype, rows, cols, stride=None, addr=0, n_cu=256, schedule=0):
 
 def test_plan_for_the_five_workloads():
     p1 = plan(F32, 64, 32000)
-    assert p1["schedule"] == B.LSE_SCHED_ROW_PER_WG and p1["grid"] == 64 and p1["unroll"] == 8
+    assert p1["schedule"] == B.LSE_SCHED_ROW_PER_WG and p1["grid"] == 64 and p1["block"] == 512
     p2 = plan(BF16, 512, 128256)
     assert p2["schedule"] == B.LSE_SCHED_ROW_PER_WG and p2["grid"] == 512
+    assert (p2["block"], p2["unroll"]) == (256, 4)
     p3 = plan(BF16, 4096, 262144)
     assert p3["schedule"] == B.LSE_SCHED_ROW_PER_WG and p3["grid"] == 4096
     p4 = plan(F32, 65536, 4096)
-    assert p4["schedule"] == B.LSE_SCHED_ROWS_PER_WAVE
-    assert (p4["lanes_per_row"], p4["loads_per_lane"], p4["vector_loads"]) == (64, 16, 1)
+    assert p4["schedule"] == B.LSE_SCHED_ROW_PER_WG and (p4["block"], p4["unroll"]) == (256, 4)
     p5 = plan(F32, 1 << 24, 16)
     assert p5["schedule"] == B.LSE_SCHED_ROWS_PER_WAVE
     assert (p5["lanes_per_row"], p5["loads_per_lane"], p5["rows_per_wave"]) == (4, 1, 64)
-    assert p5["grid"] == 256 * 32 // 4
+    assert p5["grid"] == 256 * 64 // 4
 
 
 def test_plan_rows_zero():
     assert plan(F32, 0, 100)["schedule"] == 0 and plan(F32, 0, 100)["grid"] == 0
 
 
+def regs_instance(g, vpl, vec):
+    """The register-rows kernel instances that exist (lse_kernels.hip)."""
+    if vpl == 1:
+        return True
+    if vpl in (2, 4):
+        return g <= 4 or g == 64
+    return not vec and g == 64 and vpl in (8, 16)
+
+
 @pytest.mark.parametrize("dtype", [F32, BF16])
 def test_plan_register_rows_cover_every_element(dtype):
     k = 4 if dtype == F32 else 8
-    for cols in list(range(0, 80)) + [127, 128, 129, 255, 256, 257, 1023, 1024, 1025, 4095, 4096,
-                                      4097, 8191, 8192, 8193]:
+    esize = 16 // k
+    for cols in list(range(0, 80)) + [127, 128, 129, 255, 256, 257, 1023, 1024, 1025, 2047,
+                                      2048, 2049, 4095, 4096, 4097]:
         for stride_pad, addr in [(0, 0), (k, 0), (1, 0), (0, 4 if dtype == F32 else 2)]:
             stride = cols + stride_pad
             p = plan(dtype, 100, cols, stride, addr)
-            if p["schedule"] != B.LSE_SCHED_ROWS_PER_WAVE:
+            aligned = addr % 16 == 0 and (stride * esize) % 16 == 0
+            if cols == 0 or (aligned and 1 <= cols // k <= 256) or \
+                    ((not aligned or cols < k) and cols <= 1024):
+                assert p["schedule"] == B.LSE_SCHED_ROWS_PER_WAVE, (cols, stride, addr)
+            else:
+                assert p["schedule"] != B.LSE_SCHED_ROWS_PER_WAVE, (cols, stride, addr)
                 continue
             g, vpl = p["lanes_per_row"], p["loads_per_lane"]
-            assert g in (1, 2, 4, 8, 16, 32, 64) and vpl in (1, 2, 4, 8, 16)
-            assert vpl == 1 or g == 64
+            assert g in (1, 2, 4, 8, 16, 32, 64)
+            assert regs_instance(g, vpl, p["vector_loads"] == 1), (cols, g, vpl)
             if p["vector_loads"]:
-                esize = 16 // k
-                assert addr % 16 == 0 and (stride * esize) % 16 == 0
-                assert g * vpl * k + (cols % k) >= cols and g >= cols % k
+                assert aligned
+                assert g * vpl >= cols // k and g >= cols % k and cols // k >= 1
             else:
                 assert g * vpl >= cols
             assert p["rows_per_wave"] == (64 // g) * (4 if vpl == 1 else 2 if vpl == 2 else 1)
+
+
+def test_plan_streaming_block_follows_row_length():
+    # about 32 fp32 or 64 bf16 elements per lane, 64..256 threads
+    assert plan(F32, 100000, 2048)["block"] == 128      # 8 KiB rows
+    assert plan(F32, 100000, 4096)["block"] == 256      # 16 KiB rows
+    assert plan(F32, 100000, 1 << 16)["block"] == 256
+    assert plan(BF16, 100000, 4096)["block"] == 64      # 8 KiB rows
+    assert plan(BF16, 100000, 8192)["block"] == 128
+    assert plan(F32, 100, 1 << 16)["block"] == 512      # fewer rows than CUs
 
 
 def test_plan_long_rows_and_few_rows():

@@ -80,8 +80,9 @@ def test_row_counts(torch_gpu, handle, oracle, rows):
                     f"rows={rows} {dtype} cols={cols} {sched}")
 
 
-@pytest.mark.parametrize("tuning", [(256, 4, 0), (256, 8, 3), (512, 8, 0), (1024, 4, 0),
-                                    (1024, 8, 64), (256, 4, 1)])
+@pytest.mark.parametrize("tuning", [(64, 4, 0), (64, 8, 5), (128, 4, 0), (128, 8, 2),
+                                    (256, 4, 0), (256, 8, 3), (512, 4, 0), (512, 8, 0),
+                                    (1024, 4, 0), (1024, 8, 64), (256, 4, 1)])
 def test_streaming_tunings(torch_gpu, handle, oracle, tuning):
     """Every block/unroll instance of the streaming kernels, split and not."""
     for dtype in ["f32", "bf16"]:
