@@ -168,6 +168,9 @@ def main() -> int:
     ap.add_argument("--all-out", default="gpurun_out/bench_all.jsonl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="first run three plain device copies of BYTES bytes (the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -183,6 +186,14 @@ def main() -> int:
         log("no GPU visible")
         return 1
     B.load()
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration: 3 copies of {args.copy_calibration} bytes")
+        del src, dst
     handle = B.lse_create(0)
     try:
         log(f"timing config {args.config}: {args.steps} steps after {args.warmup} warmup")
