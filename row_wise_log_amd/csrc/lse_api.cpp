@@ -129,10 +129,10 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
     p->vector_loads = 1;
     if (sched == LSE_SCHED_ROW_PER_WG) {
         // About 32 fp32 or 64 bf16 elements per lane (one or two batches of
-        // four 16-byte loads), 64 to 256 threads; 512 threads when there are
-        // too few rows for every CU to hold one.
+        // four 16-byte loads), 64 to 256 threads; 512 threads when every CU
+        // holds at most two rows, so that each still has 16 wavefronts.
         int block = 256;
-        if (rows < n_cu) {
+        if (rows <= 2 * static_cast<int64_t>(n_cu)) {
             block = 512;
         } else {
             const int64_t per = nvec / (dtype == LSE_DTYPE_BF16 ? 8 : 4);

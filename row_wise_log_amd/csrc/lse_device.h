@@ -7,8 +7,9 @@
 // each thread keeping a register accumulator (§3.1): a running maximum and a
 // sum of exponentials, the online form its §2.2 describes. Here a lane keeps
 //
-//     m  the largest element folded so far (natural units, exact),
-//     c  = fl(clamp(m, -2^126, 2^126) * log2(e)), the base-2 reference,
+//     m  a reference: the largest element folded so far, or (fold_lazy) a
+//        value at most 32*ln2 below it (natural units, exact),
+//     c  = fl(clamp(m, -2^30, 2^30) * log2(e)), the base-2 reference,
 //     s  = sum over folded x of 2^(x*log2(e) - c),
 //
 // so the value it represents is ln2 * (c + log2 s). The exponentials run on
@@ -201,6 +202,31 @@ __device__ __forceinline__ void fold(Acc& a, const float* f) {
     a.s = sum;
     a.m = m;
     a.c = c;
+}
+
+// Fold N values lazily. The batch's terms are first taken against the lane's
+// current reference c, with no maximum computed. That sum is kept when it is
+// at most 2^32 and the reference is a finite maximum within +-2^30; otherwise
+// (a new maximum more than 32*ln2 above the reference, an infinity, a NaN, no
+// finite maximum yet, or the clamp in use) the batch is folded again by fold<N>,
+// which moves the reference to the batch maximum. So the reference stays within
+// 32*ln2 of the lane's running maximum: no term exceeds 2^38, no sum of fewer
+// than 2^31 terms overflows, and the lane's largest element contributed a term
+// of at least 2^-6, so terms that underflow are negligible. The value the lane
+// represents, m + ln2*(log2 s - (m*log2e - c)), does not need m to be the
+// maximum, only the reference that c and s were formed with.
+template <int N>
+__device__ __forceinline__ void fold_lazy(Acc& a, const float* f) {
+    const float t = sum_exp_of<N>(f, a.c);
+    if (t <= 0x1p32f && __builtin_fabsf(a.m) <= kClamp) {
+        const float s = a.s;
+        const float sum = s + t;
+        const float bp = sum - s;
+        a.e += (s - (sum - bp)) + (t - bp);
+        a.s = sum;
+    } else {
+        fold<N>(a, f);
+    }
 }
 
 // True when |m| is finite and beyond 2^30: one unsigned range test on the bits.

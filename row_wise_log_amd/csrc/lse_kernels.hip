@@ -7,7 +7,9 @@
 // bound by HBM bandwidth (the paper's §4.2 finds fused LSE time approaching
 // the memory lower bound), so the kernels aim at full 16-byte coalesced,
 // non-temporal loads with many bytes in flight per compute unit, and keep the
-// per-element VALU work to decode, max, one fma, one v_exp_f32 and one add.
+// per-element VALU work of the streaming loop to decode, one fma, one
+// v_exp_f32 and one add (the running maximum is only refreshed when a batch
+// outgrows it: fold_lazy).
 //
 // Three schedules, picked on the host by shape (lse_api.cpp):
 //
@@ -314,43 +316,52 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
 
     // Batches of U vectors per lane: nfull whole batches, then one guarded
     // batch holding the last rem < U * BLOCK vectors. Software-pipelined:
-    // the loads of the next batch are in flight while a batch is folded, so
-    // the fold's VALU time stays off each wavefront's load-to-load path. All
-    // branches are uniform; in the guarded batch, lanes past the end load the
-    // part's last vector (in bounds) and replace it by -inf, so the loads
-    // need no divergent control flow and the hardware wait counts stay exact.
+    // the loads of the next batch are issued before a batch is folded, and a
+    // scheduling barrier after each group of loads keeps the compiler from
+    // moving them into the fold (interleaved, the fold's first wait would
+    // also wait for the next batch). Every batch issues exactly U loads with
+    // no branch around them, so the hardware wait counts stay exact: in the
+    // guarded batch, lanes past the end load the part's last vector (in
+    // bounds), and the fold replaces those vectors by -inf.
     const int64_t n = v1 - v0;
     const u32x4* p0 = vp + v0 + tid;
     const int64_t nfull = n / (static_cast<int64_t>(U) * BLOCK);
     const int64_t rem = n - nfull * U * BLOCK;
+    const int64_t gbase = nfull * U * BLOCK + tid;  // this lane's first index in the guarded batch
 
     auto load_full = [&](u32x4 (&w)[U], int64_t k) {
         const u32x4* q = p0 + k * (U * BLOCK);
 #pragma unroll
         for (int u = 0; u < U; ++u) w[u] = load_vec(q + u * BLOCK);
+        __builtin_amdgcn_sched_barrier(0);
     };
     auto load_guarded = [&](u32x4 (&w)[U]) {
         const u32x4* q = vp + v0;
-        const int64_t base = nfull * U * BLOCK;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t j = base + tid + u * BLOCK;
-            const u32x4 v = load_vec(q + (j < n ? j : n - 1));
-            w[u] = j < n ? v : neg_inf_vec<D>();
+            const int64_t j = gbase + u * BLOCK;
+            w[u] = load_vec(q + (j < n ? j : n - 1));
         }
+        __builtin_amdgcn_sched_barrier(0);
     };
     auto fold_batch = [&](const u32x4 (&w)[U]) {
         float f[U * K];
 #pragma unroll
         for (int u = 0; u < U; ++u) decode<D>(w[u], &f[u * K]);
-        fold<U * K>(a, f);
+        fold_lazy<U * K>(a, f);
+    };
+    auto fold_guarded = [&](const u32x4 (&w)[U]) {
+        u32x4 m[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) m[u] = gbase + u * BLOCK < n ? w[u] : neg_inf_vec<D>();
+        fold_batch(m);
     };
 
     if (n > 0) {
         u32x4 wa[U], wb[U], wc[U];
         if (nfull == 0) {
             load_guarded(wc);
-            fold_batch(wc);
+            fold_guarded(wc);
         } else {
             load_full(wa, 0);
             int64_t k = 0;
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
                 load_guarded(wc);
                 fold_batch(wa);
             }
-            if (rem > 0) fold_batch(wc);
+            if (rem > 0) fold_guarded(wc);
         }
     }
 

@@ -121,7 +121,7 @@ def test_plan_for_the_five_workloads():
     assert p1["schedule"] == B.LSE_SCHED_ROW_PER_WG and p1["grid"] == 64 and p1["block"] == 512
     p2 = plan(BF16, 512, 128256)
     assert p2["schedule"] == B.LSE_SCHED_ROW_PER_WG and p2["grid"] == 512
-    assert (p2["block"], p2["unroll"]) == (256, 4)
+    assert (p2["block"], p2["unroll"]) == (512, 4)        # two rows per CU
     p3 = plan(BF16, 4096, 262144)
     assert p3["schedule"] == B.LSE_SCHED_ROW_PER_WG and p3["grid"] == 4096
     p4 = plan(F32, 65536, 4096)
@@ -180,6 +180,8 @@ def test_plan_streaming_block_follows_row_length():
     assert plan(BF16, 100000, 4096)["block"] == 64      # 8 KiB rows
     assert plan(BF16, 100000, 8192)["block"] == 128
     assert plan(F32, 100, 1 << 16)["block"] == 512      # fewer rows than CUs
+    assert plan(F32, 512, 1 << 16)["block"] == 512      # at most two rows per CU
+    assert plan(F32, 513, 1 << 16)["block"] == 256
 
 
 def test_plan_long_rows_and_few_rows():
