@@ -129,7 +129,7 @@ def test_plan_for_the_five_workloads():
     p5 = plan(F32, 1 << 24, 16)
     assert p5["schedule"] == B.LSE_SCHED_ROWS_PER_WAVE
     assert (p5["lanes_per_row"], p5["loads_per_lane"], p5["rows_per_wave"]) == (4, 1, 64)
-    assert p5["grid"] == 256 * 64 // 4
+    assert p5["grid"] == 256 * 8 // 4                    # 8 wavefronts per CU, 4 per block
 
 
 def test_plan_rows_zero():
