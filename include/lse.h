@@ -107,6 +107,35 @@ lse_status_t lse_forward(lse_handle_t h, const void *x, lse_dtype_t dtype,
                          int64_t rows, int64_t cols, int64_t row_stride,
                          float *out, hipStream_t stream);
 
+/*
+ * Token log-probabilities, fused into the same pass over x: for each row r
+ * with t = targets[r],
+ *
+ *     logp[r] = x[r, t] - LSE(x[r, 0:cols])
+ *
+ * the log-probability of column t under a softmax over the row. The pages'
+ * motivating workload computes exactly this per generated token in RLHF
+ * training: the log-probability of the sampled token under the model's logits
+ * over the vocabulary, which the paper names as LSE's use in per-token LLM
+ * log-probabilities (§1, §5.1). The subtraction is one fp32 operation on the
+ * decoded element and the fp32 LSE; x is read once, as by lse_forward.
+ *   targets    device pointer to rows int64 column indices, 8-byte aligned.
+ *              A target outside [0, cols) gives logp[r] = NaN.
+ *   logp       device pointer to rows fp32 outputs, 4-byte aligned.
+ *   lse_out    optional (NULL allowed) device pointer to rows fp32 values that
+ *              receive LSE(x[r, :]) exactly as lse_forward writes them.
+ * Other arguments, streams and errors as for lse_forward. IEEE arithmetic
+ * gives the special values: a target at -inf gives -inf; a row of only -inf
+ * gives NaN (-inf - -inf); a +inf elsewhere in the row gives -inf and a +inf
+ * at the target NaN; a NaN in the row gives NaN.
+ * Errors: as lse_forward, plus INVALID_ARG for NULL or misaligned targets or
+ * logp when rows > 0.
+ */
+lse_status_t lse_token_logprob(lse_handle_t h, const void *x, lse_dtype_t dtype,
+                               int64_t rows, int64_t cols, int64_t row_stride,
+                               const int64_t *targets, float *logp, float *lse_out,
+                               hipStream_t stream);
+
 /* Release the handle and its workspace. NULL is allowed and returns LSE_OK.
  * The caller must ensure no work using the handle is still pending. */
 lse_status_t lse_destroy(lse_handle_t h);

@@ -8,7 +8,9 @@ it.
 ``lse(x, dtype)`` returns, for each row of a 2-D array, log(sum_j exp(x_ij))
 in float64, computed by ``lse_oracle.c`` (plain two-pass max-subtract with
 libm ``exp``/``log``; its header states the definition and the special
-cases). bf16 inputs are passed as uint16 bit patterns.
+cases). ``token_logprob(x, targets, dtype)`` returns x[r, targets[r]] minus
+that LSE (NaN for a target outside [0, cols)). bf16 inputs are passed as
+uint16 bit patterns.
 """
 from __future__ import annotations
 
@@ -51,6 +53,42 @@ class Oracle:
         fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_int]
         self._fn = fn
+        fn = self._lib.lse_oracle_token_logprob_f64
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        self._fn_tok = fn
+
+    @staticmethod
+    def _prepare(x: np.ndarray, dtype: str | None):
+        x = np.asarray(x)
+        if dtype is None:
+            dtype = "bf16" if x.dtype == np.uint16 else "f32"
+        want = np.uint16 if dtype == "bf16" else np.float32
+        if x.dtype != want:
+            raise TypeError(f"dtype {dtype} needs a {np.dtype(want)} array, got {x.dtype}")
+        if x.ndim != 2:
+            raise ValueError("x must be 2-D")
+        rows, cols = x.shape
+        if (cols > 1 and x.strides[1] != x.itemsize) or \
+                (rows > 1 and (x.strides[0] < cols * x.itemsize or x.strides[0] % x.itemsize)):
+            x = np.ascontiguousarray(x)
+        stride = x.strides[0] // x.itemsize if rows > 1 else cols
+        return x, dtype, rows, cols, stride
+
+    def token_logprob(self, x: np.ndarray, targets, dtype: str | None = None,
+                      threads: int = 1) -> np.ndarray:
+        """x[r, targets[r]] - LSE(x[r, :]) in float64 (NaN for a target outside [0, cols))."""
+        x, dtype, rows, cols, stride = self._prepare(x, dtype)
+        t = np.ascontiguousarray(np.asarray(targets, dtype=np.int64))
+        if t.shape != (rows,):
+            raise ValueError("targets must hold one int64 per row")
+        out = np.full(rows, np.nan, dtype=np.float64)
+        rc = self._fn_tok(x.ctypes.data if x.size else None, DTYPES[dtype], rows, cols, stride,
+                          t.ctypes.data if rows else None, out.ctypes.data, int(threads))
+        if rc != 0:
+            raise ValueError("lse_oracle_token_logprob_f64 rejected its arguments")
+        return out
 
     def lse(self, x: np.ndarray, dtype: str | None = None, threads: int = 1) -> np.ndarray:
         """Row-wise LSE of a 2-D array in float64.
@@ -96,3 +134,7 @@ def default() -> Oracle:
 
 def lse(x: np.ndarray, dtype: str | None = None, threads: int = 1) -> np.ndarray:
     return default().lse(x, dtype, threads)
+
+
+def token_logprob(x: np.ndarray, targets, dtype: str | None = None, threads: int = 1) -> np.ndarray:
+    return default().token_logprob(x, targets, dtype, threads)

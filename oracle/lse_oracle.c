@@ -31,6 +31,14 @@
  *     cols == 0, or every x = -inf  -> -inf
  *     otherwise a +inf in the row   -> +inf
  *
+ * Token log-probabilities (lse_oracle_token_logprob_f64). The paper names
+ * per-token LLM log-probabilities as a use of LSE (§1) and benchmarks the
+ * RLHF log-probability computation over vocabularies of 32K to 256K (§2,
+ * §5.1): the log-probability of token t under a softmax over the row,
+ *     logp[r] = x[r, t] - LSE(x[r, :]),   t = targets[r],
+ * in float64 with the LSE above. A target outside [0, cols) gives NaN; the
+ * special values follow from IEEE arithmetic on the definition.
+ *
  * The rows are split over `nthreads` POSIX threads; a row's arithmetic does
  * not depend on the thread count.
  *
@@ -92,10 +100,20 @@ static double lse_one_row(const void *x, int dtype, int64_t start, int64_t cols)
     return m + log(s);
 }
 
+/* The log-probability of column t of one row: the element minus the row's LSE. */
+static double token_logprob_one_row(const void *x, int dtype, int64_t start, int64_t cols,
+                                    int64_t t)
+{
+    if (t < 0 || t >= cols)
+        return NAN;
+    return load_elem(x, dtype, start + t) - lse_one_row(x, dtype, start, cols);
+}
+
 struct job {
     const void *x;
     int dtype;
     int64_t row_begin, row_end, cols, row_stride;
+    const int64_t *targets;  /* NULL: LSE; else the target column of each row */
     double *out;
 };
 
@@ -103,21 +121,20 @@ static void *run_rows(void *arg)
 {
     const struct job *jb = (const struct job *)arg;
     int64_t r;
-    for (r = jb->row_begin; r < jb->row_end; ++r)
-        jb->out[r] = lse_one_row(jb->x, jb->dtype, r * jb->row_stride, jb->cols);
+    for (r = jb->row_begin; r < jb->row_end; ++r) {
+        if (jb->targets == NULL)
+            jb->out[r] = lse_one_row(jb->x, jb->dtype, r * jb->row_stride, jb->cols);
+        else
+            jb->out[r] = token_logprob_one_row(jb->x, jb->dtype, r * jb->row_stride, jb->cols,
+                                               jb->targets[r]);
+    }
     return NULL;
 }
 
 #define ORACLE_MAX_THREADS 256
 
-/*
- * out[r] = LSE of row r, r in [0, rows). `x` is a host pointer to the first
- * element; row r starts `r * row_stride` elements after it. Returns 0, or -1
- * for an invalid argument (unknown dtype, negative size, row_stride < cols
- * with more than one row, null pointer with work to do).
- */
-int lse_oracle_f64(const void *x, int dtype, int64_t rows, int64_t cols,
-                   int64_t row_stride, double *out, int nthreads)
+static int run_all(const void *x, int dtype, int64_t rows, int64_t cols, int64_t row_stride,
+                   const int64_t *targets, double *out, int nthreads)
 {
     pthread_t tid[ORACLE_MAX_THREADS];
     struct job jobs[ORACLE_MAX_THREADS];
@@ -148,6 +165,7 @@ int lse_oracle_f64(const void *x, int dtype, int64_t rows, int64_t cols,
         jobs[t].row_end = jobs[t].row_begin + per < rows ? jobs[t].row_begin + per : rows;
         jobs[t].cols = cols;
         jobs[t].row_stride = row_stride;
+        jobs[t].targets = targets;
         jobs[t].out = out;
     }
     if (nthreads == 1) {
@@ -164,4 +182,30 @@ int lse_oracle_f64(const void *x, int dtype, int64_t rows, int64_t cols,
     for (t = 0; t < started; ++t)
         pthread_join(tid[t], NULL);
     return 0;
+}
+
+/*
+ * out[r] = LSE of row r, r in [0, rows). `x` is a host pointer to the first
+ * element; row r starts `r * row_stride` elements after it. Returns 0, or -1
+ * for an invalid argument (unknown dtype, negative size, row_stride < cols
+ * with more than one row, null pointer with work to do).
+ */
+int lse_oracle_f64(const void *x, int dtype, int64_t rows, int64_t cols,
+                   int64_t row_stride, double *out, int nthreads)
+{
+    return run_all(x, dtype, rows, cols, row_stride, NULL, out, nthreads);
+}
+
+/*
+ * out[r] = x[r, t] - LSE of row r with t = targets[r] (NaN when t is outside
+ * [0, cols)), r in [0, rows). Arguments as lse_oracle_f64; `targets` is a
+ * host pointer to rows int64 values and must not be null when rows > 0.
+ */
+int lse_oracle_token_logprob_f64(const void *x, int dtype, int64_t rows, int64_t cols,
+                                 int64_t row_stride, const int64_t *targets, double *out,
+                                 int nthreads)
+{
+    if (rows > 0 && targets == NULL)
+        return -1;
+    return run_all(x, dtype, rows, cols, row_stride, targets, out, nthreads);
 }

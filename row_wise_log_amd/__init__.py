@@ -1,15 +1,18 @@
 """Row-wise log-sum-exp on MI355X (gfx950): a C-ABI HIP library and its binding.
 
 ``logsumexp(x)`` returns log(sum(exp(x), dim=-1)) in fp32 for a 2-D fp32 or
-bf16 CUDA/HIP tensor whose last axis is contiguous. PyTorch only provides the
-device memory and the current stream; the computation is the HIP library's
-``lse_forward`` (see include/lse.h). The library is loaded on first use and a
-missing library is an error, never a fallback.
+bf16 CUDA/HIP tensor whose last axis is contiguous; ``token_logprob(x, t)``
+returns x[r, t[r]] - logsumexp(x)[r] from the same single pass. PyTorch only
+provides the device memory and the current stream; the computation is the HIP
+library's ``lse_forward`` / ``lse_token_logprob`` (see include/lse.h). The
+library is loaded on first use and a missing library is an error, never a
+fallback.
 """
 from __future__ import annotations
 
 from .binding import (LseError, lse_create, lse_destroy, lse_forward, lse_plan,  # noqa: F401
-                      lse_set_schedule, lse_set_tuning, lse_status_string, load)
+                      lse_set_schedule, lse_set_tuning, lse_status_string, lse_token_logprob,
+                      load)
 
 _handles: dict[int, int] = {}
 
@@ -23,8 +26,7 @@ def handle(device: int) -> int:
     return h
 
 
-def logsumexp(x, out=None, handle_=None):
-    """LSE over the last axis of a 2-D fp32/bf16 GPU tensor, as fp32[rows]."""
+def _check_input(x):
     import torch
 
     from .binding import LSE_DTYPE_BF16, LSE_DTYPE_F32
@@ -39,12 +41,39 @@ def logsumexp(x, out=None, handle_=None):
     rows, cols = x.shape
     if cols > 1 and x.stride(1) != 1:
         raise ValueError("the last axis must be contiguous")
+    return codes[x.dtype], rows, cols, (x.stride(0) if rows > 1 else cols)
+
+
+def logsumexp(x, out=None, handle_=None):
+    """LSE over the last axis of a 2-D fp32/bf16 GPU tensor, as fp32[rows]."""
+    import torch
+
+    code, rows, cols, stride = _check_input(x)
     if out is None:
         out = torch.empty(rows, dtype=torch.float32, device=x.device)
     elif out.dtype != torch.float32 or out.shape != (rows,) or not out.is_contiguous():
         raise ValueError("out must be a contiguous fp32 tensor of shape (rows,)")
     h = handle_ if handle_ is not None else handle(x.device.index or 0)
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    lse_forward(h, x.data_ptr(), codes[x.dtype], rows, cols, x.stride(0) if rows > 1 else cols,
-                out.data_ptr(), stream)
+    lse_forward(h, x.data_ptr(), code, rows, cols, stride, out.data_ptr(), stream)
     return out
+
+
+def token_logprob(x, targets, return_lse=False, handle_=None):
+    """x[r, targets[r]] - LSE(x[r, :]) for a 2-D fp32/bf16 GPU tensor and an
+    int64 GPU tensor of rows targets, as fp32[rows] (and the LSE, if asked).
+    A target outside [0, cols) gives NaN."""
+    import torch
+
+    code, rows, cols, stride = _check_input(x)
+    if targets.dtype != torch.int64 or targets.shape != (rows,) or not targets.is_contiguous():
+        raise ValueError("targets must be a contiguous int64 tensor of shape (rows,)")
+    if targets.device != x.device:
+        raise ValueError("targets must be on the same device as x")
+    logp = torch.empty(rows, dtype=torch.float32, device=x.device)
+    lse = torch.empty(rows, dtype=torch.float32, device=x.device) if return_lse else None
+    h = handle_ if handle_ is not None else handle(x.device.index or 0)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    lse_token_logprob(h, x.data_ptr(), code, rows, cols, stride, targets.data_ptr(),
+                      logp.data_ptr(), lse.data_ptr() if lse is not None else None, stream)
+    return (logp, lse) if return_lse else logp

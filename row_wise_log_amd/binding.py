@@ -31,7 +31,7 @@ SCHEDULES = {"auto": 0, "rows_per_wave": 1, "row_per_wg": 2, "split_row": 3}
 LSE_SPLIT_MAX_ROWS = 1024
 LSE_SPLIT_MAX_PARTS = 64
 
-EXPORTS = ["lse_create", "lse_forward", "lse_destroy", "lse_status_string",
+EXPORTS = ["lse_create", "lse_forward", "lse_token_logprob", "lse_destroy", "lse_status_string",
            "lse_set_schedule", "lse_set_tuning", "lse_plan"]
 
 
@@ -69,6 +69,7 @@ def load(path: Path | str = LIBRARY) -> ctypes.CDLL:
     sig = {
         "lse_create": (i32, [ctypes.POINTER(vp), ctypes.c_int]),
         "lse_forward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp]),
+        "lse_token_logprob": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]),
         "lse_destroy": (i32, [vp]),
         "lse_status_string": (ctypes.c_char_p, [i32]),
         "lse_set_schedule": (i32, [vp, i32]),
@@ -115,6 +116,20 @@ def lse_forward(handle: int, x_ptr: int, dtype: int, rows: int, cols: int, row_s
 def lse_forward_status(handle, x_ptr, dtype, rows, cols, row_stride, out_ptr, stream=None) -> int:
     """lse_forward returning the raw status instead of raising (for argument tests)."""
     return load().lse_forward(handle, x_ptr, dtype, rows, cols, row_stride, out_ptr, stream)
+
+
+def lse_token_logprob(handle: int, x_ptr: int, dtype: int, rows: int, cols: int,
+                      row_stride: int, targets_ptr: int, logp_ptr: int, lse_ptr: int | None = None,
+                      stream: int | None = None) -> None:
+    _check(load().lse_token_logprob(handle, x_ptr, dtype, rows, cols, row_stride, targets_ptr,
+                                    logp_ptr, lse_ptr, stream), "lse_token_logprob")
+
+
+def lse_token_logprob_status(handle, x_ptr, dtype, rows, cols, row_stride, targets_ptr, logp_ptr,
+                             lse_ptr=None, stream=None) -> int:
+    """lse_token_logprob returning the raw status instead of raising (for argument tests)."""
+    return load().lse_token_logprob(handle, x_ptr, dtype, rows, cols, row_stride, targets_ptr,
+                                    logp_ptr, lse_ptr, stream)
 
 
 def lse_set_schedule(handle: int, schedule: int | str) -> None:

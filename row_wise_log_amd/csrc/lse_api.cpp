@@ -281,19 +281,22 @@ lse_status_t lse_set_tuning(lse_handle_t h, int32_t block, int32_t unroll, int32
     return LSE_OK;
 }
 
-lse_status_t lse_forward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,
-                         int64_t cols, int64_t row_stride, float* out, hipStream_t stream) {
-    const uint64_t x_addr = reinterpret_cast<uint64_t>(x);
-    lse_status_t st = check_sizes(dtype, rows, cols, row_stride, x_addr);
-    if (st != LSE_OK) return st;
-    if (rows == 0) return h == nullptr ? LSE_ERR_INVALID_ARG : LSE_OK;
-    if (out == nullptr || (cols > 0 && x == nullptr)) return LSE_ERR_INVALID_ARG;
-    if (reinterpret_cast<uint64_t>(out) % 4 != 0) return LSE_ERR_INVALID_ARG;
-    if (h == nullptr) return LSE_ERR_INVALID_ARG;
+}  // extern "C"
 
+namespace {
+
+// Plan and launch one call; the arguments were checked by the caller. With
+// targets set, the kernels also write logp (and write out only if it is not
+// NULL).
+lse_status_t run(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows, int64_t cols,
+                 int64_t row_stride, float* out, const int64_t* targets, float* logp,
+                 hipStream_t stream) {
     lse_plan_t p;
-    st = make_plan(dtype, rows, cols, row_stride, x_addr, h->n_cu, h->schedule,
-                   Tuning{h->block, h->unroll, h->parts, h->waves_per_cu, h->lanes_per_row}, &p);
+    lse_status_t st = make_plan(dtype, rows, cols, row_stride, reinterpret_cast<uint64_t>(x),
+                                h->n_cu, h->schedule,
+                                Tuning{h->block, h->unroll, h->parts, h->waves_per_cu,
+                                       h->lanes_per_row},
+                                &p);
     if (st != LSE_OK) return st;
 
     const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
@@ -313,6 +316,8 @@ lse_status_t lse_forward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64
     a.cols = cols;
     a.stride_bytes = (rows > 1 ? row_stride : cols) * esize;
     a.out = out;
+    a.targets = targets;
+    a.logp = logp;
     a.ws_pairs = h->ws_pairs;
     a.counters = h->counters;
     a.stream = stream;
@@ -329,7 +334,9 @@ lse_status_t lse_forward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64
             const int64_t n = rows - r0 < LSE_SPLIT_MAX_ROWS ? rows - r0 : LSE_SPLIT_MAX_ROWS;
             lse::LaunchArgs b = a;
             b.x = a.x + r0 * a.stride_bytes;
-            b.out = a.out + r0;
+            b.out = a.out ? a.out + r0 : nullptr;
+            b.targets = a.targets ? a.targets + r0 : nullptr;
+            b.logp = a.logp ? a.logp + r0 : nullptr;
             b.rows = n;
             b.grid = n * p.parts;
             err = lse::launch(b);
@@ -339,6 +346,38 @@ lse_status_t lse_forward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64
     }
     if (prev != h->device) (void)hipSetDevice(prev);
     return err == hipSuccess ? LSE_OK : LSE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+lse_status_t lse_forward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,
+                         int64_t cols, int64_t row_stride, float* out, hipStream_t stream) {
+    const uint64_t x_addr = reinterpret_cast<uint64_t>(x);
+    lse_status_t st = check_sizes(dtype, rows, cols, row_stride, x_addr);
+    if (st != LSE_OK) return st;
+    if (rows == 0) return h == nullptr ? LSE_ERR_INVALID_ARG : LSE_OK;
+    if (out == nullptr || (cols > 0 && x == nullptr)) return LSE_ERR_INVALID_ARG;
+    if (reinterpret_cast<uint64_t>(out) % 4 != 0) return LSE_ERR_INVALID_ARG;
+    if (h == nullptr) return LSE_ERR_INVALID_ARG;
+    return run(h, x, dtype, rows, cols, row_stride, out, nullptr, nullptr, stream);
+}
+
+lse_status_t lse_token_logprob(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,
+                               int64_t cols, int64_t row_stride, const int64_t* targets,
+                               float* logp, float* lse_out, hipStream_t stream) {
+    const uint64_t x_addr = reinterpret_cast<uint64_t>(x);
+    lse_status_t st = check_sizes(dtype, rows, cols, row_stride, x_addr);
+    if (st != LSE_OK) return st;
+    if (rows == 0) return h == nullptr ? LSE_ERR_INVALID_ARG : LSE_OK;
+    if (targets == nullptr || logp == nullptr || (cols > 0 && x == nullptr))
+        return LSE_ERR_INVALID_ARG;
+    if (reinterpret_cast<uint64_t>(targets) % 8 != 0 || reinterpret_cast<uint64_t>(logp) % 4 != 0 ||
+        reinterpret_cast<uint64_t>(lse_out) % 4 != 0)
+        return LSE_ERR_INVALID_ARG;
+    if (h == nullptr) return LSE_ERR_INVALID_ARG;
+    return run(h, x, dtype, rows, cols, row_stride, lse_out, targets, logp, stream);
 }
 
 }  // extern "C"

@@ -72,20 +72,23 @@ struct RegTile {
     u32x4 w[ROUNDS][VEC ? VPL : 1];  // 16-byte units (VEC)
     float e[ROUNDS][VEC ? 1 : VPL];  // single elements (not VEC)
     float tv[ROUNDS];                // tail element (TAIL)
+    int64_t tg[ROUNDS];              // target column of the round's row (TOK)
 };
 
 // What every iteration of one wavefront shares.
 struct RegRows {
     const char* x;     // element (0, 0)
     int64_t rows;
+    int64_t cols;
     int64_t units;     // whole units per row
     int64_t stride;    // bytes between row starts
     int64_t last_it;   // index of the last iteration
     int64_t lane_off;  // sub * stride + g * (bytes per unit): this lane's first unit in round 0
+    const int64_t* targets;  // TOK: target column per row
     int g, sub, tail;
 };
 
-template <DType D, int G, int VPL, bool VEC, bool TAIL, bool FAST, int ROUNDS>
+template <DType D, int G, int VPL, bool VEC, bool TAIL, bool FAST, int ROUNDS, bool TOK>
 __device__ __forceinline__ void load_tile(RegTile<D, VPL, VEC, ROUNDS>& t, const RegRows& rr,
                                           int64_t it) {
     constexpr int EB = Elem<D>::kBytes;
@@ -97,10 +100,10 @@ __device__ __forceinline__ void load_tile(RegTile<D, VPL, VEC, ROUNDS>& t, const
 #pragma unroll
     for (int q = 0; q < ROUNDS; ++q) {
         const char* row_start;
+        int64_t row = it * RW + q * R + rr.sub;
         if constexpr (FAST) {
             row_start = base + q * R * rr.stride + rr.lane_off - rr.g * UB;
         } else {
-            int64_t row = it * RW + q * R + rr.sub;
             row = row < rr.rows ? row : rr.rows - 1;
             row_start = rr.x + row * rr.stride;
         }
@@ -116,18 +119,32 @@ __device__ __forceinline__ void load_tile(RegTile<D, VPL, VEC, ROUNDS>& t, const
         }
         if constexpr (TAIL)
             t.tv[q] = load_scalar<D>(row_start + (rr.units * K + (rr.g < rr.tail ? rr.g : 0)) * EB);
+        if constexpr (TOK) t.tg[q] = rr.targets[row];
     }
 }
 
-// Fold one tile: every round's row max and rescaled sum, then the finish, and
-// store the iteration's RW results.
-template <DType D, int G, int VPL, bool VEC, bool TAIL, bool FAST, int ROUNDS>
+// v[idx] for a power-of-two N and 0 <= idx < N, by a select tree on the bits
+// of idx (N - 1 selects, no indexed register access).
+template <int N>
+__device__ __forceinline__ float pick(const float* v, int idx) {
+    if constexpr (N == 1) {
+        return v[0];
+    } else {
+        constexpr int H = N / 2;
+        const float lo = pick<H>(v, idx & (H - 1));
+        const float hi = pick<H>(v + H, idx & (H - 1));
+        return (idx & H) ? hi : lo;
+    }
+}
+
+// Fold one tile: every round's row max and rescaled sum, then the finish of
+// each row into `stage` (and, with TOK, its token log-probability into
+// `stage_lp`), RW slots in row order.
+template <DType D, int G, int VPL, bool VEC, bool TAIL, bool FAST, int ROUNDS, bool TOK>
 __device__ __forceinline__ void fold_tile(const RegTile<D, VPL, VEC, ROUNDS>& t,
-                                          const RegRows& rr, int64_t it, float* out,
-                                          float* stage) {
+                                          const RegRows& rr, float* stage, float* stage_lp) {
     constexpr int K = VEC ? Elem<D>::kPerVec : 1;
     constexpr int R = 64 / G;
-    constexpr int RW = R * ROUNDS;
     constexpr int NV = VPL * K;
     const int g = rr.g;
     // Decode, with -inf in place of every clamped unit.
@@ -163,6 +180,28 @@ __device__ __forceinline__ void fold_tile(const RegTile<D, VPL, VEC, ROUNDS>& t,
         sq[q] = group_reduce<G>(sum, OpSum{});
         any_slow |= beyond_clamp(mx[q]);
     }
+    // TOK: the target element of each round's row. Column c lies in unit
+    // c / K, held by member (c / K) % G as its unit (c / K) / G, or in the
+    // tail (member c - units*K). The holder contributes the element and the
+    // other members +0, so the group sum is the element itself (+-inf and
+    // NaN included). A target outside [0, cols) is flagged for NaN.
+    float xt[ROUNDS];
+    bool tok_ok[ROUNDS];
+    if constexpr (TOK) {
+#pragma unroll
+        for (int q = 0; q < ROUNDS; ++q) {
+            const int64_t c = t.tg[q];
+            tok_ok[q] = c >= 0 && c < rr.cols;
+            const int64_t unit = c / K;
+            float mine = 0.0f;
+            if (tok_ok[q] && unit < rr.units && static_cast<int>(unit % G) == g)
+                mine = pick<NV>(v[q], static_cast<int>(unit / G) * K + static_cast<int>(c - unit * K));
+            if constexpr (TAIL) {
+                if (tok_ok[q] && c >= rr.units * K && c - rr.units * K == g) mine = tv[q];
+            }
+            xt[q] = group_reduce<G>(mine, OpSum{});
+        }
+    }
     if (any_slow) {  // rare: a row's max is finite and beyond +-2^30
 #pragma unroll
         for (int q = 0; q < ROUNDS; ++q) {
@@ -179,64 +218,86 @@ __device__ __forceinline__ void fold_tile(const RegTile<D, VPL, VEC, ROUNDS>& t,
     }
     // Every lane of a group holds every round's result; member g finishes
     // rounds g, g + G, ..., so the log and the special-value checks run once
-    // per row. The results go through this wavefront's LDS slots in row order
-    // so that lane l stores row it*RW + l: consecutive lanes write
-    // consecutive words.
+    // per row. The results go to this wavefront's LDS slots in row order.
 #pragma unroll
     for (int j = 0; j < (ROUNDS + G - 1) / G; ++j) {
         const int q = g + j * G;
-        float m = mx[0], sum = sq[0];
+        float m = mx[0], sum = sq[0], x_t = 0.0f;
+        bool ok_t = false;
 #pragma unroll
-        for (int k = 1; k < ROUNDS; ++k) {
+        for (int k = 0; k < ROUNDS; ++k) {
             m = q == k ? mx[k] : m;
             sum = q == k ? sq[k] : sum;
+            if constexpr (TOK) {
+                x_t = q == k ? xt[k] : x_t;
+                ok_t = q == k ? tok_ok[k] : ok_t;
+            }
         }
-        if (G <= ROUNDS || q < ROUNDS)
-            stage[q * R + rr.sub] = sum < 0.0f ? __builtin_fmaf(log2_hw(-sum), kLn2, m)
-                                               : finish(m, base2_ref(m), sum);
+        if (G <= ROUNDS || q < ROUNDS) {
+            const float r = sum < 0.0f ? __builtin_fmaf(log2_hw(-sum), kLn2, m)
+                                       : finish(m, base2_ref(m), sum);
+            stage[q * R + rr.sub] = r;
+            if constexpr (TOK) stage_lp[q * R + rr.sub] = ok_t ? x_t - r : __builtin_nanf("");
+        }
     }
+}
+
+// Store one iteration's RW staged results: lane l writes row it*RW + l, so
+// consecutive lanes write consecutive words. `out` may be NULL (TOK only).
+template <int RW, bool FAST, bool TOK>
+__device__ __forceinline__ void store_stage(const float* stage, const float* stage_lp, int64_t it,
+                                            int64_t rows, float* out, float* logp) {
     __builtin_amdgcn_wave_barrier();
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < (RW + 63) / 64; ++i) {
         const int slot = lane + 64 * i;
         const int64_t r = it * RW + slot;
-        if ((RW % 64 == 0 || slot < RW) && (FAST || r < rr.rows)) out[r] = stage[slot];
+        if ((RW % 64 == 0 || slot < RW) && (FAST || r < rows)) {
+            if (!TOK || out != nullptr) out[r] = stage[slot];
+            if constexpr (TOK) logp[r] = stage_lp[slot];
+        }
     }
     __builtin_amdgcn_wave_barrier();
 }
 
 // The wavefront's loop over iterations wave, wave + nwaves, ...: the next
 // iteration's tile is loaded (into the other buffer) before this one is folded.
-template <DType D, int G, int VPL, bool VEC, bool TAIL, bool FAST, int ROUNDS>
-__device__ __forceinline__ void fold_rows(const RegRows& rr, float* out, int64_t wave,
+template <DType D, int G, int VPL, bool VEC, bool TAIL, bool FAST, int ROUNDS, bool TOK>
+__device__ __forceinline__ void fold_rows(const RegRows& rr, float* out, float* logp, int64_t wave,
                                           int64_t nwaves) {
     constexpr int RW = (64 / G) * ROUNDS;
-    __shared__ float stage_all[4][RW];  // per-wavefront output staging (4 per block)
+    __shared__ float stage_all[4][RW];                  // per-wavefront output staging (4 per block)
+    __shared__ float stage_lp_all[TOK ? 4 : 1][TOK ? RW : 1];
     float* stage = stage_all[threadIdx.x >> 6];
+    float* stage_lp = stage_lp_all[TOK ? threadIdx.x >> 6 : 0];
     RegTile<D, VPL, VEC, ROUNDS> ta, tb;
     int64_t it = wave;
     if (it > rr.last_it) return;
-    load_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS>(ta, rr, it);
+    load_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS, TOK>(ta, rr, it);
     while (true) {
         int64_t next = it + nwaves;
-        load_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS>(tb, rr, next < rr.last_it ? next : rr.last_it);
-        fold_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS>(ta, rr, it, out, stage);
+        load_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS, TOK>(tb, rr, next < rr.last_it ? next : rr.last_it);
+        fold_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS, TOK>(ta, rr, stage, stage_lp);
+        store_stage<RW, FAST, TOK>(stage, stage_lp, it, rr.rows, out, logp);
         it = next;
         if (it > rr.last_it) break;
         next = it + nwaves;
-        load_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS>(ta, rr, next < rr.last_it ? next : rr.last_it);
-        fold_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS>(tb, rr, it, out, stage);
+        load_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS, TOK>(ta, rr, next < rr.last_it ? next : rr.last_it);
+        fold_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS, TOK>(tb, rr, stage, stage_lp);
+        store_stage<RW, FAST, TOK>(stage, stage_lp, it, rr.rows, out, logp);
         it = next;
         if (it > rr.last_it) break;
     }
 }
 
-template <DType D, int G, int VPL, bool VEC, bool TAIL, int ROUNDS>
+template <DType D, int G, int VPL, bool VEC, bool TAIL, int ROUNDS, bool TOK>
 __global__ __launch_bounds__(256) void rows_in_registers(const char* __restrict__ x,
                                                          int64_t rows, int64_t cols,
                                                          int64_t stride_bytes,
-                                                         float* __restrict__ out) {
+                                                         float* __restrict__ out,
+                                                         const int64_t* __restrict__ targets,
+                                                         float* __restrict__ logp) {
     constexpr int K = VEC ? Elem<D>::kPerVec : 1;
     constexpr int UB = VEC ? 16 : Elem<D>::kBytes;
     constexpr int RW = (64 / G) * ROUNDS;
@@ -244,24 +305,29 @@ __global__ __launch_bounds__(256) void rows_in_registers(const char* __restrict_
     const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
     const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
 
-    if (cols == 0) {  // the empty sum: every row is -inf
-        for (int64_t r = wave * 64 + lane; r < rows; r += nwaves * 64) out[r] = -kInf;
+    if (cols == 0) {  // the empty sum: every row is -inf, and no target is in range
+        for (int64_t r = wave * 64 + lane; r < rows; r += nwaves * 64) {
+            if (!TOK || out != nullptr) out[r] = -kInf;
+            if constexpr (TOK) logp[r] = __builtin_nanf("");
+        }
         return;
     }
     RegRows rr;
     rr.x = x;
     rr.rows = rows;
+    rr.cols = cols;
     rr.units = cols / K;
     rr.stride = stride_bytes;
     rr.last_it = (rows + RW - 1) / RW - 1;
+    rr.targets = targets;
     rr.g = lane & (G - 1);
     rr.sub = lane / G;
     rr.tail = static_cast<int>(cols - rr.units * K);
     rr.lane_off = rr.sub * stride_bytes + rr.g * UB;
     if (rr.units == G * VPL && rows % RW == 0)
-        fold_rows<D, G, VPL, VEC, TAIL, true, ROUNDS>(rr, out, wave, nwaves);
+        fold_rows<D, G, VPL, VEC, TAIL, true, ROUNDS, TOK>(rr, out, logp, wave, nwaves);
     else
-        fold_rows<D, G, VPL, VEC, TAIL, false, ROUNDS>(rr, out, wave, nwaves);
+        fold_rows<D, G, VPL, VEC, TAIL, false, ROUNDS, TOK>(rr, out, logp, wave, nwaves);
 }
 
 // ---------------------------------------------------------------------------
@@ -273,13 +339,15 @@ __global__ __launch_bounds__(256) void rows_in_registers(const char* __restrict_
 // [nvec*p/P, nvec*(p+1)/P); part 0 also takes the head, part P-1 the tail.
 // Lane t takes vectors t, t + BLOCK, ... in batches of U loads issued before
 // any is used.
-template <DType D, int BLOCK, int U, bool SPLIT>
+template <DType D, int BLOCK, int U, bool SPLIT, bool TOK>
 __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
                                                      int64_t rows, int64_t cols,
                                                      int64_t stride_bytes,
                                                      float* __restrict__ out, int parts,
                                                      unsigned* __restrict__ ws_pairs,
-                                                     unsigned* __restrict__ counters) {
+                                                     unsigned* __restrict__ counters,
+                                                     const int64_t* __restrict__ targets,
+                                                     float* __restrict__ logp) {
     constexpr int EB = Elem<D>::kBytes;
     constexpr int K = Elem<D>::kPerVec;
     __shared__ float pairs[2 * (BLOCK / 64)];
@@ -303,6 +371,32 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
         v0 = nvec * part / nparts;
         v1 = nvec * (part + 1) / nparts;
     }
+
+    // TOK: the row's target column and, once the first batches are in flight,
+    // the aligned 32-bit word that holds its element. Both are uniform in the
+    // workgroup and read through the scalar unit (constant address space), so
+    // their wait counter is not the one the streaming loads count on; the word
+    // is decoded only by the finish, where its wait costs nothing.
+    int64_t tgt = 0;
+    unsigned t_word = 0;
+    bool t_hi = false, t_ok = false;
+    if constexpr (TOK) tgt = targets[row];
+    auto fetch_target = [&]() {
+        if constexpr (TOK) {
+            // The empty asm makes the index opaque here, so the address (and
+            // the wait for the index) is not hoisted ahead of the first
+            // batches' loads.
+            int64_t tg = tgt;
+            asm volatile("" : "+s"(tg));
+            t_ok = tg >= 0 && tg < cols;
+            const uintptr_t ad = reinterpret_cast<uintptr_t>(rp + (t_ok ? tg : 0) * EB);
+            // an aligned word never crosses a page, so reading the whole word
+            // around a bf16 element stays inside the caller's allocation
+            t_word = *reinterpret_cast<const __attribute__((address_space(4))) unsigned*>(
+                ad & ~uintptr_t{3});
+            t_hi = (ad & 2) != 0;
+        }
+    };
 
     Acc a = acc_empty();
     if (part == 0 && tid < head) {
@@ -357,6 +451,10 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
         fold_batch(m);
     };
 
+    // TOK: the target's word is fetched at one place, in the first pass of the
+    // steady-state loop once two batches are in flight; parts too short to
+    // enter that loop fetch it after their loads (no other path holds a
+    // pending scalar load, which would make the compiler wait for it early).
     if (n > 0) {
         u32x4 wa[U], wb[U], wc[U];
         if (nfull == 0) {
@@ -367,6 +465,7 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
             int64_t k = 0;
             for (; k + 2 < nfull; k += 2) {
                 load_full(wb, k + 1);
+                if (TOK && k == 0) fetch_target();
                 fold_batch(wa);
                 load_full(wa, k + 2);
                 fold_batch(wb);
@@ -383,6 +482,7 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
             if (rem > 0) fold_guarded(wc);
         }
     }
+    if (TOK && nfull < 3) fetch_target();
 
     // Merge the lanes (one barrier), then across parts for a split row.
     Merged b = block_merge<BLOCK>(a.m, a.c, acc_sum(a), pairs);
@@ -430,13 +530,36 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
     } else {
         r = finish(b.m, b.c, b.s);
     }
-    if (tid == 0) out[row] = r;
+    if (tid == 0) {
+        if (!TOK || out != nullptr) out[row] = r;
+        if constexpr (TOK) {
+            float x_t;
+            if constexpr (D == DType::F32)
+                x_t = __uint_as_float(t_word);
+            else
+                x_t = __uint_as_float(t_hi ? (t_word & 0xFFFF0000u) : (t_word << 16));
+            logp[row] = t_ok ? x_t - r : __builtin_nanf("");
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
 // Dispatch from a host launch plan to a template instance.
 
 namespace {
+
+template <DType D, int G, int VPL, bool VEC, bool TAIL, int ROUNDS>
+hipError_t launch_regs_tok(const LaunchArgs& a) {
+    if (a.targets != nullptr)
+        hipLaunchKernelGGL((rows_in_registers<D, G, VPL, VEC, TAIL, ROUNDS, true>), dim3(a.grid),
+                           dim3(256), 0, a.stream, a.x, a.rows, a.cols, a.stride_bytes, a.out,
+                           a.targets, a.logp);
+    else
+        hipLaunchKernelGGL((rows_in_registers<D, G, VPL, VEC, TAIL, ROUNDS, false>), dim3(a.grid),
+                           dim3(256), 0, a.stream, a.x, a.rows, a.cols, a.stride_bytes, a.out,
+                           nullptr, nullptr);
+    return hipGetLastError();
+}
 
 template <DType D, int G, int VPL, bool VEC>
 hipError_t launch_regs(const LaunchArgs& a) {
@@ -445,13 +568,8 @@ hipError_t launch_regs(const LaunchArgs& a) {
     if (a.rows_per_wave != (64 / G) * ROUNDS) return hipErrorInvalidConfiguration;
     const int k = VEC ? (a.bf16 ? 8 : 4) : 1;
     const bool tail = a.cols % k != 0;
-    if (tail)
-        hipLaunchKernelGGL((rows_in_registers<D, G, VPL, VEC, VEC, ROUNDS>), dim3(a.grid),
-                           dim3(256), 0, a.stream, a.x, a.rows, a.cols, a.stride_bytes, a.out);
-    else
-        hipLaunchKernelGGL((rows_in_registers<D, G, VPL, VEC, false, ROUNDS>), dim3(a.grid),
-                           dim3(256), 0, a.stream, a.x, a.rows, a.cols, a.stride_bytes, a.out);
-    return hipGetLastError();
+    if (tail) return launch_regs_tok<D, G, VPL, VEC, VEC, ROUNDS>(a);
+    return launch_regs_tok<D, G, VPL, VEC, false, ROUNDS>(a);
 }
 
 // Instances: VPL 1, 2, 4 for G = 1, 2, 4 and 64 (G = 64 also holds scalar rows
@@ -485,9 +603,14 @@ hipError_t launch_regs_g(const LaunchArgs& a) {
 
 template <DType D, int BLOCK, int U, bool SPLIT>
 hipError_t launch_stream(const LaunchArgs& a) {
-    hipLaunchKernelGGL((stream_rows<D, BLOCK, U, SPLIT>), dim3(a.grid), dim3(BLOCK), 0, a.stream,
-                       a.x, a.rows, a.cols, a.stride_bytes, a.out, a.parts, a.ws_pairs,
-                       a.counters);
+    if (a.targets != nullptr)
+        hipLaunchKernelGGL((stream_rows<D, BLOCK, U, SPLIT, true>), dim3(a.grid), dim3(BLOCK), 0,
+                           a.stream, a.x, a.rows, a.cols, a.stride_bytes, a.out, a.parts,
+                           a.ws_pairs, a.counters, a.targets, a.logp);
+    else
+        hipLaunchKernelGGL((stream_rows<D, BLOCK, U, SPLIT, false>), dim3(a.grid), dim3(BLOCK), 0,
+                           a.stream, a.x, a.rows, a.cols, a.stride_bytes, a.out, a.parts,
+                           a.ws_pairs, a.counters, nullptr, nullptr);
     return hipGetLastError();
 }
 

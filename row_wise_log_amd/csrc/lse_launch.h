@@ -26,7 +26,9 @@ struct LaunchArgs {
     int64_t rows;
     int64_t cols;
     int64_t stride_bytes;
-    float* out;
+    float* out;          // LSE per row; may be NULL when targets is set
+    const int64_t* targets;  // token log-probabilities: target column per row (NULL: LSE only)
+    float* logp;         // x[r, targets[r]] - LSE per row (with targets)
     unsigned* ws_pairs;  // split-row (max, sum) pairs, 2 words each
     unsigned* counters;  // split-row arrival counters, one per row, zero between calls
     hipStream_t stream;

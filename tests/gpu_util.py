@@ -83,3 +83,57 @@ def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, rows=None) 
     assert ratio[worst] <= 1.0, (f"{what}: row {idx[fin][worst]} got {got[fin][worst]!r} "
                                  f"want {ref[fin][worst]!r} ({ratio[worst]:.2f} x tol)")
     return float(ratio.max())
+
+
+def gpu_token_logprob(torch, handle, x: np.ndarray, targets: np.ndarray, dtype: str,
+                      schedule: str = "auto", pad_front: int = 0, with_lse: bool = True,
+                      tuning=(0, 0, 0, 0, 0)):
+    """Run lse_token_logprob on a host array; returns (logp, lse or None) on the host."""
+    rows, cols = x.shape
+    t, ptr, stride = upload(torch, x, pad_front)
+    tg = torch.from_numpy(np.ascontiguousarray(targets, dtype=np.int64)).to("cuda")
+    logp = torch.full((max(rows, 1),), 123.0, dtype=torch.float32, device="cuda")
+    lse = torch.full((max(rows, 1),), 123.0, dtype=torch.float32, device="cuda") if with_lse else None
+    B.lse_set_schedule(handle, schedule)
+    B.lse_set_tuning(handle, *tuning)
+    try:
+        B.lse_token_logprob(handle, ptr if x.size else 0, DTYPE_CODE[dtype], rows, cols, stride,
+                            tg.data_ptr(), logp.data_ptr(),
+                            lse.data_ptr() if lse is not None else None,
+                            torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    finally:
+        B.lse_set_schedule(handle, "auto")
+        B.lse_set_tuning(handle, 0, 0, 0, 0, 0)
+    del t, tg
+    return (logp.cpu().numpy()[:rows], lse.cpu().numpy()[:rows] if lse is not None else None)
+
+
+def compare_logp(got: np.ndarray, ref: np.ndarray, ref_lse: np.ndarray, dtype: str, what: str,
+                 rows=None) -> float:
+    """The log-probability rule: NaN and +-inf exactly, otherwise
+    |g - r| <= tol * max(1, |LSE|, |logp|). logp = x_t - LSE carries the LSE's
+    error (tol * max(1, |LSE|)) plus one fp32 rounding of the difference."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    ref_lse = np.asarray(ref_lse, dtype=np.float64)
+    assert got.shape == ref.shape, what
+    tol = TOL[dtype]
+    idx = np.arange(len(ref)) if rows is None else np.asarray(rows)
+    nan = np.isnan(ref)
+    bad = nan & ~np.isnan(got)
+    assert not bad.any(), f"{what}: rows {idx[bad][:8]} want NaN, got {got[bad][:8]}"
+    inf = np.isinf(ref)
+    bad = inf & (got != ref)
+    assert not bad.any(), f"{what}: rows {idx[bad][:8]} want {ref[bad][:8]}, got {got[bad][:8]}"
+    fin = ~nan & ~inf
+    if not fin.any():
+        return 0.0
+    assert np.all(np.isfinite(got[fin])), f"{what}: non-finite logp for a finite reference"
+    scale = np.maximum(1.0, np.maximum(np.abs(ref[fin]), np.abs(ref_lse[fin])))
+    ratio = np.abs(got[fin] - ref[fin]) / (tol * scale)
+    worst = int(np.argmax(ratio))
+    assert ratio[worst] <= 1.0, (f"{what}: row {idx[fin][worst]} logp {got[fin][worst]!r} "
+                                 f"want {ref[fin][worst]!r} ({ratio[worst]:.2f} x tol)")
+    return float(ratio.max())
+

@@ -215,6 +215,125 @@ def pin_argument_checks(orc):
     assert orc.raw(None, 0, 4, 4, 4, out.ctypes.data) == -1, "null x accepted"
 
 
+# --- token log-probabilities ---------------------------------------------
+#
+# logp = x[t] - LSE(x): the log-probability of column t under a softmax over
+# the row, the per-token quantity the paper's RLHF workload computes (§1, §5.1).
+
+def _close_logp(got, want, scale, what):
+    """|got - want| <= 1e-14 * max(1, |scale|): logp inherits the LSE's error."""
+    got, want = float(got), float(want)
+    if math.isnan(want) or math.isinf(want):
+        _close(got, want, 0.0, what)
+        return
+    tol = 1e-14 * max(1.0, abs(scale))
+    assert abs(got - want) <= tol, f"{what}: |{got!r} - {want!r}| > {tol:.3g}"
+
+
+def pin_logprob_softmax_normalised(orc):
+    """exp(logp) summed over every target of a row is 1: a softmax is a distribution."""
+    rng = np.random.default_rng(12)
+    for cols in (1, 2, 3, 7, 33, 100):
+        for r in range(3):
+            row = rng.normal(0, 4, size=cols).astype(np.float32)
+            copies = np.repeat(row[None, :], cols, axis=0)   # copy j asks for column j
+            lp = orc.token_logprob(copies, np.arange(cols), "f32")
+            s = math.fsum(math.exp(v) for v in lp)
+            assert abs(s - 1.0) <= 1e-13 * cols, f"softmax over cols={cols} sums to {s!r}"
+            # and the largest element has the largest log-probability
+            assert int(np.argmax(lp)) == int(np.argmax(row)), f"argmax cols={cols}"
+
+
+def pin_logprob_two_elements(orc):
+    """Two-element rows: logp(t) = x_t - lse(a, b) in the base-2 pairwise form (§A.1)."""
+    rng = np.random.default_rng(13)
+    pairs = [(0.0, 0.0), (1.0, 0.0), (0.0, 1.0), (800.0, 0.0), (-1000.0, 1000.0),
+             (3.5, -2.25), (-60.0, -61.0)]
+    pairs += [tuple(v) for v in rng.uniform(-40, 40, size=(30, 2)).astype(np.float32)]
+    x = np.array(pairs, dtype=np.float32)
+    for t in (0, 1):
+        got = orc.token_logprob(x, np.full(len(pairs), t), "f32")
+        for (a, b), g in zip(x.astype(np.float64), got):
+            pl = pair_lse(a, b)
+            _close_logp(g, (a, b)[t] - pl, pl, f"pair ({a}, {b}) t={t}")
+
+
+def pin_logprob_constant_rows(orc):
+    """A row of N copies of c gives -ln N for every target, whatever c."""
+    for c in (0.0, -7.25, 800.0, -800.0):
+        for n in (1, 2, 7, 1000):
+            x = np.full((3, n), c, dtype=np.float32)
+            got = orc.token_logprob(x, [0, n // 2, n - 1], "f32")
+            for g in got:
+                _close_logp(g, -math.log(n), c + math.log(n), f"const c={c} N={n}")
+
+
+def pin_logprob_brute_force(orc):
+    """Tiny strided rows, fp32 and bf16 (decoded with struct), against x_t - log(fsum(exp))."""
+    rng = np.random.default_rng(14)
+    for cols in (1, 2, 5, 16, 33):
+        buf = rng.uniform(-50, 50, size=(6, cols + 3)).astype(np.float32)
+        view = buf[:, :cols]
+        t = rng.integers(0, cols, size=6)
+        got = orc.token_logprob(view, t, "f32")
+        for r in range(6):
+            bl = brute_lse(view[r])
+            _close_logp(got[r], float(view[r, t[r]]) - bl, bl, f"f32 brute cols={cols} r={r}")
+        bits = rng.integers(0x3F00, 0x4248, size=(6, cols + 3)).astype(np.uint16)  # 0.5 .. 50
+        bits[::2] |= 0x8000                                                       # some negatives
+        bview = bits[:, :cols]
+        got = orc.token_logprob(bview, t, "bf16")
+        for r in range(6):
+            vals = [_bf16_value(b) for b in bview[r]]
+            bl = brute_lse(vals)
+            _close_logp(got[r], vals[t[r]] - bl, bl, f"bf16 brute cols={cols} r={r}")
+
+
+def pin_logprob_special_values(orc):
+    """IEEE arithmetic on x_t - LSE, and NaN for a target outside the row."""
+    inf, nan = math.inf, math.nan
+    cases = [
+        ([-inf, 0.0, 1.0], 0, -inf),        # target at -inf
+        ([-inf, -inf], 1, nan),            # -inf - -inf
+        ([inf, 0.0], 1, -inf),             # +inf elsewhere
+        ([inf, 0.0], 0, nan),              # +inf at the target: inf - inf
+        ([nan, 0.0], 1, nan),
+        ([0.0, 0.0], -1, nan),             # targets out of range
+        ([0.0, 0.0], 2, nan),
+        ([0.0, 0.0], 1 << 40, nan),
+        ([0.0, -inf], 0, 0.0),             # a single finite element: probability 1
+    ]
+    for row, t, want in cases:
+        x = np.array([row], dtype=np.float32)
+        _close(orc.token_logprob(x, [t], "f32")[0], want, 1e-15, f"special {row} t={t}")
+    got = orc.token_logprob(np.zeros((2, 0), dtype=np.float32), [0, -1], "f32")
+    assert np.all(np.isnan(got)), f"cols=0 gave {got}"
+
+
+def pin_logprob_shift_invariance(orc):
+    """A softmax is invariant to adding c to the row (x on a 1/64 grid: exact in fp32)."""
+    rng = np.random.default_rng(15)
+    x = (rng.integers(-640, 640, size=(8, 300)) / 64.0).astype(np.float32)
+    t = rng.integers(0, 300, size=8)
+    base = orc.token_logprob(x, t, "f32")
+    lse = orc.lse(x, "f32")
+    for k in (-3, 4, 7):
+        shifted = orc.token_logprob(x + np.float32(2.0 ** k), t, "f32")
+        for r in range(8):
+            _close_logp(shifted[r], base[r], lse[r] + 2.0 ** k, f"logp shift 2^{k} r={r}")
+
+
+def pin_logprob_argument_checks(orc):
+    x = np.zeros((4, 4), np.float32)
+    out = np.empty(4)
+    fn = orc._fn_tok
+    assert fn(x.ctypes.data, 0, 4, 4, 4, None, out.ctypes.data, 1) == -1, "null targets accepted"
+    t = np.zeros(4, np.int64)
+    assert fn(x.ctypes.data, 0, 4, 4, 3, t.ctypes.data, out.ctypes.data, 1) == -1, \
+        "stride < cols accepted"
+    assert fn(None, 0, 0, 4, 4, None, None, 1) == 0, "rows = 0 must be a no-op"
+
+
 def _close_all(got, want, rel, what):
     assert got.shape == want.shape, f"{what}: shape"
     for i, (g, w) in enumerate(zip(got, want)):
@@ -231,4 +350,11 @@ CHEAP_PINS = [
     pin_permutation_invariance,
     pin_concat_merge,
     pin_thread_count_invariance,
+    pin_logprob_argument_checks,
+    pin_logprob_softmax_normalised,
+    pin_logprob_two_elements,
+    pin_logprob_constant_rows,
+    pin_logprob_brute_force,
+    pin_logprob_special_values,
+    pin_logprob_shift_invariance,
 ]

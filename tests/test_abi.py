@@ -99,6 +99,26 @@ def test_forward_argument_checks(lib, args, status):
     assert B.lse_forward_status(None, x, dtype, rows, cols, stride, out) == status
 
 
+@pytest.mark.parametrize("args, status", [
+    # (x, dtype, rows, cols, row_stride, targets, logp, lse_out) with a NULL handle
+    ((16, 7, 4, 4, 4, 64, 16, None), B.LSE_ERR_UNSUPPORTED_DTYPE),
+    ((16, F32, -1, 4, 4, 64, 16, None), B.LSE_ERR_INVALID_ARG),
+    ((16, F32, 4, 8, 7, 64, 16, None), B.LSE_ERR_INVALID_ARG),      # stride < cols
+    ((18, F32, 4, 4, 4, 64, 16, None), B.LSE_ERR_INVALID_ARG),      # x misaligned
+    ((16, F32, 4, 4, 4, None, 16, None), B.LSE_ERR_INVALID_ARG),    # NULL targets
+    ((16, F32, 4, 4, 4, 68, 16, None), B.LSE_ERR_INVALID_ARG),      # targets not 8-byte aligned
+    ((16, F32, 4, 4, 4, 64, None, None), B.LSE_ERR_INVALID_ARG),    # NULL logp
+    ((16, F32, 4, 4, 4, 64, 18, None), B.LSE_ERR_INVALID_ARG),      # logp misaligned
+    ((16, F32, 4, 4, 4, 64, 16, 18), B.LSE_ERR_INVALID_ARG),        # lse_out misaligned
+    ((16, F32, 4, 4, 4, 64, 16, 32), B.LSE_ERR_INVALID_ARG),        # all fine but the handle
+    ((None, F32, 0, 4, 4, None, None, None), B.LSE_ERR_INVALID_ARG),  # rows = 0 needs a handle
+])
+def test_token_logprob_argument_checks(lib, args, status):
+    x, dtype, rows, cols, stride, targets, logp, lse = args
+    assert B.lse_token_logprob_status(None, x, dtype, rows, cols, stride, targets, logp,
+                                      lse) == status
+
+
 def test_forward_accepts_stride_below_cols_for_one_row(lib):
     # one row: row_stride is ignored, so only the handle is wrong
     assert B.lse_forward_status(None, 16, F32, 1, 8, 0, 16) == B.LSE_ERR_INVALID_ARG

@@ -1,0 +1,219 @@
+"""GPU parity of the fused token log-probability, lse_token_logprob, against
+the float64 oracle: logp[r] = x[r, t_r] - LSE(x[r, :]) from the same single
+pass over x, with the LSE written beside it.
+
+* Every workload's row prefix with its seeded targets, under every schedule.
+* Every workload at full size in the benchmark's launch configuration
+  (AUTO): sampled rows against the oracle, logp <= 0 and exp(logp) <= 1 on
+  every row, and the LSE equal to lse_forward's.
+* Ragged, padded and misaligned rows with special rows, and targets at the
+  ends of the row, in the tail, out of range, at -inf, +inf and NaN.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import SCHEDULES, compare, compare_logp, gpu_lse, gpu_token_logprob, note
+from row_wise_log_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+PREFIX = {1: 64, 2: 40, 3: 12, 4: 3000, 5: 300_000}
+COLS = [1, 2, 3, 7, 8, 9, 16, 17, 33, 255, 257, 1023, 1025, 4097, 32001, 128257]
+LAYOUTS = ["contiguous", "padded", "misaligned"]
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def handle(torch_gpu):
+    h = B.lse_create(0)
+    yield h
+    torch_gpu.cuda.synchronize()
+    B.lse_destroy(h)
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_prefix_all_rows(torch_gpu, handle, oracle, cfg, schedule):
+    w = workloads.make(cfg, rows=PREFIX[cfg])
+    t = workloads.targets(cfg, rows=w.rows)
+    note(f"token logprob prefix cfg={cfg} rows={w.rows} schedule={schedule}")
+    logp, lse = gpu_token_logprob(torch_gpu, handle, w.x, t, w.dtype, schedule)
+    ref_lse = oracle.lse(w.x, w.dtype, threads=8)
+    ref = oracle.token_logprob(w.x, t, w.dtype, threads=8)
+    compare(lse, ref_lse, w.dtype, f"cfg{cfg} prefix {schedule} lse")
+    compare_logp(logp, ref, ref_lse, w.dtype, f"cfg{cfg} prefix {schedule} logp")
+
+
+def _rows_sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(n, size=min(k, n), replace=False)
+    return np.unique(np.concatenate([pick, [0, n - 1]]))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_size_sampled(torch_gpu, handle, oracle, cfg):
+    """The full workload, AUTO: sampled rows against the oracle, bounds on all."""
+    w = workloads.make(cfg)
+    t = workloads.targets(cfg)
+    note(f"token logprob full cfg={cfg} shape={w.x.shape} dtype={w.dtype}")
+    logp, lse = gpu_token_logprob(torch_gpu, handle, w.x, t, w.dtype, "auto")
+    note(f"token logprob full cfg={cfg}: lse_forward for comparison")
+    plain = gpu_lse(torch_gpu, handle, w.x, w.dtype, "auto")
+    # the fused call's LSE is the plain call's, within the parity rule
+    fin = np.isfinite(plain)
+    assert np.array_equal(np.isfinite(lse), fin)
+    compare(lse[fin], plain[fin].astype(np.float64), w.dtype, f"cfg{cfg} fused vs plain lse")
+    rows = _rows_sample(w.rows, 4096 if cfg != 3 else 512, seed=cfg)
+    sub = np.ascontiguousarray(w.x[rows])
+    ref_lse = oracle.lse(sub, w.dtype, threads=8)
+    ref = oracle.token_logprob(sub, t[rows], w.dtype, threads=8)
+    compare(lse[rows], ref_lse, w.dtype, f"cfg{cfg} full lse", rows)
+    compare_logp(logp[rows], ref, ref_lse, w.dtype, f"cfg{cfg} full logp", rows)
+    # every row: a log-probability is at most 0 (within the parity rule)
+    ok = np.isfinite(logp)
+    tol = 1e-5 if w.dtype == "bf16" else 2e-6
+    assert np.all(logp[ok] <= tol * np.maximum(1.0, np.abs(lse[ok]))), f"cfg{cfg}: logp > 0"
+    if cfg == 5:
+        # rows of only -inf give NaN (-inf - -inf); a target at -inf gives -inf
+        neg = workloads.allneg_rows(w.rows)
+        assert np.all(np.isnan(logp[neg]))
+
+
+def _special_rows(dtype, rows, cols, layout, seed):
+    rng = np.random.default_rng(seed)
+    pad = {"contiguous": 0, "padded": 5, "misaligned": 0}[layout]
+    v = rng.normal(0, 5, size=(rows, cols + pad)).astype(np.float32)
+    t = rng.integers(0, cols, size=rows).astype(np.int64)
+    t[0] = 0
+    t[1 % rows] = cols - 1                        # last column (often in the tail)
+    t[2 % rows] = -1                              # out of range: NaN
+    t[4 % rows] = cols                            # out of range: NaN
+    t[6 % rows] = 1 << 40                         # out of range: NaN
+    v[3 % rows] = -np.inf                         # empty sum: NaN
+    v[5 % rows, rng.integers(cols)] = np.nan      # NaN anywhere: NaN
+    v[7 % rows, t[7 % rows]] = np.inf             # +inf at the target: NaN
+    v[8 % rows, (t[8 % rows] + 1) % cols] = np.inf  # +inf elsewhere: -inf (or NaN if cols == 1)
+    v[9 % rows, t[9 % rows]] = -np.inf            # target at -inf: -inf
+    v[11 % rows] = 2.5                            # constant: -ln cols
+    v[13 % rows, : cols // 2] = -np.inf           # half -inf
+    v[17 % rows] -= 200.0                         # far below zero
+    v[19 % rows, t[19 % rows]] = 60.0             # a dominant target: logp near 0
+    x = workloads.f32_to_bf16_bits(v) if dtype == "bf16" else v
+    x = x[:, :cols] if pad else x
+    front = 1 if layout == "misaligned" else 0
+    return x, t, front
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("cols", COLS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_edges(torch_gpu, handle, oracle, dtype, cols, layout):
+    x, t, front = _special_rows(dtype, 37, cols, layout, seed=cols * 5 + len(layout))
+    ref_lse = oracle.lse(x, dtype)
+    ref = oracle.token_logprob(x, t, dtype)
+    for sched in SCHEDULES:
+        note(f"token logprob edges dtype={dtype} cols={cols} layout={layout} schedule={sched}")
+        logp, lse = gpu_token_logprob(torch_gpu, handle, x, t, dtype, sched, pad_front=front,
+                                      with_lse=(sched != "rows_per_wave"))
+        if lse is not None:
+            compare(lse, ref_lse, dtype, f"edges lse {dtype} cols={cols} {layout} {sched}")
+        compare_logp(logp, ref, ref_lse, dtype, f"edges logp {dtype} cols={cols} {layout} {sched}")
+
+
+def test_every_target_of_a_row(torch_gpu, handle, oracle):
+    """One row repeated with every column as its target: every position of
+    every unit, lane and tail element is picked once; exp(logp) sums to 1."""
+    rng = np.random.default_rng(3)
+    for dtype in ["f32", "bf16"]:
+        for cols in (5, 16, 31, 64, 100, 513, 1031, 5000):
+            row = rng.normal(0, 3, size=cols).astype(np.float32)
+            v = np.repeat(row[None, :], cols, axis=0)
+            x = workloads.f32_to_bf16_bits(v) if dtype == "bf16" else v
+            t = np.arange(cols, dtype=np.int64)
+            ref_lse = oracle.lse(x, dtype)
+            ref = oracle.token_logprob(x, t, dtype)
+            for sched in SCHEDULES:
+                note(f"every target dtype={dtype} cols={cols} schedule={sched}")
+                logp, _ = gpu_token_logprob(torch_gpu, handle, x, t, dtype, sched,
+                                            with_lse=False)
+                compare_logp(logp, ref, ref_lse, dtype, f"every target {dtype} {cols} {sched}")
+                s = float(np.sum(np.exp(logp.astype(np.float64))))
+                assert abs(s - 1.0) <= 1e-4, f"softmax sums to {s} ({dtype} cols={cols} {sched})"
+
+
+@pytest.mark.parametrize("tuning", [(64, 4, 0), (128, 8, 2), (256, 4, 0), (512, 8, 3),
+                                    (1024, 4, 0), (1024, 8, 64), (256, 4, 1)])
+def test_streaming_tunings(torch_gpu, handle, oracle, tuning):
+    """Every block/unroll instance of the fused streaming kernels, split and not."""
+    for dtype in ["f32", "bf16"]:
+        x, t, front = _special_rows(dtype, 9, 100_003, "misaligned", seed=sum(tuning))
+        ref_lse = oracle.lse(x, dtype)
+        ref = oracle.token_logprob(x, t, dtype)
+        for sched in ["row_per_wg", "split_row"]:
+            note(f"token logprob tuning={tuning} dtype={dtype} schedule={sched}")
+            logp, lse = gpu_token_logprob(torch_gpu, handle, x, t, dtype, sched, pad_front=front,
+                                          tuning=tuning)
+            compare(lse, ref_lse, dtype, f"tuning {tuning} {dtype} {sched} lse")
+            compare_logp(logp, ref, ref_lse, dtype, f"tuning {tuning} {dtype} {sched} logp")
+
+
+def test_split_batches_offset_targets(torch_gpu, handle, oracle):
+    """More rows than one split launch holds: each launch's targets and
+    outputs are offset by its first row."""
+    rng = np.random.default_rng(21)
+    v = rng.normal(0, 2, size=(2 * B.LSE_SPLIT_MAX_ROWS + 37, 700)).astype(np.float32)
+    t = rng.integers(0, 700, size=v.shape[0]).astype(np.int64)
+    note("token logprob split batches")
+    logp, lse = gpu_token_logprob(torch_gpu, handle, v, t, "f32", "split_row")
+    ref_lse = oracle.lse(v, "f32", threads=8)
+    compare(lse, ref_lse, "f32", "split batches lse")
+    compare_logp(logp, oracle.token_logprob(v, t, "f32", threads=8), ref_lse, "f32",
+                 "split batches logp")
+
+
+def test_empty_inputs(torch_gpu, handle):
+    torch = torch_gpu
+    stream = torch.cuda.current_stream().cuda_stream
+    # rows = 0: no work, pointers may be NULL
+    B.lse_token_logprob(handle, 0, B.LSE_DTYPE_F32, 0, 10, 10, 0, 0, None, stream)
+    # cols = 0: every target is out of range (NaN), the LSE is -inf
+    t = torch.zeros(5, dtype=torch.int64, device="cuda")
+    logp = torch.zeros(5, device="cuda")
+    lse = torch.zeros(5, device="cuda")
+    x = torch.zeros(1, device="cuda")
+    note("token logprob cols=0")
+    B.lse_token_logprob(handle, x.data_ptr(), B.LSE_DTYPE_F32, 5, 0, 0, t.data_ptr(),
+                        logp.data_ptr(), lse.data_ptr(), stream)
+    torch.cuda.synchronize()
+    assert torch.isnan(logp).all() and (lse == -float("inf")).all()
+
+
+def test_package_function(torch_gpu, oracle):
+    """row_wise_log_amd.token_logprob on torch tensors (pointer, stride and stream only)."""
+    import row_wise_log_amd as R
+    torch = torch_gpu
+    rng = np.random.default_rng(4)
+    v = rng.normal(0, 4, size=(33, 4100)).astype(np.float32)
+    t = rng.integers(0, 4100, size=33)
+    xt = torch.from_numpy(v).cuda()
+    tt = torch.from_numpy(t).cuda()
+    note("token logprob package function")
+    logp, lse = R.token_logprob(xt, tt, return_lse=True)
+    ref_lse = oracle.lse(v, "f32")
+    compare_logp(logp.cpu().numpy(), oracle.token_logprob(v, t, "f32"), ref_lse, "f32",
+                 "package fp32")
+    xb = xt.to(torch.bfloat16)
+    bits = xb.view(torch.int16).cpu().numpy().view(np.uint16)
+    logp_b = R.token_logprob(xb, tt)
+    compare_logp(logp_b.cpu().numpy(), oracle.token_logprob(bits, t, "bf16"),
+                 oracle.lse(bits, "bf16"), "bf16", "package bf16")
+    with pytest.raises(ValueError):
+        R.token_logprob(xt, tt.to(torch.int32))

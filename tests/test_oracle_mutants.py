@@ -25,7 +25,21 @@ MUTANTS = {
     "bf16_shift_15": ("w = (uint32_t)h << 16;", "w = (uint32_t)h << 15;"),
     "bf16_low_half": ("w = (uint32_t)h << 16;", "w = (uint32_t)h;"),
     "f32_wrong_width": ("(const char *)x + 4 * index", "(const char *)x + 2 * index"),
-    "row_start_uses_cols": ("r * jb->row_stride", "r * jb->cols"),
+    "row_start_uses_cols": ("jb->out[r] = lse_one_row(jb->x, jb->dtype, r * jb->row_stride",
+                            "jb->out[r] = lse_one_row(jb->x, jb->dtype, r * jb->cols"),
+    "logprob_row_start_uses_cols": ("token_logprob_one_row(jb->x, jb->dtype, r * jb->row_stride",
+                                    "token_logprob_one_row(jb->x, jb->dtype, r * jb->cols"),
+    "logprob_sign": ("return load_elem(x, dtype, start + t) - lse_one_row(",
+                     "return lse_one_row(x, dtype, start, cols) - load_elem(x, dtype, start + t) + 0 * lse_one_row("),
+    "logprob_next_column": ("return load_elem(x, dtype, start + t) - lse_one_row(",
+                            "return load_elem(x, dtype, start + (t + 1) % cols) - lse_one_row("),
+    "logprob_drops_lse": ("return load_elem(x, dtype, start + t) - lse_one_row(x, dtype, start, cols);",
+                          "return load_elem(x, dtype, start + t);"),
+    "logprob_drops_element": ("return load_elem(x, dtype, start + t) - lse_one_row(x, dtype, start, cols);",
+                              "return -lse_one_row(x, dtype, start, cols);"),
+    "logprob_out_of_range_zero": ("if (t < 0 || t >= cols)\n        return NAN;",
+                                  "if (t < 0 || t >= cols)\n        return 0.0;"),
+    "logprob_wrong_row_target": ("jb->targets[r]);", "jb->targets[r == jb->row_begin ? r : r - 1]);"),
     "nan_not_checked_with_inf": ("if (m == INFINITY)\n        return INFINITY;",
                                  "if (m == INFINITY && 0)\n        return INFINITY;"),
     "nan_check_removed": ("if (isnan(v))\n            return NAN;", ""),

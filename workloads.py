@@ -216,5 +216,20 @@ def make(cfg: int, rows: int | None = None, aux: bool = False,
     return Workload(spec=spec, x=x, rows=n, aux=out_aux)
 
 
+_TARGET_KEY = 1 << 40  # spawn key of the target-column stream, apart from the chunk keys
+
+
+def targets(cfg: int, rows: int | None = None) -> np.ndarray:
+    """Seeded target columns for the token log-probability workloads: one
+    uniform draw from [0, cols) per row (the sampled token of each position),
+    int64. A prefix of rows matches the same rows of the full draw."""
+    spec = SPECS[cfg]
+    n = spec.rows if rows is None else int(rows)
+    if not 0 <= n <= spec.rows:
+        raise ValueError(f"rows must be in [0, {spec.rows}]")
+    t = _rng(_TARGET_KEY).integers(0, spec.cols, size=spec.rows, dtype=np.int64)
+    return t[:n].copy()
+
+
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).view(np.uint8).data).hexdigest()
