@@ -33,6 +33,7 @@ sys.path.insert(0, str(ROOT))
 import workloads  # noqa: E402
 
 METRIC = "LSE input GB/s (% of HBM peak) at [512,128256] bf16; µs/call small shapes"
+METRIC_LOGPROB = "token log-prob input GB/s (x plus int64 targets) at the workload's shape"
 HBM_PEAK_GBS = 8000.0
 CACHE_BYTES = 256 << 20
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.txt"
@@ -76,12 +77,17 @@ def plan_name(plan: dict) -> str:
     return f"{s}(block={plan['block']},unroll={plan['unroll']},parts={plan['parts']},grid={plan['grid']})"
 
 
-def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int | None):
+def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int | None,
+                op: str = "lse"):
     w = workloads.make(cfg)
     rows, cols = w.rows, w.cols
     esize = 2 if w.dtype == "bf16" else 4
     in_bytes = rows * cols * esize
     out_bytes = rows * 4
+    targets = None
+    if op == "logprob":
+        targets = torch.from_numpy(workloads.targets(cfg)).to("cuda")
+        in_bytes += rows * 8  # one int64 target per row
     dtype_code = B.LSE_DTYPE_BF16 if w.dtype == "bf16" else B.LSE_DTYPE_F32
     if rotate is None:
         rotate = max(1, -(-2 * CACHE_BYTES // in_bytes) + 1)
@@ -93,8 +99,12 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
     plan = B.lse_plan(dtype_code, rows, cols, cols, bufs[0].data_ptr(), 256, 0)
 
     def step(i):
-        B.lse_forward(handle, bufs[i % rotate].data_ptr(), dtype_code, rows, cols, cols,
-                      out.data_ptr(), sh)
+        if targets is None:
+            B.lse_forward(handle, bufs[i % rotate].data_ptr(), dtype_code, rows, cols, cols,
+                          out.data_ptr(), sh)
+        else:
+            B.lse_token_logprob(handle, bufs[i % rotate].data_ptr(), dtype_code, rows, cols, cols,
+                                targets.data_ptr(), out.data_ptr(), None, sh)
 
     for i in range(warmup):
         step(i)
@@ -122,22 +132,26 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
         "ms_per_step": ms_step, "launch_ms_mean": mean_launch,
         "value_gbs": in_bytes / (ms_step * 1e-3) / 1e9,
         "achieved_gbs": (in_bytes + out_bytes) / (mean_launch * 1e-3) / 1e9,
-        "out": out,
+        "out": out, "op": op,
     }
 
 
-def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0) -> dict:
+def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0, op: str = "lse") -> dict:
     """The float64 oracle on the host cores over the same input; its first
     pass also checks the GPU output of the timed steps."""
     import oracle
     threads = len(os.sched_getaffinity(0))
     orc = oracle.default()
     nbytes = w.x.nbytes
+    tg = workloads.targets(w.spec.cfg) if op == "logprob" else None
     passes = 0
     t0 = time.perf_counter()
     ref = None
     while True:
-        r = orc.lse(w.x, w.dtype, threads=threads)
+        if tg is None:
+            r = orc.lse(w.x, w.dtype, threads=threads)
+        else:
+            r = orc.token_logprob(w.x, tg, w.dtype, threads=threads)
         if ref is None:
             ref = r
         passes += 1
@@ -147,13 +161,18 @@ def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0) -> dict:
     tol = 1e-5 if w.dtype == "bf16" else 2e-6
     fin = np.isfinite(ref)
     exact = np.array_equal(gpu_out[~fin], ref[~fin].astype(np.float32), equal_nan=True)
-    err = np.abs(gpu_out[fin] - ref[fin]) / (tol * np.maximum(1.0, np.abs(ref[fin])))
+    scale = np.maximum(1.0, np.abs(ref[fin]))
+    if tg is not None:  # logp carries the LSE's error: scale by the LSE too
+        lse = orc.lse(w.x, w.dtype, threads=threads)
+        scale = np.maximum(scale, np.abs(lse[fin]))
+    err = np.abs(gpu_out[fin] - ref[fin]) / (tol * scale)
     log(f"GPU output vs oracle: max |err|/tol = {err.max(initial=0):.3f}, non-finite match {exact}")
     return {"value": round(nbytes * passes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": (f"the whole {w.rows}x{w.cols} {w.dtype} input, {passes} passes in "
                        f"{el:.1f} s wall on {threads} threads (float64 two-pass max-subtract, "
-                       "libm exp/log)")}
+                       "libm exp/log" + (", minus the target element" if tg is not None else "")
+                       + ")")}
 
 
 def main() -> int:
@@ -168,6 +187,9 @@ def main() -> int:
     ap.add_argument("--all-out", default="gpurun_out/bench_all.jsonl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--op", choices=["lse", "logprob"], default="lse",
+                    help="lse: lse_forward (the headline); logprob: lse_token_logprob with one "
+                         "seeded int64 target per row")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run three plain device copies of BYTES bytes (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -196,12 +218,13 @@ def main() -> int:
         del src, dst
     handle = B.lse_create(0)
     try:
-        log(f"timing config {args.config}: {args.steps} steps after {args.warmup} warmup")
-        r = time_config(torch, B, handle, args.config, args.steps, args.warmup, args.rotate)
+        log(f"timing config {args.config} ({args.op}): {args.steps} steps after {args.warmup} warmup")
+        r = time_config(torch, B, handle, args.config, args.steps, args.warmup, args.rotate,
+                        args.op)
         w = r["w"]
-        traffic = recorded_traffic(args.config)
+        traffic = recorded_traffic(args.config) if args.op == "lse" else None
         line = {
-            "metric": METRIC,
+            "metric": METRIC if args.op == "lse" else METRIC_LOGPROB,
             "value": round(r["value_gbs"], 1),
             "unit": "GB/s",
             "n_gpus": 1,
@@ -216,6 +239,7 @@ def main() -> int:
             "config": {
                 "workload": f"config{args.config} {w.spec.name}: {w.spec.recipe}",
                 "rows": w.rows, "cols": w.cols, "input_dtype": w.dtype,
+                "op": args.op,
                 "input_bytes": r["in_bytes"], "output_bytes": r["out_bytes"],
                 "rotating_copies": r["rotate"], "plan": plan_name(r["plan"]),
                 "pct_of_hbm_peak": round(100 * r["value_gbs"] / HBM_PEAK_GBS, 2),
@@ -239,8 +263,8 @@ def main() -> int:
                 for cfg in [1, 2, 3, 4, 5]:
                     log(f"timing config {cfg}")
                     rc = r if cfg == args.config else time_config(
-                        torch, B, handle, cfg, args.steps, args.warmup, None)
-                    rec = {"config": cfg, "workload": rc["w"].spec.name,
+                        torch, B, handle, cfg, args.steps, args.warmup, None, args.op)
+                    rec = {"config": cfg, "op": args.op, "workload": rc["w"].spec.name,
                            "plan": plan_name(rc["plan"]),
                            "input_GBs": round(rc["value_gbs"], 1),
                            "pct_hbm_peak": round(100 * rc["value_gbs"] / HBM_PEAK_GBS, 2),
@@ -255,7 +279,7 @@ def main() -> int:
         if not args.no_cpu_baseline:
             log("timing the float64 oracle on the host cores")
             gpu_out = r["out"].cpu().numpy().astype(np.float64)
-            line["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds)
+            line["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds, args.op)
         else:
             line["cpu_baseline"] = None
         print(json.dumps(line), flush=True)
