@@ -34,6 +34,8 @@ import workloads  # noqa: E402
 
 METRIC = "LSE input GB/s (% of HBM peak) at [512,128256] bf16; µs/call small shapes"
 METRIC_LOGPROB = "token log-prob input GB/s (x plus int64 targets) at the workload's shape"
+METRIC_BACKWARD = ("LSE backward input GB/s (x, lse, grad_out read; grad_x written) at the "
+                   "workload's shape")
 HBM_PEAK_GBS = 8000.0
 CACHE_BYTES = 256 << 20
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.txt"
@@ -85,6 +87,19 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
     in_bytes = rows * cols * esize
     out_bytes = rows * 4
     targets = None
+    bwd = None
+    if op == "backward":
+        # the forward value comes from the float64 oracle (rounded to fp32), so
+        # the check of the timed output never feeds the GPU's own results back
+        import oracle
+        lse32 = oracle.lse(w.x, w.dtype, threads=len(os.sched_getaffinity(0))).astype(np.float32)
+        g = np.random.default_rng(7).normal(0, 1, size=rows).astype(np.float32)
+        bwd = {"lse": torch.from_numpy(lse32).to("cuda"), "g": torch.from_numpy(g).to("cuda"),
+               "grad": torch.empty(rows * cols, dtype=torch.int16 if w.dtype == "bf16"
+                                   else torch.float32, device="cuda"),
+               "lse_host": lse32, "g_host": g}
+        out_bytes += rows * cols * esize  # grad_x
+        in_bytes += rows * 8              # lse and grad_out
     if op == "logprob":
         targets = torch.from_numpy(workloads.targets(cfg)).to("cuda")
         in_bytes += rows * 8  # one int64 target per row
@@ -99,7 +114,11 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
     plan = B.lse_plan(dtype_code, rows, cols, cols, bufs[0].data_ptr(), 256, 0)
 
     def step(i):
-        if targets is None:
+        if bwd is not None:
+            B.lse_backward(handle, bufs[i % rotate].data_ptr(), dtype_code, rows, cols, cols,
+                           bwd["lse"].data_ptr(), bwd["g"].data_ptr(), bwd["grad"].data_ptr(),
+                           cols, sh)
+        elif targets is None:
             B.lse_forward(handle, bufs[i % rotate].data_ptr(), dtype_code, rows, cols, cols,
                           out.data_ptr(), sh)
         else:
@@ -132,8 +151,52 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
         "ms_per_step": ms_step, "launch_ms_mean": mean_launch,
         "value_gbs": in_bytes / (ms_step * 1e-3) / 1e9,
         "achieved_gbs": (in_bytes + out_bytes) / (mean_launch * 1e-3) / 1e9,
-        "out": out, "op": op,
+        "out": out, "op": op, "bwd": bwd,
     }
+
+
+def cpu_baseline_backward(w, r, seconds: float = 10.0) -> dict:
+    """The float64 oracle's backward pass on the host cores over a bounded
+    sample of rows (at most 256 MB of input); its first pass also checks the
+    GPU gradient of those rows."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    orc = oracle.default()
+    row_bytes = w.cols * w.x.itemsize
+    n = max(1, min(w.rows, (256 << 20) // row_bytes))
+    x = w.x[:n]
+    lse32, g = r["bwd"]["lse_host"][:n], r["bwd"]["g_host"][:n]
+    passes, ref = 0, None
+    t0 = time.perf_counter()
+    while True:
+        out = orc.softmax_grad(x, lse32, g, w.dtype, threads=threads)
+        if ref is None:
+            ref = out
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or passes >= 1000:
+            break
+    raw = r["bwd"]["grad"][: n * w.cols].cpu().numpy()
+    if w.dtype == "bf16":
+        got = (raw.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    else:
+        got = raw
+    got = got.reshape(n, w.cols).astype(np.float64)
+    fin = np.isfinite(ref)
+    rel = 2.0 ** -8 + 1e-6 if w.dtype == "bf16" else 4e-7
+    xv = (workloads.bf16_bits_to_f32(x) if w.dtype == "bf16" else x).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        d = np.abs(xv - lse32.astype(np.float64)[:, None])
+    gg = np.broadcast_to(np.maximum(1.0, np.abs(g.astype(np.float64)))[:, None], ref.shape)
+    tol = (rel + 2e-7 * np.where(np.isfinite(d), d, 0.0)[fin]) * np.abs(ref[fin]) + \
+        2.0 ** -125 * gg[fin]
+    err = np.abs(got[fin] - ref[fin]) / tol
+    log(f"GPU gradient vs oracle ({n} rows): max |err|/tol = {err.max(initial=0):.3f}, "
+        f"non-finite match {np.array_equal(got[~fin], ref[~fin], equal_nan=True)}")
+    return {"value": round(x.nbytes * passes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"the first {n} of {w.rows} rows ({x.nbytes} input bytes), {passes} passes "
+                       f"in {el:.1f} s wall on {threads} threads (float64 g * exp(x - lse))")}
 
 
 def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0, op: str = "lse") -> dict:
@@ -187,9 +250,10 @@ def main() -> int:
     ap.add_argument("--all-out", default="gpurun_out/bench_all.jsonl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--op", choices=["lse", "logprob"], default="lse",
+    ap.add_argument("--op", choices=["lse", "logprob", "backward"], default="lse",
                     help="lse: lse_forward (the headline); logprob: lse_token_logprob with one "
-                         "seeded int64 target per row")
+                         "seeded int64 target per row; backward: lse_backward (reads x, writes "
+                         "grad_x)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run three plain device copies of BYTES bytes (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -224,7 +288,7 @@ def main() -> int:
         w = r["w"]
         traffic = recorded_traffic(args.config) if args.op == "lse" else None
         line = {
-            "metric": METRIC if args.op == "lse" else METRIC_LOGPROB,
+            "metric": {"lse": METRIC, "logprob": METRIC_LOGPROB, "backward": METRIC_BACKWARD}[args.op],
             "value": round(r["value_gbs"], 1),
             "unit": "GB/s",
             "n_gpus": 1,
@@ -241,7 +305,8 @@ def main() -> int:
                 "rows": w.rows, "cols": w.cols, "input_dtype": w.dtype,
                 "op": args.op,
                 "input_bytes": r["in_bytes"], "output_bytes": r["out_bytes"],
-                "rotating_copies": r["rotate"], "plan": plan_name(r["plan"]),
+                "rotating_copies": r["rotate"],
+                "plan": plan_name(r["plan"]) if args.op != "backward" else "lse_backward",
                 "pct_of_hbm_peak": round(100 * r["value_gbs"] / HBM_PEAK_GBS, 2),
                 "us_per_call": round(r["ms_per_step"] * 1e3, 2),
                 "rows_per_s": round(w.rows / (r["ms_per_step"] * 1e-3), 1),
@@ -265,7 +330,8 @@ def main() -> int:
                     rc = r if cfg == args.config else time_config(
                         torch, B, handle, cfg, args.steps, args.warmup, None, args.op)
                     rec = {"config": cfg, "op": args.op, "workload": rc["w"].spec.name,
-                           "plan": plan_name(rc["plan"]),
+                           "plan": plan_name(rc["plan"]) if args.op != "backward"
+                           else "lse_backward",
                            "input_GBs": round(rc["value_gbs"], 1),
                            "pct_hbm_peak": round(100 * rc["value_gbs"] / HBM_PEAK_GBS, 2),
                            "us_per_call": round(rc["ms_per_step"] * 1e3, 2),
@@ -279,7 +345,10 @@ def main() -> int:
         if not args.no_cpu_baseline:
             log("timing the float64 oracle on the host cores")
             gpu_out = r["out"].cpu().numpy().astype(np.float64)
-            line["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds, args.op)
+            if args.op == "backward":
+                line["cpu_baseline"] = cpu_baseline_backward(w, r, args.cpu_seconds)
+            else:
+                line["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds, args.op)
         else:
             line["cpu_baseline"] = None
         print(json.dumps(line), flush=True)

@@ -136,6 +136,33 @@ lse_status_t lse_token_logprob(lse_handle_t h, const void *x, lse_dtype_t dtype,
                                const int64_t *targets, float *logp, float *lse_out,
                                hipStream_t stream);
 
+/*
+ * Backward pass: the gradient of lse[r] = LSE(x[r, :]) with respect to x,
+ *
+ *     grad_x[r, j] = grad_out[r] * exp(x[r, j] - lse[r]),
+ *
+ * the row's softmax scaled by the incoming gradient; backward support is
+ * one of the properties the paper tabulates for its kernels (Table 3). One
+ * streaming pass: x is read once and grad_x written once, in x's element
+ * type (bf16 results are rounded to nearest even from fp32 arithmetic).
+ *   x, dtype, rows, cols, row_stride   as for lse_forward.
+ *   lse        device pointer to rows fp32 values, normally lse_forward's
+ *              output for the same x (any values are accepted: the formula is
+ *              applied as written, with IEEE special values).
+ *   grad_out   device pointer to rows fp32 incoming gradients.
+ *   grad_x     device pointer to rows x cols elements of dtype, row r at
+ *              grad_x + r * grad_row_stride elements, aligned to its element
+ *              size; must not overlap x, lse or grad_out.
+ *   grad_row_stride  >= cols when rows > 1.
+ * No allocation, no synchronisation; nothing outside the rows of grad_x is
+ * written. Errors: as lse_forward, plus INVALID_ARG for NULL or misaligned
+ * lse, grad_out or grad_x, or grad_row_stride < cols.
+ */
+lse_status_t lse_backward(lse_handle_t h, const void *x, lse_dtype_t dtype,
+                          int64_t rows, int64_t cols, int64_t row_stride,
+                          const float *lse, const float *grad_out, void *grad_x,
+                          int64_t grad_row_stride, hipStream_t stream);
+
 /* Release the handle and its workspace. NULL is allowed and returns LSE_OK.
  * The caller must ensure no work using the handle is still pending. */
 lse_status_t lse_destroy(lse_handle_t h);

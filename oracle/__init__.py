@@ -9,8 +9,9 @@ it.
 in float64, computed by ``lse_oracle.c`` (plain two-pass max-subtract with
 libm ``exp``/``log``; its header states the definition and the special
 cases). ``token_logprob(x, targets, dtype)`` returns x[r, targets[r]] minus
-that LSE (NaN for a target outside [0, cols)). bf16 inputs are passed as
-uint16 bit patterns.
+that LSE (NaN for a target outside [0, cols)); ``softmax_grad(x, lse, g,
+dtype)`` returns the backward pass g[r] * exp(x[r, j] - lse[r]) in float64.
+bf16 inputs are passed as uint16 bit patterns.
 """
 from __future__ import annotations
 
@@ -58,6 +59,29 @@ class Oracle:
         fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         self._fn_tok = fn
+        fn = self._lib.lse_oracle_softmax_grad_f64
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                       ctypes.c_int]
+        self._fn_grad = fn
+
+    def softmax_grad(self, x: np.ndarray, lse, grad_out, dtype: str | None = None,
+                     threads: int = 1) -> np.ndarray:
+        """grad_out[r] * exp(x[r, j] - lse[r]) in float64, shape (rows, cols);
+        lse and grad_out are taken as fp32, as a caller of the backward pass holds them."""
+        x, dtype, rows, cols, stride = self._prepare(x, dtype)
+        lse = np.ascontiguousarray(np.asarray(lse, dtype=np.float32))
+        g = np.ascontiguousarray(np.asarray(grad_out, dtype=np.float32))
+        if lse.shape != (rows,) or g.shape != (rows,):
+            raise ValueError("lse and grad_out must hold one value per row")
+        out = np.full((rows, cols), np.nan, dtype=np.float64)
+        rc = self._fn_grad(x.ctypes.data if x.size else None, DTYPES[dtype], rows, cols, stride,
+                           lse.ctypes.data if rows else None, g.ctypes.data if rows else None,
+                           out.ctypes.data, int(threads))
+        if rc != 0:
+            raise ValueError("lse_oracle_softmax_grad_f64 rejected its arguments")
+        return out
 
     @staticmethod
     def _prepare(x: np.ndarray, dtype: str | None):
@@ -138,3 +162,8 @@ def lse(x: np.ndarray, dtype: str | None = None, threads: int = 1) -> np.ndarray
 
 def token_logprob(x: np.ndarray, targets, dtype: str | None = None, threads: int = 1) -> np.ndarray:
     return default().token_logprob(x, targets, dtype, threads)
+
+
+def softmax_grad(x: np.ndarray, lse, grad_out, dtype: str | None = None,
+                 threads: int = 1) -> np.ndarray:
+    return default().softmax_grad(x, lse, grad_out, dtype, threads)

@@ -39,6 +39,14 @@
  * in float64 with the LSE above. A target outside [0, cols) gives NaN; the
  * special values follow from IEEE arithmetic on the definition.
  *
+ * Backward pass (lse_oracle_softmax_grad_f64). The gradient of LSE(x[r, :])
+ * with respect to x[r, j] is exp(x[r, j] - LSE(x[r, :])), the row's softmax;
+ * the paper tabulates backward support for its kernels (Table 3). Given the
+ * forward value lse[r] and an incoming gradient grad_out[r] (both fp32, as a
+ * caller holds them), the oracle writes
+ *     out[r, j] = grad_out[r] * exp(x[r, j] - lse[r])
+ * in float64, row r at out + r * cols.
+ *
  * The rows are split over `nthreads` POSIX threads; a row's arithmetic does
  * not depend on the thread count.
  *
@@ -109,11 +117,21 @@ static double token_logprob_one_row(const void *x, int dtype, int64_t start, int
     return load_elem(x, dtype, start + t) - lse_one_row(x, dtype, start, cols);
 }
 
+/* One row of the backward pass: grad_out * exp(x_j - lse) for every j. */
+static void softmax_grad_one_row(const void *x, int dtype, int64_t start, int64_t cols,
+                                 double lse, double grad_out, double *out)
+{
+    int64_t j;
+    for (j = 0; j < cols; ++j)
+        out[j] = grad_out * exp(load_elem(x, dtype, start + j) - lse);
+}
+
 struct job {
     const void *x;
     int dtype;
     int64_t row_begin, row_end, cols, row_stride;
     const int64_t *targets;  /* NULL: LSE; else the target column of each row */
+    const float *lse, *grad_out;  /* non-NULL: the backward pass, out holds rows x cols */
     double *out;
 };
 
@@ -122,7 +140,11 @@ static void *run_rows(void *arg)
     const struct job *jb = (const struct job *)arg;
     int64_t r;
     for (r = jb->row_begin; r < jb->row_end; ++r) {
-        if (jb->targets == NULL)
+        if (jb->lse != NULL)
+            softmax_grad_one_row(jb->x, jb->dtype, r * jb->row_stride, jb->cols,
+                                 (double)jb->lse[r], (double)jb->grad_out[r],
+                                 jb->out + r * jb->cols);
+        else if (jb->targets == NULL)
             jb->out[r] = lse_one_row(jb->x, jb->dtype, r * jb->row_stride, jb->cols);
         else
             jb->out[r] = token_logprob_one_row(jb->x, jb->dtype, r * jb->row_stride, jb->cols,
@@ -134,7 +156,8 @@ static void *run_rows(void *arg)
 #define ORACLE_MAX_THREADS 256
 
 static int run_all(const void *x, int dtype, int64_t rows, int64_t cols, int64_t row_stride,
-                   const int64_t *targets, double *out, int nthreads)
+                   const int64_t *targets, const float *lse, const float *grad_out,
+                   double *out, int nthreads)
 {
     pthread_t tid[ORACLE_MAX_THREADS];
     struct job jobs[ORACLE_MAX_THREADS];
@@ -166,6 +189,8 @@ static int run_all(const void *x, int dtype, int64_t rows, int64_t cols, int64_t
         jobs[t].cols = cols;
         jobs[t].row_stride = row_stride;
         jobs[t].targets = targets;
+        jobs[t].lse = lse;
+        jobs[t].grad_out = grad_out;
         jobs[t].out = out;
     }
     if (nthreads == 1) {
@@ -193,7 +218,7 @@ static int run_all(const void *x, int dtype, int64_t rows, int64_t cols, int64_t
 int lse_oracle_f64(const void *x, int dtype, int64_t rows, int64_t cols,
                    int64_t row_stride, double *out, int nthreads)
 {
-    return run_all(x, dtype, rows, cols, row_stride, NULL, out, nthreads);
+    return run_all(x, dtype, rows, cols, row_stride, NULL, NULL, NULL, out, nthreads);
 }
 
 /*
@@ -207,5 +232,19 @@ int lse_oracle_token_logprob_f64(const void *x, int dtype, int64_t rows, int64_t
 {
     if (rows > 0 && targets == NULL)
         return -1;
-    return run_all(x, dtype, rows, cols, row_stride, targets, out, nthreads);
+    return run_all(x, dtype, rows, cols, row_stride, targets, NULL, NULL, out, nthreads);
+}
+
+/*
+ * out[r * cols + j] = grad_out[r] * exp(x[r, j] - lse[r]) for r in [0, rows),
+ * j in [0, cols). Arguments as lse_oracle_f64; `lse` and `grad_out` are host
+ * pointers to rows fp32 values and must not be null when rows > 0.
+ */
+int lse_oracle_softmax_grad_f64(const void *x, int dtype, int64_t rows, int64_t cols,
+                                int64_t row_stride, const float *lse, const float *grad_out,
+                                double *out, int nthreads)
+{
+    if (rows > 0 && (lse == NULL || grad_out == NULL))
+        return -1;
+    return run_all(x, dtype, rows, cols, row_stride, NULL, lse, grad_out, out, nthreads);
 }

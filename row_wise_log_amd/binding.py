@@ -31,8 +31,8 @@ SCHEDULES = {"auto": 0, "rows_per_wave": 1, "row_per_wg": 2, "split_row": 3}
 LSE_SPLIT_MAX_ROWS = 1024
 LSE_SPLIT_MAX_PARTS = 64
 
-EXPORTS = ["lse_create", "lse_forward", "lse_token_logprob", "lse_destroy", "lse_status_string",
-           "lse_set_schedule", "lse_set_tuning", "lse_plan"]
+EXPORTS = ["lse_create", "lse_forward", "lse_token_logprob", "lse_backward", "lse_destroy",
+           "lse_status_string", "lse_set_schedule", "lse_set_tuning", "lse_plan"]
 
 
 class LseError(RuntimeError):
@@ -70,6 +70,7 @@ def load(path: Path | str = LIBRARY) -> ctypes.CDLL:
         "lse_create": (i32, [ctypes.POINTER(vp), ctypes.c_int]),
         "lse_forward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp]),
         "lse_token_logprob": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]),
+        "lse_backward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, i64, vp]),
         "lse_destroy": (i32, [vp]),
         "lse_status_string": (ctypes.c_char_p, [i32]),
         "lse_set_schedule": (i32, [vp, i32]),
@@ -130,6 +131,20 @@ def lse_token_logprob_status(handle, x_ptr, dtype, rows, cols, row_stride, targe
     """lse_token_logprob returning the raw status instead of raising (for argument tests)."""
     return load().lse_token_logprob(handle, x_ptr, dtype, rows, cols, row_stride, targets_ptr,
                                     logp_ptr, lse_ptr, stream)
+
+
+def lse_backward(handle: int, x_ptr: int, dtype: int, rows: int, cols: int, row_stride: int,
+                 lse_ptr: int, grad_out_ptr: int, grad_x_ptr: int, grad_row_stride: int,
+                 stream: int | None = None) -> None:
+    _check(load().lse_backward(handle, x_ptr, dtype, rows, cols, row_stride, lse_ptr,
+                               grad_out_ptr, grad_x_ptr, grad_row_stride, stream), "lse_backward")
+
+
+def lse_backward_status(handle, x_ptr, dtype, rows, cols, row_stride, lse_ptr, grad_out_ptr,
+                        grad_x_ptr, grad_row_stride, stream=None) -> int:
+    """lse_backward returning the raw status instead of raising (for argument tests)."""
+    return load().lse_backward(handle, x_ptr, dtype, rows, cols, row_stride, lse_ptr,
+                               grad_out_ptr, grad_x_ptr, grad_row_stride, stream)
 
 
 def lse_set_schedule(handle: int, schedule: int | str) -> None:

@@ -171,6 +171,53 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
     return LSE_OK;
 }
 
+// The backward pass's work split: units are 16-byte vectors when every row
+// of x and grad_x starts 16-byte aligned, else single elements. Rows of at
+// least one batch (256 lanes x 4 units) are cut into chunks of 1 to 4
+// batches, sized so the grid has about 4 workgroups per CU; shorter rows are
+// packed several to a workgroup (up to 4 batches of units). A block's byte
+// span stays below 2^30 (its buffer offsets are 32-bit) and its unit count
+// below 2^22 (the kernel's float row index is exact there).
+lse_status_t make_grad_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t row_stride,
+                            int64_t grad_row_stride, uint64_t x_addr, uint64_t g_addr, int n_cu,
+                            lse::GradArgs* a) {
+    const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
+    const int k = 16 / esize;
+    const int64_t xs = (rows > 1 ? row_stride : cols) * esize;
+    const int64_t gs = (rows > 1 ? grad_row_stride : cols) * esize;
+    const bool vec = cols / k >= 1 && x_addr % 16 == 0 && g_addr % 16 == 0 &&
+                     (rows == 1 || (xs % 16 == 0 && gs % 16 == 0));
+    const int64_t units = vec ? cols / k : cols;
+    const int64_t ub = vec ? 16 : esize;
+    constexpr int64_t kBatch = 256 * 4;
+    a->bf16 = dtype == LSE_DTYPE_BF16;
+    a->vector_units = vec;
+    a->rows = rows;
+    a->cols = cols;
+    a->xs_bytes = xs;
+    a->gs_bytes = gs;
+    const int64_t target_wgs = 4 * static_cast<int64_t>(n_cu);
+    if (units >= kBatch) {
+        int64_t chunk = ceil_div(ceil_div(rows * units, target_wgs), kBatch) * kBatch;
+        chunk = std::min<int64_t>(std::max<int64_t>(chunk, kBatch), 4 * kBatch);
+        a->rows_per_wg = 1;
+        a->chunk_units = chunk;
+        a->chunks_per_row = ceil_div(units, chunk);
+        a->grid = rows * a->chunks_per_row;
+    } else {
+        int64_t r = std::max<int64_t>(1, (4 * kBatch) / units);
+        r = std::min<int64_t>(r, std::max<int64_t>(1, ceil_div(rows, target_wgs)));
+        const int64_t span = std::max(xs, gs);
+        r = std::min<int64_t>(r, std::max<int64_t>(1, ((int64_t{1} << 30) - units * ub) / std::max<int64_t>(span, 1)));
+        a->rows_per_wg = r;
+        a->chunk_units = units;
+        a->chunks_per_row = 1;
+        a->grid = ceil_div(rows, r);
+    }
+    (void)ub;
+    return LSE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -362,6 +409,42 @@ lse_status_t lse_forward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64
     if (reinterpret_cast<uint64_t>(out) % 4 != 0) return LSE_ERR_INVALID_ARG;
     if (h == nullptr) return LSE_ERR_INVALID_ARG;
     return run(h, x, dtype, rows, cols, row_stride, out, nullptr, nullptr, stream);
+}
+
+lse_status_t lse_backward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,
+                          int64_t cols, int64_t row_stride, const float* lse,
+                          const float* grad_out, void* grad_x, int64_t grad_row_stride,
+                          hipStream_t stream) {
+    const uint64_t x_addr = reinterpret_cast<uint64_t>(x);
+    lse_status_t st = check_sizes(dtype, rows, cols, row_stride, x_addr);
+    if (st != LSE_OK) return st;
+    const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
+    if (rows > 1 && (grad_row_stride < cols || grad_row_stride > (INT64_MAX / 4) / rows))
+        return LSE_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return h == nullptr ? LSE_ERR_INVALID_ARG : LSE_OK;
+    if (x == nullptr || lse == nullptr || grad_out == nullptr || grad_x == nullptr)
+        return LSE_ERR_INVALID_ARG;
+    const uint64_t g_addr = reinterpret_cast<uint64_t>(grad_x);
+    if (reinterpret_cast<uint64_t>(lse) % 4 != 0 || reinterpret_cast<uint64_t>(grad_out) % 4 != 0 ||
+        g_addr % esize != 0)
+        return LSE_ERR_INVALID_ARG;
+    if (h == nullptr) return LSE_ERR_INVALID_ARG;
+
+    lse::GradArgs a{};
+    st = make_grad_plan(dtype, rows, cols, row_stride, grad_row_stride, x_addr, g_addr, h->n_cu, &a);
+    if (st != LSE_OK) return st;
+    a.x = static_cast<const char*>(x);
+    a.lse = lse;
+    a.grad_out = grad_out;
+    a.grad_x = static_cast<char*>(grad_x);
+    a.stream = stream;
+
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return LSE_ERR_HIP;
+    if (prev != h->device && hipSetDevice(h->device) != hipSuccess) return LSE_ERR_HIP;
+    const hipError_t err = lse::launch_grad(a);
+    if (prev != h->device) (void)hipSetDevice(prev);
+    return err == hipSuccess ? LSE_OK : LSE_ERR_HIP;
 }
 
 lse_status_t lse_token_logprob(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,

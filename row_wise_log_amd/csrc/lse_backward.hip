@@ -1,0 +1,261 @@
+// lse_backward.hip - the backward pass of the row-wise log-sum-exp for gfx950:
+//
+//     grad_x[r, j] = grad_out[r] * exp(x[r, j] - lse[r]),
+//
+// the gradient of lse[r] = LSE(x[r, :]) with respect to x (the row's softmax,
+// scaled by the incoming gradient). The paper "Speeding up Log-Sum-Exp: Kernel
+// Fusion at the Memory Wall, Integer Arithmetic at the Compute Wall" lists
+// backward support among its kernels' properties (Table 3); this is that
+// step for the fused forward in lse_kernels.hip. It is a second streaming pass
+// over x that writes as many bytes as it reads, so it is bound by HBM
+// bandwidth like the forward pass: 16-byte loads and stores, one per-row
+// scalar pair (lse, grad_out), and per element one subtract, one multiply,
+// one v_exp_f32 and one multiply.
+//
+// Work split (planned on the host, lse_api.cpp): the row's units (16-byte
+// vectors when every row of x and of grad_x starts 16-byte aligned, single
+// elements otherwise) are cut into workgroup items. A long row gives several
+// workgroups a contiguous chunk each (R == 1; the row's lse and grad_out are
+// uniform and read through the scalar unit); short rows are packed R per
+// workgroup, whose lanes walk the R x W units of the block (the row index
+// from an exact float reciprocal). All loads and stores of x and grad_x are
+// raw buffer operations: a lane past the end gets an offset beyond the
+// buffer's range, where loads return zero without touching memory and stores
+// are dropped, so every batch issues the same instructions and the hardware
+// wait counts stay exact.
+#include "lse_device.h"
+#include "lse_launch.h"
+
+namespace lse {
+
+namespace {
+
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer resource, gfx9 data format
+constexpr int kOffFar = 0x7FFFFFF0;            // an offset past any buffer's range
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                             static_cast<int>(bytes), kRsrcWord3);
+}
+
+// One unit's grad: g * 2^((x - L) * log2 e) per element, packed back into the
+// element type (bf16 rounds to nearest even from fp32).
+template <DType D>
+__device__ __forceinline__ u32x4 grad_vec(u32x4 w, float lse, float g) {
+    float f[Elem<D>::kPerVec];
+    decode<D>(w, f);
+    float o[Elem<D>::kPerVec];
+#pragma unroll
+    for (int k = 0; k < Elem<D>::kPerVec; ++k) o[k] = g * exp2_hw((f[k] - lse) * kLog2e);
+    u32x4 r;
+    if constexpr (D == DType::F32) {
+        r = u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                  __float_as_uint(o[3])};
+    } else {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        unsigned p[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            p[k] = __builtin_bit_cast(unsigned, __builtin_convertvector(f2{o[2 * k], o[2 * k + 1]}, b2));
+        r = u32x4{p[0], p[1], p[2], p[3]};
+    }
+    return r;
+}
+
+template <DType D>
+__device__ __forceinline__ float grad_scalar(float x, float lse, float g) {
+    return g * exp2_hw((x - lse) * kLog2e);
+}
+
+template <DType D>
+__device__ __forceinline__ void store_scalar(char* p, float v) {
+    if constexpr (D == DType::F32) {
+        *reinterpret_cast<float*>(p) = v;
+    } else {
+        *reinterpret_cast<__bf16*>(p) = static_cast<__bf16>(v);
+    }
+}
+
+}  // namespace
+
+// VEC: units are 16-byte vectors (K elements); otherwise single elements.
+// ONE_ROW: the workgroup takes one chunk of one row (rows_per_wg == 1), so
+// the row's lse and grad_out are uniform; otherwise every unit loads its own
+// row's pair. Each instance issues the same loads in every batch.
+template <DType D, int BLOCK, int U, bool VEC, bool ONE_ROW>
+__global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, int64_t rows,
+                                                  int64_t cols, int64_t xs_bytes,
+                                                  const float* __restrict__ lse,
+                                                  const float* __restrict__ gout,
+                                                  char* __restrict__ gx, int64_t gs_bytes,
+                                                  int64_t rows_per_wg, int64_t chunks_per_row,
+                                                  int64_t chunk_units) {
+    constexpr int EB = Elem<D>::kBytes;
+    constexpr int K = VEC ? Elem<D>::kPerVec : 1;
+    constexpr int UB = VEC ? 16 : EB;  // bytes per unit
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const int64_t nunits = cols / K;
+    const int tail = VEC ? static_cast<int>(cols - nunits * K) : 0;
+
+    // This workgroup's block: rows [r0, r0 + nr), units [u0, u0 + W) of each.
+    int64_t r0, u0, W;
+    int nr;
+    if constexpr (ONE_ROW) {
+        r0 = b / chunks_per_row;
+        const int64_t chunk = b - r0 * chunks_per_row;
+        u0 = chunk * chunk_units;
+        W = nunits - u0 < chunk_units ? nunits - u0 : chunk_units;
+        nr = 1;
+    } else {
+        r0 = b * rows_per_wg;
+        nr = static_cast<int>(rows - r0 < rows_per_wg ? rows - r0 : rows_per_wg);
+        u0 = 0;
+        W = nunits;
+    }
+    const int n = static_cast<int>(nr * W);  // the planner keeps this below 2^22
+    // The block's bytes as one buffer each for x and grad_x (offsets are
+    // relative to the block's first unit; the planner keeps them below 2^31).
+    const char* xb = x + r0 * xs_bytes + u0 * UB;
+    char* gb = gx + r0 * gs_bytes + u0 * UB;
+    const int64_t xspan = (nr - 1) * xs_bytes + W * UB;
+    const int64_t gspan = (nr - 1) * gs_bytes + W * UB;
+    const auto xr = make_rsrc(xb, xspan);
+    const auto gr = make_rsrc(gb, gspan);
+    const float inv_w = 1.0f / static_cast<float>(W);
+
+    // uniform per-row scalars in the one-row case
+    float l0 = 0.0f, g0 = 0.0f;
+    if (ONE_ROW && n > 0) {
+        l0 = lse[r0];
+        g0 = gout[r0];
+    }
+
+    // Item j of the block: its row (local) and unit, as byte offsets.
+    auto offsets = [&](int j, int& rl, int& xo, int& go) {
+        const bool in = j < n;
+        rl = 0;
+        if constexpr (!ONE_ROW) {
+            // exact for j < 2^22: (j + 0.5) / W stays 0.5 / W away from integers
+            rl = static_cast<int>((static_cast<float>(j) + 0.5f) * inv_w);
+            rl = rl < nr ? rl : nr - 1;
+        }
+        const int u = j - rl * static_cast<int>(W);
+        xo = in ? static_cast<int>(rl * xs_bytes) + u * UB : kOffFar;
+        go = in ? static_cast<int>(rl * gs_bytes) + u * UB : kOffFar;
+    };
+
+    struct Batch {
+        u32x4 w[VEC ? U : 1];
+        float e[VEC ? 1 : U];
+        float l[U], g[U];
+        int go[U];
+    };
+    auto load_batch = [&](Batch& t, int j0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int rl, xo, go;
+            offsets(j0 + u * BLOCK, rl, xo, go);
+            t.go[u] = go;
+            if constexpr (VEC) {
+                t.w[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, 2));
+            } else if constexpr (D == DType::F32) {
+                t.e[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xo, 0, 2));
+            } else {
+                t.e[u] = __uint_as_float(
+                    static_cast<unsigned>(__builtin_amdgcn_raw_buffer_load_b16(xr, xo, 0, 2)) << 16);
+            }
+            if constexpr (!ONE_ROW) {
+                t.l[u] = lse[r0 + rl];
+                t.g[u] = gout[r0 + rl];
+            } else {
+                t.l[u] = l0;
+                t.g[u] = g0;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto store_batch = [&](const Batch& t) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (VEC) {
+                const u32x4 r = grad_vec<D>(t.w[u], t.l[u], t.g[u]);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, r), gr, t.go[u], 0, 2);
+            } else {
+                const float v = grad_scalar<D>(t.e[u], t.l[u], t.g[u]);
+                if constexpr (D == DType::F32)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), gr, t.go[u], 0, 2);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        __builtin_bit_cast(unsigned short, static_cast<__bf16>(v)), gr, t.go[u], 0, 2);
+            }
+        }
+    };
+
+    // Software-pipelined: the next batch's loads are issued before this
+    // batch is computed and stored.
+    const int per_batch = U * BLOCK;
+    const int nb = (n + per_batch - 1) / per_batch;
+    if (nb > 0) {
+        Batch ta, tb;
+        load_batch(ta, tid);
+        int k = 0;
+        for (; k + 2 <= nb - 1; k += 2) {
+            load_batch(tb, (k + 1) * per_batch + tid);
+            store_batch(ta);
+            load_batch(ta, (k + 2) * per_batch + tid);
+            store_batch(tb);
+        }
+        if (k + 1 <= nb - 1) {
+            load_batch(tb, (k + 1) * per_batch + tid);
+            store_batch(ta);
+            store_batch(tb);
+        } else {
+            store_batch(ta);
+        }
+    }
+
+    // The last cols % K elements of each row (vector units only): the row's
+    // last chunk in the one-row case, every row of the block otherwise.
+    if constexpr (VEC) {
+        if (tail > 0 && (!ONE_ROW || u0 + W == nunits)) {
+            for (int i = tid; i < nr * tail; i += BLOCK) {
+                const int rl = i / tail;
+                const int e = i - rl * tail;
+                const int64_t row = r0 + rl;
+                const int64_t col = nunits * K + e;
+                const float xv = load_scalar<D>(x + row * xs_bytes + col * EB);
+                store_scalar<D>(gx + row * gs_bytes + col * EB,
+                                grad_scalar<D>(xv, lse[row], gout[row]));
+            }
+        }
+    }
+}
+
+namespace {
+
+template <DType D, bool VEC, bool ONE_ROW>
+hipError_t launch_grad_k(const GradArgs& a) {
+    constexpr int BLOCK = 256, U = 4;
+    hipLaunchKernelGGL((lse_grad<D, BLOCK, U, VEC, ONE_ROW>), dim3(a.grid), dim3(BLOCK), 0,
+                       a.stream, a.x, a.rows, a.cols, a.xs_bytes, a.lse, a.grad_out, a.grad_x,
+                       a.gs_bytes, a.rows_per_wg, a.chunks_per_row, a.chunk_units);
+    return hipGetLastError();
+}
+
+template <DType D, bool VEC>
+hipError_t launch_grad_d(const GradArgs& a) {
+    return a.rows_per_wg == 1 ? launch_grad_k<D, VEC, true>(a) : launch_grad_k<D, VEC, false>(a);
+}
+
+}  // namespace
+
+hipError_t launch_grad(const GradArgs& a) {
+    if (a.grid <= 0) return hipSuccess;
+    if (a.bf16) return a.vector_units ? launch_grad_d<DType::BF16, true>(a)
+                                      : launch_grad_d<DType::BF16, false>(a);
+    return a.vector_units ? launch_grad_d<DType::F32, true>(a) : launch_grad_d<DType::F32, false>(a);
+}
+
+}  // namespace lse

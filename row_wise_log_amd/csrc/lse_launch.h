@@ -37,4 +37,23 @@ struct LaunchArgs {
 // Launches the kernel the plan names; returns hipGetLastError() after it.
 hipError_t launch(const LaunchArgs& a);
 
+// The backward pass, grad_x = grad_out * exp(x - lse) (lse_backward.hip).
+struct GradArgs {
+    bool bf16;
+    bool vector_units;     // 16-byte units (every row of x and grad_x 16-byte aligned)
+    int64_t grid;
+    int64_t rows_per_wg;   // 1: a workgroup takes one chunk of one row
+    int64_t chunks_per_row;
+    int64_t chunk_units;   // units per chunk (rows_per_wg == 1)
+    const char* x;
+    int64_t rows, cols;
+    int64_t xs_bytes, gs_bytes;  // bytes between row starts of x and of grad_x
+    const float* lse;
+    const float* grad_out;
+    char* grad_x;
+    hipStream_t stream;
+};
+
+hipError_t launch_grad(const GradArgs& a);
+
 }  // namespace lse

@@ -137,3 +137,76 @@ def compare_logp(got: np.ndarray, ref: np.ndarray, ref_lse: np.ndarray, dtype: s
                                  f"want {ref[fin][worst]!r} ({ratio[worst]:.2f} x tol)")
     return float(ratio.max())
 
+
+def gpu_backward(torch, handle, x: np.ndarray, lse: np.ndarray, g: np.ndarray, dtype: str,
+                 pad_front: int = 0, grad_pad: int = 0, grad_front: int = 0):
+    """Run lse_backward on a host array; returns (grad as float32 rows x cols,
+    untouched) where untouched says every element outside the grad rows kept its
+    sentinel. grad_pad elements pad each grad row; grad_front elements precede it."""
+    rows, cols = x.shape
+    t, ptr, stride = upload(torch, x, pad_front)
+    lt = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to("cuda")
+    gt = torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to("cuda")
+    gstride = cols + grad_pad
+    total = grad_front + (rows - 1) * gstride + cols + 64 if rows else 64
+    sentinel = 0x7F7F if dtype == "bf16" else 0x7F7F7F7F
+    store = torch.int16 if dtype == "bf16" else torch.int32
+    buf = torch.full((total,), sentinel if dtype != "bf16" else 0x7F7F, dtype=store, device="cuda")
+    esz = ESIZE[dtype]
+    B.lse_backward(handle, ptr, DTYPE_CODE[dtype], rows, cols, stride, lt.data_ptr(), gt.data_ptr(),
+                   buf.data_ptr() + grad_front * esz, gstride,
+                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    del t, lt, gt, buf
+    host = host.view(np.uint16) if dtype == "bf16" else host.view(np.uint32)
+    want_sentinel = np.uint16(0x7F7F) if dtype == "bf16" else np.uint32(0x7F7F7F7F)
+    if gstride == cols:  # the rows are one contiguous block
+        n = rows * cols
+        untouched = bool(np.all(host[:grad_front] == want_sentinel) and
+                         np.all(host[grad_front + n:] == want_sentinel))
+        vals = host[grad_front:grad_front + n].reshape(rows, cols)
+    else:
+        mask = np.zeros(total, dtype=bool)
+        idx = grad_front + np.arange(rows)[:, None] * gstride + np.arange(cols)[None, :]
+        mask[idx.ravel()] = True
+        untouched = bool(np.all(host[~mask] == want_sentinel))
+        vals = host[idx]
+    if dtype == "bf16":
+        out = (vals.astype(np.uint32) << 16).view(np.float32)
+    else:
+        out = np.ascontiguousarray(vals).view(np.float32)
+    return out, untouched
+
+
+def compare_grad(got: np.ndarray, ref: np.ndarray, d: np.ndarray, g: np.ndarray, dtype: str,
+                 what: str) -> float:
+    """The backward rule: NaN and +-inf exactly; otherwise
+    |got - ref| <= (rel + 2e-7 |x - lse|) |ref| + 2^-125 max(1, |g|), rel = 4e-7 for
+    fp32 output (roundings of x - lse and of the log2(e) scaling, v_exp_f32's ulp, the
+    multiply) and 2^-8 + 1e-6 for bf16 output (one rounding to 8 significant bits,
+    at most 2^-8 relative, on top of the fp32 value's error)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, what
+    nan = np.isnan(ref)
+    bad = nan & ~np.isnan(got)
+    assert not bad.any(), f"{what}: {np.argwhere(bad)[:4].tolist()} want NaN, got {got[bad][:4]}"
+    inf = np.isinf(ref)
+    bad = inf & (got != ref)
+    assert not bad.any(), f"{what}: {np.argwhere(bad)[:4].tolist()} want {ref[bad][:4]}, got {got[bad][:4]}"
+    fin = ~nan & ~inf
+    if not fin.any():
+        return 0.0
+    rel = 2.0 ** -8 + 1e-6 if dtype == "bf16" else 4e-7
+    dd = np.where(np.isfinite(d), np.abs(d), 0.0)
+    gg = np.broadcast_to(np.maximum(1.0, np.abs(np.asarray(g, np.float64)))[:, None], ref.shape)
+    tol = (rel + 2e-7 * dd[fin]) * np.abs(ref[fin]) + 2.0 ** -125 * gg[fin]
+    err = np.abs(got[fin] - ref[fin])
+    assert np.all(np.isfinite(got[fin])), f"{what}: non-finite grad for a finite reference"
+    ratio = err / tol
+    worst = int(np.argmax(ratio))
+    assert ratio[worst] <= 1.0, (f"{what}: element {np.argwhere(fin)[worst].tolist()} got "
+                                 f"{got[fin][worst]!r} want {ref[fin][worst]!r} ({ratio[worst]:.2f} x tol)")
+    return float(ratio.max())
+

@@ -334,6 +334,115 @@ def pin_logprob_argument_checks(orc):
     assert fn(None, 0, 0, 4, 4, None, None, 1) == 0, "rows = 0 must be a no-op"
 
 
+# --- backward: the gradient of LSE ---------------------------------------
+#
+# d LSE(x) / d x_j = exp(x_j - LSE(x)), the row's softmax (backward support,
+# Table 3). The oracle takes the forward value as fp32 (lse32), so the exact
+# result is g * exp(x_j - L) * exp(L - lse32) with L the exact LSE; the
+# factor exp(L - lse32) is computed here from the brute-force L.
+
+def _fd_softmax(vals, j, h=1e-4):
+    """d LSE / d x_j by a central difference of the brute-force LSE."""
+    up = list(vals)
+    dn = list(vals)
+    up[j] += h
+    dn[j] -= h
+    return (brute_lse(up) - brute_lse(dn)) / (2 * h)
+
+
+def pin_grad_finite_difference(orc):
+    """The backward pass is the derivative of LSE: central differences of the
+    brute-force LSE, element by element, and the softmax sums to one."""
+    rng = np.random.default_rng(16)
+    for cols in (1, 2, 3, 7, 20):
+        x = rng.uniform(-20, 20, size=(4, cols + 2)).astype(np.float32)[:, :cols]
+        vals = [[float(v) for v in row] for row in x]
+        exact = [brute_lse(v) for v in vals]
+        lse32 = np.array(exact, dtype=np.float32)
+        g = np.array([1.0, -2.5, 0.125, 3.0], dtype=np.float32)
+        got = orc.softmax_grad(x, lse32, g, "f32")
+        for r in range(4):
+            corr = math.exp(exact[r] - float(lse32[r]))
+            for j in range(cols):
+                want = float(g[r]) * _fd_softmax(vals[r], j) * corr
+                assert abs(got[r, j] - want) <= 1e-7 * abs(float(g[r])) + 1e-7 * abs(want), \
+                    f"finite difference r={r} j={j}: {got[r, j]!r} vs {want!r}"
+            s = math.fsum(got[r])
+            assert abs(s - float(g[r]) * corr) <= 1e-13 * max(1.0, abs(float(g[r]))), \
+                f"softmax sum r={r}: {s!r}"
+
+
+def pin_grad_two_elements(orc):
+    """Two-element rows: the softmax of (a, b) against the base-2 pairwise form (§A.1)."""
+    rng = np.random.default_rng(17)
+    x = rng.uniform(-30, 30, size=(20, 2)).astype(np.float32)
+    pl = [pair_lse(float(a), float(b)) for a, b in x]
+    lse32 = np.array(pl, dtype=np.float32)
+    g = np.full(20, 1.5, dtype=np.float32)
+    got = orc.softmax_grad(x, lse32, g, "f32")
+    for r in range(20):
+        for j in range(2):
+            want = 1.5 * math.exp(float(x[r, j]) - pl[r]) * math.exp(pl[r] - float(lse32[r]))
+            _close(got[r, j], want, 1e-14, f"pair grad r={r} j={j}")
+
+
+def pin_grad_constant_rows(orc):
+    """A constant row of N gives g / N in every column (with lse = c + ln N exactly)."""
+    for n in (1, 2, 4, 64, 1024):
+        c = 3.0
+        lse = c + math.log(n)
+        x = np.full((2, n), c, dtype=np.float32)
+        lse32 = np.full(2, lse, dtype=np.float32)
+        got = orc.softmax_grad(x, lse32, [2.0, -1.0], "f32")
+        corr = math.exp(lse - float(lse32[0]))
+        for r, g in enumerate((2.0, -1.0)):
+            for j in (0, n - 1):
+                _close(got[r, j], g / n * corr, 1e-14, f"const grad N={n}")
+
+
+def pin_grad_brute_force_bf16(orc):
+    """bf16 rows decoded with struct, against fsum-based LSE and exp."""
+    rng = np.random.default_rng(18)
+    bits = rng.integers(0x3F00, 0x4200, size=(5, 9)).astype(np.uint16)   # 0.5 .. 32
+    bits[1::2] |= 0x8000
+    vals = [[_bf16_value(b) for b in row] for row in bits]
+    exact = [brute_lse(v) for v in vals]
+    lse32 = np.array(exact, dtype=np.float32)
+    got = orc.softmax_grad(bits, lse32, np.ones(5, np.float32), "bf16")
+    for r in range(5):
+        corr = math.exp(exact[r] - float(lse32[r]))
+        for j in range(9):
+            want = _fd_softmax(vals[r], j) * corr
+            assert abs(got[r, j] - want) <= 1e-7 * (1 + abs(want)), f"bf16 grad r={r} j={j}"
+
+
+def pin_grad_special_values(orc):
+    """IEEE arithmetic on grad_out * exp(x - lse)."""
+    inf, nan = math.inf, math.nan
+    x = np.array([[-inf, -inf], [-inf, 0.0], [inf, 0.0], [nan, 0.0], [1.0, 2.0]],
+                 dtype=np.float32)
+    lse = np.array([-inf, 0.0, inf, nan, 0.0], dtype=np.float32)
+    g = np.array([1.0, 1.0, 1.0, 1.0, 0.0], dtype=np.float32)
+    got = orc.softmax_grad(x, lse, g, "f32")
+    assert np.isnan(got[0]).all(), "all -inf row: -inf - -inf"
+    assert got[1, 0] == 0.0 and got[1, 1] == 1.0, "a -inf element gets 0"
+    assert np.isnan(got[2, 0]) and got[2, 1] == 0.0, "+inf at lse +inf: NaN and 0"
+    assert np.isnan(got[3]).all(), "NaN lse"
+    assert np.all(got[4] == 0.0), "zero incoming gradient"
+    got = orc.softmax_grad(np.zeros((3, 0), np.float32), np.zeros(3), np.ones(3), "f32")
+    assert got.shape == (3, 0)
+
+
+def pin_grad_argument_checks(orc):
+    x = np.zeros((4, 4), np.float32)
+    out = np.empty((4, 4))
+    lse = np.zeros(4, np.float32)
+    fn = orc._fn_grad
+    assert fn(x.ctypes.data, 0, 4, 4, 4, None, lse.ctypes.data, out.ctypes.data, 1) == -1
+    assert fn(x.ctypes.data, 0, 4, 4, 4, lse.ctypes.data, None, out.ctypes.data, 1) == -1
+    assert fn(x.ctypes.data, 0, 4, 4, 3, lse.ctypes.data, lse.ctypes.data, out.ctypes.data, 1) == -1
+
+
 def _close_all(got, want, rel, what):
     assert got.shape == want.shape, f"{what}: shape"
     for i, (g, w) in enumerate(zip(got, want)):
@@ -357,4 +466,10 @@ CHEAP_PINS = [
     pin_logprob_brute_force,
     pin_logprob_special_values,
     pin_logprob_shift_invariance,
+    pin_grad_argument_checks,
+    pin_grad_finite_difference,
+    pin_grad_two_elements,
+    pin_grad_constant_rows,
+    pin_grad_brute_force_bf16,
+    pin_grad_special_values,
 ]

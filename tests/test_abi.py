@@ -119,6 +119,27 @@ def test_token_logprob_argument_checks(lib, args, status):
                                       lse) == status
 
 
+@pytest.mark.parametrize("args, status", [
+    # (x, dtype, rows, cols, row_stride, lse, grad_out, grad_x, grad_row_stride), NULL handle
+    ((16, 7, 4, 4, 4, 64, 64, 128, 4), B.LSE_ERR_UNSUPPORTED_DTYPE),
+    ((16, F32, -1, 4, 4, 64, 64, 128, 4), B.LSE_ERR_INVALID_ARG),
+    ((16, F32, 4, 8, 7, 64, 64, 128, 8), B.LSE_ERR_INVALID_ARG),      # x stride < cols
+    ((16, F32, 4, 8, 8, 64, 64, 128, 7), B.LSE_ERR_INVALID_ARG),      # grad stride < cols
+    ((16, F32, 4, 8, 8, 64, 64, 128, 1 << 62), B.LSE_ERR_INVALID_ARG),  # grad offsets overflow
+    ((16, F32, 4, 4, 4, None, 64, 128, 4), B.LSE_ERR_INVALID_ARG),    # NULL lse
+    ((16, F32, 4, 4, 4, 64, None, 128, 4), B.LSE_ERR_INVALID_ARG),    # NULL grad_out
+    ((16, F32, 4, 4, 4, 64, 64, None, 4), B.LSE_ERR_INVALID_ARG),     # NULL grad_x
+    ((16, F32, 4, 4, 4, 66, 64, 128, 4), B.LSE_ERR_INVALID_ARG),      # lse misaligned
+    ((16, F32, 4, 4, 4, 64, 66, 128, 4), B.LSE_ERR_INVALID_ARG),      # grad_out misaligned
+    ((16, F32, 4, 4, 4, 64, 64, 130, 4), B.LSE_ERR_INVALID_ARG),      # fp32 grad_x misaligned
+    ((16, BF16, 4, 4, 4, 64, 64, 129, 4), B.LSE_ERR_INVALID_ARG),     # bf16 grad_x misaligned
+    ((16, F32, 4, 4, 4, 64, 64, 128, 4), B.LSE_ERR_INVALID_ARG),      # all fine but the handle
+    ((None, F32, 0, 4, 4, None, None, None, 4), B.LSE_ERR_INVALID_ARG),  # rows = 0 needs a handle
+])
+def test_backward_argument_checks(lib, args, status):
+    assert B.lse_backward_status(None, *args) == status
+
+
 def test_forward_accepts_stride_below_cols_for_one_row(lib):
     # one row: row_stride is ignored, so only the handle is wrong
     assert B.lse_forward_status(None, 16, F32, 1, 8, 0, 16) == B.LSE_ERR_INVALID_ARG

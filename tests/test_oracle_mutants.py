@@ -39,6 +39,16 @@ MUTANTS = {
                               "return -lse_one_row(x, dtype, start, cols);"),
     "logprob_out_of_range_zero": ("if (t < 0 || t >= cols)\n        return NAN;",
                                   "if (t < 0 || t >= cols)\n        return 0.0;"),
+    "grad_sign": ("out[j] = grad_out * exp(load_elem(x, dtype, start + j) - lse);",
+                  "out[j] = grad_out * exp(lse - load_elem(x, dtype, start + j));"),
+    "grad_drops_grad_out": ("out[j] = grad_out * exp(load_elem(x, dtype, start + j) - lse);",
+                            "out[j] = exp(load_elem(x, dtype, start + j) - lse);"),
+    "grad_exp2": ("out[j] = grad_out * exp(load_elem(", "out[j] = grad_out * exp2(load_elem("),
+    "grad_wrong_row_lse": ("(double)jb->lse[r], (double)jb->grad_out[r],",
+                           "(double)jb->lse[r == jb->row_begin ? r : r - 1], (double)jb->grad_out[r],"),
+    "grad_column_shift": ("exp(load_elem(x, dtype, start + j) - lse)",
+                          "exp(load_elem(x, dtype, start + (j + 1) % cols) - lse)"),
+    "grad_every_row_into_row0": ("jb->out + r * jb->cols);", "jb->out);"),
     "logprob_wrong_row_target": ("jb->targets[r]);", "jb->targets[r == jb->row_begin ? r : r - 1]);"),
     "nan_not_checked_with_inf": ("if (m == INFINITY)\n        return INFINITY;",
                                  "if (m == INFINITY && 0)\n        return INFINITY;"),
