@@ -34,6 +34,7 @@ import workloads  # noqa: E402
 
 METRIC = "LSE input GB/s (% of HBM peak) at [512,128256] bf16; µs/call small shapes"
 METRIC_LOGPROB = "token log-prob input GB/s (x plus int64 targets) at the workload's shape"
+METRIC_DIM = "LSE over the first axis input GB/s (outer 1, n rows, inner cols) at the workload's shape"
 METRIC_BACKWARD = ("LSE backward input GB/s (x, lse, grad_out read; grad_x written) at the "
                    "workload's shape")
 HBM_PEAK_GBS = 8000.0
@@ -108,13 +109,18 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
         rotate = max(1, -(-2 * CACHE_BYTES // in_bytes) + 1)
     host = torch.from_numpy(w.x.view(np.int16) if w.dtype == "bf16" else w.x)
     bufs = [host.to("cuda") for _ in range(rotate)]
-    out = torch.empty(rows, dtype=torch.float32, device="cuda")
+    out = torch.empty(cols if op == "dim" else rows, dtype=torch.float32, device="cuda")
+    if op == "dim":
+        out_bytes = cols * 4
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     plan = B.lse_plan(dtype_code, rows, cols, cols, bufs[0].data_ptr(), 256, 0)
 
     def step(i):
-        if bwd is not None:
+        if op == "dim":
+            B.lse_forward_dim(handle, bufs[i % rotate].data_ptr(), dtype_code, 1, rows, cols,
+                              out.data_ptr(), sh)
+        elif bwd is not None:
             B.lse_backward(handle, bufs[i % rotate].data_ptr(), dtype_code, rows, cols, cols,
                            bwd["lse"].data_ptr(), bwd["g"].data_ptr(), bwd["grad"].data_ptr(),
                            cols, sh)
@@ -211,7 +217,9 @@ def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0, op: str = "lse")
     t0 = time.perf_counter()
     ref = None
     while True:
-        if tg is None:
+        if op == "dim":
+            r = oracle.lse_dim(w.x.reshape(1, w.rows, w.cols), w.dtype, threads=threads).ravel()
+        elif tg is None:
             r = orc.lse(w.x, w.dtype, threads=threads)
         else:
             r = orc.token_logprob(w.x, tg, w.dtype, threads=threads)
@@ -235,6 +243,7 @@ def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0, op: str = "lse")
             "sample": (f"the whole {w.rows}x{w.cols} {w.dtype} input, {passes} passes in "
                        f"{el:.1f} s wall on {threads} threads (float64 two-pass max-subtract, "
                        "libm exp/log" + (", minus the target element" if tg is not None else "")
+                       + (", over the first axis of a transposed copy" if op == "dim" else "")
                        + ")")}
 
 
@@ -250,10 +259,10 @@ def main() -> int:
     ap.add_argument("--all-out", default="gpurun_out/bench_all.jsonl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--op", choices=["lse", "logprob", "backward"], default="lse",
+    ap.add_argument("--op", choices=["lse", "logprob", "backward", "dim"], default="lse",
                     help="lse: lse_forward (the headline); logprob: lse_token_logprob with one "
                          "seeded int64 target per row; backward: lse_backward (reads x, writes "
-                         "grad_x)")
+                         "grad_x); dim: lse_forward_dim over the workload's first axis")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run three plain device copies of BYTES bytes (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -288,7 +297,8 @@ def main() -> int:
         w = r["w"]
         traffic = recorded_traffic(args.config) if args.op == "lse" else None
         line = {
-            "metric": {"lse": METRIC, "logprob": METRIC_LOGPROB, "backward": METRIC_BACKWARD}[args.op],
+            "metric": {"lse": METRIC, "logprob": METRIC_LOGPROB, "backward": METRIC_BACKWARD,
+                       "dim": METRIC_DIM}[args.op],
             "value": round(r["value_gbs"], 1),
             "unit": "GB/s",
             "n_gpus": 1,
@@ -306,7 +316,7 @@ def main() -> int:
                 "op": args.op,
                 "input_bytes": r["in_bytes"], "output_bytes": r["out_bytes"],
                 "rotating_copies": r["rotate"],
-                "plan": plan_name(r["plan"]) if args.op != "backward" else "lse_backward",
+                "plan": plan_name(r["plan"]) if args.op in ("lse", "logprob") else f"lse_{args.op}",
                 "pct_of_hbm_peak": round(100 * r["value_gbs"] / HBM_PEAK_GBS, 2),
                 "us_per_call": round(r["ms_per_step"] * 1e3, 2),
                 "rows_per_s": round(w.rows / (r["ms_per_step"] * 1e-3), 1),
@@ -330,8 +340,8 @@ def main() -> int:
                     rc = r if cfg == args.config else time_config(
                         torch, B, handle, cfg, args.steps, args.warmup, None, args.op)
                     rec = {"config": cfg, "op": args.op, "workload": rc["w"].spec.name,
-                           "plan": plan_name(rc["plan"]) if args.op != "backward"
-                           else "lse_backward",
+                           "plan": plan_name(rc["plan"]) if args.op in ("lse", "logprob")
+                           else f"lse_{args.op}",
                            "input_GBs": round(rc["value_gbs"], 1),
                            "pct_hbm_peak": round(100 * rc["value_gbs"] / HBM_PEAK_GBS, 2),
                            "us_per_call": round(rc["ms_per_step"] * 1e3, 2),

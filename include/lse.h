@@ -77,9 +77,10 @@ typedef enum {
 
 /*
  * Create a handle on HIP device `device` (an index as for hipSetDevice).
- * Queries the compute-unit count, allocates and zeroes the split-row
- * workspace (LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS (max, sum) pairs plus
- * one counter per row, about 0.5 MiB), and synchronises once. On success
+ * Queries the compute-unit count, allocates the split-row workspace
+ * (LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS (max, sum) pairs plus one
+ * counter per row, about 0.5 MiB, the counters zeroed) and lse_forward_dim's
+ * workspace (LSE_DIM_MAX_PAIRS pairs, 32 MiB), and synchronises once. On success
  * *out receives the handle; on failure *out is set to NULL.
  * Errors: INVALID_ARG (out NULL, device out of range), NO_DEVICE (no device
  * or not gfx950), ALLOC, HIP.
@@ -163,6 +164,30 @@ lse_status_t lse_backward(lse_handle_t h, const void *x, lse_dtype_t dtype,
                           const float *lse, const float *grad_out, void *grad_x,
                           int64_t grad_row_stride, hipStream_t stream);
 
+/*
+ * LSE over the middle axis of a contiguous [outer, n, inner] array:
+ *
+ *     out[o * inner + i] = log( sum_{j < n} exp(x[(o * n + j) * inner + i]) ),
+ *
+ * which is torch.logsumexp(x, dim=d) for a contiguous x, with outer the
+ * product of the sizes before d, n the size of d and inner the product of
+ * the sizes after it; the paper offers its kernels as drop-in replacements
+ * for torch.logsumexp (abstract, §6). inner == 1 is lse_forward over rows of
+ * n. Same accuracy, special values and stream semantics as lse_forward.
+ *   x      device pointer, aligned to its element size.
+ *   outer, n, inner  >= 0; n < 2^31; outer * inner < 2^40 and the element
+ *          count must fit in int64.
+ *   out    device pointer to outer * inner fp32 values, 4-byte aligned, not
+ *          overlapping x. n == 0 writes -inf.
+ * Uses the handle's workspace when there are too few outputs to fill the GPU
+ * (so, like lse_forward, calls sharing a handle must not run concurrently).
+ * Errors: UNSUPPORTED_DTYPE; INVALID_ARG (sizes, NULL or misaligned
+ * pointers with work to do, NULL handle); HIP.
+ */
+lse_status_t lse_forward_dim(lse_handle_t h, const void *x, lse_dtype_t dtype,
+                             int64_t outer, int64_t n, int64_t inner, float *out,
+                             hipStream_t stream);
+
 /* Release the handle and its workspace. NULL is allowed and returns LSE_OK.
  * The caller must ensure no work using the handle is still pending. */
 lse_status_t lse_destroy(lse_handle_t h);
@@ -202,6 +227,9 @@ typedef struct {
 /* Capacity of a handle's split-row workspace. */
 #define LSE_SPLIT_MAX_ROWS 1024
 #define LSE_SPLIT_MAX_PARTS 64
+/* Capacity, in (max, sum) pairs (8 bytes each, 32 MiB), of a handle's
+ * workspace for lse_forward_dim's split of the reduced axis. */
+#define LSE_DIM_MAX_PAIRS (1 << 22)
 
 /*
  * The launch plan lse_forward would use, computed on the host with no HIP

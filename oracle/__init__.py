@@ -10,7 +10,10 @@ in float64, computed by ``lse_oracle.c`` (plain two-pass max-subtract with
 libm ``exp``/``log``; its header states the definition and the special
 cases). ``token_logprob(x, targets, dtype)`` returns x[r, targets[r]] minus
 that LSE (NaN for a target outside [0, cols)); ``softmax_grad(x, lse, g,
-dtype)`` returns the backward pass g[r] * exp(x[r, j] - lse[r]) in float64.
+dtype)`` returns the backward pass g[r] * exp(x[r, j] - lse[r]) in float64;
+``lse_dim(x3, dtype)`` reduces the middle axis of an [outer, n, inner] array
+(torch.logsumexp over a non-last axis) by moving that axis last and calling
+the row oracle.
 bf16 inputs are passed as uint16 bit patterns.
 """
 from __future__ import annotations
@@ -167,3 +170,20 @@ def token_logprob(x: np.ndarray, targets, dtype: str | None = None, threads: int
 def softmax_grad(x: np.ndarray, lse, grad_out, dtype: str | None = None,
                  threads: int = 1) -> np.ndarray:
     return default().softmax_grad(x, lse, grad_out, dtype, threads)
+
+
+def lse_dim(x3: np.ndarray, dtype: str | None = None, threads: int = 1) -> np.ndarray:
+    """LSE over the middle axis of an [outer, n, inner] array, float64 [outer, inner].
+
+    The plain definition: the same log-sum-exp, over a different axis. The
+    reduced axis is moved last (a transposed copy) and each (o, i) is one row
+    of the row oracle. The paper presents its kernels as drop-in replacements
+    for torch.logsumexp, whose `dim` may be any axis (abstract, §6).
+    """
+    x3 = np.asarray(x3)
+    if x3.ndim != 3:
+        raise ValueError("x3 must be 3-D [outer, n, inner]")
+    outer, n, inner = x3.shape
+    rows = np.ascontiguousarray(np.transpose(x3, (0, 2, 1))).reshape(outer * inner, n)
+    return default().lse(rows, dtype, threads).reshape(outer, inner)
+

@@ -1,7 +1,8 @@
 """Row-wise log-sum-exp on MI355X (gfx950): a C-ABI HIP library and its binding.
 
 ``logsumexp(x)`` returns log(sum(exp(x), dim=-1)) in fp32 for a 2-D fp32 or
-bf16 CUDA/HIP tensor whose last axis is contiguous; ``token_logprob(x, t)``
+bf16 CUDA/HIP tensor whose last axis is contiguous; ``logsumexp_dim(x, d)``
+reduces any axis of a contiguous tensor; ``token_logprob(x, t)``
 returns x[r, t[r]] - logsumexp(x)[r] from the same single pass. PyTorch only
 provides the device memory and the current stream; the computation is the HIP
 library's ``lse_forward`` / ``lse_token_logprob`` (see include/lse.h). The
@@ -42,6 +43,34 @@ def _check_input(x):
     if cols > 1 and x.stride(1) != 1:
         raise ValueError("the last axis must be contiguous")
     return codes[x.dtype], rows, cols, (x.stride(0) if rows > 1 else cols)
+
+
+def logsumexp_dim(x, dim: int, handle_=None):
+    """LSE over axis `dim` of a contiguous fp32/bf16 GPU tensor of any rank,
+    as fp32 with that axis removed (torch.logsumexp(x, dim) semantics)."""
+    import torch
+
+    from .binding import LSE_DTYPE_BF16, LSE_DTYPE_F32, lse_forward_dim
+
+    codes = {torch.float32: LSE_DTYPE_F32, torch.bfloat16: LSE_DTYPE_BF16}
+    if x.dtype not in codes:
+        raise TypeError(f"unsupported dtype {x.dtype}: fp32 or bf16")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous GPU tensor")
+    d = dim % x.dim()
+    shape = list(x.shape)
+    outer = 1
+    for s in shape[:d]:
+        outer *= s
+    inner = 1
+    for s in shape[d + 1:]:
+        inner *= s
+    out = torch.empty(shape[:d] + shape[d + 1:], dtype=torch.float32, device=x.device)
+    h = handle_ if handle_ is not None else handle(x.device.index or 0)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    lse_forward_dim(h, x.data_ptr(), codes[x.dtype], outer, shape[d], inner, out.data_ptr(),
+                    stream)
+    return out
 
 
 def logsumexp(x, out=None, handle_=None):

@@ -31,8 +31,8 @@ SCHEDULES = {"auto": 0, "rows_per_wave": 1, "row_per_wg": 2, "split_row": 3}
 LSE_SPLIT_MAX_ROWS = 1024
 LSE_SPLIT_MAX_PARTS = 64
 
-EXPORTS = ["lse_create", "lse_forward", "lse_token_logprob", "lse_backward", "lse_destroy",
-           "lse_status_string", "lse_set_schedule", "lse_set_tuning", "lse_plan"]
+EXPORTS = ["lse_create", "lse_forward", "lse_forward_dim", "lse_token_logprob", "lse_backward",
+           "lse_destroy", "lse_status_string", "lse_set_schedule", "lse_set_tuning", "lse_plan"]
 
 
 class LseError(RuntimeError):
@@ -71,6 +71,7 @@ def load(path: Path | str = LIBRARY) -> ctypes.CDLL:
         "lse_forward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp]),
         "lse_token_logprob": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]),
         "lse_backward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, i64, vp]),
+        "lse_forward_dim": (i32, [vp, vp, i32, i64, i64, i64, vp, vp]),
         "lse_destroy": (i32, [vp]),
         "lse_status_string": (ctypes.c_char_p, [i32]),
         "lse_set_schedule": (i32, [vp, i32]),
@@ -145,6 +146,17 @@ def lse_backward_status(handle, x_ptr, dtype, rows, cols, row_stride, lse_ptr, g
     """lse_backward returning the raw status instead of raising (for argument tests)."""
     return load().lse_backward(handle, x_ptr, dtype, rows, cols, row_stride, lse_ptr,
                                grad_out_ptr, grad_x_ptr, grad_row_stride, stream)
+
+
+def lse_forward_dim(handle: int, x_ptr: int, dtype: int, outer: int, n: int, inner: int,
+                    out_ptr: int, stream: int | None = None) -> None:
+    _check(load().lse_forward_dim(handle, x_ptr, dtype, outer, n, inner, out_ptr, stream),
+           "lse_forward_dim")
+
+
+def lse_forward_dim_status(handle, x_ptr, dtype, outer, n, inner, out_ptr, stream=None) -> int:
+    """lse_forward_dim returning the raw status instead of raising (for argument tests)."""
+    return load().lse_forward_dim(handle, x_ptr, dtype, outer, n, inner, out_ptr, stream)
 
 
 def lse_set_schedule(handle: int, schedule: int | str) -> None:

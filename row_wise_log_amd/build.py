@@ -19,7 +19,8 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIBRARY = PKG / "liblse_amd.so"
-SOURCES = [CSRC / "lse_kernels.hip", CSRC / "lse_backward.hip", CSRC / "lse_api.cpp"]
+SOURCES = [CSRC / "lse_kernels.hip", CSRC / "lse_backward.hip", CSRC / "lse_dim.hip",
+           CSRC / "lse_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -20,6 +20,7 @@ struct lse_handle_s {
     int n_cu;
     unsigned* ws_pairs;  // LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS (max, sum) pairs
     unsigned* counters;  // LSE_SPLIT_MAX_ROWS arrival counters, zero between calls
+    unsigned* dim_pairs; // LSE_DIM_MAX_PAIRS (max, sum) pairs for lse_forward_dim's split
     int schedule;        // lse_schedule_t forced for later calls (AUTO = by shape)
     int block, unroll, parts, waves_per_cu, lanes_per_row;  // tuning overrides, 0 = planner default
 };
@@ -269,12 +270,15 @@ lse_status_t lse_create(lse_handle_t* out, int device) {
         h->n_cu = prop.multiProcessorCount;
         const size_t pair_bytes = size_t{LSE_SPLIT_MAX_ROWS} * LSE_SPLIT_MAX_PARTS * 8;
         const size_t count_bytes = size_t{LSE_SPLIT_MAX_ROWS} * 4;
+        const size_t dim_bytes = size_t{LSE_DIM_MAX_PAIRS} * 8;
         void* mem = nullptr;
-        if (hipMalloc(&mem, pair_bytes + count_bytes) != hipSuccess) {
+        if (hipMalloc(&mem, pair_bytes + count_bytes + dim_bytes) != hipSuccess) {
             st = LSE_ERR_ALLOC;
         } else {
             h->ws_pairs = static_cast<unsigned*>(mem);
             h->counters = reinterpret_cast<unsigned*>(static_cast<char*>(mem) + pair_bytes);
+            h->dim_pairs = reinterpret_cast<unsigned*>(static_cast<char*>(mem) + pair_bytes +
+                                                       count_bytes);
             if (hipMemset(h->counters, 0, count_bytes) != hipSuccess ||
                 hipDeviceSynchronize() != hipSuccess)
                 st = LSE_ERR_HIP;
@@ -443,6 +447,72 @@ lse_status_t lse_backward(lse_handle_t h, const void* x, lse_dtype_t dtype, int6
     if (hipGetDevice(&prev) != hipSuccess) return LSE_ERR_HIP;
     if (prev != h->device && hipSetDevice(h->device) != hipSuccess) return LSE_ERR_HIP;
     const hipError_t err = lse::launch_grad(a);
+    if (prev != h->device) (void)hipSetDevice(prev);
+    return err == hipSuccess ? LSE_OK : LSE_ERR_HIP;
+}
+
+lse_status_t lse_forward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t outer,
+                             int64_t n, int64_t inner, float* out, hipStream_t stream) {
+    if (dtype != LSE_DTYPE_F32 && dtype != LSE_DTYPE_BF16) return LSE_ERR_UNSUPPORTED_DTYPE;
+    const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
+    if (outer < 0 || n < 0 || inner < 0 || n > kMaxDim) return LSE_ERR_INVALID_ARG;
+    constexpr int64_t kMaxOut = int64_t{1} << 40;
+    if (inner > 0 && outer > kMaxOut / inner) return LSE_ERR_INVALID_ARG;
+    const int64_t nout = outer * inner;
+    if (nout > 0 && n > (INT64_MAX / esize) / nout) return LSE_ERR_INVALID_ARG;
+    const uint64_t x_addr = reinterpret_cast<uint64_t>(x);
+    if (nout == 0) return h == nullptr ? LSE_ERR_INVALID_ARG : LSE_OK;
+    if (out == nullptr || (n > 0 && x == nullptr)) return LSE_ERR_INVALID_ARG;
+    if ((n > 0 && x_addr % esize != 0) || reinterpret_cast<uint64_t>(out) % 4 != 0)
+        return LSE_ERR_INVALID_ARG;
+    if (h == nullptr) return LSE_ERR_INVALID_ARG;
+    if (inner == 1) return lse_forward(h, x, dtype, outer, n, n, out, stream);
+
+    const int k = 16 / esize;
+    const bool vec = inner % k == 0 && x_addr % 16 == 0;
+    lse::DimArgs a{};
+    a.bf16 = dtype == LSE_DTYPE_BF16;
+    a.vector_cols = vec;
+    a.x = static_cast<const char*>(x);
+    a.n = n;
+    a.inner = inner;
+    a.ncv = vec ? nout / k : nout;
+    a.out = out;
+    a.ws_pairs = h->dim_pairs;
+    a.stream = stream;
+    const int cols_per_lane = vec ? k : 1;
+    const int64_t cvs = vec ? inner / k : inner;  // column groups per j-row
+    a.gw = static_cast<int>(std::min<int64_t>(256, cvs));
+    const int64_t rw = 256 / a.gw;                // j-rows per load step
+    const int64_t tiles = ceil_div(a.ncv, a.gw);
+    // Workgroups per tile along n: about 4 workgroups per CU in all, each
+    // lane keeping at least 16 steps of j, at most 1024 (and one tile's pairs
+    // must fit the workspace); a forced value from lse_set_tuning's `parts`
+    // wins. Split tiles go in batches whose pairs fit the workspace.
+    const int64_t cap_pairs = LSE_DIM_MAX_PAIRS;
+    const int64_t tile_pairs = static_cast<int64_t>(a.gw) * cols_per_lane;
+    int64_t parts = h->parts;
+    if (parts == 0) {
+        parts = 1;
+        const int64_t want = 4 * static_cast<int64_t>(h->n_cu);
+        if (tiles < want)
+            parts = std::min<int64_t>({ceil_div(want, tiles), int64_t{1024},
+                                       std::max<int64_t>(1, n / (16 * rw))});
+    }
+    parts = std::min<int64_t>({parts, int64_t{1024}, cap_pairs / tile_pairs});
+    const int64_t batch = parts > 1 ? std::min<int64_t>(tiles, cap_pairs / (tile_pairs * parts))
+                                    : tiles;
+    a.parts = static_cast<int>(parts);
+
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return LSE_ERR_HIP;
+    if (prev != h->device && hipSetDevice(h->device) != hipSuccess) return LSE_ERR_HIP;
+    hipError_t err = hipSuccess;
+    for (int64_t t0 = 0; t0 < tiles && err == hipSuccess; t0 += batch) {
+        a.tile0 = t0;
+        a.grid = std::min<int64_t>(batch, tiles - t0) * parts;
+        err = lse::launch_cols(a);
+    }
     if (prev != h->device) (void)hipSetDevice(prev);
     return err == hipSuccess ? LSE_OK : LSE_ERR_HIP;
 }

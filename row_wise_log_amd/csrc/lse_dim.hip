@@ -1,0 +1,290 @@
+// lse_dim.hip - log-sum-exp over the middle axis of a contiguous
+// [outer, n, inner] array, for gfx950:
+//
+//     out[o * inner + i] = log( sum_j exp(x[(o * n + j) * inner + i]) ),
+//
+// torch.logsumexp(x, dim=d) for a contiguous x (outer = prod(shape[:d]),
+// n = shape[d], inner = prod(shape[d+1:])). The paper "Speeding up
+// Log-Sum-Exp: Kernel Fusion at the Memory Wall, Integer Arithmetic at the
+// Compute Wall" presents its kernels as drop-in replacements for
+// torch.logsumexp (abstract, §6); this covers the reduction axes other than
+// the last (inner == 1 is lse_forward). Same arithmetic as the row kernels:
+// each element read once, a per-lane (max, exp-sum) accumulator folded lazily
+// (fold_lazy), pairwise merges, one fp32 per output.
+//
+// Layout. The reduced elements of one output are inner elements apart, and
+// neighbouring outputs are neighbours in memory. A lane owns K adjacent
+// outputs (a 16-byte group of columns when inner is a multiple of K and x is
+// 16-byte aligned, else one column) and walks j, loading 16 bytes per step;
+// no lane talks to another while streaming. The workgroup's 256 lanes cover
+// a block of gw column groups x rw = 256 / gw steps of j: gw = 256 when a
+// j-row holds that many groups (a load step reads 4 KB of one row), or the
+// whole row (gw = inner / K) when it is shorter, so that rw consecutive rows,
+// again contiguous, are read at once (inner = 16 fp32: 64 rows of 64 bytes).
+// The lanes that share columns are merged through LDS at the end. When there
+// are too few column blocks (tiles) to fill the GPU, P workgroups split j and
+// write their (max, sum) pairs to the handle's workspace; a second kernel
+// merges each column's P pairs (a lane per column, or a wavefront per column
+// when P > 64).
+#include "lse_device.h"
+#include "lse_launch.h"
+
+namespace lse {
+
+template <DType D, bool VEC, int U, bool SPLIT>
+__global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int64_t n,
+                                                int64_t inner, int64_t ncv, int gw, int64_t tile0,
+                                                float* __restrict__ out, int parts,
+                                                unsigned* __restrict__ ws_pairs) {
+    constexpr int K = VEC ? Elem<D>::kPerVec : 1;
+    constexpr int EB = Elem<D>::kBytes;
+    __shared__ float lds_m[256 * K];
+    __shared__ float lds_s[256 * K];
+
+    const int t = threadIdx.x;
+    const int rw = 256 / gw;             // steps of j per load
+    const int col = t % gw;
+    const int jr = t / gw;               // this lane's step within a load
+    const bool active = jr < rw;         // lanes past rw * gw hold nothing
+    const int64_t tl = blockIdx.x / parts;
+    const int part = static_cast<int>(blockIdx.x - tl * parts);
+    const int64_t cvs = VEC ? inner / K : inner;  // column groups per outer slice
+    const int64_t cv_raw = (tile0 + tl) * gw + col;
+    const int64_t cv = cv_raw < ncv ? cv_raw : ncv - 1;  // past the end: read a real column
+    const int64_t o = cv / cvs;
+    const int64_t iv = cv - o * cvs;
+    const char* base = x + (o * n * inner + iv * K) * EB;  // element (o, 0, iv*K)
+    const int64_t jstride = inner * EB;
+
+    // This part's j range; the lane takes j = pj0 + jr + s * rw for steps s.
+    const int64_t pj0 = n * part / parts;
+    const int64_t pj1 = n * (part + 1) / parts;
+    const int64_t len = pj1 - pj0;
+    const int64_t full_steps = len / rw;             // every lane's j is in range
+    const int64_t steps = (len + rw - 1) / rw;       // the last may be partial
+    const int64_t nfull = full_steps / U;            // whole batches of U steps
+    const int64_t rem = steps - nfull * U;           // steps in the guarded batch
+
+    Acc a[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) a[k] = acc_empty();
+
+    struct Batch {
+        u32x4 w[VEC ? U : 1];
+        float e[VEC ? 1 : U];
+    };
+    auto load_at = [&](Batch& b, int u, int64_t j) {
+        const char* p = base + j * jstride;
+        if constexpr (VEC)
+            b.w[u] = load_vec(reinterpret_cast<const u32x4*>(p));
+        else
+            b.e[u] = load_scalar<D>(p);
+    };
+    auto load_full = [&](Batch& b, int64_t kb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_at(b, u, pj0 + jr + (kb * U + u) * rw);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // The guarded batch: steps nfull*U .. steps-1; a step past this lane's
+    // range reloads the part's last row (in bounds) and is masked to -inf.
+    auto load_guarded = [&](Batch& b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = pj0 + jr + (nfull * U + u) * rw;
+            load_at(b, u, j < pj1 ? j : pj1 - 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto fold_batch = [&](const Batch& b, bool guarded) {
+        float f[U][K];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (VEC)
+                decode<D>(b.w[u], f[u]);
+            else
+                f[u][0] = b.e[u];
+            if (guarded && !(u < rem && pj0 + jr + (nfull * U + u) * rw < pj1)) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) f[u][k] = -kInf;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            float g[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) g[u] = f[u][k];
+            fold_lazy<U>(a[k], g);
+        }
+    };
+
+    if (len > 0 && active) {
+        Batch ba, bb, bc;
+        if (nfull == 0) {
+            load_guarded(bc);
+            fold_batch(bc, true);
+        } else {
+            load_full(ba, 0);
+            int64_t kb = 0;
+            for (; kb + 2 < nfull; kb += 2) {
+                load_full(bb, kb + 1);
+                fold_batch(ba, false);
+                load_full(ba, kb + 2);
+                fold_batch(bb, false);
+            }
+            if (kb + 1 < nfull) {
+                load_full(bb, kb + 1);
+                load_guarded(bc);
+                fold_batch(ba, false);
+                fold_batch(bb, false);
+            } else {
+                load_guarded(bc);
+                fold_batch(ba, false);
+            }
+            if (rem > 0) fold_batch(bc, true);
+        }
+    }
+
+    // Merge the rw lanes of each column through LDS: entry q = col * K + k of
+    // this tile collects the pairs (jr, col, k) for jr < rw.
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        lds_m[t * K + k] = active ? a[k].m : -kInf;
+        lds_s[t * K + k] = active ? acc_sum(a[k]) : 0.0f;
+    }
+    __syncthreads();
+    for (int q = t; q < gw * K; q += 256) {
+        const int c = q / K;
+        const int k = q - c * K;
+        float m = -kInf;
+        for (int r = 0; r < rw; ++r) m = max3f(m, lds_m[(r * gw + c) * K + k], m);
+        const float cm = base2_ref(m);
+        float s = 0.0f;
+        for (int r = 0; r < rw; ++r) {
+            const int i = (r * gw + c) * K + k;
+            s = __builtin_fmaf(lds_s[i], exp2_hw(base2_ref(lds_m[i]) - cm), s);
+        }
+        const int64_t qcv = (tile0 + tl) * gw + c;
+        if (qcv >= ncv) continue;
+        if constexpr (SPLIT) {
+            // part-major: consecutive lanes write consecutive pairs
+            const int64_t entries = static_cast<int64_t>(gridDim.x / parts) * gw * K;
+            unsigned* slot = ws_pairs + 2 * (part * entries + tl * gw * K + q);
+            slot[0] = __float_as_uint(m);
+            slot[1] = __float_as_uint(s);
+        } else {
+            const int64_t qo = qcv / cvs;
+            const int64_t qi = qcv - qo * cvs;
+            float r;
+            if (needs_natural_units(m, s)) {  // maximum beyond +-2^30: all of j again
+                const char* p = x + (qo * n * inner + qi * K + k) * EB;
+                float s2 = 0.0f;
+                for (int64_t j = 0; j < n; ++j)
+                    s2 += exp2_hw((load_scalar<D>(p + j * jstride) - m) * kLog2e);
+                r = __builtin_fmaf(log2_hw(s2), kLn2, m);
+            } else {
+                r = finish(m, cm, s);
+            }
+            out[qo * inner + qi * K + k] = r;
+        }
+    }
+}
+
+// The parts' pairs of each column entry (workspace laid out part-major:
+// pair (part, entry) at part * entries + entry), merged into the output.
+// LANES = 1: one lane per entry, looping over the parts (parts <= 64);
+// LANES = 64: one wavefront per entry, its lanes taking parts lane,
+// lane + 64, ... (parts <= 1024), then a max and a rescaled sum across it.
+template <DType D, bool VEC, int LANES>
+__global__ __launch_bounds__(256) void lse_cols_merge(const char* __restrict__ x, int64_t n,
+                                                      int64_t inner, int64_t ncv, int gw,
+                                                      int64_t tile0, int64_t entries,
+                                                      float* __restrict__ out, int parts,
+                                                      const unsigned* __restrict__ ws_pairs) {
+    constexpr int K = VEC ? Elem<D>::kPerVec : 1;
+    constexpr int EB = Elem<D>::kBytes;
+    const int lane = threadIdx.x & (LANES - 1);
+    const int64_t e = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / LANES;
+    if (e >= entries) return;  // uniform across the entry's lanes
+    const int64_t tl = e / (static_cast<int64_t>(gw) * K);
+    const int q = static_cast<int>(e - tl * gw * K);
+    const int c = q / K;
+    const int k = q - c * K;
+    const int64_t qcv = (tile0 + tl) * gw + c;
+    if (qcv >= ncv) return;
+    auto pair_m = [&](int p) { return __uint_as_float(ws_pairs[2 * (p * entries + e)]); };
+    auto pair_s = [&](int p) { return __uint_as_float(ws_pairs[2 * (p * entries + e) + 1]); };
+    float m = -kInf, s = 0.0f, cm;
+    if constexpr (LANES == 1) {
+        for (int p = 0; p < parts; ++p) m = max3f(m, pair_m(p), m);
+        cm = base2_ref(m);
+        for (int p = 0; p < parts; ++p)
+            s = __builtin_fmaf(pair_s(p), exp2_hw(base2_ref(pair_m(p)) - cm), s);
+    } else {
+        float pm[16], ps[16];  // parts <= 1024: at most 16 per lane
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int p = lane + 64 * i;
+            pm[i] = p < parts ? pair_m(p) : -kInf;
+            ps[i] = p < parts ? pair_s(p) : 0.0f;
+            m = max3f(m, pm[i], m);
+        }
+        m = group_reduce<64>(m, OpMax{});
+        cm = base2_ref(m);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s = __builtin_fmaf(ps[i], exp2_hw(base2_ref(pm[i]) - cm), s);
+        s = group_reduce<64>(s, OpSum{});
+    }
+    const int64_t cvs = VEC ? inner / K : inner;
+    const int64_t qo = qcv / cvs;
+    const int64_t qi = qcv - qo * cvs;
+    float r;
+    if (needs_natural_units(m, s)) {  // maximum beyond +-2^30: sum all of j again
+        const char* p = x + (qo * n * inner + qi * K + k) * EB;
+        float s2 = 0.0f;
+        for (int64_t j = lane; j < n; j += LANES)
+            s2 += exp2_hw((load_scalar<D>(p + j * inner * EB) - m) * kLog2e);
+        if constexpr (LANES == 64) s2 = group_reduce<64>(s2, OpSum{});
+        r = __builtin_fmaf(log2_hw(s2), kLn2, m);
+    } else {
+        r = finish(m, cm, s);
+    }
+    if (lane == 0) out[qo * inner + qi * K + k] = r;
+}
+
+namespace {
+
+template <DType D, bool VEC>
+hipError_t launch_cols_d(const DimArgs& a) {
+    constexpr int U = 4;
+    if (a.parts == 1) {
+        hipLaunchKernelGGL((lse_cols<D, VEC, U, false>), dim3(a.grid), dim3(256), 0, a.stream, a.x,
+                           a.n, a.inner, a.ncv, a.gw, a.tile0, a.out, 1, a.ws_pairs);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((lse_cols<D, VEC, U, true>), dim3(a.grid), dim3(256), 0, a.stream, a.x,
+                       a.n, a.inner, a.ncv, a.gw, a.tile0, a.out, a.parts, a.ws_pairs);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int k = VEC ? Elem<D>::kPerVec : 1;
+    const int64_t entries = (a.grid / a.parts) * a.gw * k;
+    if (a.parts <= 64)
+        hipLaunchKernelGGL((lse_cols_merge<D, VEC, 1>), dim3((entries + 255) / 256), dim3(256), 0,
+                           a.stream, a.x, a.n, a.inner, a.ncv, a.gw, a.tile0, entries, a.out,
+                           a.parts, a.ws_pairs);
+    else
+        hipLaunchKernelGGL((lse_cols_merge<D, VEC, 64>), dim3((entries + 3) / 4), dim3(256), 0,
+                           a.stream, a.x, a.n, a.inner, a.ncv, a.gw, a.tile0, entries, a.out,
+                           a.parts, a.ws_pairs);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cols(const DimArgs& a) {
+    if (a.grid <= 0) return hipSuccess;
+    if (a.bf16) return a.vector_cols ? launch_cols_d<DType::BF16, true>(a)
+                                     : launch_cols_d<DType::BF16, false>(a);
+    return a.vector_cols ? launch_cols_d<DType::F32, true>(a) : launch_cols_d<DType::F32, false>(a);
+}
+
+}  // namespace lse

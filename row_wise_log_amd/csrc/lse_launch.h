@@ -56,4 +56,24 @@ struct GradArgs {
 
 hipError_t launch_grad(const GradArgs& a);
 
+// LSE over the middle axis of [outer, n, inner] (lse_dim.hip): one launch
+// covers tiles [tile0, tile0 + grid / parts) of gw column groups each; with
+// parts > 1 a second kernel merges the parts' pairs from ws_pairs.
+struct DimArgs {
+    bool bf16;
+    bool vector_cols;      // 16-byte groups of columns (inner % K == 0, x 16-byte aligned)
+    int64_t grid;
+    int parts;             // workgroups per tile along the reduced axis (<= 1024)
+    int gw;                // column groups per tile (<= 256; 256 / gw steps of j per load)
+    const char* x;
+    int64_t n, inner;
+    int64_t ncv;           // column groups in all (outer * inner / K)
+    int64_t tile0;
+    float* out;
+    unsigned* ws_pairs;    // tiles * gw * K * parts (max, sum) pairs of one launch
+    hipStream_t stream;
+};
+
+hipError_t launch_cols(const DimArgs& a);
+
 }  // namespace lse

@@ -1,0 +1,146 @@
+"""GPU parity of the LSE over a non-last axis, lse_forward_dim, against the
+float64 oracle (the reduced axis moved last, then the row oracle).
+
+Shapes [outer, n, inner] with vector and single-column paths, the split of
+n across workgroups (forced and planned, in batches of tiles), special and
+huge-magnitude columns, n == 0, inner == 1 (the row path), a misaligned base,
+two workloads reduced over their first axis at full size, and the package's
+torch-tensor entry against torch.logsumexp in float64.
+"""
+import numpy as np
+import pytest
+
+import oracle as oracle_mod
+import workloads
+from gpu_util import DTYPE_CODE, compare, note
+from row_wise_log_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def handle(torch_gpu):
+    h = B.lse_create(0)
+    yield h
+    torch_gpu.cuda.synchronize()
+    B.lse_destroy(h)
+
+
+def gpu_dim(torch, handle, x3: np.ndarray, dtype: str, front: int = 0, parts: int = 0):
+    outer, n, inner = x3.shape
+    flat = np.zeros(front + x3.size, dtype=x3.dtype)
+    flat[front:] = x3.ravel()
+    t = torch.from_numpy(flat.view(np.int16 if dtype == "bf16" else np.int32)).to("cuda")
+    out = torch.full((max(outer * inner, 1),), 123.0, dtype=torch.float32, device="cuda")
+    B.lse_set_tuning(handle, 0, 0, parts, 0, 0)
+    try:
+        B.lse_forward_dim(handle, t.data_ptr() + front * x3.itemsize, DTYPE_CODE[dtype], outer, n,
+                          inner, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    finally:
+        B.lse_set_tuning(handle, 0, 0, 0, 0, 0)
+    return out.cpu().numpy()[: outer * inner].reshape(outer, inner)
+
+
+def make(shape, dtype, seed, scale=4.0):
+    v = np.random.default_rng(seed).normal(0, scale, size=shape).astype(np.float32)
+    return workloads.f32_to_bf16_bits(v) if dtype == "bf16" else v
+
+
+SHAPES = [(1, 8192, 4096), (64, 1000, 32), (3, 5, 7), (2, 100_000, 3), (128, 17, 1024),
+          (1, 1, 100), (10, 300, 1), (7, 33, 12), (1, 3, 65), (16, 257, 40), (1, 64, 4 * 64 * 300)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_shapes(torch_gpu, handle, dtype, shape):
+    x = make(shape, dtype, seed=sum(shape))
+    ref = oracle_mod.lse_dim(x, dtype, threads=8)
+    for front in (0, 1):
+        note(f"dim shape={shape} dtype={dtype} front={front}")
+        got = gpu_dim(torch_gpu, handle, x, dtype, front=front)
+        compare(got.ravel(), ref.ravel(), dtype, f"dim {shape} {dtype} front={front}")
+
+
+@pytest.mark.parametrize("parts", [1, 2, 7, 64])
+def test_forced_parts(torch_gpu, handle, parts):
+    for dtype in ["f32", "bf16"]:
+        x = make((3, 5000, 256), dtype, seed=parts)
+        ref = oracle_mod.lse_dim(x, dtype, threads=8)
+        note(f"dim forced parts={parts} dtype={dtype}")
+        compare(gpu_dim(torch_gpu, handle, x, dtype, parts=parts).ravel(), ref.ravel(), dtype,
+                f"parts={parts} {dtype}")
+
+
+def test_split_in_tile_batches(torch_gpu, handle):
+    """More tiles than one split launch holds: several launches, counters reused."""
+    x = make((1, 40, 4 * 64 * 1100), "f32", seed=5)   # 1100 tiles of 64 column vectors
+    ref = oracle_mod.lse_dim(x, "f32", threads=8)
+    for parts in (2, 5):
+        note(f"dim tile batches parts={parts}")
+        compare(gpu_dim(torch_gpu, handle, x, "f32", parts=parts).ravel(), ref.ravel(), "f32",
+                f"tile batches parts={parts}")
+
+
+def test_special_and_huge_columns(torch_gpu, handle):
+    rng = np.random.default_rng(8)
+    for dtype in ["f32", "bf16"]:
+        v = rng.normal(0, 2, size=(2, 3000, 64)).astype(np.float32)
+        v[0, :, 0] = -np.inf                     # a column of only -inf
+        v[0, 1234, 1] = np.nan                   # NaN
+        v[0, 2999, 2] = np.inf                   # +inf, last step
+        v[1, :, 3] = 7.0                         # constant: 7 + ln 3000
+        v[1, :1500, 4] = -np.inf                 # half -inf
+        v[1, 2000, 5] = 2.0e9                    # maximum beyond 2^30: natural units
+        v[1, :, 6] -= 2.0e9                      # every element beyond -2^30
+        v[0, :, 7] = 3.0e38                      # near the largest float
+        v[0, 0, 8] = 60.0                        # first step holds the maximum
+        v[0, 2999, 9] = 60.0                     # last step holds the maximum
+        x = workloads.f32_to_bf16_bits(v) if dtype == "bf16" else v
+        ref = oracle_mod.lse_dim(x, dtype, threads=8)
+        for parts in (0, 1, 3):
+            note(f"dim special columns dtype={dtype} parts={parts}")
+            compare(gpu_dim(torch_gpu, handle, x, dtype, parts=parts).ravel(), ref.ravel(), dtype,
+                    f"special {dtype} parts={parts}")
+
+
+def test_empty_reduction(torch_gpu, handle):
+    x = np.zeros((3, 0, 9), np.float32)
+    note("dim n=0")
+    got = gpu_dim(torch_gpu, handle, x, "f32")
+    assert np.all(got == -np.inf)
+    B.lse_forward_dim(handle, 0, B.LSE_DTYPE_F32, 0, 5, 5, 0,
+                      torch_gpu.cuda.current_stream().cuda_stream)
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_workload_first_axis_full_size(torch_gpu, handle, cfg):
+    """A workload reduced over its first axis (outer = 1, n = rows, inner = cols)."""
+    w = workloads.make(cfg)
+    x3 = w.x.reshape(1, w.rows, w.cols)
+    ref = oracle_mod.lse_dim(x3, w.dtype, threads=16)
+    note(f"dim workload {cfg} over axis 0")
+    compare(gpu_dim(torch_gpu, handle, x3, w.dtype).ravel(), ref.ravel(), w.dtype,
+            f"workload {cfg} axis 0")
+
+
+def test_package_logsumexp_dim(torch_gpu):
+    import row_wise_log_amd as R
+    torch = torch_gpu
+    rng = np.random.default_rng(12)
+    v = rng.normal(0, 3, size=(6, 50, 7, 33)).astype(np.float32)
+    xt = torch.from_numpy(v).cuda()
+    for d in range(4):
+        note(f"package logsumexp_dim dim={d}")
+        got = R.logsumexp_dim(xt, d).cpu().numpy().astype(np.float64)
+        want = torch.logsumexp(torch.from_numpy(v).double(), dim=d).numpy()
+        assert got.shape == want.shape
+        assert np.all(np.abs(got - want) <= 2e-6 * np.maximum(1.0, np.abs(want))), d

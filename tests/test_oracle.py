@@ -151,3 +151,37 @@ def test_golden_edge_cases(oracle):
                     assert np.isnan(want[r]), c["name"]
                 else:
                     assert abs(want[r] - w) <= 1e-14 * max(1.0, abs(w)) or want[r] == w, c["name"]
+
+
+# --- LSE over a non-last axis --------------------------------------------
+
+def test_lse_dim_against_scipy_and_brute_force(oracle):
+    """The middle-axis oracle against scipy.special.logsumexp(axis=1) and, on
+    tiny arrays, against log(fsum(exp)) of each gathered column."""
+    from scipy.special import logsumexp
+    import oracle as orc_mod
+    rng = np.random.default_rng(30)
+    for shape in [(1, 7, 5), (3, 1, 4), (2, 33, 17), (4, 100, 1), (1, 513, 64), (5, 2, 9)]:
+        x = rng.normal(0, 6, size=shape).astype(np.float32)
+        got = orc_mod.lse_dim(x, "f32")
+        want = logsumexp(x.astype(np.float64), axis=1)
+        assert got.shape == want.shape
+        assert np.all(np.abs(got - want) <= 1e-13 * np.maximum(1.0, np.abs(want))), shape
+        if x.size <= 2000:
+            for o in range(shape[0]):
+                for i in range(shape[2]):
+                    w = oracle_pins.brute_lse(x[o, :, i])
+                    assert abs(got[o, i] - w) <= 1e-14 * max(1.0, abs(w)), (shape, o, i)
+    bits = workloads.f32_to_bf16_bits(rng.normal(0, 3, size=(3, 40, 11)).astype(np.float32))
+    got = orc_mod.lse_dim(bits, "bf16")
+    vals = workloads.bf16_bits_to_f32(bits).astype(np.float64)
+    assert np.all(np.abs(got - logsumexp(vals, axis=1)) <= 1e-13 * np.maximum(1, np.abs(got)))
+    # special columns: all -inf, a NaN, a +inf; and n = 0 gives -inf
+    x = np.zeros((1, 4, 3), np.float32)
+    x[0, :, 0] = -np.inf
+    x[0, 2, 1] = np.nan
+    x[0, 1, 2] = np.inf
+    got = orc_mod.lse_dim(x, "f32")
+    assert got[0, 0] == -np.inf and np.isnan(got[0, 1]) and got[0, 2] == np.inf
+    assert np.all(orc_mod.lse_dim(np.zeros((2, 0, 3), np.float32), "f32") == -np.inf)
+
