@@ -38,6 +38,14 @@ constexpr int kWavesPerCUNarrow = 8;
 constexpr int kWavesPerCUWide = 16;
 constexpr int64_t kSplitMinRowBytes = 256 << 10;  // shorter rows stream faster unsplit
 constexpr int64_t kSplitPartBytes = 128 << 10;    // target bytes per split part
+// lse_forward_dim: column groups per workgroup (the other 256 / 32 = 8 lanes
+// of each column group take consecutive j), doubled where there are columns
+// enough for two 64-group tiles per CU. Measured on [n, inner] of
+// [512, 128256] bf16, [4096, 262144] bf16, [65536, 4096] fp32 and
+// [16777216, 16] fp32 against 4 to 256 groups and 1 to 1024 parts, the
+// fastest plans keep one or two workgroups per CU, each streaming a long
+// stretch of j, and split j only when the tiles alone do not reach every CU.
+constexpr int kDimGroups = 32;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -482,19 +490,26 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, i
     a.stream = stream;
     const int cols_per_lane = vec ? k : 1;
     const int64_t cvs = vec ? inner / k : inner;  // column groups per j-row
-    a.gw = static_cast<int>(std::min<int64_t>(256, cvs));
+    // Column groups per workgroup: 64 when a j-row holds that many and that
+    // still leaves two tiles per CU, else 32 (or the whole j-row when it is
+    // shorter, so that a workgroup reads consecutive short rows).
+    a.gw = static_cast<int>(cvs >= 2 * kDimGroups &&
+                                    ceil_div(a.ncv, 2 * kDimGroups) >= 2 * int64_t{h->n_cu}
+                                ? 2 * kDimGroups
+                                : std::min<int64_t>(kDimGroups, cvs));
     const int64_t rw = 256 / a.gw;                // j-rows per load step
     const int64_t tiles = ceil_div(a.ncv, a.gw);
-    // Workgroups per tile along n: about 4 workgroups per CU in all, each
-    // lane keeping at least 16 steps of j, at most 1024 (and one tile's pairs
-    // must fit the workspace); a forced value from lse_set_tuning's `parts`
-    // wins. Split tiles go in batches whose pairs fit the workspace.
+    // Workgroups per tile along n: none while the tiles alone give every CU
+    // a workgroup, else enough for about one per CU, each lane keeping at
+    // least 16 steps of j, at most 1024 (and one tile's pairs must fit the
+    // workspace); a forced value from lse_set_tuning's `parts` wins. Split
+    // tiles go in batches whose pairs fit the workspace.
     const int64_t cap_pairs = LSE_DIM_MAX_PAIRS;
     const int64_t tile_pairs = static_cast<int64_t>(a.gw) * cols_per_lane;
     int64_t parts = h->parts;
     if (parts == 0) {
         parts = 1;
-        const int64_t want = 4 * static_cast<int64_t>(h->n_cu);
+        const int64_t want = h->n_cu;
         if (tiles < want)
             parts = std::min<int64_t>({ceil_div(want, tiles), int64_t{1024},
                                        std::max<int64_t>(1, n / (16 * rw))});
