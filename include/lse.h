@@ -179,8 +179,10 @@ lse_status_t lse_backward(lse_handle_t h, const void *x, lse_dtype_t dtype,
  *          count must fit in int64.
  *   out    device pointer to outer * inner fp32 values, 4-byte aligned, not
  *          overlapping x. n == 0 writes -inf.
- * Uses the handle's workspace when there are too few outputs to fill the GPU
- * (so, like lse_forward, calls sharing a handle must not run concurrently).
+ * When there are too few outputs to fill the GPU, several workgroups share
+ * each output's n and meet through the handle's workspace and arrival
+ * counters (so, like lse_forward, calls sharing a handle must not run
+ * concurrently).
  * Errors: UNSUPPORTED_DTYPE; INVALID_ARG (sizes, NULL or misaligned
  * pointers with work to do, NULL handle); HIP.
  */

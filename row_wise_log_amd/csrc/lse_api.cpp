@@ -487,6 +487,7 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, i
     a.ncv = vec ? nout / k : nout;
     a.out = out;
     a.ws_pairs = h->dim_pairs;
+    a.counters = h->counters;
     a.stream = stream;
     const int cols_per_lane = vec ? k : 1;
     const int64_t cvs = vec ? inner / k : inner;  // column groups per j-row
@@ -503,7 +504,8 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, i
     // a workgroup, else enough for about one per CU, each lane keeping at
     // least 16 steps of j, at most 1024 (and one tile's pairs must fit the
     // workspace); a forced value from lse_set_tuning's `parts` wins. Split
-    // tiles go in batches whose pairs fit the workspace.
+    // tiles go in batches whose pairs fit the workspace and whose tiles fit
+    // the arrival counters.
     const int64_t cap_pairs = LSE_DIM_MAX_PAIRS;
     const int64_t tile_pairs = static_cast<int64_t>(a.gw) * cols_per_lane;
     int64_t parts = h->parts;
@@ -515,8 +517,10 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, i
                                        std::max<int64_t>(1, n / (16 * rw))});
     }
     parts = std::min<int64_t>({parts, int64_t{1024}, cap_pairs / tile_pairs});
-    const int64_t batch = parts > 1 ? std::min<int64_t>(tiles, cap_pairs / (tile_pairs * parts))
-                                    : tiles;
+    const int64_t batch =
+        parts > 1 ? std::min<int64_t>({tiles, cap_pairs / (tile_pairs * parts),
+                                       int64_t{LSE_SPLIT_MAX_ROWS}})  // one counter per tile
+                  : tiles;
     a.parts = static_cast<int>(parts);
 
     int prev = -1;

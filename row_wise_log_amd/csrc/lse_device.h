@@ -43,6 +43,9 @@ constexpr float kLog2e = 0x1.715476p+0f;  // log2(e) rounded to fp32
 constexpr float kLn2 = 0x1.62e430p-1f;    // ln(2) rounded to fp32
 constexpr float kClamp = 0x1p30f;         // |m| beyond this takes the slow pass
 constexpr float kInf = __builtin_inff();
+// s_waitcnt immediate for gfx9: vmcnt = 0, expcnt and lgkmcnt left at their
+// maxima (not waited on).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 enum class DType : int { F32 = 0, BF16 = 1 };
 

@@ -23,9 +23,9 @@
 // again contiguous, are read at once (inner = 16 fp32: 64 rows of 64 bytes).
 // The lanes that share columns are merged through LDS at the end. When there
 // are too few column blocks (tiles) to fill the GPU, P workgroups split j and
-// write their (max, sum) pairs to the handle's workspace; a second kernel
-// merges each column's P pairs (a lane per column, or a wavefront per column
-// when P > 64).
+// write their (max, sum) pairs to the handle's workspace; the last of a
+// tile's P workgroups to arrive (an agent-scope counter per tile) merges the
+// tile's pairs in the same launch and resets the counter.
 #include "lse_device.h"
 #include "lse_launch.h"
 
@@ -35,7 +35,8 @@ template <DType D, bool VEC, int U, bool SPLIT>
 __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int64_t n,
                                                 int64_t inner, int64_t ncv, int gw, int64_t tile0,
                                                 float* __restrict__ out, int parts,
-                                                unsigned* __restrict__ ws_pairs) {
+                                                unsigned* __restrict__ ws_pairs,
+                                                unsigned* __restrict__ counters) {
     constexpr int K = VEC ? Elem<D>::kPerVec : 1;
     constexpr int EB = Elem<D>::kBytes;
     __shared__ float lds_m[256 * K];
@@ -144,6 +145,88 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
         }
     }
 
+    // The tile's pairs from all parts, entry q = col * K + k: L lanes per
+    // entry (a power of two, L * entries <= 256, L <= 64) take parts l,
+    // l + L, ..., and their partial (max, sum) meet in LDS. A merged maximum
+    // beyond +-2^30 sums the column's j again, over the same L lanes.
+    auto merge_parts = [&](int64_t tlm) {
+        const int ent = gw * K;
+        const int64_t entries = static_cast<int64_t>(gridDim.x / parts) * ent;
+        const unsigned long long* wp = reinterpret_cast<const unsigned long long*>(ws_pairs);
+        int L = 1;
+        while (L < 64 && 2 * L * ent <= 256) L *= 2;
+        const int l = t & (L - 1);
+        for (int q0 = 0; q0 < ent; q0 += 256 / L) {
+            const int q = q0 + t / L;
+            const int c = q / K;
+            const int k = q - c * K;
+            const int64_t qcv = (tile0 + tlm) * gw + c;
+            const bool live = q < ent && qcv < ncv;
+            // This lane's parts in batches of 8 loads issued together; each
+            // batch raises the running maximum and rescales the sum once.
+            float pm = -kInf, ps = 0.0f;
+            if (live) {
+                const unsigned long long* e0 = wp + tlm * ent + q;
+                for (int p0 = l; p0 < parts; p0 += 8 * L) {
+                    float bm[8], bs[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int p = p0 + i * L;
+                        const unsigned long long v =
+                            p < parts ? __hip_atomic_load(e0 + p * entries, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT)
+                                      : 0xFF800000ull;  // (-inf, 0)
+                        bm[i] = __uint_as_float(static_cast<unsigned>(v));
+                        bs[i] = __uint_as_float(static_cast<unsigned>(v >> 32));
+                    }
+                    float m2 = pm;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) m2 = max3f(m2, bm[i], m2);
+                    const float c2 = base2_ref(m2);
+                    ps *= exp2_hw(base2_ref(pm) - c2);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        ps = __builtin_fmaf(bs[i], exp2_hw(base2_ref(bm[i]) - c2), ps);
+                    pm = m2;
+                }
+            }
+            lds_m[t] = pm;
+            lds_s[t] = ps;
+            __syncthreads();
+            const int g0 = t - l;  // the entry's first lane
+            float m = -kInf;
+            for (int i = 0; i < L; ++i) m = max3f(m, lds_m[g0 + i], m);
+            const float cm = base2_ref(m);
+            float sum = 0.0f;
+            for (int i = 0; i < L; ++i)
+                sum = __builtin_fmaf(lds_s[g0 + i], exp2_hw(base2_ref(lds_m[g0 + i]) - cm), sum);
+            const bool slow = live && needs_natural_units(m, sum);
+            const int64_t qo = live ? qcv / cvs : 0;
+            const int64_t qi = qcv - qo * cvs;
+            float s2 = 0.0f;
+            if (slow) {
+                const char* p = x + (qo * n * inner + qi * K + k) * EB;
+                for (int64_t j = l; j < n; j += L)
+                    s2 += exp2_hw((load_scalar<D>(p + j * jstride) - m) * kLog2e);
+            }
+            __syncthreads();  // every lane has read the partials
+            lds_s[t] = s2;
+            __syncthreads();
+            if (live && l == 0) {
+                float r;
+                if (slow) {
+                    float t2 = 0.0f;
+                    for (int i = 0; i < L; ++i) t2 += lds_s[g0 + i];
+                    r = __builtin_fmaf(log2_hw(t2), kLn2, m);
+                } else {
+                    r = finish(m, cm, sum);
+                }
+                out[qo * inner + qi * K + k] = r;
+            }
+            __syncthreads();
+        }
+    };
+
     // Merge the rw lanes of each column through LDS: entry q = col * K + k of
     // this tile collects the pairs (jr, col, k) for jr < rw.
 #pragma unroll
@@ -166,11 +249,15 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
         const int64_t qcv = (tile0 + tl) * gw + c;
         if (qcv >= ncv) continue;
         if constexpr (SPLIT) {
-            // part-major: consecutive lanes write consecutive pairs
+            // Part-major (consecutive lanes write consecutive pairs), one
+            // agent-scope 8-byte store per pair: coherent across the XCDs'
+            // L2s, so the merging workgroup reads it wherever it runs.
             const int64_t entries = static_cast<int64_t>(gridDim.x / parts) * gw * K;
-            unsigned* slot = ws_pairs + 2 * (part * entries + tl * gw * K + q);
-            slot[0] = __float_as_uint(m);
-            slot[1] = __float_as_uint(s);
+            const unsigned long long pair =
+                (static_cast<unsigned long long>(__float_as_uint(s)) << 32) | __float_as_uint(m);
+            __hip_atomic_store(reinterpret_cast<unsigned long long*>(ws_pairs) +
+                                   (part * entries + tl * gw * K + q),
+                               pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             const int64_t qo = qcv / cvs;
             const int64_t qi = qcv - qo * cvs;
@@ -187,68 +274,25 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
             out[qo * inner + qi * K + k] = r;
         }
     }
-}
 
-// The parts' pairs of each column entry (workspace laid out part-major:
-// pair (part, entry) at part * entries + entry), merged into the output.
-// LANES = 1: one lane per entry, looping over the parts (parts <= 64);
-// LANES = 64: one wavefront per entry, its lanes taking parts lane,
-// lane + 64, ... (parts <= 1024), then a max and a rescaled sum across it.
-template <DType D, bool VEC, int LANES>
-__global__ __launch_bounds__(256) void lse_cols_merge(const char* __restrict__ x, int64_t n,
-                                                      int64_t inner, int64_t ncv, int gw,
-                                                      int64_t tile0, int64_t entries,
-                                                      float* __restrict__ out, int parts,
-                                                      const unsigned* __restrict__ ws_pairs) {
-    constexpr int K = VEC ? Elem<D>::kPerVec : 1;
-    constexpr int EB = Elem<D>::kBytes;
-    const int lane = threadIdx.x & (LANES - 1);
-    const int64_t e = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / LANES;
-    if (e >= entries) return;  // uniform across the entry's lanes
-    const int64_t tl = e / (static_cast<int64_t>(gw) * K);
-    const int q = static_cast<int>(e - tl * gw * K);
-    const int c = q / K;
-    const int k = q - c * K;
-    const int64_t qcv = (tile0 + tl) * gw + c;
-    if (qcv >= ncv) return;
-    auto pair_m = [&](int p) { return __uint_as_float(ws_pairs[2 * (p * entries + e)]); };
-    auto pair_s = [&](int p) { return __uint_as_float(ws_pairs[2 * (p * entries + e) + 1]); };
-    float m = -kInf, s = 0.0f, cm;
-    if constexpr (LANES == 1) {
-        for (int p = 0; p < parts; ++p) m = max3f(m, pair_m(p), m);
-        cm = base2_ref(m);
-        for (int p = 0; p < parts; ++p)
-            s = __builtin_fmaf(pair_s(p), exp2_hw(base2_ref(pair_m(p)) - cm), s);
-    } else {
-        float pm[16], ps[16];  // parts <= 1024: at most 16 per lane
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int p = lane + 64 * i;
-            pm[i] = p < parts ? pair_m(p) : -kInf;
-            ps[i] = p < parts ? pair_s(p) : 0.0f;
-            m = max3f(m, pm[i], m);
+    if constexpr (SPLIT) {
+        // Count this workgroup in once every lane's pair stores have
+        // completed; the last of the tile's parts to arrive merges them.
+        __shared__ int is_last;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __syncthreads();
+        if (t == 0) {
+            const unsigned prev =
+                __hip_atomic_fetch_add(counters + tl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            is_last = prev == static_cast<unsigned>(parts - 1);
         }
-        m = group_reduce<64>(m, OpMax{});
-        cm = base2_ref(m);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s = __builtin_fmaf(ps[i], exp2_hw(base2_ref(pm[i]) - cm), s);
-        s = group_reduce<64>(s, OpSum{});
+        __syncthreads();
+        if (!is_last) return;
+        merge_parts(tl);
+        if (t == 0) __hip_atomic_store(counters + tl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    const int64_t cvs = VEC ? inner / K : inner;
-    const int64_t qo = qcv / cvs;
-    const int64_t qi = qcv - qo * cvs;
-    float r;
-    if (needs_natural_units(m, s)) {  // maximum beyond +-2^30: sum all of j again
-        const char* p = x + (qo * n * inner + qi * K + k) * EB;
-        float s2 = 0.0f;
-        for (int64_t j = lane; j < n; j += LANES)
-            s2 += exp2_hw((load_scalar<D>(p + j * inner * EB) - m) * kLog2e);
-        if constexpr (LANES == 64) s2 = group_reduce<64>(s2, OpSum{});
-        r = __builtin_fmaf(log2_hw(s2), kLn2, m);
-    } else {
-        r = finish(m, cm, s);
-    }
-    if (lane == 0) out[qo * inner + qi * K + k] = r;
 }
 
 namespace {
@@ -256,25 +300,13 @@ namespace {
 template <DType D, bool VEC>
 hipError_t launch_cols_d(const DimArgs& a) {
     constexpr int U = 4;
-    if (a.parts == 1) {
+    if (a.parts == 1)
         hipLaunchKernelGGL((lse_cols<D, VEC, U, false>), dim3(a.grid), dim3(256), 0, a.stream, a.x,
-                           a.n, a.inner, a.ncv, a.gw, a.tile0, a.out, 1, a.ws_pairs);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((lse_cols<D, VEC, U, true>), dim3(a.grid), dim3(256), 0, a.stream, a.x,
-                       a.n, a.inner, a.ncv, a.gw, a.tile0, a.out, a.parts, a.ws_pairs);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const int k = VEC ? Elem<D>::kPerVec : 1;
-    const int64_t entries = (a.grid / a.parts) * a.gw * k;
-    if (a.parts <= 64)
-        hipLaunchKernelGGL((lse_cols_merge<D, VEC, 1>), dim3((entries + 255) / 256), dim3(256), 0,
-                           a.stream, a.x, a.n, a.inner, a.ncv, a.gw, a.tile0, entries, a.out,
-                           a.parts, a.ws_pairs);
+                           a.n, a.inner, a.ncv, a.gw, a.tile0, a.out, 1, a.ws_pairs, a.counters);
     else
-        hipLaunchKernelGGL((lse_cols_merge<D, VEC, 64>), dim3((entries + 3) / 4), dim3(256), 0,
-                           a.stream, a.x, a.n, a.inner, a.ncv, a.gw, a.tile0, entries, a.out,
-                           a.parts, a.ws_pairs);
+        hipLaunchKernelGGL((lse_cols<D, VEC, U, true>), dim3(a.grid), dim3(256), 0, a.stream, a.x,
+                           a.n, a.inner, a.ncv, a.gw, a.tile0, a.out, a.parts, a.ws_pairs,
+                           a.counters);
     return hipGetLastError();
 }
 

@@ -31,10 +31,6 @@
 
 namespace lse {
 
-// s_waitcnt immediate for gfx9: vmcnt = 0, expcnt and lgkmcnt left at their
-// maxima (not waited on).
-constexpr int kWaitVmcnt0 = 0x0F70;
-
 // ---------------------------------------------------------------------------
 // Slow pass for rows whose maximum m is finite but beyond +-2^30: the sum of
 // 2^((x - m) * log2 e) in natural units. Each lane sums elements j = first,

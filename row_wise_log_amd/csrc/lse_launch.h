@@ -71,6 +71,7 @@ struct DimArgs {
     int64_t tile0;
     float* out;
     unsigned* ws_pairs;    // tiles * gw * K * parts (max, sum) pairs of one launch
+    unsigned* counters;    // one arrival counter per tile of a launch, zero between calls
     hipStream_t stream;
 };
 
