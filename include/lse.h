@@ -79,7 +79,8 @@ typedef enum {
  * Create a handle on HIP device `device` (an index as for hipSetDevice).
  * Queries the compute-unit count, allocates the split-row workspace
  * (LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS (max, sum) pairs plus one
- * counter per row, about 0.5 MiB, the counters zeroed) and lse_forward_dim's
+ * counter per row, each in its own 256 bytes, about 0.75 MiB, the counters
+ * zeroed) and lse_forward_dim's
  * workspace (LSE_DIM_MAX_PAIRS pairs, 32 MiB), and synchronises once. On success
  * *out receives the handle; on failure *out is set to NULL.
  * Errors: INVALID_ARG (out NULL, device out of range), NO_DEVICE (no device

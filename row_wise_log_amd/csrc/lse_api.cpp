@@ -19,7 +19,7 @@ struct lse_handle_s {
     int device;
     int n_cu;
     unsigned* ws_pairs;  // LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS (max, sum) pairs
-    unsigned* counters;  // LSE_SPLIT_MAX_ROWS arrival counters, zero between calls
+    unsigned* counters;  // LSE_SPLIT_MAX_ROWS arrival counters, 256 bytes apart, zero between calls
     unsigned* dim_pairs; // LSE_DIM_MAX_PAIRS (max, sum) pairs for lse_forward_dim's split
     int schedule;        // lse_schedule_t forced for later calls (AUTO = by shape)
     int block, unroll, parts, waves_per_cu, lanes_per_row;  // tuning overrides, 0 = planner default
@@ -277,7 +277,7 @@ lse_status_t lse_create(lse_handle_t* out, int device) {
         h->device = device;
         h->n_cu = prop.multiProcessorCount;
         const size_t pair_bytes = size_t{LSE_SPLIT_MAX_ROWS} * LSE_SPLIT_MAX_PARTS * 8;
-        const size_t count_bytes = size_t{LSE_SPLIT_MAX_ROWS} * 4;
+        const size_t count_bytes = size_t{LSE_SPLIT_MAX_ROWS} * lse::kCounterWords * 4;
         const size_t dim_bytes = size_t{LSE_DIM_MAX_PAIRS} * 8;
         void* mem = nullptr;
         if (hipMalloc(&mem, pair_bytes + count_bytes + dim_bytes) != hipSuccess) {

@@ -285,13 +285,13 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
         __syncthreads();
         if (t == 0) {
             const unsigned prev =
-                __hip_atomic_fetch_add(counters + tl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(counters + tl * kCounterWords, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             is_last = prev == static_cast<unsigned>(parts - 1);
         }
         __syncthreads();
         if (!is_last) return;
         merge_parts(tl);
-        if (t == 0) __hip_atomic_store(counters + tl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t == 0) __hip_atomic_store(counters + tl * kCounterWords, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -499,7 +499,7 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const unsigned prev = __hip_atomic_fetch_add(counters + row, 1u, __ATOMIC_RELAXED,
+            const unsigned prev = __hip_atomic_fetch_add(counters + row * kCounterWords, 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
             is_last = (prev == static_cast<unsigned>(nparts - 1));
         }
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
         }
         b = block_merge<BLOCK>(pm, base2_ref(pm), ps, pairs);
         if (tid == 0)
-            __hip_atomic_store(counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(counters + row * kCounterWords, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     float r;
