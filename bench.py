@@ -161,6 +161,68 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
     }
 
 
+def launch_floor_us(torch, B, handle, calls: int = 1000) -> float:
+    """Mean time per call of 1000 back-to-back lse_forward calls on a single
+    fp32 element: the library's own launch floor, beside which the small
+    shapes' microseconds per call are read."""
+    x = torch.zeros(1, dtype=torch.float32, device="cuda")
+    out = torch.empty(1, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def call():
+        B.lse_forward(handle, x.data_ptr(), B.LSE_DTYPE_F32, 1, 1, 1, out.data_ptr(), sh)
+
+    for _ in range(50):
+        call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / calls
+
+
+def warm_us_per_call(torch, B, handle, cfg: int, calls: int = 1000) -> float:
+    """Microseconds per call of back-to-back lse_forward calls on ONE copy of
+    a workload (cache-resident when it fits the 256 MiB Infinity Cache)."""
+    w = workloads.make(cfg)
+    host = torch.from_numpy(w.x.view(np.int16) if w.dtype == "bf16" else w.x)
+    x = host.to("cuda")
+    out = torch.empty(w.rows, dtype=torch.float32, device="cuda")
+    code = B.LSE_DTYPE_BF16 if w.dtype == "bf16" else B.LSE_DTYPE_F32
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def call():
+        B.lse_forward(handle, x.data_ptr(), code, w.rows, w.cols, w.cols, out.data_ptr(), sh)
+
+    for _ in range(50):
+        call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / calls
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.partition(":")[2].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_backward(w, r, seconds: float = 10.0) -> dict:
     """The float64 oracle's backward pass on the host cores over a bounded
     sample of rows (at most 256 MB of input); its first pass also checks the
@@ -238,8 +300,24 @@ def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0, op: str = "lse")
         scale = np.maximum(scale, np.abs(lse[fin]))
     err = np.abs(gpu_out[fin] - ref[fin]) / (tol * scale)
     log(f"GPU output vs oracle: max |err|/tol = {err.max(initial=0):.3f}, non-finite match {exact}")
+    # one thread, over a bounded prefix of the rows (the pages time their CPU
+    # LSE single-threaded)
+    one = {}
+    if op == "lse":
+        n1 = max(1, min(w.rows, (32 << 20) // (w.cols * w.x.itemsize)))
+        x1 = w.x[:n1]
+        p1 = 0
+        t1 = time.perf_counter()
+        while True:
+            orc.lse(x1, w.dtype, threads=1)
+            p1 += 1
+            e1 = time.perf_counter() - t1
+            if e1 >= min(3.0, seconds) or p1 >= 1000:
+                break
+        one = {"value_1thread": round(x1.nbytes * p1 / e1 / 1e9, 3),
+               "sample_1thread": f"the first {n1} rows ({x1.nbytes} bytes), {p1} passes in {e1:.1f} s"}
     return {"value": round(nbytes * passes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), **one,
             "sample": (f"the whole {w.rows}x{w.cols} {w.dtype} input, {passes} passes in "
                        f"{el:.1f} s wall on {threads} threads (float64 two-pass max-subtract, "
                        "libm exp/log" + (", minus the target element" if tg is not None else "")
@@ -296,6 +374,8 @@ def main() -> int:
                         args.op)
         w = r["w"]
         traffic = recorded_traffic(args.config) if args.op == "lse" else None
+        floor = launch_floor_us(torch, B, handle)
+        log(f"launch floor (lse_forward on one element, back to back): {floor:.2f} us per call")
         line = {
             "metric": {"lse": METRIC, "logprob": METRIC_LOGPROB, "backward": METRIC_BACKWARD,
                        "dim": METRIC_DIM}[args.op],
@@ -320,6 +400,7 @@ def main() -> int:
                 "pct_of_hbm_peak": round(100 * r["value_gbs"] / HBM_PEAK_GBS, 2),
                 "us_per_call": round(r["ms_per_step"] * 1e3, 2),
                 "rows_per_s": round(w.rows / (r["ms_per_step"] * 1e-3), 1),
+                "launch_floor_us": round(floor, 2),
             },
             "roofline": {
                 "bound": "hbm",
@@ -347,7 +428,10 @@ def main() -> int:
                            "us_per_call": round(rc["ms_per_step"] * 1e3, 2),
                            "launch_us_mean": round(rc["launch_ms_mean"] * 1e3, 2),
                            "achieved_GBs_per_launch": round(rc["achieved_gbs"], 1),
-                           "rows_per_s": round(rc["w"].rows / (rc["ms_per_step"] * 1e-3), 1)}
+                           "rows_per_s": round(rc["w"].rows / (rc["ms_per_step"] * 1e-3), 1),
+                           "launch_floor_us": round(floor, 2)}
+                    if args.op == "lse" and rc["in_bytes"] <= CACHE_BYTES // 4:
+                        rec["us_per_call_warm"] = round(warm_us_per_call(torch, B, handle, cfg), 2)
                     log(json.dumps(rec))
                     f.write(json.dumps(rec) + "\n")
                     if cfg != args.config:
