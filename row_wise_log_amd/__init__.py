@@ -1,13 +1,15 @@
 """Row-wise log-sum-exp on MI355X (gfx950): a C-ABI HIP library and its binding.
 
 ``logsumexp(x)`` returns log(sum(exp(x), dim=-1)) in fp32 for a 2-D fp32 or
-bf16 CUDA/HIP tensor whose last axis is contiguous; ``logsumexp_dim(x, d)``
-reduces any axis of a contiguous tensor; ``token_logprob(x, t)``
-returns x[r, t[r]] - logsumexp(x)[r] from the same single pass. PyTorch only
-provides the device memory and the current stream; the computation is the HIP
-library's ``lse_forward`` / ``lse_token_logprob`` (see include/lse.h). The
-library is loaded on first use and a missing library is an error, never a
-fallback.
+bf16 CUDA/HIP tensor whose last axis is contiguous; ``logsumexp_autograd(x)``
+is the same value with a gradient (the library's backward pass, grad_out *
+exp(x - lse), in x's dtype); ``logsumexp_dim(x, d)`` reduces any axis of a
+contiguous tensor; ``token_logprob(x, t)`` returns x[r, t[r]] -
+logsumexp(x)[r] from the same single pass. PyTorch only provides the device
+memory and the current stream; the computation is the HIP library's
+``lse_forward`` / ``lse_backward`` / ``lse_forward_dim`` /
+``lse_token_logprob`` (see include/lse.h). The library is loaded on first use
+and a missing library is an error, never a fallback.
 """
 from __future__ import annotations
 
@@ -106,3 +108,46 @@ def token_logprob(x, targets, return_lse=False, handle_=None):
     lse_token_logprob(h, x.data_ptr(), code, rows, cols, stride, targets.data_ptr(),
                       logp.data_ptr(), lse.data_ptr() if lse is not None else None, stream)
     return (logp, lse) if return_lse else logp
+
+
+def _autograd_function():
+    import torch
+
+    from .binding import lse_backward
+
+    class _LogSumExp(torch.autograd.Function):
+        """LSE over the last axis with the library's backward pass."""
+
+        @staticmethod
+        def forward(ctx, x):
+            out = logsumexp(x)
+            ctx.save_for_backward(x, out)
+            return out
+
+        @staticmethod
+        def backward(ctx, grad_out):
+            x, out = ctx.saved_tensors
+            code, rows, cols, stride = _check_input(x)
+            g = grad_out.to(torch.float32).contiguous()
+            grad = torch.empty((rows, cols), dtype=x.dtype, device=x.device)
+            h = handle(x.device.index or 0)
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+            lse_backward(h, x.data_ptr(), code, rows, cols, stride, out.data_ptr(), g.data_ptr(),
+                         grad.data_ptr(), cols, stream)
+            return grad
+
+    return _LogSumExp
+
+
+_LSE_FN = None
+
+
+def logsumexp_autograd(x):
+    """LSE over the last axis of a 2-D fp32/bf16 GPU tensor, as fp32[rows],
+    differentiable: the gradient with respect to x is grad_out[r] *
+    exp(x[r, j] - lse[r]) (the row's softmax scaled by the incoming gradient),
+    computed by the library's lse_backward and returned in x's dtype."""
+    global _LSE_FN
+    if _LSE_FN is None:
+        _LSE_FN = _autograd_function()
+    return _LSE_FN.apply(x)

@@ -189,3 +189,35 @@ def test_forward_then_backward_matches_torch_autograd(torch_gpu, handle):
     # the forward LSE is within 2e-6 * max(1, |LSE|) (|LSE| about 13 here), which
     # the backward carries as a relative error, plus its own 1e-6
     assert np.allclose(got, ref, rtol=3e-5, atol=1e-30), float(np.max(np.abs(got - ref)))
+
+
+def test_package_autograd_against_torch(torch_gpu):
+    """logsumexp_autograd: value and gradient (the library's lse_forward and
+    lse_backward) against torch.logsumexp's float64 autograd on the CPU, for
+    fp32 and bf16 inputs, contiguous and row-padded views."""
+    import row_wise_log_amd as R
+    torch = torch_gpu
+    rng = np.random.default_rng(13)
+    for dtype in (torch.float32, torch.bfloat16):
+        for cols, pad in ((2049, 0), (1000, 24), (17, 3)):
+            v = rng.normal(0, 3, size=(37, cols + pad)).astype(np.float32)
+            big = torch.from_numpy(v).to("cuda", dtype).requires_grad_(True)
+            x = big[:, :cols]
+            note(f"package autograd dtype={dtype} cols={cols} pad={pad}")
+            y = R.logsumexp_autograd(x)
+            w = torch.from_numpy(rng.normal(0, 1, size=37).astype(np.float32)).cuda()
+            (y * w).sum().backward()
+            torch.cuda.synchronize()
+            xc = x.detach().to(torch.float32).cpu().double().requires_grad_(True)
+            yc = torch.logsumexp(xc, dim=1)
+            (yc * w.cpu().double()).sum().backward()
+            yv = y.detach().cpu().double().numpy()
+            assert np.all(np.abs(yv - yc.detach().numpy()) <= 2e-6 * np.maximum(1, np.abs(yv)))
+            assert big.grad.dtype == dtype
+            g = big.grad.to(torch.float32).cpu().double().numpy()
+            ref = xc.grad.numpy()
+            # fp32: the forward's 2e-6 relative LSE error times |x - lse| (< 30 here)
+            # plus the backward's own; bf16 output adds one rounding to 8 bits
+            rel = 2.0 ** -8 + 1e-4 if dtype == torch.bfloat16 else 1e-4
+            assert np.all(np.abs(g[:, :cols] - ref) <= rel * np.abs(ref) + 1e-30), (dtype, cols)
+            assert np.all(g[:, cols:] == 0), "gradient leaked into the padding"
