@@ -64,7 +64,8 @@ hipError_t launch_grad(const GradArgs& a);
 
 // LSE over the middle axis of [outer, n, inner] (lse_dim.hip): one launch
 // covers tiles [tile0, tile0 + grid / parts) of gw column groups each; with
-// parts > 1 a second kernel merges the parts' pairs from ws_pairs.
+// parts > 1 the last workgroup of each tile to arrive merges the parts' pairs
+// from ws_pairs in the same launch.
 struct DimArgs {
     bool bf16;
     bool vector_cols;      // 16-byte groups of columns (inner % K == 0, x 16-byte aligned)
