@@ -27,7 +27,10 @@
  * pointers owned by the caller and must stay valid until the stream reaches
  * the call. A handle owns a small device workspace for the split-row
  * schedule; calls that share one handle must not run concurrently (use one
- * handle per stream).
+ * handle per stream). The compute entry points allocate nothing, never
+ * synchronise and enqueue no memset (the split schedules' arrival counters
+ * are reset by the kernels that use them), so they may be captured into a
+ * HIP graph and the graph replayed.
  *
  * Errors. Every entry point returns an lse_status_t; nothing aborts. The
  * arguments of lse_forward are checked on the host before any HIP call, in
