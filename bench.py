@@ -334,7 +334,7 @@ def main() -> int:
     ap.add_argument("--rotate", type=int, default=None,
                     help="input copies cycled through (default: enough to exceed 2x the 256 MiB cache)")
     ap.add_argument("--all", action="store_true", help="also time the other four workloads")
-    ap.add_argument("--all-out", default="gpurun_out/bench_all.jsonl")
+    ap.add_argument("--all-out", default="bench_all.jsonl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--op", choices=["lse", "logprob", "backward", "dim"], default="lse",
