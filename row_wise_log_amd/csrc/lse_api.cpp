@@ -132,7 +132,8 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
         p->rows_per_wave = (64 / g) * rounds;
         const int64_t iters = ceil_div(rows, p->rows_per_wave);
         int64_t waves = iters;
-        const int wpc = tune.waves_per_cu ? tune.waves_per_cu : (g <= 4 ? kWavesPerCUNarrow : kWavesPerCUWide);
+        const int wpc = tune.waves_per_cu ? tune.waves_per_cu
+                                          : (g <= 4 ? kWavesPerCUNarrow : kWavesPerCUWide);
         const int64_t cap = static_cast<int64_t>(n_cu) * wpc;
         if (waves > cap) waves = cap;
         p->grid = ceil_div(waves, 4);
@@ -217,7 +218,8 @@ lse_status_t make_grad_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64
         int64_t r = std::max<int64_t>(1, (4 * kBatch) / units);
         r = std::min<int64_t>(r, std::max<int64_t>(1, ceil_div(rows, target_wgs)));
         const int64_t span = std::max(xs, gs);
-        r = std::min<int64_t>(r, std::max<int64_t>(1, ((int64_t{1} << 30) - units * ub) / std::max<int64_t>(span, 1)));
+        r = std::min<int64_t>(
+            r, std::max<int64_t>(1, ((int64_t{1} << 30) - units * ub) / std::max<int64_t>(span, 1)));
         a->rows_per_wg = r;
         a->chunk_units = units;
         a->chunks_per_row = 1;

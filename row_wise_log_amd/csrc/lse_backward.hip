@@ -181,7 +181,8 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
         for (int u = 0; u < U; ++u) {
             if constexpr (VEC) {
                 const u32x4 r = grad_vec<D>(t.w[u], t.l[u], t.g[u]);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, r), gr, t.go[u], 0, 2);
+                typedef unsigned v4u __attribute__((ext_vector_type(4)));
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, r), gr, t.go[u], 0, 2);
             } else {
                 const float v = grad_scalar<D>(t.e[u], t.l[u], t.g[u]);
                 if constexpr (D == DType::F32)

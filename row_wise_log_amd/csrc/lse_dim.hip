@@ -17,8 +17,8 @@
 // outputs (a 16-byte group of columns when inner is a multiple of K and x is
 // 16-byte aligned, else one column) and walks j, loading 16 bytes per step;
 // no lane talks to another while streaming. The workgroup's 256 lanes cover
-// a block of gw column groups x rw = 256 / gw steps of j: gw = 256 when a
-// j-row holds that many groups (a load step reads 4 KB of one row), or the
+// a block of gw column groups x rw = 256 / gw steps of j. The planner takes
+// gw = 32 or 64 (a load step reads rw pieces of 512 or 1024 bytes), or the
 // whole row (gw = inner / K) when it is shorter, so that rw consecutive rows,
 // again contiguous, are read at once (inner = 16 fp32: 64 rows of 64 bytes).
 // The lanes that share columns are merged through LDS at the end. When there
@@ -284,14 +284,16 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __syncthreads();
         if (t == 0) {
-            const unsigned prev =
-                __hip_atomic_fetch_add(counters + tl * kCounterWords, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned prev = __hip_atomic_fetch_add(counters + tl * kCounterWords, 1u,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             is_last = prev == static_cast<unsigned>(parts - 1);
         }
         __syncthreads();
         if (!is_last) return;
         merge_parts(tl);
-        if (t == 0) __hip_atomic_store(counters + tl * kCounterWords, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t == 0)
+            __hip_atomic_store(counters + tl * kCounterWords, 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -78,7 +78,8 @@ struct DimArgs {
     int64_t tile0;
     float* out;
     unsigned* ws_pairs;    // tiles * gw * K * parts (max, sum) pairs of one launch
-    unsigned* counters;    // one arrival counter per tile of a launch (kCounterWords apart), zero between calls
+    unsigned* counters;    // one arrival counter per tile of a launch (kCounterWords apart),
+                           // zero between calls
     hipStream_t stream;
 };
 
