@@ -277,3 +277,63 @@ def test_plan_rejects_bad_args():
         B.lse_plan(F32, 4, 8, 8, 0, 256, 9)
     with pytest.raises(B.LseError):
         B.lse_plan(5, 4, 8, 8, 0, 256, 0)
+
+
+# --- planner invariants over random shapes (hypothesis) -------------------
+
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+
+def _log_int(lo, hi):
+    """Integers spread over magnitudes, with the edges of each power of two."""
+    return st.one_of(st.integers(lo, min(hi, 64)),
+                     st.builds(lambda e, d: max(lo, min(hi, (1 << e) + d)),
+                               st.integers(0, hi.bit_length()), st.integers(-2, 2)))
+
+
+@settings(max_examples=600, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(dtype=st.sampled_from([F32, BF16]), rows=_log_int(1, 1 << 24), cols=_log_int(0, 1 << 26),
+       pad=st.sampled_from([0, 1, 3, 8, 64]), mis=st.integers(0, 7),
+       n_cu=st.sampled_from([1, 32, 104, 256, 304]), schedule=st.sampled_from([0, 1, 2, 3]))
+def test_plan_invariants(dtype, rows, cols, pad, mis, n_cu, schedule):
+    """Whatever the shape, the plan is one the kernels can run: an existing
+    instance, every element covered, grids and workspace within their limits."""
+    k = 4 if dtype == F32 else 8
+    esize = 16 // k
+    stride = cols + pad
+    addr = (mis * esize) % 16
+    p = B.lse_plan(dtype, rows, cols, stride, addr, n_cu, schedule)
+    aligned = addr % 16 == 0 and (rows == 1 or (stride * esize) % 16 == 0)
+    assert p["schedule"] in (B.LSE_SCHED_ROWS_PER_WAVE, B.LSE_SCHED_ROW_PER_WG,
+                             B.LSE_SCHED_SPLIT_ROW)
+    assert p["block"] in (64, 128, 256, 512, 1024)
+    assert 1 <= p["grid"] < (1 << 31)
+    if cols == 0:
+        assert p["schedule"] == B.LSE_SCHED_ROWS_PER_WAVE
+    if p["schedule"] == B.LSE_SCHED_ROWS_PER_WAVE:
+        g, vpl = p["lanes_per_row"], p["loads_per_lane"]
+        assert g in (1, 2, 4, 8, 16, 32, 64)
+        assert regs_instance(g, vpl, p["vector_loads"] == 1), (g, vpl)
+        if p["vector_loads"]:
+            assert aligned and cols // k >= 1
+            assert g * vpl >= cols // k and g >= cols % k and cols // k <= 256
+        else:
+            assert cols <= 1024 and g * vpl >= cols
+        rounds = 4 if vpl == 1 else 2 if vpl == 2 else 1
+        assert p["rows_per_wave"] == (64 // g) * rounds
+        waves = -(-rows // p["rows_per_wave"])
+        assert p["grid"] == -(-min(waves, n_cu * (8 if g <= 4 else 16)) // 4)
+    elif p["schedule"] == B.LSE_SCHED_ROW_PER_WG:
+        assert p["grid"] == rows and p["unroll"] in (4, 8) and p["vector_loads"] == 1
+        assert schedule == B.LSE_SCHED_ROW_PER_WG or not (schedule == 0 and rows < n_cu and
+                                                           cols * esize >= (256 << 10))
+    else:
+        batch = min(rows, B.LSE_SPLIT_MAX_ROWS)
+        assert 2 <= p["parts"] <= B.LSE_SPLIT_MAX_PARTS
+        assert p["grid"] == batch * p["parts"] and p["unroll"] in (4, 8)
+        assert p["workspace_bytes"] == batch * p["parts"] * 8 + batch * 4
+    if schedule == B.LSE_SCHED_SPLIT_ROW and cols > 0:
+        assert p["schedule"] == B.LSE_SCHED_SPLIT_ROW
+    if schedule == B.LSE_SCHED_ROW_PER_WG and cols > 0:
+        assert p["schedule"] == B.LSE_SCHED_ROW_PER_WG

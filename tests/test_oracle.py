@@ -185,3 +185,69 @@ def test_lse_dim_against_scipy_and_brute_force(oracle):
     assert got[0, 0] == -np.inf and np.isnan(got[0, 1]) and got[0, 2] == np.inf
     assert np.all(orc_mod.lse_dim(np.zeros((2, 0, 3), np.float32), "f32") == -np.inf)
 
+
+
+# --- the oracle against 50-digit decimal arithmetic (hypothesis) ------------
+
+import math  # noqa: E402
+from decimal import Decimal, localcontext  # noqa: E402
+
+from hypothesis import given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+
+def decimal_lse(values) -> float:
+    """log(sum(exp(v))) in 50-digit decimal arithmetic, which shares nothing
+    with the oracle's libm exp/log: each float converts to Decimal exactly,
+    -inf entries contribute nothing, and no exponent can overflow."""
+    fin = [v for v in values if v != -math.inf]
+    if not fin:
+        return -math.inf
+    with localcontext() as ctx:
+        ctx.prec, ctx.Emax, ctx.Emin = 50, 10 ** 9, -10 ** 9
+        m = Decimal(max(fin))
+        total = sum((Decimal(v) - m).exp() for v in fin)
+        return float(m + total.ln())
+
+
+_F32 = st.floats(min_value=-2.0 ** 100, max_value=2.0 ** 100, width=32, allow_nan=False)
+_ROW = st.lists(st.one_of(_F32, st.floats(-60, 60, width=32), st.just(-math.inf)),
+                min_size=1, max_size=48)
+
+
+@settings(max_examples=300, deadline=None)
+@given(rows=st.lists(_ROW, min_size=1, max_size=6))
+def test_oracle_matches_decimal_arithmetic_f32(oracle, rows):
+    """Rows of mixed magnitudes (up to 2^100), clustered values and -inf."""
+    width = max(len(r) for r in rows)
+    x = np.full((len(rows), width), -np.inf, dtype=np.float32)
+    for i, r in enumerate(rows):
+        x[i, :len(r)] = r
+    got = oracle.lse(x, "f32")
+    for i in range(len(rows)):
+        want = decimal_lse([float(v) for v in x[i]])
+        if math.isinf(want):
+            assert got[i] == want
+        else:
+            assert abs(got[i] - want) <= 1e-13 * max(1.0, abs(want)), (rows[i], got[i], want)
+
+
+@settings(max_examples=200, deadline=None)
+@given(bits=st.lists(st.lists(st.integers(0, 0xFFFF).filter(
+    lambda b: (b & 0x7F80) != 0x7F80 or b == 0xFF80), min_size=1, max_size=40),
+    min_size=1, max_size=4))
+def test_oracle_matches_decimal_arithmetic_bf16(oracle, bits):
+    """Every finite bf16 pattern (and -inf), decoded by placing the 16 bits
+    high in an fp32 word, against the decimal reference."""
+    width = max(len(r) for r in bits)
+    x = np.full((len(bits), width), 0xFF80, dtype=np.uint16)
+    for i, r in enumerate(bits):
+        x[i, :len(r)] = r
+    got = oracle.lse(x, "bf16")
+    vals = (x.astype(np.uint32) << 16).view(np.float32)
+    for i in range(len(bits)):
+        want = decimal_lse([float(v) for v in vals[i]])
+        if math.isinf(want):
+            assert got[i] == want
+        else:
+            assert abs(got[i] - want) <= 1e-13 * max(1.0, abs(want)), (bits[i], got[i], want)
