@@ -1,0 +1,134 @@
+"""A seeded sweep of random shapes through the C ABI, against the oracle.
+
+Each case draws a dtype, a row count, a row length (spread over magnitudes,
+1 to 400000, sometimes 0), a row padding, a misaligned start, a forced or
+automatic schedule and sometimes a block / unroll / parts tuning within the
+documented sets, plus rows of special values; lse_forward and
+lse_token_logprob (targets in and out of range) are compared with the
+float64 oracle. A second sweep does the same for lse_forward_dim over random
+[outer, n, inner] with forced or planned splits. The seeds are fixed, so every
+run checks the same cases; each case is printed before it runs.
+"""
+import numpy as np
+import pytest
+
+import oracle as oracle_mod
+import workloads
+from gpu_util import (DTYPE_CODE, SCHEDULES, compare, compare_logp, gpu_lse, gpu_token_logprob,
+                      note)
+from row_wise_log_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+MAX_ELEMS = 3_000_000  # keeps each case's oracle call short
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def handle(torch_gpu):
+    h = B.lse_create(0)
+    yield h
+    torch_gpu.cuda.synchronize()
+    B.lse_destroy(h)
+
+
+def log_int(rng, lo, hi):
+    """An integer spread evenly over orders of magnitude in [lo, hi]."""
+    v = np.exp(rng.uniform(np.log(lo), np.log(hi + 1)))
+    return int(min(hi, max(lo, v)))
+
+
+def make_rows(rng, rows, width, dtype, scale):
+    v = rng.normal(0.0, scale, size=(rows, width)).astype(np.float32)
+    if rows >= 4 and width > 0 and rng.random() < 0.5:
+        r = rng.integers(rows, size=4)
+        v[r[0]] = -np.inf                                  # a row of -inf
+        v[r[1], rng.integers(width)] = np.nan              # a NaN
+        v[r[2], rng.integers(width)] = np.inf              # a +inf
+        v[r[3]] += rng.choice([-1e3, 1e3, 3e9])            # large offsets, one beyond 2^30
+    return workloads.f32_to_bf16_bits(v) if dtype == "bf16" else v
+
+
+def row_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        dtype = ["f32", "bf16"][rng.integers(2)]
+        cols = 0 if rng.random() < 0.04 else log_int(rng, 1, 400_000)
+        rows = log_int(rng, 1, 4000)
+        while rows > 1 and rows * max(cols, 1) > MAX_ELEMS:
+            rows //= 2
+        pad = int(rng.choice([0, 0, 1, 5, 8, 24]))
+        front = int(rng.choice([0, 0, 1, 2, 3]))
+        sched = SCHEDULES[rng.integers(len(SCHEDULES))]
+        tuning = (0, 0, 0, 0, 0)
+        if rng.random() < 0.3:
+            tuning = (int(rng.choice([0, 64, 128, 256, 512, 1024])), int(rng.choice([0, 4, 8])),
+                      int(rng.choice([0, 2, 3, 7, 64])), int(rng.choice([0, 1, 8, 64])),
+                      int(rng.choice([0, 1, 2, 4, 64])))
+        scale = float(rng.choice([0.5, 3.0, 30.0]))
+        yield i, dtype, rows, cols, pad, front, sched, tuning, scale, rng
+
+
+@pytest.mark.parametrize("block", range(8))
+def test_random_rows(torch_gpu, handle, oracle, block):
+    for i, dtype, rows, cols, pad, front, sched, tuning, scale, rng in row_cases(100 + block, 50):
+        full = make_rows(rng, rows, cols + pad, dtype, scale)
+        x = full[:, :cols]
+        what = (f"block {block} case {i}: {dtype} rows={rows} cols={cols} pad={pad} front={front} "
+                f"schedule={sched} tuning={tuning}")
+        note(what)
+        got = gpu_lse(torch_gpu, handle, x, dtype, sched, pad_front=front, tuning=tuning)
+        xc = np.ascontiguousarray(x)
+        ref = oracle.lse(xc, dtype, threads=8)
+        compare(got, ref, dtype, what)
+        if cols > 0 and rows > 0:
+            targets = rng.integers(-2, cols + 2, size=rows)
+            logp, lse = gpu_token_logprob(torch_gpu, handle, x, targets, dtype, sched,
+                                          pad_front=front, tuning=tuning)
+            compare(lse, ref, dtype, what + " (token path LSE)")
+            compare_logp(logp, oracle.token_logprob(xc, targets, dtype, threads=8), ref, dtype,
+                         what + " (logp)")
+
+
+def gpu_dim(torch, handle, x3, dtype, front, parts):
+    outer, n, inner = x3.shape
+    flat = np.zeros(front + x3.size, dtype=x3.dtype)
+    flat[front:] = x3.ravel()
+    t = torch.from_numpy(flat.view(np.int16 if dtype == "bf16" else np.int32)).to("cuda")
+    out = torch.full((max(outer * inner, 1),), 123.0, dtype=torch.float32, device="cuda")
+    B.lse_set_tuning(handle, 0, 0, parts, 0, 0)
+    try:
+        B.lse_forward_dim(handle, t.data_ptr() + front * x3.itemsize, DTYPE_CODE[dtype], outer,
+                          n, inner, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    finally:
+        B.lse_set_tuning(handle, 0, 0, 0, 0, 0)
+    return out.cpu().numpy()[: outer * inner]
+
+
+@pytest.mark.parametrize("block", range(6))
+def test_random_dims(torch_gpu, handle, block):
+    rng = np.random.default_rng(200 + block)
+    for i in range(30):
+        dtype = ["f32", "bf16"][rng.integers(2)]
+        outer, n, inner = log_int(rng, 1, 64), log_int(rng, 1, 60_000), log_int(rng, 1, 5000)
+        while outer * n * inner > MAX_ELEMS:
+            if n > 1:
+                n //= 2
+            else:
+                inner = max(1, inner // 2)
+        front = int(rng.choice([0, 0, 1]))
+        parts = int(rng.choice([0, 0, 1, 2, 5, 64]))
+        x = make_rows(rng, outer * n, inner, dtype, float(rng.choice([0.5, 3.0, 30.0])))
+        x3 = x.reshape(outer, n, inner)
+        what = f"dim block {block} case {i}: {dtype} {x3.shape} front={front} parts={parts}"
+        note(what)
+        got = gpu_dim(torch_gpu, handle, x3, dtype, front, parts)
+        compare(got, oracle_mod.lse_dim(x3, dtype, threads=8).ravel(), dtype, what)
