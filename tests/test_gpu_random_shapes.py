@@ -7,15 +7,17 @@ documented sets, plus rows of special values; lse_forward and
 lse_token_logprob (targets in and out of range) are compared with the
 float64 oracle. A second sweep does the same for lse_forward_dim over random
 [outer, n, inner] with forced or planned splits. The seeds are fixed, so every
-run checks the same cases; each case is printed before it runs.
+run checks the same cases; each case is printed before it runs. A third
+sweep runs lse_backward on random shapes with padded and misaligned x and
+gradient rows.
 """
 import numpy as np
 import pytest
 
 import oracle as oracle_mod
 import workloads
-from gpu_util import (DTYPE_CODE, SCHEDULES, compare, compare_logp, gpu_lse, gpu_token_logprob,
-                      note)
+from gpu_util import (DTYPE_CODE, SCHEDULES, compare, compare_grad, compare_logp, gpu_backward,
+                      gpu_lse, gpu_token_logprob, note)
 from row_wise_log_amd import binding as B
 
 pytestmark = pytest.mark.gpu
@@ -132,3 +134,33 @@ def test_random_dims(torch_gpu, handle, block):
         note(what)
         got = gpu_dim(torch_gpu, handle, x3, dtype, front, parts)
         compare(got, oracle_mod.lse_dim(x3, dtype, threads=8).ravel(), dtype, what)
+
+
+@pytest.mark.parametrize("block", range(4))
+def test_random_backward(torch_gpu, handle, oracle, block):
+    rng = np.random.default_rng(300 + block)
+    for i in range(30):
+        dtype = ["f32", "bf16"][rng.integers(2)]
+        cols = log_int(rng, 1, 300_000)
+        rows = log_int(rng, 1, 3000)
+        while rows > 1 and rows * cols > MAX_ELEMS // 2:
+            rows //= 2
+        pad = int(rng.choice([0, 0, 1, 8]))
+        front, gpad, gfront = (int(rng.choice([0, 0, 1])), int(rng.choice([0, 0, 3, 8])),
+                               int(rng.choice([0, 0, 2])))
+        full = make_rows(rng, rows, cols + pad, dtype, float(rng.choice([0.5, 3.0, 30.0])))
+        x = full[:, :cols]
+        xc = np.ascontiguousarray(x)
+        lse32 = oracle.lse(xc, dtype, threads=8).astype(np.float32)
+        g = rng.normal(0, 2, size=rows).astype(np.float32)
+        what = (f"backward block {block} case {i}: {dtype} rows={rows} cols={cols} pad={pad} "
+                f"front={front} grad_pad={gpad} grad_front={gfront}")
+        note(what)
+        got, untouched = gpu_backward(torch_gpu, handle, x, lse32, g, dtype, pad_front=front,
+                                      grad_pad=gpad, grad_front=gfront)
+        assert untouched, what + ": bytes outside grad_x's rows were written"
+        ref = oracle.softmax_grad(xc, lse32, g, dtype, threads=8)
+        vals = (workloads.bf16_bits_to_f32(xc) if dtype == "bf16" else xc).astype(np.float64)
+        with np.errstate(invalid="ignore"):
+            d = vals - lse32.astype(np.float64)[:, None]
+        compare_grad(got, ref, d, g, dtype, what)
