@@ -336,8 +336,7 @@ __global__ __launch_bounds__(256) void rows_in_registers(const char* __restrict_
 // Lane t takes vectors t, t + BLOCK, ... in batches of U loads issued before
 // any is used.
 template <DType D, int BLOCK, int U, bool SPLIT, bool TOK>
-__global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
-                                                     int64_t rows, int64_t cols,
+__global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x, int64_t cols,
                                                      int64_t stride_bytes,
                                                      float* __restrict__ out, int parts,
                                                      unsigned* __restrict__ ws_pairs,
@@ -514,7 +513,8 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
         }
         b = block_merge<BLOCK>(pm, base2_ref(pm), ps, pairs);
         if (tid == 0)
-            __hip_atomic_store(counters + row * kCounterWords, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(counters + row * kCounterWords, 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 
     float r;
@@ -601,11 +601,11 @@ template <DType D, int BLOCK, int U, bool SPLIT>
 hipError_t launch_stream(const LaunchArgs& a) {
     if (a.targets != nullptr)
         hipLaunchKernelGGL((stream_rows<D, BLOCK, U, SPLIT, true>), dim3(a.grid), dim3(BLOCK), 0,
-                           a.stream, a.x, a.rows, a.cols, a.stride_bytes, a.out, a.parts,
+                           a.stream, a.x, a.cols, a.stride_bytes, a.out, a.parts,
                            a.ws_pairs, a.counters, a.targets, a.logp);
     else
         hipLaunchKernelGGL((stream_rows<D, BLOCK, U, SPLIT, false>), dim3(a.grid), dim3(BLOCK), 0,
-                           a.stream, a.x, a.rows, a.cols, a.stride_bytes, a.out, a.parts,
+                           a.stream, a.x, a.cols, a.stride_bytes, a.out, a.parts,
                            a.ws_pairs, a.counters, nullptr, nullptr);
     return hipGetLastError();
 }
