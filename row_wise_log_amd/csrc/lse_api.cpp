@@ -208,8 +208,15 @@ lse_status_t make_grad_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64
     a->gs_bytes = gs;
     const int64_t target_wgs = 4 * static_cast<int64_t>(n_cu);
     if (units >= kBatch) {
-        int64_t chunk = ceil_div(ceil_div(rows * units, target_wgs), kBatch) * kBatch;
-        chunk = std::min<int64_t>(std::max<int64_t>(chunk, kBatch), 4 * kBatch);
+        // Long rows: one batch per workgroup once there are at least 16 per
+        // CU (measured on 130 MB to 2 GB inputs, 3-11 % faster than chunks of
+        // up to four batches); smaller inputs keep chunks of one to four
+        // batches, about four workgroups per CU.
+        int64_t chunk = kBatch;
+        if (rows * units < 16 * static_cast<int64_t>(n_cu) * kBatch) {
+            chunk = ceil_div(ceil_div(rows * units, target_wgs), kBatch) * kBatch;
+            chunk = std::min<int64_t>(std::max<int64_t>(chunk, kBatch), 4 * kBatch);
+        }
         a->rows_per_wg = 1;
         a->chunk_units = chunk;
         a->chunks_per_row = ceil_div(units, chunk);
