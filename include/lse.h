@@ -83,9 +83,9 @@ typedef enum {
  * Queries the compute-unit count, allocates the split-row workspace
  * (LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS (max, sum) pairs plus one
  * counter per row, each in its own 256 bytes, about 0.75 MiB, the counters
- * zeroed) and lse_forward_dim's
- * workspace (LSE_DIM_MAX_PAIRS pairs, 32 MiB), and synchronises once. On success
- * *out receives the handle; on failure *out is set to NULL.
+ * zeroed) and lse_forward_dim's workspace (LSE_DIM_MAX_PAIRS pairs, 32 MiB),
+ * and synchronises once. On success *out receives the handle; on failure
+ * *out is set to NULL.
  * Errors: INVALID_ARG (out NULL, device out of range), NO_DEVICE (no device
  * or not gfx950), ALLOC, HIP.
  */
@@ -118,12 +118,11 @@ lse_status_t lse_forward(lse_handle_t h, const void *x, lse_dtype_t dtype,
  *
  *     logp[r] = x[r, t] - LSE(x[r, 0:cols])
  *
- * the log-probability of column t under a softmax over the row. The pages'
- * motivating workload computes exactly this per generated token in RLHF
- * training: the log-probability of the sampled token under the model's logits
- * over the vocabulary, which the paper names as LSE's use in per-token LLM
- * log-probabilities (§1, §5.1). The subtraction is one fp32 operation on the
- * decoded element and the fp32 LSE; x is read once, as by lse_forward.
+ * the log-probability of column t under a softmax over the row. This is the
+ * quantity behind the paper's motivating workload (§1, §5.1): per generated
+ * token in RLHF training, the log-probability of the sampled token under the
+ * model's logits over the vocabulary. The subtraction is one fp32 operation on
+ * the decoded element and the fp32 LSE; x is read once, as by lse_forward.
  *   targets    device pointer to rows int64 column indices, 8-byte aligned.
  *              A target outside [0, cols) gives logp[r] = NaN.
  *   logp       device pointer to rows fp32 outputs, 4-byte aligned.
@@ -207,7 +206,8 @@ lse_status_t lse_set_schedule(lse_handle_t h, lse_schedule_t s);
 
 /* Tuning overrides, for measurement. Streaming schedules: threads per
  * workgroup `block` (64, 128, 256, 512 or 1024), 16-byte loads per lane per
- * batch `unroll` (4 or 8), SPLIT_ROW workgroups per row `parts` (1..64).
+ * batch `unroll` (4 or 8), SPLIT_ROW workgroups per row `parts` (1..64;
+ * lse_forward_dim takes it as its workgroups per tile along n).
  * ROWS_PER_WAVE: at most `waves_per_cu` wavefronts per compute unit in the
  * grid (1..1024; the wavefronts loop over the rest) and `lanes_per_row` lanes
  * sharing a row (a power of two up to 64; ignored where no kernel instance
