@@ -1,0 +1,123 @@
+"""Byte offsets beyond 2^31 and 2^32: rows 4 GiB apart, and a non-last-axis
+reduction over arrays of 6 to 9 GB (an MI355X holds 288 GB).
+
+* lse_forward, lse_token_logprob and lse_backward on 3 rows placed 2^30 + 64
+  fp32 elements (4 GiB + 256 bytes) or 2^31 + 64 bf16 elements apart, for a
+  register-rows width and a streaming width; results against the oracle, and
+  the backward's output buffer (filled with a pattern no gradient can take)
+  changes in exactly rows x cols elements.
+* lse_forward_dim over [1, n, inner] with inner = 2^30 + 8 (bf16, vector
+  path) and 2^29 + 3 (fp32, element path): all columns zero except 64
+  sampled ones, so every untouched output must be ln n; the sampled columns
+  against the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as oracle_mod
+import workloads
+from gpu_util import DTYPE_CODE, compare, compare_grad, compare_logp, note
+from row_wise_log_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def handle(torch_gpu):
+    h = B.lse_create(0)
+    yield h
+    torch_gpu.cuda.synchronize()
+    B.lse_destroy(h)
+
+
+def _rows(dtype, rows, cols, seed):
+    v = np.random.default_rng(seed).normal(0, 4, size=(rows, cols)).astype(np.float32)
+    v[1, cols // 3] = 40.0
+    return workloads.f32_to_bf16_bits(v) if dtype == "bf16" else v
+
+
+@pytest.mark.parametrize("dtype,stride", [("f32", (1 << 30) + 64), ("bf16", (1 << 31) + 64)])
+@pytest.mark.parametrize("cols", [1000, 300_000])
+def test_rows_four_gib_apart(torch_gpu, handle, oracle, dtype, stride, cols):
+    torch = torch_gpu
+    rows = 3
+    st = torch.int16 if dtype == "bf16" else torch.int32
+    host = _rows(dtype, rows, cols, seed=cols)
+    hv = host.view(np.int16 if dtype == "bf16" else np.int32)
+    n = (rows - 1) * stride + cols
+    note(f"large offsets {dtype} stride={stride} cols={cols}: {n * host.itemsize / 2**30:.1f} GiB")
+    x = torch.zeros(n, dtype=st, device="cuda")
+    for r in range(rows):
+        x[r * stride: r * stride + cols] = torch.from_numpy(hv[r].copy()).cuda()
+    code, s = DTYPE_CODE[dtype], torch.cuda.current_stream().cuda_stream
+    ref = oracle.lse(host, dtype)
+    out = torch.full((rows,), float("nan"), device="cuda")
+    B.lse_forward(handle, x.data_ptr(), code, rows, cols, stride, out.data_ptr(), s)
+    torch.cuda.synchronize()
+    compare(out.cpu().numpy(), ref, dtype, f"forward {dtype} cols={cols}")
+    targets = np.array([0, cols // 3, cols - 1], dtype=np.int64)
+    logp = torch.empty(rows, device="cuda")
+    tg = torch.from_numpy(targets).cuda()   # kept alive until the call has run
+    B.lse_token_logprob(handle, x.data_ptr(), code, rows, cols, stride, tg.data_ptr(),
+                        logp.data_ptr(), None, s)
+    torch.cuda.synchronize()
+    compare_logp(logp.cpu().numpy(), oracle.token_logprob(host, targets, dtype), ref, dtype,
+                 f"token logprob {dtype} cols={cols}")
+    # backward into an equally spread gradient buffer, pre-filled with a pattern
+    # (bf16 0x7F7F, fp32 0x7F7F7F7F: about 3.4e38) that no gradient here can take
+    lse32 = ref.astype(np.float32)
+    g = np.array([1.0, -2.0, 0.5], dtype=np.float32)
+    sentinel = 0x7F7F if dtype == "bf16" else 0x7F7F7F7F
+    gx = torch.full((n,), sentinel, dtype=st, device="cuda")
+    # the device copies of lse and g must outlive the call: a temporary freed
+    # while the arguments are evaluated would hand its memory to the next one
+    lt, gt = torch.from_numpy(lse32).cuda(), torch.from_numpy(g).cuda()
+    B.lse_backward(handle, x.data_ptr(), code, rows, cols, stride, lt.data_ptr(), gt.data_ptr(),
+                   gx.data_ptr(), stride, s)
+    torch.cuda.synchronize()
+    assert int((gx != sentinel).sum()) == rows * cols, "writes outside grad_x's rows"
+    got = np.stack([gx[r * stride: r * stride + cols].cpu().numpy() for r in range(rows)])
+    got = (workloads.bf16_bits_to_f32(got.view(np.uint16)) if dtype == "bf16"
+           else got.view(np.float32))
+    vals = (workloads.bf16_bits_to_f32(host) if dtype == "bf16" else host).astype(np.float64)
+    compare_grad(got, oracle.softmax_grad(host, lse32, g, dtype),
+                 vals - lse32.astype(np.float64)[:, None], g, dtype, f"backward {dtype} cols={cols}")
+    del x, gx, lt, gt, tg
+
+
+@pytest.mark.parametrize("dtype,n,inner", [("bf16", 3, (1 << 30) + 8), ("f32", 4, (1 << 29) + 3)])
+def test_dim_over_large_arrays(torch_gpu, handle, dtype, n, inner):
+    torch = torch_gpu
+    st = torch.int16 if dtype == "bf16" else torch.int32
+    note(f"large dim {dtype} n={n} inner={inner}: {n * inner * (2 if dtype == 'bf16' else 4) / 1e9:.1f} GB")
+    x = torch.zeros((n, inner), dtype=st, device="cuda")
+    rng = np.random.default_rng(inner)
+    cols = np.unique(np.concatenate([rng.integers(0, inner, size=60), [0, 1, inner - 2, inner - 1]]))
+    vals = rng.normal(0, 5, size=(n, len(cols))).astype(np.float32)
+    vals[0, 0] = 60.0
+    hv = workloads.f32_to_bf16_bits(vals) if dtype == "bf16" else vals
+    idx = torch.from_numpy(cols).cuda()
+    x[:, idx] = torch.from_numpy(hv.view(np.int16 if dtype == "bf16" else np.int32)).cuda()
+    out = torch.full((inner,), float("nan"), device="cuda")
+    B.lse_forward_dim(handle, x.data_ptr(), DTYPE_CODE[dtype], 1, n, inner, out.data_ptr(),
+                      torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ln_n = math.log(n)
+    mask = torch.ones(inner, dtype=torch.bool, device="cuda")
+    mask[idx] = False
+    tol = 1e-5 if dtype == "bf16" else 2e-6
+    bad = int(((out - ln_n).abs() > tol * max(1.0, ln_n))[mask].sum())
+    assert bad == 0, f"{bad} untouched columns differ from ln {n}"
+    ref = oracle_mod.lse(np.ascontiguousarray(hv.T), dtype)   # each sampled column is a row of n
+    compare(out[idx].cpu().numpy(), ref, dtype, f"dim {dtype} sampled columns")
+    del x, out
