@@ -8,6 +8,18 @@ if str(ROOT) not in sys.path:
     sys.path.insert(0, str(ROOT))
 
 
+def pytest_sessionstart(session):
+    """Build the HIP library in-tree when it is not there yet (a fresh checkout
+    on a machine with hipcc); a library that is already built is used as is.
+    The float64 oracle builds itself on first use the same way."""
+    lib = ROOT / "row_wise_log_amd" / "liblse_amd.so"
+    if not lib.exists():
+        import shutil
+        if shutil.which("hipcc") or Path("/opt/rocm/bin/hipcc").exists():
+            from row_wise_log_amd import build
+            build.build()
+
+
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP library through its C ABI")
