@@ -47,9 +47,11 @@ def _check_input(x):
     return codes[x.dtype], rows, cols, (x.stride(0) if rows > 1 else cols)
 
 
-def logsumexp_dim(x, dim: int, handle_=None):
-    """LSE over axis `dim` of a contiguous fp32/bf16 GPU tensor of any rank,
-    as fp32 with that axis removed (torch.logsumexp(x, dim) semantics)."""
+def logsumexp_dim(x, dim, keepdim: bool = False, handle_=None):
+    """LSE over axis `dim` of a contiguous fp32/bf16 GPU tensor of any rank, as
+    fp32 (torch.logsumexp(x, dim, keepdim) semantics). `dim` may also be a
+    tuple of adjacent axes, which a contiguous tensor holds as one axis; other
+    tuples raise NotImplementedError."""
     import torch
 
     from .binding import LSE_DTYPE_BF16, LSE_DTYPE_F32, lse_forward_dim
@@ -59,19 +61,29 @@ def logsumexp_dim(x, dim: int, handle_=None):
         raise TypeError(f"unsupported dtype {x.dtype}: fp32 or bf16")
     if not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous GPU tensor")
-    d = dim % x.dim()
+    if x.dim() == 0:
+        raise ValueError("x must have at least one axis")
+    dims = sorted({d % x.dim() for d in (dim if isinstance(dim, (tuple, list)) else (dim,))})
+    if not dims:
+        raise ValueError("dim must name at least one axis")
+    if dims != list(range(dims[0], dims[-1] + 1)):
+        raise NotImplementedError("the reduced axes must be adjacent")
+    d0, d1 = dims[0], dims[-1]
     shape = list(x.shape)
     outer = 1
-    for s in shape[:d]:
-        outer *= s
+    for s_ in shape[:d0]:
+        outer *= s_
+    n = 1
+    for s_ in shape[d0:d1 + 1]:
+        n *= s_
     inner = 1
-    for s in shape[d + 1:]:
-        inner *= s
-    out = torch.empty(shape[:d] + shape[d + 1:], dtype=torch.float32, device=x.device)
+    for s_ in shape[d1 + 1:]:
+        inner *= s_
+    kept = shape[:d0] + ([1] * (d1 - d0 + 1) if keepdim else []) + shape[d1 + 1:]
+    out = torch.empty(kept, dtype=torch.float32, device=x.device)
     h = handle_ if handle_ is not None else handle(x.device.index or 0)
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    lse_forward_dim(h, x.data_ptr(), codes[x.dtype], outer, shape[d], inner, out.data_ptr(),
-                    stream)
+    lse_forward_dim(h, x.data_ptr(), codes[x.dtype], outer, n, inner, out.data_ptr(), stream)
     return out
 
 

@@ -144,3 +144,26 @@ def test_package_logsumexp_dim(torch_gpu):
         want = torch.logsumexp(torch.from_numpy(v).double(), dim=d).numpy()
         assert got.shape == want.shape
         assert np.all(np.abs(got - want) <= 2e-6 * np.maximum(1.0, np.abs(want))), d
+
+
+def test_package_keepdim_and_adjacent_axes(torch_gpu):
+    """logsumexp_dim against torch.logsumexp in float64 on the CPU: keepdim,
+    negative axes, tuples of adjacent axes (one reduced axis of a contiguous
+    tensor), every axis of a rank-1 tensor, and the refusal of other tuples."""
+    import row_wise_log_amd as R
+    torch = torch_gpu
+    rng = np.random.default_rng(13)
+    v = rng.normal(0, 3, size=(4, 6, 5, 7)).astype(np.float32)
+    xt = torch.from_numpy(v).cuda()
+    xc = torch.from_numpy(v).double()
+    for dim in [0, -1, 2, (1, 2), (0, 1), (2, 3), (0, 1, 2, 3), (-2, -1)]:
+        for keepdim in (False, True):
+            note(f"package logsumexp_dim dim={dim} keepdim={keepdim}")
+            got = R.logsumexp_dim(xt, dim, keepdim=keepdim).cpu().double()
+            want = torch.logsumexp(xc, dim=dim, keepdim=keepdim)
+            assert got.shape == want.shape, (dim, keepdim, got.shape, want.shape)
+            assert torch.all((got - want).abs() <= 2e-6 * torch.clamp(want.abs(), min=1.0)), (dim, keepdim)
+    one = torch.from_numpy(v[0, 0, 0]).cuda()
+    assert abs(float(R.logsumexp_dim(one, 0)) - float(torch.logsumexp(one.double().cpu(), 0))) < 2e-5
+    with pytest.raises(NotImplementedError):
+        R.logsumexp_dim(xt, (0, 2))

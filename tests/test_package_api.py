@@ -33,6 +33,8 @@ def test_logsumexp_dim_rejects_bad_tensors():
         R.logsumexp_dim(torch.zeros(2, 3, dtype=torch.float16), 1)
     with pytest.raises(ValueError, match="contiguous GPU"):
         R.logsumexp_dim(torch.zeros(2, 3), 1)
+    with pytest.raises(ValueError, match="contiguous GPU"):
+        R.logsumexp_dim(torch.zeros(2, 3), (0, 1), keepdim=True)
 
 
 def test_missing_library_is_an_error(tmp_path):
