@@ -46,3 +46,17 @@ def test_missing_library_is_an_error(tmp_path):
             B.load(tmp_path / "liblse_amd.so")
     finally:
         B._lib = saved
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with a message."""
+    import json
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parent.parent
+    proc = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"],
+                          capture_output=True, text=True, timeout=300, cwd=root)
+    assert proc.returncode == 2
+    msg = json.loads(proc.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
