@@ -11,6 +11,8 @@ libm ``exp``/``log``; its header states the definition and the special
 cases). ``token_logprob(x, targets, dtype)`` returns x[r, targets[r]] minus
 that LSE (NaN for a target outside [0, cols)); ``softmax_grad(x, lse, g,
 dtype)`` returns the backward pass g[r] * exp(x[r, j] - lse[r]) in float64;
+``token_logprob_grad(x, targets, lse, g, dtype)`` returns the token
+log-probability's backward pass g[r] * ([j == t_r] - exp(x[r, j] - lse[r]));
 ``lse_dim(x3, dtype)`` reduces the middle axis of an [outer, n, inner] array
 (torch.logsumexp over a non-last axis) by moving that axis last and calling
 the row oracle.
@@ -68,6 +70,12 @@ class Oracle:
                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                        ctypes.c_int]
         self._fn_grad = fn
+        fn = self._lib.lse_oracle_token_logprob_grad_f64
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                       ctypes.c_void_p, ctypes.c_int]
+        self._fn_tok_grad = fn
 
     def softmax_grad(self, x: np.ndarray, lse, grad_out, dtype: str | None = None,
                      threads: int = 1) -> np.ndarray:
@@ -84,6 +92,26 @@ class Oracle:
                            out.ctypes.data, int(threads))
         if rc != 0:
             raise ValueError("lse_oracle_softmax_grad_f64 rejected its arguments")
+        return out
+
+    def token_logprob_grad(self, x: np.ndarray, targets, lse, grad_logp,
+                           dtype: str | None = None, threads: int = 1) -> np.ndarray:
+        """grad_logp[r] * ([j == t_r] - exp(x[r, j] - lse[r])) in float64, shape
+        (rows, cols); a row of NaN for a target outside [0, cols). lse and
+        grad_logp are taken as fp32."""
+        x, dtype, rows, cols, stride = self._prepare(x, dtype)
+        t = np.ascontiguousarray(np.asarray(targets, dtype=np.int64))
+        lse = np.ascontiguousarray(np.asarray(lse, dtype=np.float32))
+        g = np.ascontiguousarray(np.asarray(grad_logp, dtype=np.float32))
+        if t.shape != (rows,) or lse.shape != (rows,) or g.shape != (rows,):
+            raise ValueError("targets, lse and grad_logp must hold one value per row")
+        out = np.full((rows, cols), np.nan, dtype=np.float64)
+        rc = self._fn_tok_grad(x.ctypes.data if x.size else None, DTYPES[dtype], rows, cols,
+                               stride, t.ctypes.data if rows else None,
+                               lse.ctypes.data if rows else None, g.ctypes.data if rows else None,
+                               out.ctypes.data, int(threads))
+        if rc != 0:
+            raise ValueError("lse_oracle_token_logprob_grad_f64 rejected its arguments")
         return out
 
     @staticmethod
@@ -170,6 +198,11 @@ def token_logprob(x: np.ndarray, targets, dtype: str | None = None, threads: int
 def softmax_grad(x: np.ndarray, lse, grad_out, dtype: str | None = None,
                  threads: int = 1) -> np.ndarray:
     return default().softmax_grad(x, lse, grad_out, dtype, threads)
+
+
+def token_logprob_grad(x: np.ndarray, targets, lse, grad_logp, dtype: str | None = None,
+                       threads: int = 1) -> np.ndarray:
+    return default().token_logprob_grad(x, targets, lse, grad_logp, dtype, threads)
 
 
 def lse_dim(x3: np.ndarray, dtype: str | None = None, threads: int = 1) -> np.ndarray:

@@ -47,6 +47,14 @@
  *     out[r, j] = grad_out[r] * exp(x[r, j] - lse[r])
  * in float64, row r at out + r * cols.
  *
+ * Backward of the token log-probability (lse_oracle_token_logprob_grad_f64).
+ * logp[r] = x[r, t] - LSE(x[r, :]) has derivative [j == t] - softmax_j with
+ * respect to x[r, j]; with the forward LSE lse[r] and an incoming gradient
+ * grad_logp[r] (both fp32), the oracle writes
+ *     out[r, j] = grad_logp[r] * ([j == t] - exp(x[r, j] - lse[r]))
+ * in float64. A target outside [0, cols) (whose log-probability is NaN)
+ * gives a row of NaN.
+ *
  * The rows are split over `nthreads` POSIX threads; a row's arithmetic does
  * not depend on the thread count.
  *
@@ -126,6 +134,19 @@ static void softmax_grad_one_row(const void *x, int dtype, int64_t start, int64_
         out[j] = grad_out * exp(load_elem(x, dtype, start + j) - lse);
 }
 
+/* One row of the token log-probability's backward pass:
+ * g * ([j == t] - exp(x_j - lse)); a row of NaN when t is outside [0, cols). */
+static void token_grad_one_row(const void *x, int dtype, int64_t start, int64_t cols, int64_t t,
+                               double lse, double g, double *out)
+{
+    const int valid = t >= 0 && t < cols;
+    int64_t k;
+    for (k = 0; k < cols; ++k) {
+        const double p = exp(load_elem(x, dtype, start + k) - lse);   /* softmax_k */
+        out[k] = valid ? g * ((k == t ? 1.0 : 0.0) - p) : NAN;
+    }
+}
+
 struct job {
     const void *x;
     int dtype;
@@ -140,7 +161,10 @@ static void *run_rows(void *arg)
     const struct job *jb = (const struct job *)arg;
     int64_t r;
     for (r = jb->row_begin; r < jb->row_end; ++r) {
-        if (jb->lse != NULL)
+        if (jb->lse != NULL && jb->targets != NULL)
+            token_grad_one_row(jb->x, jb->dtype, r * jb->row_stride, jb->cols, jb->targets[r],
+                               jb->lse[r], jb->grad_out[r], &jb->out[r * jb->cols]);
+        else if (jb->lse != NULL)
             softmax_grad_one_row(jb->x, jb->dtype, r * jb->row_stride, jb->cols,
                                  (double)jb->lse[r], (double)jb->grad_out[r],
                                  jb->out + r * jb->cols);
@@ -247,4 +271,21 @@ int lse_oracle_softmax_grad_f64(const void *x, int dtype, int64_t rows, int64_t 
     if (rows > 0 && (lse == NULL || grad_out == NULL))
         return -1;
     return run_all(x, dtype, rows, cols, row_stride, NULL, lse, grad_out, out, nthreads);
+}
+
+/*
+ * out[r * cols + j] = grad_logp[r] * ([j == t] - exp(x[r, j] - lse[r])) with
+ * t = targets[r], for r in [0, rows), j in [0, cols); a row of NaN when t is
+ * outside [0, cols). Arguments as lse_oracle_f64; `targets`, `lse` and
+ * `grad_logp` are host pointers to rows values and must not be null when
+ * rows > 0.
+ */
+int lse_oracle_token_logprob_grad_f64(const void *x, int dtype, int64_t rows, int64_t cols,
+                                      int64_t row_stride, const int64_t *targets,
+                                      const float *lse, const float *grad_logp, double *out,
+                                      int nthreads)
+{
+    if (rows > 0 && (targets == NULL || lse == NULL || grad_logp == NULL))
+        return -1;
+    return run_all(x, dtype, rows, cols, row_stride, targets, lse, grad_logp, out, nthreads);
 }

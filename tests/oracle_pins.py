@@ -443,6 +443,100 @@ def pin_grad_argument_checks(orc):
     assert fn(x.ctypes.data, 0, 4, 4, 3, lse.ctypes.data, lse.ctypes.data, out.ctypes.data, 1) == -1
 
 
+# --- backward of the token log-probability ----------------------------------
+# logp = x_t - LSE(x) has derivative [j == t] - softmax_j. The oracle takes the
+# forward LSE as fp32 (lse32), so its exact result is
+# g * ([j == t] - softmax_j * exp(L - lse32)) with L the exact LSE.
+
+def _logp(vals, t):
+    return vals[t] - brute_lse(vals)
+
+
+def _fd_logp(vals, t, j, h=1e-4):
+    up = list(vals)
+    dn = list(vals)
+    up[j] += h
+    dn[j] -= h
+    return (_logp(up, t) - _logp(dn, t)) / (2 * h)
+
+
+def pin_tokgrad_finite_difference(orc):
+    """Central differences of the brute-force log-probability, element by element."""
+    rng = np.random.default_rng(30)
+    for cols in (1, 2, 5, 16):
+        x = rng.uniform(-15, 15, size=(4, cols + 3)).astype(np.float32)[:, :cols]  # padded rows
+        t = rng.integers(0, cols, size=4)
+        vals = [[float(v) for v in row] for row in x]
+        exact = [brute_lse(v) for v in vals]
+        lse32 = np.array(exact, dtype=np.float32)
+        g = np.array([1.0, -3.0, 0.25, 2.0], dtype=np.float32)
+        got = orc.token_logprob_grad(x, t, lse32, g, "f32")
+        for r in range(4):
+            corr = math.exp(exact[r] - float(lse32[r]))
+            for j in range(cols):
+                fd = _fd_logp(vals[r], int(t[r]), j)          # [j == t] - softmax_j
+                delta = 1.0 if j == t[r] else 0.0
+                want = float(g[r]) * (delta - (delta - fd) * corr)
+                assert abs(got[r, j] - want) <= 1e-7 * max(1.0, abs(float(g[r]))), \
+                    f"token grad finite difference r={r} j={j}: {got[r, j]!r} vs {want!r}"
+
+
+def pin_tokgrad_row_sums(orc):
+    """The one-hot term and the softmax each sum to one: a row sums to
+    g * (1 - exp(L - lse32))."""
+    rng = np.random.default_rng(31)
+    x = rng.normal(0, 4, size=(6, 300)).astype(np.float32)
+    t = rng.integers(0, 300, size=6)
+    exact = [brute_lse([float(v) for v in row]) for row in x]
+    lse32 = np.array(exact, dtype=np.float32)
+    g = rng.normal(0, 2, size=6).astype(np.float32)
+    got = orc.token_logprob_grad(x, t, lse32, g, "f32")
+    for r in range(6):
+        want = float(g[r]) * (1.0 - math.exp(exact[r] - float(lse32[r])))
+        assert abs(math.fsum(got[r]) - want) <= 1e-12 * max(1.0, abs(float(g[r]))), f"row sum r={r}"
+
+
+def pin_tokgrad_two_elements(orc):
+    """Rows (a, b): the softmax of column 0 is 1 / (1 + e^(b - a))."""
+    rng = np.random.default_rng(32)
+    x = rng.uniform(-20, 20, size=(12, 2)).astype(np.float32)
+    t = np.array([0, 1] * 6)
+    pl = [pair_lse(float(a), float(b)) for a, b in x]
+    lse32 = np.array(pl, dtype=np.float32)
+    g = np.full(12, -0.75, dtype=np.float32)
+    got = orc.token_logprob_grad(x, t, lse32, g, "f32")
+    for r in range(12):
+        a, b = float(x[r, 0]), float(x[r, 1])
+        p0 = 1.0 / (1.0 + math.exp(b - a))
+        corr = math.exp(pl[r] - float(lse32[r]))
+        p = (p0 * corr, (1.0 - p0) * corr)
+        for j in range(2):
+            want = -0.75 * ((1.0 if j == t[r] else 0.0) - p[j])
+            assert abs(got[r, j] - want) <= 1e-13, f"pair token grad r={r} j={j}"
+
+
+def pin_tokgrad_targets(orc):
+    """A target outside [0, cols) gives a row of NaN; other rows are untouched."""
+    x = np.zeros((4, 5), dtype=np.float32)
+    lse32 = np.full(4, math.log(5.0), dtype=np.float32)
+    got = orc.token_logprob_grad(x, [-1, 5, 2, 1 << 40], lse32, np.ones(4, np.float32), "f32")
+    assert np.isnan(got[0]).all() and np.isnan(got[1]).all() and np.isnan(got[3]).all()
+    corr = math.exp(math.log(5.0) - float(lse32[2]))
+    for j in range(5):
+        _close(got[2, j], (1.0 if j == 2 else 0.0) - 0.2 * corr, 1e-14, f"target row j={j}")
+
+
+def pin_tokgrad_argument_checks(orc):
+    x = np.zeros((4, 4), np.float32)
+    out = np.empty((4, 4))
+    v = np.zeros(4, np.float32)
+    t = np.zeros(4, np.int64)
+    fn = orc._fn_tok_grad
+    assert fn(x.ctypes.data, 0, 4, 4, 4, None, v.ctypes.data, v.ctypes.data, out.ctypes.data, 1) == -1
+    assert fn(x.ctypes.data, 0, 4, 4, 4, t.ctypes.data, None, v.ctypes.data, out.ctypes.data, 1) == -1
+    assert fn(x.ctypes.data, 0, 4, 4, 4, t.ctypes.data, v.ctypes.data, None, out.ctypes.data, 1) == -1
+
+
 def _close_all(got, want, rel, what):
     assert got.shape == want.shape, f"{what}: shape"
     for i, (g, w) in enumerate(zip(got, want)):
@@ -450,6 +544,11 @@ def _close_all(got, want, rel, what):
 
 
 CHEAP_PINS = [
+    pin_tokgrad_argument_checks,
+    pin_tokgrad_finite_difference,
+    pin_tokgrad_row_sums,
+    pin_tokgrad_two_elements,
+    pin_tokgrad_targets,
     pin_argument_checks,
     pin_constant_rows,
     pin_two_element_closed_form,

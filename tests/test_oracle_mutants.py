@@ -58,6 +58,16 @@ MUTANTS = {
                               "per = rows / nthreads;"),
     "log2_not_ln": ("return m + log(s);", "return m + log2(s);"),
     "exp2_not_exp": ("s += exp(load_elem", "s += exp2(load_elem"),
+    "tokgrad_sign": ("out[k] = valid ? g * ((k == t ? 1.0 : 0.0) - p) : NAN;",
+                     "out[k] = valid ? g * ((k == t ? 1.0 : 0.0) + p) : NAN;"),
+    "tokgrad_onehot_next_column": ("(k == t ? 1.0 : 0.0)", "(k == (t + 1) % cols ? 1.0 : 0.0)"),
+    "tokgrad_onehot_not_scaled": ("g * ((k == t ? 1.0 : 0.0) - p)", "((k == t ? 1.0 : 0.0) - g * p)"),
+    "tokgrad_invalid_target_zero": ("out[k] = valid ? g * ((k == t ? 1.0 : 0.0) - p) : NAN;",
+                                    "out[k] = valid ? g * ((k == t ? 1.0 : 0.0) - p) : 0.0;"),
+    "tokgrad_row_start_uses_cols": ("token_grad_one_row(jb->x, jb->dtype, r * jb->row_stride",
+                                    "token_grad_one_row(jb->x, jb->dtype, r * jb->cols"),
+    "tokgrad_wrong_row_lse": ("jb->lse[r], jb->grad_out[r], &jb->out[r * jb->cols]);",
+                              "jb->lse[r == jb->row_begin ? r : r - 1], jb->grad_out[r], &jb->out[r * jb->cols]);"),
 }
 
 
