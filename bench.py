@@ -37,6 +37,8 @@ METRIC_LOGPROB = "token log-prob input GB/s (x plus int64 targets) at the worklo
 METRIC_DIM = "LSE over the first axis input GB/s (outer 1, n rows, inner cols) at the workload's shape"
 METRIC_BACKWARD = ("LSE backward input GB/s (x, lse, grad_out read; grad_x written) at the "
                    "workload's shape")
+METRIC_TOKEN_BACKWARD = ("token log-prob backward input GB/s (x, int64 targets, lse, grad_logp "
+                         "read; grad_x written) at the workload's shape")
 HBM_PEAK_GBS = 8000.0
 CACHE_BYTES = 256 << 20
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.txt"
@@ -89,7 +91,7 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
     out_bytes = rows * 4
     targets = None
     bwd = None
-    if op == "backward":
+    if op in ("backward", "logprob_backward"):
         # the forward value comes from the float64 oracle (rounded to fp32), so
         # the check of the timed output never feeds the GPU's own results back
         import oracle
@@ -101,6 +103,10 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
                "lse_host": lse32, "g_host": g}
         out_bytes += rows * cols * esize  # grad_x
         in_bytes += rows * 8              # lse and grad_out
+        if op == "logprob_backward":
+            bwd["targets_host"] = workloads.targets(cfg)
+            bwd["targets"] = torch.from_numpy(bwd["targets_host"]).to("cuda")
+            in_bytes += rows * 8          # int64 targets
     if op == "logprob":
         targets = torch.from_numpy(workloads.targets(cfg)).to("cuda")
         in_bytes += rows * 8  # one int64 target per row
@@ -120,6 +126,11 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
         if op == "dim":
             B.lse_forward_dim(handle, bufs[i % rotate].data_ptr(), dtype_code, 1, rows, cols,
                               out.data_ptr(), sh)
+        elif bwd is not None and "targets" in bwd:
+            B.lse_token_logprob_backward(handle, bufs[i % rotate].data_ptr(), dtype_code, rows,
+                                         cols, cols, bwd["targets"].data_ptr(),
+                                         bwd["lse"].data_ptr(), bwd["g"].data_ptr(),
+                                         bwd["grad"].data_ptr(), cols, sh)
         elif bwd is not None:
             B.lse_backward(handle, bufs[i % rotate].data_ptr(), dtype_code, rows, cols, cols,
                            bwd["lse"].data_ptr(), bwd["g"].data_ptr(), bwd["grad"].data_ptr(),
@@ -234,10 +245,14 @@ def cpu_baseline_backward(w, r, seconds: float = 10.0) -> dict:
     n = max(1, min(w.rows, (256 << 20) // row_bytes))
     x = w.x[:n]
     lse32, g = r["bwd"]["lse_host"][:n], r["bwd"]["g_host"][:n]
+    tg = r["bwd"]["targets_host"][:n] if "targets_host" in r["bwd"] else None
     passes, ref = 0, None
     t0 = time.perf_counter()
     while True:
-        out = orc.softmax_grad(x, lse32, g, w.dtype, threads=threads)
+        if tg is None:
+            out = orc.softmax_grad(x, lse32, g, w.dtype, threads=threads)
+        else:
+            out = orc.token_logprob_grad(x, tg, lse32, g, w.dtype, threads=threads)
         if ref is None:
             ref = out
         passes += 1
@@ -256,15 +271,31 @@ def cpu_baseline_backward(w, r, seconds: float = 10.0) -> dict:
     with np.errstate(invalid="ignore"):
         d = np.abs(xv - lse32.astype(np.float64)[:, None])
     gg = np.broadcast_to(np.maximum(1.0, np.abs(g.astype(np.float64)))[:, None], ref.shape)
-    tol = (rel + 2e-7 * np.where(np.isfinite(d), d, 0.0)[fin]) * np.abs(ref[fin]) + \
-        2.0 ** -125 * gg[fin]
+    if tg is None:
+        tol = (rel + 2e-7 * np.where(np.isfinite(d), d, 0.0)[fin]) * np.abs(ref[fin]) + \
+            2.0 ** -125 * gg[fin]
+    else:
+        # the softmax term's error, the added term's rounding at the target
+        # column, and for bf16 one rounding of the result (as the GPU tests)
+        soft = np.abs(orc.softmax_grad(x, lse32, g, w.dtype, threads=threads))
+        onehot = np.zeros(ref.shape, dtype=bool)
+        ok = (tg >= 0) & (tg < w.cols)
+        onehot[np.arange(n)[ok], tg[ok]] = True
+        dd = np.where(np.isfinite(d), d, 0.0)
+        t_ = (4e-7 + 2e-7 * dd) * np.where(np.isfinite(soft), soft, 0.0) + \
+            np.where(onehot, 2.0 ** -23 * np.maximum(np.abs(gg), soft), 0.0) + 2.0 ** -125 * gg
+        if w.dtype == "bf16":
+            t_ = t_ + (2.0 ** -8 + 1e-6) * (np.abs(np.where(np.isfinite(ref), ref, 0.0)) + t_)
+        tol = t_[fin]
     err = np.abs(got[fin] - ref[fin]) / tol
     log(f"GPU gradient vs oracle ({n} rows): max |err|/tol = {err.max(initial=0):.3f}, "
         f"non-finite match {np.array_equal(got[~fin], ref[~fin], equal_nan=True)}")
     return {"value": round(x.nbytes * passes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": (f"the first {n} of {w.rows} rows ({x.nbytes} input bytes), {passes} passes "
-                       f"in {el:.1f} s wall on {threads} threads (float64 g * exp(x - lse))")}
+                       f"in {el:.1f} s wall on {threads} threads (float64 "
+                       + ("g * exp(x - lse)" if tg is None else "g * ([j == t] - exp(x - lse))")
+                       + ")")}
 
 
 def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0, op: str = "lse") -> dict:
@@ -337,10 +368,12 @@ def main() -> int:
     ap.add_argument("--all-out", default="bench_all.jsonl")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--op", choices=["lse", "logprob", "backward", "dim"], default="lse",
+    ap.add_argument("--op", choices=["lse", "logprob", "backward", "logprob_backward", "dim"],
+                    default="lse",
                     help="lse: lse_forward (the headline); logprob: lse_token_logprob with one "
                          "seeded int64 target per row; backward: lse_backward (reads x, writes "
-                         "grad_x); dim: lse_forward_dim over the workload's first axis")
+                         "grad_x); logprob_backward: lse_token_logprob_backward (the same, with "
+                         "the targets); dim: lse_forward_dim over the workload's first axis")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run three plain device copies of BYTES bytes (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -378,6 +411,7 @@ def main() -> int:
         log(f"launch floor (lse_forward on one element, back to back): {floor:.2f} us per call")
         line = {
             "metric": {"lse": METRIC, "logprob": METRIC_LOGPROB, "backward": METRIC_BACKWARD,
+                       "logprob_backward": METRIC_TOKEN_BACKWARD,
                        "dim": METRIC_DIM}[args.op],
             "value": round(r["value_gbs"], 1),
             "unit": "GB/s",
@@ -439,7 +473,7 @@ def main() -> int:
         if not args.no_cpu_baseline:
             log("timing the float64 oracle on the host cores")
             gpu_out = r["out"].cpu().numpy().astype(np.float64)
-            if args.op == "backward":
+            if args.op in ("backward", "logprob_backward"):
                 line["cpu_baseline"] = cpu_baseline_backward(w, r, args.cpu_seconds)
             else:
                 line["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds, args.op)

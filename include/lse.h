@@ -168,6 +168,33 @@ lse_status_t lse_backward(lse_handle_t h, const void *x, lse_dtype_t dtype,
                           int64_t grad_row_stride, hipStream_t stream);
 
 /*
+ * Backward pass of the token log-probability: the gradient of
+ * logp[r] = x[r, t] - LSE(x[r, :]) (t = targets[r]) with respect to x,
+ *
+ *     grad_x[r, j] = grad_logp[r] * ([j == t] - exp(x[r, j] - lse[r])),
+ *
+ * what training back-propagates through the per-token log-probabilities of
+ * the paper's motivating workload (§1, §5.1): lse_backward's pass with the
+ * incoming gradient negated and grad_logp[r] added at the target column.
+ *   x, dtype, rows, cols, row_stride   as for lse_forward.
+ *   targets    device pointer to rows int64 column indices, 8-byte aligned; a
+ *              target outside [0, cols) (whose logp is NaN) gives a row of NaN.
+ *   lse        device pointer to rows fp32 values, normally the forward LSE
+ *              (lse_token_logprob's lse_out or lse_forward's output).
+ *   grad_logp  device pointer to rows fp32 incoming gradients.
+ *   grad_x, grad_row_stride   as for lse_backward.
+ * One streaming pass, x read once and grad_x written once, in x's element type.
+ * No allocation, no synchronisation; nothing outside the rows of grad_x is
+ * written. Errors: as lse_backward, plus INVALID_ARG for NULL or misaligned
+ * targets.
+ */
+lse_status_t lse_token_logprob_backward(lse_handle_t h, const void *x, lse_dtype_t dtype,
+                                        int64_t rows, int64_t cols, int64_t row_stride,
+                                        const int64_t *targets, const float *lse,
+                                        const float *grad_logp, void *grad_x,
+                                        int64_t grad_row_stride, hipStream_t stream);
+
+/*
  * LSE over the middle axis of a contiguous [outer, n, inner] array:
  *
  *     out[o * inner + i] = log( sum_{j < n} exp(x[(o * n + j) * inner + i]) ),

@@ -8,7 +8,9 @@ contiguous tensor; ``token_logprob(x, t)`` returns x[r, t[r]] -
 logsumexp(x)[r] from the same single pass. PyTorch only provides the device
 memory and the current stream; the computation is the HIP library's
 ``lse_forward`` / ``lse_backward`` / ``lse_forward_dim`` /
-``lse_token_logprob`` (see include/lse.h). The library is loaded on first use
+``lse_token_logprob`` / ``lse_token_logprob_backward`` (see include/lse.h);
+``token_logprob_autograd(x, t)`` is the token log-probability with its
+gradient. The library is loaded on first use
 and a missing library is an error, never a fallback.
 """
 from __future__ import annotations
@@ -163,3 +165,58 @@ def logsumexp_autograd(x):
     if _LSE_FN is None:
         _LSE_FN = _autograd_function()
     return _LSE_FN.apply(x)
+
+
+def _token_autograd_function():
+    import torch
+
+    from .binding import lse_token_logprob, lse_token_logprob_backward
+
+    class _TokenLogprob(torch.autograd.Function):
+        """x[r, t[r]] - LSE(x[r, :]) with the library's backward pass."""
+
+        @staticmethod
+        def forward(ctx, x, targets):
+            code, rows, cols, stride = _check_input(x)
+            if targets.dtype != torch.int64 or targets.shape != (rows,) or \
+                    not targets.is_contiguous() or targets.device != x.device:
+                raise ValueError("targets must be a contiguous int64 tensor of shape (rows,) "
+                                 "on x's device")
+            logp = torch.empty(rows, dtype=torch.float32, device=x.device)
+            lse = torch.empty(rows, dtype=torch.float32, device=x.device)
+            h = handle(x.device.index or 0)
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+            lse_token_logprob(h, x.data_ptr(), code, rows, cols, stride, targets.data_ptr(),
+                              logp.data_ptr(), lse.data_ptr(), stream)
+            ctx.save_for_backward(x, targets, lse)
+            return logp
+
+        @staticmethod
+        def backward(ctx, grad_logp):
+            x, targets, lse = ctx.saved_tensors
+            code, rows, cols, stride = _check_input(x)
+            g = grad_logp.to(torch.float32).contiguous()
+            grad = torch.empty((rows, cols), dtype=x.dtype, device=x.device)
+            h = handle(x.device.index or 0)
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+            lse_token_logprob_backward(h, x.data_ptr(), code, rows, cols, stride,
+                                       targets.data_ptr(), lse.data_ptr(), g.data_ptr(),
+                                       grad.data_ptr(), cols, stream)
+            return grad, None
+
+    return _TokenLogprob
+
+
+_TOK_FN = None
+
+
+def token_logprob_autograd(x, targets):
+    """x[r, targets[r]] - LSE(x[r, :]) for a 2-D fp32/bf16 GPU tensor, as
+    fp32[rows], differentiable with respect to x: the gradient is
+    grad_logp[r] * ([j == t] - exp(x[r, j] - lse[r])), computed by the
+    library's lse_token_logprob_backward in x's dtype (NaN rows for targets
+    outside [0, cols))."""
+    global _TOK_FN
+    if _TOK_FN is None:
+        _TOK_FN = _token_autograd_function()
+    return _TOK_FN.apply(x, targets)

@@ -32,6 +32,7 @@ LSE_SPLIT_MAX_ROWS = 1024
 LSE_SPLIT_MAX_PARTS = 64
 
 EXPORTS = ["lse_create", "lse_forward", "lse_forward_dim", "lse_token_logprob", "lse_backward",
+           "lse_token_logprob_backward",
            "lse_destroy", "lse_status_string", "lse_set_schedule", "lse_set_tuning", "lse_plan"]
 
 
@@ -71,6 +72,7 @@ def load(path: Path | str = LIBRARY) -> ctypes.CDLL:
         "lse_forward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp]),
         "lse_token_logprob": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]),
         "lse_backward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, i64, vp]),
+        "lse_token_logprob_backward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, vp]),
         "lse_forward_dim": (i32, [vp, vp, i32, i64, i64, i64, vp, vp]),
         "lse_destroy": (i32, [vp]),
         "lse_status_string": (ctypes.c_char_p, [i32]),
@@ -139,6 +141,25 @@ def lse_backward(handle: int, x_ptr: int, dtype: int, rows: int, cols: int, row_
                  stream: int | None = None) -> None:
     _check(load().lse_backward(handle, x_ptr, dtype, rows, cols, row_stride, lse_ptr,
                                grad_out_ptr, grad_x_ptr, grad_row_stride, stream), "lse_backward")
+
+
+def lse_token_logprob_backward(handle: int, x_ptr: int, dtype: int, rows: int, cols: int,
+                               row_stride: int, targets_ptr: int, lse_ptr: int,
+                               grad_logp_ptr: int, grad_x_ptr: int, grad_row_stride: int,
+                               stream: int | None = None) -> None:
+    _check(load().lse_token_logprob_backward(handle, x_ptr, dtype, rows, cols, row_stride,
+                                             targets_ptr, lse_ptr, grad_logp_ptr, grad_x_ptr,
+                                             grad_row_stride, stream),
+           "lse_token_logprob_backward")
+
+
+def lse_token_logprob_backward_status(handle, x_ptr, dtype, rows, cols, row_stride, targets_ptr,
+                                      lse_ptr, grad_logp_ptr, grad_x_ptr, grad_row_stride,
+                                      stream=None) -> int:
+    """lse_token_logprob_backward returning the raw status (for argument tests)."""
+    return load().lse_token_logprob_backward(handle, x_ptr, dtype, rows, cols, row_stride,
+                                             targets_ptr, lse_ptr, grad_logp_ptr, grad_x_ptr,
+                                             grad_row_stride, stream)
 
 
 def lse_backward_status(handle, x_ptr, dtype, rows, cols, row_stride, lse_ptr, grad_out_ptr,

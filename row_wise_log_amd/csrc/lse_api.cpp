@@ -432,10 +432,16 @@ lse_status_t lse_forward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64
     return run(h, x, dtype, rows, cols, row_stride, out, nullptr, nullptr, stream);
 }
 
-lse_status_t lse_backward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,
-                          int64_t cols, int64_t row_stride, const float* lse,
-                          const float* grad_out, void* grad_x, int64_t grad_row_stride,
-                          hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// lse_backward and lse_token_logprob_backward: the same checks and plan; with
+// targets the kernels add the one-hot term of the log-probability.
+lse_status_t run_backward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,
+                          int64_t cols, int64_t row_stride, const int64_t* targets,
+                          bool with_targets, const float* lse, const float* grad_out,
+                          void* grad_x, int64_t grad_row_stride, hipStream_t stream) {
     const uint64_t x_addr = reinterpret_cast<uint64_t>(x);
     lse_status_t st = check_sizes(dtype, rows, cols, row_stride, x_addr);
     if (st != LSE_OK) return st;
@@ -444,6 +450,8 @@ lse_status_t lse_backward(lse_handle_t h, const void* x, lse_dtype_t dtype, int6
         return LSE_ERR_INVALID_ARG;
     if (rows == 0 || cols == 0) return h == nullptr ? LSE_ERR_INVALID_ARG : LSE_OK;
     if (x == nullptr || lse == nullptr || grad_out == nullptr || grad_x == nullptr)
+        return LSE_ERR_INVALID_ARG;
+    if (with_targets && (targets == nullptr || reinterpret_cast<uint64_t>(targets) % 8 != 0))
         return LSE_ERR_INVALID_ARG;
     const uint64_t g_addr = reinterpret_cast<uint64_t>(grad_x);
     if (reinterpret_cast<uint64_t>(lse) % 4 != 0 || reinterpret_cast<uint64_t>(grad_out) % 4 != 0 ||
@@ -457,6 +465,7 @@ lse_status_t lse_backward(lse_handle_t h, const void* x, lse_dtype_t dtype, int6
     a.x = static_cast<const char*>(x);
     a.lse = lse;
     a.grad_out = grad_out;
+    a.targets = with_targets ? targets : nullptr;
     a.grad_x = static_cast<char*>(grad_x);
     a.stream = stream;
 
@@ -466,6 +475,27 @@ lse_status_t lse_backward(lse_handle_t h, const void* x, lse_dtype_t dtype, int6
     const hipError_t err = lse::launch_grad(a);
     if (prev != h->device) (void)hipSetDevice(prev);
     return err == hipSuccess ? LSE_OK : LSE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+lse_status_t lse_backward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,
+                          int64_t cols, int64_t row_stride, const float* lse,
+                          const float* grad_out, void* grad_x, int64_t grad_row_stride,
+                          hipStream_t stream) {
+    return run_backward(h, x, dtype, rows, cols, row_stride, nullptr, false, lse, grad_out,
+                        grad_x, grad_row_stride, stream);
+}
+
+lse_status_t lse_token_logprob_backward(lse_handle_t h, const void* x, lse_dtype_t dtype,
+                                        int64_t rows, int64_t cols, int64_t row_stride,
+                                        const int64_t* targets, const float* lse,
+                                        const float* grad_logp, void* grad_x,
+                                        int64_t grad_row_stride, hipStream_t stream) {
+    return run_backward(h, x, dtype, rows, cols, row_stride, targets, true, lse, grad_logp,
+                        grad_x, grad_row_stride, stream);
 }
 
 lse_status_t lse_forward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t outer,

@@ -6,7 +6,14 @@
 // scaled by the incoming gradient). The paper "Speeding up Log-Sum-Exp: Kernel
 // Fusion at the Memory Wall, Integer Arithmetic at the Compute Wall" lists
 // backward support among its kernels' properties (Table 3); this is that
-// step for the fused forward in lse_kernels.hip. It is a second streaming pass
+// step for the fused forward in lse_kernels.hip. With targets (TOK), the same
+// pass is the backward of the token log-probability x[r, t] - lse[r]:
+//
+//     grad_x[r, j] = grad_logp[r] * ([j == t] - exp(x[r, j] - lse[r])),
+//
+// computed as (-g) * exp(x - lse), minus (-g) at the target column; a target
+// outside [0, cols) makes the row's lse NaN, so the whole row is NaN.
+// It is a second streaming pass
 // over x that writes as many bytes as it reads, so it is bound by HBM
 // bandwidth like the forward pass: 16-byte loads and stores, one per-row
 // scalar pair (lse, grad_out), and per element one subtract, one multiply,
@@ -39,14 +46,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 // One unit's grad: g * 2^((x - L) * log2 e) per element, packed back into the
-// element type (bf16 rounds to nearest even from fp32).
-template <DType D>
-__device__ __forceinline__ u32x4 grad_vec(u32x4 w, float lse, float g) {
+// element type (bf16 rounds to nearest even from fp32). TOK: element tk of the
+// unit (if 0 <= tk < K) is the target column and also gets -g.
+template <DType D, bool TOK>
+__device__ __forceinline__ u32x4 grad_vec(u32x4 w, float lse, float g, int tk) {
     float f[Elem<D>::kPerVec];
     decode<D>(w, f);
     float o[Elem<D>::kPerVec];
 #pragma unroll
-    for (int k = 0; k < Elem<D>::kPerVec; ++k) o[k] = g * exp2_hw((f[k] - lse) * kLog2e);
+    for (int k = 0; k < Elem<D>::kPerVec; ++k) {
+        o[k] = g * exp2_hw((f[k] - lse) * kLog2e);
+        if (TOK && k == tk) o[k] -= g;
+    }
     u32x4 r;
     if constexpr (D == DType::F32) {
         r = u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
@@ -83,11 +94,12 @@ __device__ __forceinline__ void store_scalar(char* p, float v) {
 // ONE_ROW: the workgroup takes one chunk of one row (rows_per_wg == 1), so
 // the row's lse and grad_out are uniform; otherwise every unit loads its own
 // row's pair. Each instance issues the same loads in every batch.
-template <DType D, int BLOCK, int U, bool VEC, bool ONE_ROW>
+template <DType D, int BLOCK, int U, bool VEC, bool ONE_ROW, bool TOK>
 __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, int64_t rows,
                                                   int64_t cols, int64_t xs_bytes,
                                                   const float* __restrict__ lse,
                                                   const float* __restrict__ gout,
+                                                  const int64_t* __restrict__ targets,
                                                   char* __restrict__ gx, int64_t gs_bytes,
                                                   int64_t rows_per_wg, int64_t chunks_per_row,
                                                   int64_t chunk_units) {
@@ -125,15 +137,31 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
     const auto gr = make_rsrc(gb, gspan);
     const float inv_w = 1.0f / static_cast<float>(W);
 
+    // A row's (lse, g, target): TOK negates g and makes lse NaN for a target
+    // outside [0, cols).
+    auto row_terms = [&](int64_t row, float& l, float& g, int64_t& tt) {
+        l = lse[row];
+        g = gout[row];
+        tt = -1;
+        if constexpr (TOK) {
+            tt = targets[row];
+            if (tt < 0 || tt >= cols) l = __builtin_nanf("");
+            g = -g;
+        }
+    };
+    // The target's place in a unit whose first column is c0: 0..K-1, else -1.
+    auto unit_target = [&](int64_t tt, int64_t c0) {
+        const int64_t d = tt - c0;
+        return d >= 0 && d < K ? static_cast<int>(d) : -1;
+    };
+
     // uniform per-row scalars in the one-row case
     float l0 = 0.0f, g0 = 0.0f;
-    if (ONE_ROW && n > 0) {
-        l0 = lse[r0];
-        g0 = gout[r0];
-    }
+    int64_t t0 = -1;
+    if (ONE_ROW && n > 0) row_terms(r0, l0, g0, t0);
 
     // Item j of the block: its row (local) and unit, as byte offsets.
-    auto offsets = [&](int j, int& rl, int& xo, int& go) {
+    auto offsets = [&](int j, int& rl, int& xo, int& go, int& uu) {
         const bool in = j < n;
         rl = 0;
         if constexpr (!ONE_ROW) {
@@ -142,6 +170,7 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
             rl = rl < nr ? rl : nr - 1;
         }
         const int u = j - rl * static_cast<int>(W);
+        uu = u;
         xo = in ? static_cast<int>(rl * xs_bytes) + u * UB : kOffFar;
         go = in ? static_cast<int>(rl * gs_bytes) + u * UB : kOffFar;
     };
@@ -151,12 +180,13 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
         float e[VEC ? 1 : U];
         float l[U], g[U];
         int go[U];
+        int tk[TOK ? U : 1];
     };
     auto load_batch = [&](Batch& t, int j0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int rl, xo, go;
-            offsets(j0 + u * BLOCK, rl, xo, go);
+            int rl, xo, go, uu;
+            offsets(j0 + u * BLOCK, rl, xo, go, uu);
             t.go[u] = go;
             if constexpr (VEC) {
                 t.w[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, 2));
@@ -166,13 +196,14 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
                 t.e[u] = __uint_as_float(
                     static_cast<unsigned>(__builtin_amdgcn_raw_buffer_load_b16(xr, xo, 0, 2)) << 16);
             }
+            int64_t tt = t0;
             if constexpr (!ONE_ROW) {
-                t.l[u] = lse[r0 + rl];
-                t.g[u] = gout[r0 + rl];
+                row_terms(r0 + rl, t.l[u], t.g[u], tt);
             } else {
                 t.l[u] = l0;
                 t.g[u] = g0;
             }
+            if constexpr (TOK) t.tk[u] = unit_target(tt, (u0 + uu) * static_cast<int64_t>(K));
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -180,11 +211,12 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if constexpr (VEC) {
-                const u32x4 r = grad_vec<D>(t.w[u], t.l[u], t.g[u]);
+                const u32x4 r = grad_vec<D, TOK>(t.w[u], t.l[u], t.g[u], TOK ? t.tk[u] : -1);
                 typedef unsigned v4u __attribute__((ext_vector_type(4)));
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, r), gr, t.go[u], 0, 2);
             } else {
-                const float v = grad_scalar<D>(t.e[u], t.l[u], t.g[u]);
+                float v = grad_scalar<D>(t.e[u], t.l[u], t.g[u]);
+                if (TOK && t.tk[u] == 0) v -= t.g[u];
                 if constexpr (D == DType::F32)
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), gr, t.go[u], 0, 2);
                 else
@@ -227,8 +259,12 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
                 const int64_t row = r0 + rl;
                 const int64_t col = nunits * K + e;
                 const float xv = load_scalar<D>(x + row * xs_bytes + col * EB);
-                store_scalar<D>(gx + row * gs_bytes + col * EB,
-                                grad_scalar<D>(xv, lse[row], gout[row]));
+                float l, g;
+                int64_t tt;
+                row_terms(row, l, g, tt);
+                float v = grad_scalar<D>(xv, l, g);
+                if (TOK && col == tt) v -= g;
+                store_scalar<D>(gx + row * gs_bytes + col * EB, v);
             }
         }
     }
@@ -236,18 +272,24 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
 
 namespace {
 
-template <DType D, bool VEC, bool ONE_ROW>
+template <DType D, bool VEC, bool ONE_ROW, bool TOK>
 hipError_t launch_grad_k(const GradArgs& a) {
     constexpr int BLOCK = 256, U = 4;
-    hipLaunchKernelGGL((lse_grad<D, BLOCK, U, VEC, ONE_ROW>), dim3(a.grid), dim3(BLOCK), 0,
-                       a.stream, a.x, a.rows, a.cols, a.xs_bytes, a.lse, a.grad_out, a.grad_x,
-                       a.gs_bytes, a.rows_per_wg, a.chunks_per_row, a.chunk_units);
+    hipLaunchKernelGGL((lse_grad<D, BLOCK, U, VEC, ONE_ROW, TOK>), dim3(a.grid), dim3(BLOCK), 0,
+                       a.stream, a.x, a.rows, a.cols, a.xs_bytes, a.lse, a.grad_out, a.targets,
+                       a.grad_x, a.gs_bytes, a.rows_per_wg, a.chunks_per_row, a.chunk_units);
     return hipGetLastError();
+}
+
+template <DType D, bool VEC, bool TOK>
+hipError_t launch_grad_t(const GradArgs& a) {
+    return a.rows_per_wg == 1 ? launch_grad_k<D, VEC, true, TOK>(a)
+                              : launch_grad_k<D, VEC, false, TOK>(a);
 }
 
 template <DType D, bool VEC>
 hipError_t launch_grad_d(const GradArgs& a) {
-    return a.rows_per_wg == 1 ? launch_grad_k<D, VEC, true>(a) : launch_grad_k<D, VEC, false>(a);
+    return a.targets != nullptr ? launch_grad_t<D, VEC, true>(a) : launch_grad_t<D, VEC, false>(a);
 }
 
 }  // namespace

@@ -56,6 +56,7 @@ struct GradArgs {
     int64_t xs_bytes, gs_bytes;  // bytes between row starts of x and of grad_x
     const float* lse;
     const float* grad_out;
+    const int64_t* targets;  // non-NULL: the token log-probability's backward
     char* grad_x;
     hipStream_t stream;
 };

@@ -210,3 +210,78 @@ def compare_grad(got: np.ndarray, ref: np.ndarray, d: np.ndarray, g: np.ndarray,
                                  f"{got[fin][worst]!r} want {ref[fin][worst]!r} ({ratio[worst]:.2f} x tol)")
     return float(ratio.max())
 
+
+
+def gpu_token_backward(torch, handle, x: np.ndarray, targets: np.ndarray, lse: np.ndarray,
+                       g: np.ndarray, dtype: str, pad_front: int = 0, grad_pad: int = 0,
+                       grad_front: int = 0):
+    """Run lse_token_logprob_backward on a host array; returns (grad as float32
+    rows x cols, untouched) as gpu_backward does. Every device buffer the call
+    reads is held in a local until the call has run."""
+    rows, cols = x.shape
+    t, ptr, stride = upload(torch, x, pad_front)
+    tg = torch.from_numpy(np.ascontiguousarray(targets, dtype=np.int64)).to("cuda")
+    lt = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to("cuda")
+    gt = torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to("cuda")
+    gstride = cols + grad_pad
+    total = grad_front + (rows - 1) * gstride + cols + 64 if rows else 64
+    store = torch.int16 if dtype == "bf16" else torch.int32
+    sentinel = 0x7F7F if dtype == "bf16" else 0x7F7F7F7F
+    buf = torch.full((total,), sentinel, dtype=store, device="cuda")
+    esz = ESIZE[dtype]
+    B.lse_token_logprob_backward(handle, ptr, DTYPE_CODE[dtype], rows, cols, stride, tg.data_ptr(),
+                                 lt.data_ptr(), gt.data_ptr(), buf.data_ptr() + grad_front * esz,
+                                 gstride, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    del t, tg, lt, gt, buf
+    host = host.view(np.uint16) if dtype == "bf16" else host.view(np.uint32)
+    want_sentinel = np.uint16(0x7F7F) if dtype == "bf16" else np.uint32(0x7F7F7F7F)
+    mask = np.zeros(total, dtype=bool)
+    idx = grad_front + np.arange(rows)[:, None] * gstride + np.arange(cols)[None, :]
+    mask[idx.ravel()] = True
+    untouched = bool(np.all(host[~mask] == want_sentinel))
+    vals = host[idx]
+    out = (vals.astype(np.uint32) << 16).view(np.float32) if dtype == "bf16" else \
+        np.ascontiguousarray(vals).view(np.float32)
+    return out, untouched
+
+
+def compare_token_grad(got: np.ndarray, ref: np.ndarray, soft: np.ndarray, d: np.ndarray,
+                       g: np.ndarray, targets: np.ndarray, dtype: str, what: str) -> float:
+    """The rule for grad_logp * ([j == t] - exp(x - lse)): NaN and +-inf exactly;
+    otherwise |got - ref| <= (4e-7 + 2e-7 |x - lse|) |g p| (the softmax term's
+    error, as for the backward pass) + 2^-23 max(|g|, |g p|) at the target
+    column (the added term's rounding) + 2^-125 max(1, |g|), and for bf16 output
+    2^-8 + 1e-6 of the value on top (one rounding to 8 significant bits). `soft`
+    is the oracle's g * exp(x - lse)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, what
+    nan = np.isnan(ref)
+    bad = nan & ~np.isnan(got)
+    assert not bad.any(), f"{what}: {np.argwhere(bad)[:4].tolist()} want NaN, got {got[bad][:4]}"
+    inf = np.isinf(ref)
+    bad = inf & (got != ref)
+    assert not bad.any(), f"{what}: {np.argwhere(bad)[:4].tolist()} want {ref[bad][:4]}"
+    fin = ~nan & ~inf
+    if not fin.any():
+        return 0.0
+    rows, cols = ref.shape
+    gg = np.broadcast_to(np.abs(np.asarray(g, np.float64))[:, None], ref.shape)
+    onehot = np.zeros(ref.shape, dtype=bool)
+    t = np.asarray(targets, dtype=np.int64)
+    ok = (t >= 0) & (t < cols)
+    onehot[np.arange(rows)[ok], t[ok]] = True
+    dd = np.where(np.isfinite(d), np.abs(d), 0.0)
+    sp = np.abs(np.where(np.isfinite(soft), soft, 0.0))
+    tol = (4e-7 + 2e-7 * dd) * sp + np.where(onehot, 2.0 ** -23 * np.maximum(gg, sp), 0.0) + \
+        2.0 ** -125 * np.maximum(1.0, gg)
+    if dtype == "bf16":
+        tol = tol + (2.0 ** -8 + 1e-6) * (np.abs(ref) + tol)
+    assert np.all(np.isfinite(got[fin])), f"{what}: non-finite grad for a finite reference"
+    ratio = np.abs(got[fin] - ref[fin]) / tol[fin]
+    worst = int(np.argmax(ratio))
+    assert ratio[worst] <= 1.0, (f"{what}: element {np.argwhere(fin)[worst].tolist()} got "
+                                 f"{got[fin][worst]!r} want {ref[fin][worst]!r} ({ratio[worst]:.2f} x tol)")
+    return float(ratio.max())

@@ -141,6 +141,23 @@ def test_backward_argument_checks(lib, args, status):
 
 
 @pytest.mark.parametrize("args, status", [
+    # (x, dtype, rows, cols, row_stride, targets, lse, grad_logp, grad_x, grad_row_stride)
+    ((16, 7, 4, 4, 4, 256, 64, 64, 128, 4), B.LSE_ERR_UNSUPPORTED_DTYPE),
+    ((16, F32, 4, 8, 7, 256, 64, 64, 128, 8), B.LSE_ERR_INVALID_ARG),     # x stride < cols
+    ((16, F32, 4, 8, 8, 256, 64, 64, 128, 7), B.LSE_ERR_INVALID_ARG),     # grad stride < cols
+    ((16, F32, 4, 4, 4, None, 64, 64, 128, 4), B.LSE_ERR_INVALID_ARG),    # NULL targets
+    ((16, F32, 4, 4, 4, 260, 64, 64, 128, 4), B.LSE_ERR_INVALID_ARG),     # targets misaligned
+    ((16, F32, 4, 4, 4, 256, None, 64, 128, 4), B.LSE_ERR_INVALID_ARG),   # NULL lse
+    ((16, F32, 4, 4, 4, 256, 64, None, 128, 4), B.LSE_ERR_INVALID_ARG),   # NULL grad_logp
+    ((16, F32, 4, 4, 4, 256, 64, 64, None, 4), B.LSE_ERR_INVALID_ARG),    # NULL grad_x
+    ((16, F32, 4, 4, 4, 256, 64, 64, 128, 4), B.LSE_ERR_INVALID_ARG),     # all fine but the handle
+    ((None, F32, 0, 4, 4, None, None, None, None, 4), B.LSE_ERR_INVALID_ARG),  # rows = 0
+])
+def test_token_logprob_backward_argument_checks(lib, args, status):
+    assert B.lse_token_logprob_backward_status(None, *args) == status
+
+
+@pytest.mark.parametrize("args, status", [
     # (x, dtype, outer, n, inner, out) with a NULL handle
     ((16, 7, 2, 3, 4, 16), B.LSE_ERR_UNSUPPORTED_DTYPE),
     ((16, F32, -1, 3, 4, 16), B.LSE_ERR_INVALID_ARG),
