@@ -11,8 +11,10 @@ cache), so every step streams its input from HBM.
 
 Prints ONE JSON line with the metric, the per-launch roofline of the kernel
 (algorithmic bytes / mean launch time from HIP events on the launch stream,
-against the 8 TB/s HBM peak) and the float64 CPU oracle's rate on the same
-workload as a baseline. --all also times the other four workloads and writes
+against the 8 TB/s HBM peak), the same-bytes read-only control kernel timed
+the same way with the same launch geometry (roofline.read_control: how fast
+this device reads those bytes when nothing else is done with them), and the
+float64 CPU oracle's rate on the same workload as a baseline. --all also times the other four workloads and writes
 their lines to --all-out.
 """
 from __future__ import annotations
@@ -163,13 +165,69 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
     mean_launch = e0.elapsed_time(e1) / steps
 
     ms_step = wall / steps * 1e3
+    control = None
+    if op in ("lse", "logprob", "dim"):
+        control = time_read_control(torch, bufs, rows * cols * esize, plan, steps, warmup, stream)
+        control["frac_of_read_control"] = round(control["launch_us_mean"] / (mean_launch * 1e3), 4)
     return {
         "w": w, "plan": plan, "rotate": rotate, "in_bytes": in_bytes, "out_bytes": out_bytes,
         "ms_per_step": ms_step, "launch_ms_mean": mean_launch,
         "value_gbs": in_bytes / (ms_step * 1e-3) / 1e9,
         "achieved_gbs": (in_bytes + out_bytes) / (mean_launch * 1e-3) / 1e9,
-        "out": out, "op": op, "bwd": bwd,
+        "out": out, "op": op, "bwd": bwd, "control": control,
     }
+
+
+def time_read_control(torch, bufs, nbytes: int, plan: dict, steps: int, warmup: int,
+                      stream) -> dict:
+    """The read-only control kernel over the same input copies, in the same
+    rotation, with the LSE plan's workgroup count and size: one XOR per chunk
+    of the input, so the time is that of reading the bytes and nothing else.
+    Timed like the LSE launches (one event pair around K back-to-back
+    launches)."""
+    from row_wise_log_amd import read_control as RC
+    grid, block = int(plan["grid"]), int(plan["block"])
+    out = torch.empty(grid, dtype=torch.int32, device="cuda")
+    sh = stream.cuda_stream
+
+    def step(i):
+        RC.lse_control_read(bufs[i % len(bufs)].data_ptr(), nbytes, grid, block, out.data_ptr(), sh)
+
+    for i in range(warmup):
+        step(i)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    return {"kernel": "read_chunks (XOR of each chunk's words)", "grid": grid, "block": block,
+            "launch_us_mean": round(us, 2), "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def sweep_read_control(torch, cfg: int, steps: int, warmup: int) -> list:
+    """The read-only control over workgroup counts 256..16384 and sizes
+    256..1024 on workload cfg's input (rotating copies as in the timed
+    steps); logs one JSON line per shape."""
+    w = workloads.make(cfg)
+    nbytes = w.x.nbytes
+    host = torch.from_numpy(w.x.view(np.int16) if w.dtype == "bf16" else w.x)
+    bufs = [host.to("cuda") for _ in range(max(1, -(-2 * CACHE_BYTES // nbytes) + 1))]
+    stream = torch.cuda.current_stream()
+    res = []
+    for grid in (256, 512, 1024, 2048, 4096, 8192, 16384):
+        for block in (256, 512, 1024):
+            c = time_read_control(torch, bufs, nbytes, {"grid": grid, "block": block}, steps,
+                                  warmup, stream)
+            rec = {"control_sweep": cfg, "grid": grid, "block": block,
+                   "launch_us_mean": c["launch_us_mean"], "GBs": c["GBs"]}
+            log(json.dumps(rec))
+            res.append(rec)
+    del bufs
+    return res
 
 
 def launch_floor_us(torch, B, handle, calls: int = 1000) -> float:
@@ -374,6 +432,10 @@ def main() -> int:
                          "seeded int64 target per row; backward: lse_backward (reads x, writes "
                          "grad_x); logprob_backward: lse_token_logprob_backward (the same, with "
                          "the targets); dim: lse_forward_dim over the workload's first axis")
+    ap.add_argument("--control-sweep", action="store_true",
+                    help="also time the read-only control kernel over a grid of workgroup counts "
+                         "and sizes on the workload's input, one JSON line each to stderr (is "
+                         "any launch shape a faster way to read these bytes?)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run three plain device copies of BYTES bytes (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -445,8 +507,11 @@ def main() -> int:
                 "traffic": traffic,
                 "launch_us_mean": round(r["launch_ms_mean"] * 1e3, 2),
                 "algorithmic_bytes_per_launch": r["in_bytes"] + r["out_bytes"],
+                "read_control": r["control"],
             },
         }
+        if args.control_sweep:
+            sweep_read_control(torch, args.config, args.steps, args.warmup)
         if args.all:
             Path(args.all_out).parent.mkdir(parents=True, exist_ok=True)
             with open(args.all_out, "w") as f:
@@ -464,6 +529,9 @@ def main() -> int:
                            "achieved_GBs_per_launch": round(rc["achieved_gbs"], 1),
                            "rows_per_s": round(rc["w"].rows / (rc["ms_per_step"] * 1e-3), 1),
                            "launch_floor_us": round(floor, 2)}
+                    if rc["control"] is not None:
+                        rec["read_control_us"] = rc["control"]["launch_us_mean"]
+                        rec["frac_of_read_control"] = rc["control"]["frac_of_read_control"]
                     if args.op == "lse" and rc["in_bytes"] <= CACHE_BYTES // 4:
                         rec["us_per_call_warm"] = round(warm_us_per_call(torch, B, handle, cfg), 2)
                     log(json.dumps(rec))

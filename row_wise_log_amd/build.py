@@ -22,6 +22,10 @@ LIBRARY = PKG / "liblse_amd.so"
 SOURCES = [CSRC / "lse_kernels.hip", CSRC / "lse_backward.hip", CSRC / "lse_dim.hip",
            CSRC / "lse_api.cpp"]
 ARCH = "gfx950"
+# The read-only control kernel that bench.py times beside the LSE kernels; its
+# own library, so nothing on the LSE path can reach it.
+CONTROL_LIBRARY = PKG / "libread_control.so"
+CONTROL_SOURCES = [CSRC / "read_control.hip"]
 
 
 def hipcc() -> str:
@@ -31,17 +35,23 @@ def hipcc() -> str:
     return path
 
 
-def command(output: Path, extra: list[str] | None = None) -> list[str]:
+def command(output: Path, extra: list[str] | None = None,
+            sources: list[Path] | None = None) -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Wall", "-Wno-unused-command-line-argument",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             f"-I{INCLUDE}", f"-I{CSRC}", *(extra or []),
-            "-x", "hip", *map(str, SOURCES), "-o", str(output)]
+            "-x", "hip", *map(str, sources or SOURCES), "-o", str(output)]
 
 
-def build(output: Path = LIBRARY, extra: list[str] | None = None, quiet: bool = True) -> Path:
+def build_control(quiet: bool = True) -> Path:
+    return build(CONTROL_LIBRARY, quiet=quiet, sources=CONTROL_SOURCES)
+
+
+def build(output: Path = LIBRARY, extra: list[str] | None = None, quiet: bool = True,
+          sources: list[Path] | None = None) -> Path:
     tmp = output.with_name(output.name + f".tmp{os.getpid()}")
-    proc = subprocess.run(command(tmp, extra), capture_output=True, text=True)
+    proc = subprocess.run(command(tmp, extra, sources), capture_output=True, text=True)
     if proc.returncode != 0:
         sys.stderr.write(proc.stdout + proc.stderr)
         raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
@@ -57,3 +67,4 @@ def build(output: Path = LIBRARY, extra: list[str] | None = None, quiet: bool = 
 
 if __name__ == "__main__":
     print(build(quiet=False))
+    print(build_control(quiet=False))

@@ -1,0 +1,127 @@
+// Read-only control kernel: the measuring stick for the LSE kernels.
+//
+// It reads a contiguous byte range exactly once, with the load instruction and
+// software pipeline of the streaming LSE schedule: 16-byte non-temporal loads,
+// batches of 4 per lane, the next batch in flight while one is consumed. It
+// keeps only the XOR of the 32-bit words of each chunk. Timed on the same
+// buffers, launch geometry and stream as an LSE launch, it shows how fast this
+// device streams those bytes when nothing else is done with them. The paper's
+// introduction (section 1, its motivation) sets torch's LSE against a plain
+// sum over the same tensor; this is that comparison with the sum replaced by
+// the cheapest full read.
+//
+// Measurement infrastructure only: it is built into its own library
+// (libread_control.so), and nothing on the LSE path calls it.
+//
+//   int lse_control_read(const void* x, int64_t bytes, int64_t chunks, int block,
+//                        unsigned* out, hipStream_t stream)
+//
+// x: device pointer, 16-byte aligned; bytes: a multiple of 16. The range's nvec
+// 16-byte vectors are cut into `chunks` pieces: with q = nvec / chunks and
+// r = nvec % chunks, chunk g holds q + (g < r) vectors starting at
+// g*q + min(g, r) (no division on the device); one workgroup of `block` threads (64,
+// 128, 256, 512 or 1024) reads each chunk and writes the XOR of its 32-bit
+// words to out[g] (device, `chunks` words). Returns 0 on success, 1 for an
+// invalid argument (checked before any HIP call), 2 if the launch fails.
+// Asynchronous on `stream`; allocates nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBatch = 4;  // 16-byte loads per lane per batch
+
+__device__ __forceinline__ unsigned xor4(u32x4 v) { return (v.x ^ v.y) ^ (v.z ^ v.w); }
+
+template <int BLOCK>
+__global__ __launch_bounds__(BLOCK) void read_chunks(const u32x4* __restrict__ x, int64_t q,
+                                                     int64_t r, unsigned* __restrict__ out) {
+    __shared__ unsigned wave_x[BLOCK / 64];
+    const int tid = threadIdx.x;
+    const int64_t g = blockIdx.x;
+    const int64_t v0 = g * q + (g < r ? g : r);
+    const int64_t n = q + (g < r ? 1 : 0);
+    const u32x4* p = x + v0 + tid;
+    constexpr int64_t kStep = static_cast<int64_t>(kBatch) * BLOCK;
+    const int64_t nfull = n / kStep;
+
+    unsigned acc = 0;
+    u32x4 a[kBatch], b[kBatch];
+    auto load = [&](u32x4* r, int64_t k) {
+        // The batch's addresses take an opaque zero computed from acc, so its
+        // loads issue after the batch held in the same registers has been
+        // consumed, as written. Without it the compiler hoists them above
+        // that consumption and then copies the registers back, which waits
+        // for every load in flight at the end of each iteration.
+        unsigned z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z) : "v"(acc));
+        const u32x4* q = p + k * kStep + z;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) r[u] = __builtin_nontemporal_load(q + u * BLOCK);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto consume = [&](const u32x4* r) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) acc ^= xor4(r[u]);
+    };
+    if (nfull > 0) {
+        load(a, 0);
+        int64_t k = 0;
+        for (; k + 2 < nfull; k += 2) {
+            load(b, k + 1);
+            consume(a);
+            load(a, k + 2);
+            consume(b);
+        }
+        if (k + 1 < nfull) {
+            load(b, k + 1);
+            consume(a);
+            consume(b);
+        } else {
+            consume(a);
+        }
+    }
+    // the last n - nfull*kStep < kStep vectors, each lane's in bounds only
+    for (int64_t i = nfull * kStep + tid; i < n; i += BLOCK)
+        acc ^= xor4(__builtin_nontemporal_load(x + v0 + i));
+
+    // XOR across the wavefront, then across the wavefronts through LDS
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+    if ((tid & 63) == 0) wave_x[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        unsigned r = 0;
+#pragma unroll
+        for (int w = 0; w < BLOCK / 64; ++w) r ^= wave_x[w];
+        out[g] = r;
+    }
+}
+
+template <int BLOCK>
+int launch(const void* x, int64_t nvec, int64_t chunks, unsigned* out, hipStream_t stream) {
+    hipLaunchKernelGGL(read_chunks<BLOCK>, dim3(static_cast<unsigned>(chunks)), dim3(BLOCK), 0,
+                       stream, static_cast<const u32x4*>(x), nvec / chunks, nvec % chunks, out);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+}  // namespace
+
+extern "C" int lse_control_read(const void* x, int64_t bytes, int64_t chunks, int block,
+                                unsigned* out, hipStream_t stream) {
+    if (bytes < 0 || bytes % 16 != 0 || chunks < 1 || chunks > 0x7FFFFFFF) return 1;
+    if (x == nullptr || out == nullptr || reinterpret_cast<uintptr_t>(x) % 16 != 0) return 1;
+    if (reinterpret_cast<uintptr_t>(out) % 4 != 0) return 1;
+    const int64_t nvec = bytes / 16;
+    switch (block) {
+        case 64: return launch<64>(x, nvec, chunks, out, stream);
+        case 128: return launch<128>(x, nvec, chunks, out, stream);
+        case 256: return launch<256>(x, nvec, chunks, out, stream);
+        case 512: return launch<512>(x, nvec, chunks, out, stream);
+        case 1024: return launch<1024>(x, nvec, chunks, out, stream);
+        default: return 1;
+    }
+}

@@ -1,0 +1,43 @@
+"""ctypes binding of the read-only control kernel (csrc/read_control.hip).
+
+The control reads a byte range once, with the streaming LSE schedule's loads
+and pipeline, and keeps only the XOR of each chunk's 32-bit words. bench.py
+times it on the same buffers and launch geometry as an LSE launch, which shows
+how far the LSE kernel sits from a plain read of the same bytes on the same
+device. It is measurement infrastructure: it lives in its own library and the
+LSE entry points never call it.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+LIBRARY = Path(__file__).resolve().parent / "libread_control.so"
+
+_lib: ctypes.CDLL | None = None
+
+
+def load(path: Path | str = LIBRARY) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = Path(path)
+    if not path.exists():
+        raise RuntimeError(f"{path} is missing: build it with `python -m row_wise_log_amd.build`")
+    lib = ctypes.CDLL(str(path))
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.lse_control_read.restype = ctypes.c_int
+    lib.lse_control_read.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp]
+    _lib = lib
+    return lib
+
+
+def lse_control_read(x: int, nbytes: int, chunks: int, block: int, out: int, stream: int) -> None:
+    """XOR of the 32-bit words of each of `chunks` pieces of x[0:nbytes] into
+    out[chunks] (device pointers; x 16-byte aligned, nbytes a multiple of 16)."""
+    rc = load().lse_control_read(x, nbytes, chunks, block, out, stream)
+    if rc == 1:
+        raise ValueError(f"lse_control_read: invalid argument (bytes={nbytes}, chunks={chunks}, "
+                         f"block={block})")
+    if rc != 0:
+        raise RuntimeError(f"lse_control_read: launch failed ({rc})")

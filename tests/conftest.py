@@ -12,12 +12,15 @@ def pytest_sessionstart(session):
     """Build the HIP library in-tree when it is not there yet (a fresh checkout
     on a machine with hipcc); a library that is already built is used as is.
     The float64 oracle builds itself on first use the same way."""
-    lib = ROOT / "row_wise_log_amd" / "liblse_amd.so"
-    if not lib.exists():
-        import shutil
-        if shutil.which("hipcc") or Path("/opt/rocm/bin/hipcc").exists():
-            from row_wise_log_amd import build
-            build.build()
+    import shutil
+    have_hipcc = shutil.which("hipcc") or Path("/opt/rocm/bin/hipcc").exists()
+    pkg = ROOT / "row_wise_log_amd"
+    if have_hipcc and not (pkg / "liblse_amd.so").exists():
+        from row_wise_log_amd import build
+        build.build()
+    if have_hipcc and not (pkg / "libread_control.so").exists():
+        from row_wise_log_amd import build
+        build.build_control()
 
 
 def pytest_configure(config):
