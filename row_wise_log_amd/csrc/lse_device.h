@@ -217,9 +217,32 @@ __device__ __forceinline__ void fold(Acc& a, const float* f) {
 // than 2^31 terms overflows, and the lane's largest element contributed a term
 // of at least 2^-6, so terms that underflow are negligible. The value the lane
 // represents, m + ln2*(log2 s - (m*log2e - c)), does not need m to be the
-// maximum, only the reference that c and s were formed with.
+// maximum, only the reference that c and s were formed with. A lane whose
+// reference is not a finite value within +-2^30 (its first batch, above all)
+// goes to fold<N> directly: its lazy sum would be thrown away. Where each lane
+// folds only one or two batches per row, that halves the exponentials.
 template <int N>
 __device__ __forceinline__ void fold_lazy(Acc& a, const float* f) {
+    if (__builtin_fabsf(a.m) <= kClamp) {
+        const float t = sum_exp_of<N>(f, a.c);
+        if (t <= 0x1p32f) {
+            const float s = a.s;
+            const float sum = s + t;
+            const float bp = sum - s;
+            a.e += (s - (sum - bp)) + (t - bp);
+            a.s = sum;
+            return;
+        }
+    }
+    fold<N>(a, f);
+}
+
+// fold_lazy with the lazy sum always taken first and a single branch: for
+// accumulators that fold many small batches (one per column and step in the
+// non-last-axis kernel), where a second branch per fold costs more than the
+// exponentials it saves on an accumulator's first batch.
+template <int N>
+__device__ __forceinline__ void fold_lazy_flat(Acc& a, const float* f) {
     const float t = sum_exp_of<N>(f, a.c);
     if (t <= 0x1p32f && __builtin_fabsf(a.m) <= kClamp) {
         const float s = a.s;

@@ -10,7 +10,7 @@
 // torch.logsumexp (abstract, §6); this covers the reduction axes other than
 // the last (inner == 1 is lse_forward). Same arithmetic as the row kernels:
 // each element read once, a per-lane (max, exp-sum) accumulator folded lazily
-// (fold_lazy), pairwise merges, one fp32 per output.
+// (fold_lazy_flat), pairwise merges, one fp32 per output.
 //
 // Layout. The reduced elements of one output are inner elements apart, and
 // neighbouring outputs are neighbours in memory. A lane owns K adjacent
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
             float g[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) g[u] = f[u][k];
-            fold_lazy<U>(a[k], g);
+            fold_lazy_flat<U>(a[k], g);
         }
     };
 
