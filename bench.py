@@ -169,6 +169,9 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
     if op in ("lse", "logprob", "dim"):
         control = time_read_control(torch, bufs, rows * cols * esize, plan, steps, warmup, stream)
         control["frac_of_read_control"] = round(control["launch_us_mean"] / (mean_launch * 1e3), 4)
+    else:
+        control = time_copy_control(torch, bufs, rows * cols * esize, steps, warmup, stream)
+        control["frac_of_copy_control"] = round(control["launch_us_mean"] / (mean_launch * 1e3), 4)
     return {
         "w": w, "plan": plan, "rotate": rotate, "in_bytes": in_bytes, "out_bytes": out_bytes,
         "ms_per_step": ms_step, "launch_ms_mean": mean_launch,
@@ -206,6 +209,36 @@ def time_read_control(torch, bufs, nbytes: int, plan: dict, steps: int, warmup: 
     us = e0.elapsed_time(e1) * 1e3 / steps
     return {"kernel": "read_chunks (XOR of each chunk's words)", "grid": grid, "block": block,
             "launch_us_mean": round(us, 2), "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def time_copy_control(torch, bufs, nbytes: int, steps: int, warmup: int, stream) -> dict:
+    """The copy control kernel from the same input copies, in the same
+    rotation, into a buffer of grad_x's size (its own, so the backward's
+    output stays for the oracle check): x's bytes read and written once, one
+    batch of four 16-byte vectors per lane in 256-thread workgroups (the
+    backward's chunking of long rows). Timed like the backward launches."""
+    from row_wise_log_amd import read_control as RC
+    grid, block = -(-(nbytes // 16) // 1024), 256
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sh = stream.cuda_stream
+
+    def step(i):
+        RC.lse_control_copy(bufs[i % len(bufs)].data_ptr(), dst.data_ptr(), nbytes, grid, block, sh)
+
+    for i in range(warmup):
+        step(i)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del dst
+    return {"kernel": "copy_chunks (x copied to a buffer of grad_x's size)", "grid": grid, "block": block,
+            "launch_us_mean": round(us, 2), "GBs_read_plus_written": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def sweep_read_control(torch, cfg: int, steps: int, warmup: int) -> list:
@@ -507,7 +540,8 @@ def main() -> int:
                 "traffic": traffic,
                 "launch_us_mean": round(r["launch_ms_mean"] * 1e3, 2),
                 "algorithmic_bytes_per_launch": r["in_bytes"] + r["out_bytes"],
-                "read_control": r["control"],
+                ("read_control" if args.op in ("lse", "logprob", "dim") else "copy_control"):
+                    r["control"],
             },
         }
         if args.control_sweep:
@@ -529,9 +563,12 @@ def main() -> int:
                            "achieved_GBs_per_launch": round(rc["achieved_gbs"], 1),
                            "rows_per_s": round(rc["w"].rows / (rc["ms_per_step"] * 1e-3), 1),
                            "launch_floor_us": round(floor, 2)}
-                    if rc["control"] is not None:
+                    if "frac_of_read_control" in rc["control"]:
                         rec["read_control_us"] = rc["control"]["launch_us_mean"]
                         rec["frac_of_read_control"] = rc["control"]["frac_of_read_control"]
+                    else:
+                        rec["copy_control_us"] = rc["control"]["launch_us_mean"]
+                        rec["frac_of_copy_control"] = rc["control"]["frac_of_copy_control"]
                     if args.op == "lse" and rc["in_bytes"] <= CACHE_BYTES // 4:
                         rec["us_per_call_warm"] = round(warm_us_per_call(torch, B, handle, cfg), 2)
                     log(json.dumps(rec))

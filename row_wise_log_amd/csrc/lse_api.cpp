@@ -232,7 +232,6 @@ lse_status_t make_grad_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64
         a->chunks_per_row = 1;
         a->grid = ceil_div(rows, r);
     }
-    (void)ub;
     return LSE_OK;
 }
 

@@ -1,4 +1,4 @@
-// Read-only control kernel: the measuring stick for the LSE kernels.
+// Control kernels: the measuring sticks for the LSE kernels.
 //
 // It reads a contiguous byte range exactly once, with the load instruction and
 // software pipeline of the streaming LSE schedule: 16-byte non-temporal loads,
@@ -24,6 +24,14 @@
 // words to out[g] (device, `chunks` words). Returns 0 on success, 1 for an
 // invalid argument (checked before any HIP call), 2 if the launch fails.
 // Asynchronous on `stream`; allocates nothing.
+//
+//   int lse_control_copy(const void* src, void* dst, int64_t bytes, int64_t chunks,
+//                        int block, hipStream_t stream)
+//
+// The measuring stick for the backward passes, which read x and write grad_x
+// of the same size: src[0:bytes] copied to dst with the same chunks, loads and
+// pipeline, non-temporal 16-byte stores. src and dst 16-byte aligned and not
+// overlapping; the same return codes.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -101,10 +109,66 @@ __global__ __launch_bounds__(BLOCK) void read_chunks(const u32x4* __restrict__ x
     }
 }
 
+// The copy control: the same chunks, each vector loaded and stored back to
+// dst at the same offset with 16-byte non-temporal loads and stores, the
+// next batch's loads issued before a batch is stored.
+template <int BLOCK>
+__global__ __launch_bounds__(BLOCK) void copy_chunks(const u32x4* __restrict__ src,
+                                                     u32x4* __restrict__ dst, int64_t q,
+                                                     int64_t r) {
+    const int tid = threadIdx.x;
+    const int64_t g = blockIdx.x;
+    const int64_t v0 = g * q + (g < r ? g : r);
+    const int64_t n = q + (g < r ? 1 : 0);
+    constexpr int64_t kStep = static_cast<int64_t>(kBatch) * BLOCK;
+    const int64_t nfull = n / kStep;
+    const u32x4* p = src + v0 + tid;
+    u32x4* d = dst + v0 + tid;
+
+    u32x4 a[kBatch], b[kBatch];
+    auto load = [&](u32x4* w, int64_t k) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) w[u] = __builtin_nontemporal_load(p + k * kStep + u * BLOCK);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto store = [&](const u32x4* w, int64_t k) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) __builtin_nontemporal_store(w[u], d + k * kStep + u * BLOCK);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if (nfull > 0) {
+        load(a, 0);
+        int64_t k = 0;
+        for (; k + 2 < nfull; k += 2) {
+            load(b, k + 1);
+            store(a, k);
+            load(a, k + 2);
+            store(b, k + 1);
+        }
+        if (k + 1 < nfull) {
+            load(b, k + 1);
+            store(a, k);
+            store(b, k + 1);
+        } else {
+            store(a, k);
+        }
+    }
+    for (int64_t i = nfull * kStep + tid; i < n; i += BLOCK)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + v0 + i), dst + v0 + i);
+}
+
 template <int BLOCK>
 int launch(const void* x, int64_t nvec, int64_t chunks, unsigned* out, hipStream_t stream) {
     hipLaunchKernelGGL(read_chunks<BLOCK>, dim3(static_cast<unsigned>(chunks)), dim3(BLOCK), 0,
                        stream, static_cast<const u32x4*>(x), nvec / chunks, nvec % chunks, out);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+template <int BLOCK>
+int launch_copy(const void* src, void* dst, int64_t nvec, int64_t chunks, hipStream_t stream) {
+    hipLaunchKernelGGL(copy_chunks<BLOCK>, dim3(static_cast<unsigned>(chunks)), dim3(BLOCK), 0,
+                       stream, static_cast<const u32x4*>(src), static_cast<u32x4*>(dst),
+                       nvec / chunks, nvec % chunks);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
@@ -122,6 +186,26 @@ extern "C" int lse_control_read(const void* x, int64_t bytes, int64_t chunks, in
         case 256: return launch<256>(x, nvec, chunks, out, stream);
         case 512: return launch<512>(x, nvec, chunks, out, stream);
         case 1024: return launch<1024>(x, nvec, chunks, out, stream);
+        default: return 1;
+    }
+}
+
+extern "C" int lse_control_copy(const void* src, void* dst, int64_t bytes, int64_t chunks,
+                                int block, hipStream_t stream) {
+    if (bytes < 0 || bytes % 16 != 0 || chunks < 1 || chunks > 0x7FFFFFFF) return 1;
+    if (src == nullptr || dst == nullptr) return 1;
+    if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+        return 1;
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+    if (s0 < d0 + static_cast<uintptr_t>(bytes) && d0 < s0 + static_cast<uintptr_t>(bytes))
+        return 1;  // overlapping ranges
+    const int64_t nvec = bytes / 16;
+    switch (block) {
+        case 64: return launch_copy<64>(src, dst, nvec, chunks, stream);
+        case 128: return launch_copy<128>(src, dst, nvec, chunks, stream);
+        case 256: return launch_copy<256>(src, dst, nvec, chunks, stream);
+        case 512: return launch_copy<512>(src, dst, nvec, chunks, stream);
+        case 1024: return launch_copy<1024>(src, dst, nvec, chunks, stream);
         default: return 1;
     }
 }

@@ -1,11 +1,13 @@
-"""ctypes binding of the read-only control kernel (csrc/read_control.hip).
+"""ctypes binding of the control kernels (csrc/read_control.hip).
 
-The control reads a byte range once, with the streaming LSE schedule's loads
-and pipeline, and keeps only the XOR of each chunk's 32-bit words. bench.py
-times it on the same buffers and launch geometry as an LSE launch, which shows
-how far the LSE kernel sits from a plain read of the same bytes on the same
-device. It is measurement infrastructure: it lives in its own library and the
-LSE entry points never call it.
+The read control reads a byte range once, with the streaming LSE schedule's
+loads and pipeline, and keeps only the XOR of each chunk's 32-bit words; the
+copy control reads a range and writes it to another buffer the same way.
+bench.py times them on the same buffers and launch geometry as an LSE launch
+(read) or a backward launch (copy), which shows how far each kernel sits from
+plainly moving the same bytes on the same device. They are measurement
+infrastructure: they live in their own library and the LSE entry points never
+call them.
 """
 from __future__ import annotations
 
@@ -28,6 +30,8 @@ def load(path: Path | str = LIBRARY) -> ctypes.CDLL:
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.lse_control_read.restype = ctypes.c_int
     lib.lse_control_read.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp]
+    lib.lse_control_copy.restype = ctypes.c_int
+    lib.lse_control_copy.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp]
     _lib = lib
     return lib
 
@@ -41,3 +45,14 @@ def lse_control_read(x: int, nbytes: int, chunks: int, block: int, out: int, str
                          f"block={block})")
     if rc != 0:
         raise RuntimeError(f"lse_control_read: launch failed ({rc})")
+
+
+def lse_control_copy(src: int, dst: int, nbytes: int, chunks: int, block: int, stream: int) -> None:
+    """Copy src[0:nbytes] to dst (device pointers, 16-byte aligned, not
+    overlapping; nbytes a multiple of 16) in `chunks` workgroups of `block`."""
+    rc = load().lse_control_copy(src, dst, nbytes, chunks, block, stream)
+    if rc == 1:
+        raise ValueError(f"lse_control_copy: invalid argument (bytes={nbytes}, chunks={chunks}, "
+                         f"block={block})")
+    if rc != 0:
+        raise RuntimeError(f"lse_control_copy: launch failed ({rc})")

@@ -1,12 +1,13 @@
-"""The read-only control kernel that bench.py times beside the LSE kernels.
+"""The control kernels that bench.py times beside the LSE kernels.
 
 It must read every byte it is given, or the rate it reports would flatter
 the device and understate how close the LSE kernels come to it: each chunk's
 XOR of 32-bit words is compared with numpy's over the same words, for ragged
 sizes, more chunks than vectors, every block size, and the headline
 workload's exact geometry (512 chunks of one 256512-byte row each, 512
-threads). Its argument checks run on the host before any HIP call, so they
-are tested without a GPU.
+threads). The copy control must move every byte to the same offset and
+write nothing else. The argument checks of both run on the host before any
+HIP call, so they are tested without a GPU.
 """
 import numpy as np
 import pytest
@@ -120,3 +121,42 @@ def test_headline_geometry(torch_gpu):
     got = run(torch_gpu, words, 512, 512)
     rows = words.reshape(512, -1)
     assert np.array_equal(got, np.bitwise_xor.reduce(rows, axis=1))
+
+
+@pytest.mark.parametrize("args", [
+    dict(nbytes=15),                       # not whole vectors
+    dict(nbytes=-16),
+    dict(chunks=0),
+    dict(block=96),
+    dict(src=8),                           # not 16-byte aligned
+    dict(dst=24),
+    dict(src=0),
+    dict(dst=0),
+    dict(src=1 << 20, dst=(1 << 20) + 4096, nbytes=8192),   # overlapping ranges
+    dict(src=(1 << 20) + 4096, dst=1 << 20, nbytes=8192),
+])
+def test_copy_argument_checks_on_host(args):
+    a = dict(src=1 << 20, dst=1 << 24, nbytes=4096, chunks=4, block=256)
+    a.update(args)
+    with pytest.raises(ValueError):
+        RC.lse_control_copy(a["src"], a["dst"], a["nbytes"], a["chunks"], a["block"], 0)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("block", [64, 256, 1024])
+def test_copy_moves_every_byte(torch_gpu, block):
+    torch = torch_gpu
+    rng = np.random.default_rng(100 + block)
+    for nvec in (1, 4 * block - 1, 4 * block, 8 * block + 5, 50_001):
+        for chunks in (1, 3, -(-nvec // 1024), nvec + 7):
+            print(f"copy control block={block} nvec={nvec} chunks={chunks}", flush=True)
+            data = rng.integers(0, 2 ** 32, size=4 * nvec, dtype=np.uint32)
+            src = torch.from_numpy(data.view(np.int32)).cuda()
+            guard = 64   # words of canary on each side of the destination
+            dst = torch.full((4 * nvec + 2 * guard,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+            RC.lse_control_copy(src.data_ptr(), dst[guard:].data_ptr(), 16 * nvec, chunks, block,
+                                torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            out = dst.cpu().numpy().view(np.uint32)
+            assert np.array_equal(out[guard:guard + 4 * nvec], data), (block, nvec, chunks)
+            assert np.all(out[:guard] == 0x5A5A5A5A) and np.all(out[guard + 4 * nvec:] == 0x5A5A5A5A)
