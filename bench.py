@@ -165,6 +165,7 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
     mean_launch = e0.elapsed_time(e1) / steps
 
     ms_step = wall / steps * 1e3
+    median_us = median_single_call_us(torch, step, warmup + steps, stream)
     control = None
     if op in ("lse", "logprob", "dim"):
         control = time_read_control(torch, bufs, rows * cols * esize, plan, steps, warmup, stream)
@@ -177,8 +178,25 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
         "ms_per_step": ms_step, "launch_ms_mean": mean_launch,
         "value_gbs": in_bytes / (ms_step * 1e-3) / 1e9,
         "achieved_gbs": (in_bytes + out_bytes) / (mean_launch * 1e-3) / 1e9,
-        "out": out, "op": op, "bwd": bwd, "control": control,
+        "out": out, "op": op, "bwd": bwd, "control": control, "median_us": median_us,
     }
+
+
+def median_single_call_us(torch, step, first: int, stream, calls: int = 60, skip: int = 10) -> float:
+    """Median duration of single launches, each bracketed by its own event
+    pair on the launch stream while the stream stays busy (the launches are
+    queued back to back, so each one's start event fires when the previous
+    launch ends): `calls` launches continuing the input rotation, the first
+    `skip` not counted."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(first + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs[skip:]]))
 
 
 def time_read_control(torch, bufs, nbytes: int, plan: dict, steps: int, warmup: int,
@@ -539,6 +557,7 @@ def main() -> int:
                 "frac": round(r["achieved_gbs"] / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
                 "launch_us_mean": round(r["launch_ms_mean"] * 1e3, 2),
+                "launch_us_median_single_calls": round(r["median_us"], 2),
                 "algorithmic_bytes_per_launch": r["in_bytes"] + r["out_bytes"],
                 ("read_control" if args.op in ("lse", "logprob", "dim") else "copy_control"):
                     r["control"],
@@ -560,6 +579,7 @@ def main() -> int:
                            "pct_hbm_peak": round(100 * rc["value_gbs"] / HBM_PEAK_GBS, 2),
                            "us_per_call": round(rc["ms_per_step"] * 1e3, 2),
                            "launch_us_mean": round(rc["launch_ms_mean"] * 1e3, 2),
+                           "launch_us_median_single_calls": round(rc["median_us"], 2),
                            "achieved_GBs_per_launch": round(rc["achieved_gbs"], 1),
                            "rows_per_s": round(rc["w"].rows / (rc["ms_per_step"] * 1e-3), 1),
                            "launch_floor_us": round(floor, 2)}
