@@ -85,7 +85,7 @@ def plan_name(plan: dict) -> str:
 
 
 def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int | None,
-                op: str = "lse"):
+                op: str = "lse", graph: bool = False):
     w = workloads.make(cfg)
     rows, cols = w.rows, w.cols
     esize = 2 if w.dtype == "bf16" else 4
@@ -124,7 +124,7 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
     sh = stream.cuda_stream
     plan = B.lse_plan(dtype_code, rows, cols, cols, bufs[0].data_ptr(), 256, 0)
 
-    def step(i):
+    def step(i, sh=sh):
         if op == "dim":
             B.lse_forward_dim(handle, bufs[i % rotate].data_ptr(), dtype_code, 1, rows, cols,
                               out.data_ptr(), sh)
@@ -144,28 +144,44 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
             B.lse_token_logprob(handle, bufs[i % rotate].data_ptr(), dtype_code, rows, cols, cols,
                                 targets.data_ptr(), out.data_ptr(), None, sh)
 
-    for i in range(warmup):
-        step(i)
+    warmup = run_warmup(torch, step, warmup, stream)
     # The timed region: K back-to-back launches between a synchronize on each
     # side, with one HIP event pair on the launch stream around them. The
     # wall clock gives the whole-job rate; the events give the mean launch
     # duration on the GPU (the launches are queued ahead, so host overhead
     # is hidden and the event interval is the kernels' own time plus the
     # hardware's inter-dispatch gaps).
+    # With graph=True the K steps are captured into one HIP graph first and
+    # the timed region is one replay of it (after one untimed replay).
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            hs = torch.cuda.current_stream().cuda_stream
+            for i in range(steps):
+                step(warmup + i, hs)
+        torch.cuda.synchronize()
+        g.replay()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for i in range(steps):
-        step(warmup + i)
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(steps):
+            step(warmup + i)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     mean_launch = e0.elapsed_time(e1) / steps
+    del g
 
     ms_step = wall / steps * 1e3
     median_us = median_single_call_us(torch, step, warmup + steps, stream)
+    graph_us = graph_us_per_call(torch, step, warmup + steps + 60)
     control = None
     if op in ("lse", "logprob", "dim"):
         control = time_read_control(torch, bufs, rows * cols * esize, plan, steps, warmup, stream)
@@ -179,7 +195,69 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
         "value_gbs": in_bytes / (ms_step * 1e-3) / 1e9,
         "achieved_gbs": (in_bytes + out_bytes) / (mean_launch * 1e-3) / 1e9,
         "out": out, "op": op, "bwd": bwd, "control": control, "median_us": median_us,
+        "graph_us": graph_us, "warmup": warmup,
     }
+
+
+WARMUP_SECONDS = 0.05
+
+
+def run_warmup(torch, step, warmup: int | None, stream) -> int:
+    """Run the untimed warmup steps and return how many ran. warmup=None
+    (the default) runs at least 40 steps and at least WARMUP_SECONDS of
+    back-to-back GPU work: on a GPU that was idle, launch times rise for the
+    first few milliseconds of continuous work and settle after about 20 ms
+    (workload 2: 22.4 -> 24.9 -> 21.9 us per launch), so a shorter warmup
+    times that transient instead of the steady state."""
+    if warmup is not None:
+        for i in range(warmup):
+            step(i)
+        return warmup
+    # 20 steps absorb the first call's one-time costs (code object load);
+    # the next 20, timed, give the step time that sizes the rest.
+    for i in range(20):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(20, 40):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_step = max(e0.elapsed_time(e1) * 1e-3 / 20, 1e-6)
+    extra = int(np.ceil(WARMUP_SECONDS / per_step))
+    for i in range(40, 40 + extra):
+        step(i)
+    return 40 + extra
+
+
+def graph_us_per_call(torch, step, first: int, calls: int = 100, replays: int = 20) -> float:
+    """Microseconds per call when `calls` consecutive calls (continuing the
+    input rotation) are captured into one HIP graph and the graph is
+    replayed: the per-launch host and dispatch cost that a caller replaying a
+    captured step sees. The entry points allocate nothing and enqueue no
+    memset, so they are capturable as they are."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        hs = torch.cuda.current_stream().cuda_stream
+        for i in range(calls):
+            step(first + i, hs)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (replays * calls)
+    del g
+    return us
 
 
 def median_single_call_us(torch, step, first: int, stream, calls: int = 60, skip: int = 10) -> float:
@@ -468,8 +546,10 @@ def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0, op: str = "lse")
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: at least 40 steps and at least 50 ms of "
+                         "back-to-back GPU work, so that the timed steps run at the steady state)")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--rotate", type=int, default=None,
                     help="input copies cycled through (default: enough to exceed 2x the 256 MiB cache)")
@@ -483,6 +563,10 @@ def main() -> int:
                          "seeded int64 target per row; backward: lse_backward (reads x, writes "
                          "grad_x); logprob_backward: lse_token_logprob_backward (the same, with "
                          "the targets); dim: lse_forward_dim over the workload's first axis")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K timed steps into one HIP graph and time one replay of it "
+                         "(the same K full calls on the same rotating inputs; default: K eager "
+                         "launches)")
     ap.add_argument("--control-sweep", action="store_true",
                     help="also time the read-only control kernel over a grid of workgroup counts "
                          "and sizes on the workload's input, one JSON line each to stderr (is "
@@ -515,9 +599,10 @@ def main() -> int:
         del src, dst
     handle = B.lse_create(0)
     try:
-        log(f"timing config {args.config} ({args.op}): {args.steps} steps after {args.warmup} warmup")
+        log(f"timing config {args.config} ({args.op}): {args.steps} steps after "
+            f"{'at least 50 ms of' if args.warmup is None else args.warmup} warmup")
         r = time_config(torch, B, handle, args.config, args.steps, args.warmup, args.rotate,
-                        args.op)
+                        args.op, args.graph)
         w = r["w"]
         traffic = recorded_traffic(args.config) if args.op == "lse" else None
         floor = launch_floor_us(torch, B, handle)
@@ -530,7 +615,7 @@ def main() -> int:
             "unit": "GB/s",
             "n_gpus": 1,
             "steps": args.steps,
-            "warmup": args.warmup,
+            "warmup": r["warmup"],
             "ms_per_step": round(r["ms_per_step"], 5),
             "higher_is_better": True,
             "scaling": "weak",
@@ -548,6 +633,9 @@ def main() -> int:
                 "us_per_call": round(r["ms_per_step"] * 1e3, 2),
                 "rows_per_s": round(w.rows / (r["ms_per_step"] * 1e-3), 1),
                 "launch_floor_us": round(floor, 2),
+                "graph_us_per_call": round(r["graph_us"], 2),
+                "timed_as": "one HIP graph replay of the K steps" if args.graph
+                            else "K eager launches",
             },
             "roofline": {
                 "bound": "hbm",
@@ -564,14 +652,14 @@ def main() -> int:
             },
         }
         if args.control_sweep:
-            sweep_read_control(torch, args.config, args.steps, args.warmup)
+            sweep_read_control(torch, args.config, args.steps, r["warmup"])
         if args.all:
             Path(args.all_out).parent.mkdir(parents=True, exist_ok=True)
             with open(args.all_out, "w") as f:
                 for cfg in [1, 2, 3, 4, 5]:
                     log(f"timing config {cfg}")
                     rc = r if cfg == args.config else time_config(
-                        torch, B, handle, cfg, args.steps, args.warmup, None, args.op)
+                        torch, B, handle, cfg, args.steps, args.warmup, None, args.op, args.graph)
                     rec = {"config": cfg, "op": args.op, "workload": rc["w"].spec.name,
                            "plan": plan_name(rc["plan"]) if args.op in ("lse", "logprob")
                            else f"lse_{args.op}",
@@ -580,6 +668,7 @@ def main() -> int:
                            "us_per_call": round(rc["ms_per_step"] * 1e3, 2),
                            "launch_us_mean": round(rc["launch_ms_mean"] * 1e3, 2),
                            "launch_us_median_single_calls": round(rc["median_us"], 2),
+                           "graph_us_per_call": round(rc["graph_us"], 2),
                            "achieved_GBs_per_launch": round(rc["achieved_gbs"], 1),
                            "rows_per_s": round(rc["w"].rows / (rc["ms_per_step"] * 1e-3), 1),
                            "launch_floor_us": round(floor, 2)}
