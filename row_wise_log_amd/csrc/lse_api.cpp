@@ -182,7 +182,11 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
 }
 
 // The backward pass's work split: units are 16-byte vectors when every row
-// of x and grad_x starts 16-byte aligned, else single elements. Rows of at
+// of x and grad_x starts 16-byte aligned; when the rows are not aligned but
+// x and grad_x have the same phase mod 16 (same address and same row stride
+// mod 16, as contiguous rows of an odd width have), units are 16-byte vectors
+// from each row's first 16-byte boundary, (cols - K + 1) / K of them per row,
+// with the head and tail elements done singly; else single elements. Rows of at
 // least one batch (256 lanes x 4 units) are cut into chunks of 1 to 4
 // batches, sized so the grid has about 4 workgroups per CU; shorter rows are
 // packed several to a workgroup (up to 4 batches of units). A block's byte
@@ -195,13 +199,17 @@ lse_status_t make_grad_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64
     const int k = 16 / esize;
     const int64_t xs = (rows > 1 ? row_stride : cols) * esize;
     const int64_t gs = (rows > 1 ? grad_row_stride : cols) * esize;
-    const bool vec = cols / k >= 1 && x_addr % 16 == 0 && g_addr % 16 == 0 &&
-                     (rows == 1 || (xs % 16 == 0 && gs % 16 == 0));
-    const int64_t units = vec ? cols / k : cols;
+    const bool aligned = cols / k >= 1 && x_addr % 16 == 0 && g_addr % 16 == 0 &&
+                         (rows == 1 || (xs % 16 == 0 && gs % 16 == 0));
+    const bool peel = !aligned && cols >= 2 * k - 1 && x_addr % 16 == g_addr % 16 &&
+                      (rows == 1 || xs % 16 == gs % 16);
+    const bool vec = aligned || peel;
+    const int64_t units = aligned ? cols / k : peel ? (cols - (k - 1)) / k : cols;
     const int64_t ub = vec ? 16 : esize;
     constexpr int64_t kBatch = 256 * 4;
     a->bf16 = dtype == LSE_DTYPE_BF16;
     a->vector_units = vec;
+    a->peel = peel;
     a->rows = rows;
     a->cols = cols;
     a->xs_bytes = xs;

@@ -20,8 +20,10 @@
 // one v_exp_f32 and one multiply.
 //
 // Work split (planned on the host, lse_api.cpp): the row's units (16-byte
-// vectors when every row of x and of grad_x starts 16-byte aligned, single
-// elements otherwise) are cut into workgroup items. A long row gives several
+// vectors when every row of x and of grad_x starts 16-byte aligned; also,
+// with a per-row head of fewer than K elements peeled off (PEEL), when the
+// rows are misaligned alike in x and grad_x, as contiguous rows of an odd
+// width are; single elements otherwise) are cut into workgroup items. A long row gives several
 // workgroups a contiguous chunk each (R == 1; the row's lse and grad_out are
 // uniform and read through the scalar unit); short rows are packed R per
 // workgroup, whose lanes walk the R x W units of the block (the row index
@@ -91,10 +93,14 @@ __device__ __forceinline__ void store_scalar(char* p, float v) {
 }  // namespace
 
 // VEC: units are 16-byte vectors (K elements); otherwise single elements.
+// PEEL (VEC only): row r's units start h(r) < K elements into the row, at its
+// first 16-byte boundary; x and grad_x have the same phase, so one h(r)
+// serves both. Every row then has the same nunits = (cols - K + 1) / K units
+// and cols - nunits * K elements outside them (its head and its tail).
 // ONE_ROW: the workgroup takes one chunk of one row (rows_per_wg == 1), so
 // the row's lse and grad_out are uniform; otherwise every unit loads its own
 // row's pair. Each instance issues the same loads in every batch.
-template <DType D, int BLOCK, int U, bool VEC, bool ONE_ROW, bool TOK>
+template <DType D, int BLOCK, int U, bool VEC, bool PEEL, bool ONE_ROW, bool TOK>
 __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, int64_t rows,
                                                   int64_t cols, int64_t xs_bytes,
                                                   const float* __restrict__ lse,
@@ -108,8 +114,22 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
     constexpr int UB = VEC ? 16 : EB;  // bytes per unit
     const int tid = threadIdx.x;
     const int64_t b = blockIdx.x;
-    const int64_t nunits = cols / K;
-    const int tail = VEC ? static_cast<int>(cols - nunits * K) : 0;
+    const int64_t nunits = PEEL ? (cols - (K - 1)) / K : cols / K;
+    // elements of each row outside its units: the tail (and with PEEL the head)
+    const int rest = VEC ? static_cast<int>(cols - nunits * K) : 0;
+
+    // PEEL: the head h(r) of row r from the phase of its start mod 16, which
+    // is (x + r * xs) mod 16 = (x mod 16 + (r mod 16) * (xs mod 16)) mod 16.
+    const unsigned xphase = static_cast<unsigned>(reinterpret_cast<uintptr_t>(x)) & 15u;
+    const unsigned sphase = static_cast<unsigned>(xs_bytes) & 15u;
+    auto head_of = [&](int64_t row) -> int {
+        if constexpr (!PEEL) {
+            return 0;
+        } else {
+            const unsigned ph = (xphase + (static_cast<unsigned>(row) & 15u) * sphase) & 15u;
+            return static_cast<int>(((16u - ph) & 15u) / EB);
+        }
+    };
 
     // This workgroup's block: rows [r0, r0 + nr), units [u0, u0 + W) of each.
     int64_t r0, u0, W;
@@ -128,11 +148,14 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
     }
     const int n = static_cast<int>(nr * W);  // the planner keeps this below 2^22
     // The block's bytes as one buffer each for x and grad_x (offsets are
-    // relative to the block's first unit; the planner keeps them below 2^31).
-    const char* xb = x + r0 * xs_bytes + u0 * UB;
-    char* gb = gx + r0 * gs_bytes + u0 * UB;
-    const int64_t xspan = (nr - 1) * xs_bytes + W * UB;
-    const int64_t gspan = (nr - 1) * gs_bytes + W * UB;
+    // relative to the block's first unit, or with PEEL and several rows to
+    // its first row's start; the planner keeps them below 2^31).
+    const int h0 = ONE_ROW ? head_of(r0) : 0;
+    const char* xb = x + r0 * xs_bytes + h0 * EB + u0 * UB;
+    char* gb = gx + r0 * gs_bytes + h0 * EB + u0 * UB;
+    const int64_t last_bytes = (PEEL && !ONE_ROW) ? cols * EB : W * UB;
+    const int64_t xspan = (nr - 1) * xs_bytes + last_bytes;
+    const int64_t gspan = (nr - 1) * gs_bytes + last_bytes;
     const auto xr = make_rsrc(xb, xspan);
     const auto gr = make_rsrc(gb, gspan);
     const float inv_w = 1.0f / static_cast<float>(W);
@@ -160,8 +183,9 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
     int64_t t0 = -1;
     if (ONE_ROW && n > 0) row_terms(r0, l0, g0, t0);
 
-    // Item j of the block: its row (local) and unit, as byte offsets.
-    auto offsets = [&](int j, int& rl, int& xo, int& go, int& uu) {
+    // Item j of the block: its row (local), byte offsets, and the column of
+    // its unit's first element.
+    auto offsets = [&](int j, int& rl, int& xo, int& go, int64_t& c0) {
         const bool in = j < n;
         rl = 0;
         if constexpr (!ONE_ROW) {
@@ -170,9 +194,10 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
             rl = rl < nr ? rl : nr - 1;
         }
         const int u = j - rl * static_cast<int>(W);
-        uu = u;
-        xo = in ? static_cast<int>(rl * xs_bytes) + u * UB : kOffFar;
-        go = in ? static_cast<int>(rl * gs_bytes) + u * UB : kOffFar;
+        const int h = ONE_ROW ? 0 : head_of(r0 + rl);  // ONE_ROW: in the base already
+        xo = in ? static_cast<int>(rl * xs_bytes) + h * EB + u * UB : kOffFar;
+        go = in ? static_cast<int>(rl * gs_bytes) + h * EB + u * UB : kOffFar;
+        c0 = (ONE_ROW ? h0 : h) + (u0 + u) * static_cast<int64_t>(K);
     };
 
     struct Batch {
@@ -185,8 +210,9 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
     auto load_batch = [&](Batch& t, int j0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int rl, xo, go, uu;
-            offsets(j0 + u * BLOCK, rl, xo, go, uu);
+            int rl, xo, go;
+            int64_t c0;
+            offsets(j0 + u * BLOCK, rl, xo, go, c0);
             t.go[u] = go;
             if constexpr (VEC) {
                 t.w[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, 2));
@@ -203,7 +229,7 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
                 t.l[u] = l0;
                 t.g[u] = g0;
             }
-            if constexpr (TOK) t.tk[u] = unit_target(tt, (u0 + uu) * static_cast<int64_t>(K));
+            if constexpr (TOK) t.tk[u] = unit_target(tt, c0);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -249,15 +275,21 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
         }
     }
 
-    // The last cols % K elements of each row (vector units only): the row's
-    // last chunk in the one-row case, every row of the block otherwise.
+    // The elements of each row outside its units (vector units only): item e
+    // < h(r) is head column e, the others tail column nunits * K + e. In the
+    // one-row case the row's first chunk takes the head and its last chunk the
+    // tail; otherwise the block takes every row's.
     if constexpr (VEC) {
-        if (tail > 0 && (!ONE_ROW || u0 + W == nunits)) {
-            for (int i = tid; i < nr * tail; i += BLOCK) {
-                const int rl = i / tail;
-                const int e = i - rl * tail;
+        const bool first = !ONE_ROW || u0 == 0;
+        const bool last = !ONE_ROW || u0 + W == nunits;
+        if (rest > 0 && (first || last)) {
+            for (int i = tid; i < nr * rest; i += BLOCK) {
+                const int rl = i / rest;
+                const int e = i - rl * rest;
                 const int64_t row = r0 + rl;
-                const int64_t col = nunits * K + e;
+                const int h = head_of(row);
+                if (e < h ? !first : !last) continue;
+                const int64_t col = e < h ? e : nunits * K + e;
                 const float xv = load_scalar<D>(x + row * xs_bytes + col * EB);
                 float l, g;
                 int64_t tt;
@@ -272,33 +304,38 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
 
 namespace {
 
-template <DType D, bool VEC, bool ONE_ROW, bool TOK>
+template <DType D, bool VEC, bool PEEL, bool ONE_ROW, bool TOK>
 hipError_t launch_grad_k(const GradArgs& a) {
     constexpr int BLOCK = 256, U = 4;
-    hipLaunchKernelGGL((lse_grad<D, BLOCK, U, VEC, ONE_ROW, TOK>), dim3(a.grid), dim3(BLOCK), 0,
+    hipLaunchKernelGGL((lse_grad<D, BLOCK, U, VEC, PEEL, ONE_ROW, TOK>), dim3(a.grid), dim3(BLOCK), 0,
                        a.stream, a.x, a.rows, a.cols, a.xs_bytes, a.lse, a.grad_out, a.targets,
                        a.grad_x, a.gs_bytes, a.rows_per_wg, a.chunks_per_row, a.chunk_units);
     return hipGetLastError();
 }
 
-template <DType D, bool VEC, bool TOK>
+template <DType D, bool VEC, bool PEEL, bool TOK>
 hipError_t launch_grad_t(const GradArgs& a) {
-    return a.rows_per_wg == 1 ? launch_grad_k<D, VEC, true, TOK>(a)
-                              : launch_grad_k<D, VEC, false, TOK>(a);
+    return a.rows_per_wg == 1 ? launch_grad_k<D, VEC, PEEL, true, TOK>(a)
+                              : launch_grad_k<D, VEC, PEEL, false, TOK>(a);
 }
 
-template <DType D, bool VEC>
+template <DType D, bool VEC, bool PEEL>
+hipError_t launch_grad_p(const GradArgs& a) {
+    return a.targets != nullptr ? launch_grad_t<D, VEC, PEEL, true>(a)
+                                : launch_grad_t<D, VEC, PEEL, false>(a);
+}
+
+template <DType D>
 hipError_t launch_grad_d(const GradArgs& a) {
-    return a.targets != nullptr ? launch_grad_t<D, VEC, true>(a) : launch_grad_t<D, VEC, false>(a);
+    if (!a.vector_units) return launch_grad_p<D, false, false>(a);
+    return a.peel ? launch_grad_p<D, true, true>(a) : launch_grad_p<D, true, false>(a);
 }
 
 }  // namespace
 
 hipError_t launch_grad(const GradArgs& a) {
     if (a.grid <= 0) return hipSuccess;
-    if (a.bf16) return a.vector_units ? launch_grad_d<DType::BF16, true>(a)
-                                      : launch_grad_d<DType::BF16, false>(a);
-    return a.vector_units ? launch_grad_d<DType::F32, true>(a) : launch_grad_d<DType::F32, false>(a);
+    return a.bf16 ? launch_grad_d<DType::BF16>(a) : launch_grad_d<DType::F32>(a);
 }
 
 }  // namespace lse

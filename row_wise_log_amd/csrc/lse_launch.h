@@ -46,7 +46,8 @@ hipError_t launch(const LaunchArgs& a);
 // The backward pass, grad_x = grad_out * exp(x - lse) (lse_backward.hip).
 struct GradArgs {
     bool bf16;
-    bool vector_units;     // 16-byte units (every row of x and grad_x 16-byte aligned)
+    bool vector_units;     // 16-byte units (rows 16-byte aligned, or peel below)
+    bool peel;             // each row's units start at its first 16-byte boundary
     int64_t grid;
     int64_t rows_per_wg;   // 1: a workgroup takes one chunk of one row
     int64_t chunks_per_row;
