@@ -202,6 +202,20 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
 WARMUP_SECONDS = 0.05
 
 
+def event_mean_us(torch, step, first: int, count: int, stream) -> float:
+    """Mean microseconds per launch of `count` back-to-back steps (indices
+    first .. first + count - 1), one HIP event pair on `stream` around them."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(first, first + count):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / count
+
+
 def run_warmup(torch, step, warmup: int | None, stream) -> int:
     """Run the untimed warmup steps and return how many ran. warmup=None
     (the default) runs at least 40 steps and at least WARMUP_SECONDS of
@@ -217,15 +231,7 @@ def run_warmup(torch, step, warmup: int | None, stream) -> int:
     # the next 20, timed, give the step time that sizes the rest.
     for i in range(20):
         step(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(20, 40):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    per_step = max(e0.elapsed_time(e1) * 1e-3 / 20, 1e-6)
+    per_step = max(event_mean_us(torch, step, 20, 20, stream) * 1e-6, 1e-6)
     extra = int(np.ceil(WARMUP_SECONDS / per_step))
     for i in range(40, 40 + extra):
         step(i)
@@ -294,15 +300,7 @@ def time_read_control(torch, bufs, nbytes: int, plan: dict, steps: int, warmup: 
 
     for i in range(warmup):
         step(i)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(steps):
-        step(warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+    us = event_mean_us(torch, step, warmup, steps, stream)
     return {"kernel": "read_chunks (XOR of each chunk's words)", "grid": grid, "block": block,
             "launch_us_mean": round(us, 2), "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
@@ -323,15 +321,7 @@ def time_copy_control(torch, bufs, nbytes: int, steps: int, warmup: int, stream)
 
     for i in range(warmup):
         step(i)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(steps):
-        step(warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+    us = event_mean_us(torch, step, warmup, steps, stream)
     del dst
     return {"kernel": "copy_chunks (x copied to a buffer of grad_x's size)", "grid": grid, "block": block,
             "launch_us_mean": round(us, 2), "GBs_read_plus_written": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
@@ -368,20 +358,12 @@ def launch_floor_us(torch, B, handle, calls: int = 1000) -> float:
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    def call():
+    def call(i):
         B.lse_forward(handle, x.data_ptr(), B.LSE_DTYPE_F32, 1, 1, 1, out.data_ptr(), sh)
 
-    for _ in range(50):
-        call()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(calls):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / calls
+    for i in range(50):
+        call(i)
+    return event_mean_us(torch, call, 50, calls, stream)
 
 
 def warm_us_per_call(torch, B, handle, cfg: int, calls: int = 1000) -> float:
@@ -395,20 +377,12 @@ def warm_us_per_call(torch, B, handle, cfg: int, calls: int = 1000) -> float:
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    def call():
+    def call(i):
         B.lse_forward(handle, x.data_ptr(), code, w.rows, w.cols, w.cols, out.data_ptr(), sh)
 
-    for _ in range(50):
-        call()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(calls):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / calls
+    for i in range(50):
+        call(i)
+    return event_mean_us(torch, call, 50, calls, stream)
 
 
 def cpu_model() -> str:
