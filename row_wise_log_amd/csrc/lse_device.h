@@ -75,8 +75,15 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
-// c(m): the base-2 reference of a running maximum; finite for every m.
+// c(m): the base-2 reference of a running maximum; finite for every m. It
+// must be the rounded product fl(m * log2 e) wherever it is used: merges
+// rely on two references of the same m being equal, so that 2^(c1 - C) is
+// exactly 1, and the finish recovers the rounding by an fma. A product the
+// compiler fused into a following subtraction (fp-contract) would leave the
+// rounding residual, up to half an ulp of c, in the exponent instead; the
+// pragma keeps this multiply a multiply.
 __device__ __forceinline__ float base2_ref(float m) {
+#pragma clang fp contract(off)
     return __builtin_amdgcn_fmed3f(m, -kClamp, kClamp) * kLog2e;
 }
 
@@ -269,12 +276,22 @@ __device__ __forceinline__ bool needs_natural_units(float m, float s) {
 // The finished value ln(sum exp) = m + ln2 * (log2 s - (m*log2e - c)) of a
 // reduced (m, c, s) with |m| <= 2^30 or m = +-inf: NaN if s is NaN, +inf if
 // m = +inf, -inf if m = -inf (s = 0: no element above -inf).
+//
+// The lazy reference can trail the maximum by up to 32*ln2, so s can reach
+// 2^38 and log2 s 38, where one ulp of fp32 is 4e-6: taken whole, log2 s
+// would put that much absolute error on a result near zero. So s is split
+// exactly as mant * 2^k (mant in [0.5, 1)): m + k*ln2 is one fused
+// multiply-add, and the hardware log2 sees only mant, whose log2 lies in
+// [-1, 0). The error is then a few ulps of max(|result|, 1).
 __device__ __forceinline__ float finish(float m, float c, float s) {
     if (is_nan(s)) return __builtin_nanf("");
     if (m == kInf) return kInf;
     if (m == -kInf) return -kInf;
     const float e = __builtin_fmaf(m, kLog2e, -c);  // exact residual of c = fl(m*log2e)
-    return __builtin_fmaf(log2_hw(s) - e, kLn2, m);
+    const int k = __builtin_amdgcn_frexp_expf(s);
+    const float mant = __builtin_amdgcn_frexp_mantf(s);
+    const float hi = __builtin_fmaf(static_cast<float>(k), kLn2, m);
+    return __builtin_fmaf(log2_hw(mant) - e, kLn2, hi);
 }
 
 // ---- cross-lane reductions (wave64) ---------------------------------------

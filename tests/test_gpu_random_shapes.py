@@ -8,21 +8,29 @@ lse_token_logprob (targets in and out of range) are compared with the
 float64 oracle. A second sweep does the same for lse_forward_dim over random
 [outer, n, inner] with forced or planned splits. The seeds are fixed, so every
 run checks the same cases; each case is printed before it runs. A third
-sweep runs lse_backward on random shapes with padded and misaligned x and
-gradient rows.
+sweep runs lse_backward and lse_token_logprob_backward on random shapes with
+padded and misaligned x and gradient rows (rows misaligned alike in x and
+grad_x take the peeled 16-byte path, the others the element path).
+
+LSE_SWEEP_SEED=k (default 0) shifts every seed by 1000 k, for a wider sweep
+run by hand; the default cases are the ones the suite always runs.
 """
+import os
+
 import numpy as np
 import pytest
 
 import oracle as oracle_mod
 import workloads
-from gpu_util import (DTYPE_CODE, SCHEDULES, compare, compare_grad, compare_logp, gpu_backward,
-                      gpu_lse, gpu_token_logprob, note)
+from gpu_util import (DTYPE_CODE, SCHEDULES, compare, compare_grad, compare_logp,
+                      compare_token_grad, gpu_backward, gpu_lse, gpu_token_backward,
+                      gpu_token_logprob, note)
 from row_wise_log_amd import binding as B
 
 pytestmark = pytest.mark.gpu
 
 MAX_ELEMS = 3_000_000  # keeps each case's oracle call short
+SEED = 1000 * int(os.environ.get("LSE_SWEEP_SEED", "0"))
 
 
 @pytest.fixture(scope="module")
@@ -80,7 +88,7 @@ def row_cases(seed, n):
 
 @pytest.mark.parametrize("block", range(8))
 def test_random_rows(torch_gpu, handle, oracle, block):
-    for i, dtype, rows, cols, pad, front, sched, tuning, scale, rng in row_cases(100 + block, 50):
+    for i, dtype, rows, cols, pad, front, sched, tuning, scale, rng in row_cases(SEED + 100 + block, 50):
         full = make_rows(rng, rows, cols + pad, dtype, scale)
         x = full[:, :cols]
         what = (f"block {block} case {i}: {dtype} rows={rows} cols={cols} pad={pad} front={front} "
@@ -117,7 +125,7 @@ def gpu_dim(torch, handle, x3, dtype, front, parts):
 
 @pytest.mark.parametrize("block", range(6))
 def test_random_dims(torch_gpu, handle, block):
-    rng = np.random.default_rng(200 + block)
+    rng = np.random.default_rng(SEED + 200 + block)
     for i in range(30):
         dtype = ["f32", "bf16"][rng.integers(2)]
         outer, n, inner = log_int(rng, 1, 64), log_int(rng, 1, 60_000), log_int(rng, 1, 5000)
@@ -138,7 +146,7 @@ def test_random_dims(torch_gpu, handle, block):
 
 @pytest.mark.parametrize("block", range(4))
 def test_random_backward(torch_gpu, handle, oracle, block):
-    rng = np.random.default_rng(300 + block)
+    rng = np.random.default_rng(SEED + 300 + block)
     for i in range(30):
         dtype = ["f32", "bf16"][rng.integers(2)]
         cols = log_int(rng, 1, 300_000)
@@ -164,3 +172,37 @@ def test_random_backward(torch_gpu, handle, oracle, block):
         with np.errstate(invalid="ignore"):
             d = vals - lse32.astype(np.float64)[:, None]
         compare_grad(got, ref, d, g, dtype, what)
+
+
+@pytest.mark.parametrize("block", range(3))
+def test_random_token_backward(torch_gpu, handle, oracle, block):
+    """The token log-probability's backward on random shapes and layouts, with
+    targets drawn in range and just outside it (rows of NaN)."""
+    rng = np.random.default_rng(SEED + 400 + block)
+    for i in range(25):
+        dtype = ["f32", "bf16"][rng.integers(2)]
+        cols = log_int(rng, 1, 300_000)
+        rows = log_int(rng, 1, 3000)
+        while rows > 1 and rows * cols > MAX_ELEMS // 2:
+            rows //= 2
+        pad = int(rng.choice([0, 0, 1, 8]))
+        front, gpad, gfront = (int(rng.choice([0, 0, 1])), int(rng.choice([0, 0, 3, 8])),
+                               int(rng.choice([0, 0, 2])))
+        full = make_rows(rng, rows, cols + pad, dtype, float(rng.choice([0.5, 3.0, 30.0])))
+        x = full[:, :cols]
+        xc = np.ascontiguousarray(x)
+        lse32 = oracle.lse(xc, dtype, threads=8).astype(np.float32)
+        g = rng.normal(0, 2, size=rows).astype(np.float32)
+        targets = rng.integers(-1, cols + 1, size=rows)
+        what = (f"token backward block {block} case {i}: {dtype} rows={rows} cols={cols} "
+                f"pad={pad} front={front} grad_pad={gpad} grad_front={gfront}")
+        note(what)
+        got, untouched = gpu_token_backward(torch_gpu, handle, x, targets, lse32, g, dtype,
+                                            pad_front=front, grad_pad=gpad, grad_front=gfront)
+        assert untouched, what + ": bytes outside grad_x's rows were written"
+        ref = oracle.token_logprob_grad(xc, targets, lse32, g, dtype, threads=8)
+        soft = oracle.softmax_grad(xc, lse32, g, dtype, threads=8)
+        vals = (workloads.bf16_bits_to_f32(xc) if dtype == "bf16" else xc).astype(np.float64)
+        with np.errstate(invalid="ignore"):
+            d = vals - lse32.astype(np.float64)[:, None]
+        compare_token_grad(got, ref, soft, d, g, targets, dtype, what)

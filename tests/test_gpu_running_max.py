@@ -113,3 +113,53 @@ def test_threshold_jumps_exactly(torch_gpu, handle, oracle):
             note(f"threshold jumps dtype={dtype} schedule={sched}")
             compare(gpu_lse(torch_gpu, handle, x, dtype, sched), ref, dtype,
                     f"threshold jumps {dtype} {sched}")
+
+
+def trailing_reference_rows(cols: int, seed: int) -> np.ndarray:
+    """Rows whose LSE lies near zero while a lane's reference trails the
+    maximum by up to 32*ln2 (22.18): the first elements a lane folds sit d
+    below a later maximum near 0.3, for d up to just under the refresh
+    threshold, so the lane's sum grows to about 2^(d*log2 e)."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for d in (8.0, 12.0, 16.68, 20.0, 21.5, 22.1):
+        r = np.full(cols, -np.float32(d) + 0.3, dtype=np.float64)
+        r[cols // 2 + 1] = 0.3                             # one maximum, mid-row
+        rows.append(r)
+        r = -d + 0.3 + 0.01 * rng.normal(size=cols)
+        r[-2] = 0.3                                        # near the end
+        rows.append(r)
+        r = np.full(cols, -np.inf)
+        r[0] = -d + 0.3                                    # the first element far below
+        r[1:5] = [0.47797355, -20.94657898, -26.51913834, -48.59749603][: min(4, cols - 1)]
+        rows.append(r)
+    return np.asarray(rows, dtype=np.float32)
+
+
+@pytest.mark.parametrize("cols", [5, 40, 4097, 70_001])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_reference_far_below_the_maximum(torch_gpu, handle, oracle, dtype, cols):
+    """The finish takes log2 of a sum of up to 2^38 without losing absolute
+    accuracy (it splits off the sum's binary exponent first), and no result
+    falls below the row's maximum by more than that bound. The remaining error on these rows
+    (results near 0.3-0.5) is the fp32 rounding of the largest term's
+    exponent x*log2 e - c, which is below 32 while the reference trails:
+    half an ulp, 2^-20, is 6.6e-7 in the result; with the exponential's and
+    the logarithm's own rounding the bound is 1e-6, half the fp32 bar. (Taking
+    log2 of the whole sum left 2.1e-6 on such a row.) Rows start 0-3 elements
+    past a 16-byte boundary, so the first elements are also folded singly (a
+    misaligned head) before the vectors."""
+    v = trailing_reference_rows(cols, seed=cols)
+    x = workloads.f32_to_bf16_bits(v) if dtype == "bf16" else v
+    ref = oracle.lse(x, dtype)
+    xv = workloads.bf16_bits_to_f32(x) if dtype == "bf16" else x
+    mx = xv.astype(np.float64).max(axis=1)
+    for sched, tuning in [("row_per_wg", (0, 0, 0, 0, 0)), ("row_per_wg", (128, 0, 0, 0, 0)),
+                          ("split_row", (0, 0, 0, 0, 0)), ("auto", (0, 0, 0, 0, 0))]:
+        for front in (0, 1, 3):
+            what = f"trailing reference {dtype} cols={cols} {sched} {tuning} front={front}"
+            note(what)
+            got = gpu_lse(torch_gpu, handle, x, dtype, sched, pad_front=front, tuning=tuning)
+            err = np.abs(got.astype(np.float64) - ref)
+            assert np.all(err <= 1e-6 * np.maximum(1.0, np.abs(ref))), (what, float(err.max()))
+            assert np.all(got.astype(np.float64) >= mx - 1e-6 * np.maximum(1.0, np.abs(mx))), what
