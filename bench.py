@@ -85,8 +85,8 @@ def plan_name(plan: dict) -> str:
 
 
 def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int | None,
-                op: str = "lse", graph: bool = False):
-    w = workloads.make(cfg)
+                op: str = "lse", graph: bool = False, w=None):
+    w = w if w is not None else workloads.make(cfg)
     rows, cols = w.rows, w.cols
     esize = 2 if w.dtype == "bf16" else 4
     in_bytes = rows * cols * esize
@@ -459,9 +459,12 @@ def cpu_baseline_backward(w, r, seconds: float = 10.0) -> dict:
                        + ")")}
 
 
-def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0, op: str = "lse") -> dict:
-    """The float64 oracle on the host cores over the same input; its first
-    pass also checks the GPU output of the timed steps."""
+def cpu_baseline(w, seconds: float = 10.0, op: str = "lse") -> tuple:
+    """The float64 oracle on the host cores over the same input. Returns the
+    baseline record and the reference (the first pass's result, with the
+    LSE that scales the log-probabilities' bar) that check_gpu_output later
+    holds the GPU's output of the timed steps against. bench.py runs it
+    before the GPU is timed: the host works while the GPU is idle."""
     import oracle
     threads = len(os.sched_getaffinity(0))
     orc = oracle.default()
@@ -483,15 +486,7 @@ def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0, op: str = "lse")
         el = time.perf_counter() - t0
         if el >= seconds or passes >= 1000:
             break
-    tol = 1e-5 if w.dtype == "bf16" else 2e-6
-    fin = np.isfinite(ref)
-    exact = np.array_equal(gpu_out[~fin], ref[~fin].astype(np.float32), equal_nan=True)
-    scale = np.maximum(1.0, np.abs(ref[fin]))
-    if tg is not None:  # logp carries the LSE's error: scale by the LSE too
-        lse = orc.lse(w.x, w.dtype, threads=threads)
-        scale = np.maximum(scale, np.abs(lse[fin]))
-    err = np.abs(gpu_out[fin] - ref[fin]) / (tol * scale)
-    log(f"GPU output vs oracle: max |err|/tol = {err.max(initial=0):.3f}, non-finite match {exact}")
+    lse = orc.lse(w.x, w.dtype, threads=threads) if tg is not None else None
     # one thread, over a bounded prefix of the rows (the pages time their CPU
     # LSE single-threaded)
     one = {}
@@ -508,13 +503,29 @@ def cpu_baseline(w, gpu_out: np.ndarray, seconds: float = 10.0, op: str = "lse")
                 break
         one = {"value_1thread": round(x1.nbytes * p1 / e1 / 1e9, 3),
                "sample_1thread": f"the first {n1} rows ({x1.nbytes} bytes), {p1} passes in {e1:.1f} s"}
-    return {"value": round(nbytes * passes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "cpu_model": cpu_model(), **one,
-            "sample": (f"the whole {w.rows}x{w.cols} {w.dtype} input, {passes} passes in "
-                       f"{el:.1f} s wall on {threads} threads (float64 two-pass max-subtract, "
-                       "libm exp/log" + (", minus the target element" if tg is not None else "")
-                       + (", over the first axis of a transposed copy" if op == "dim" else "")
-                       + ")")}
+    rec = {"value": round(nbytes * passes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+           "kind": "oracle", "cpu_model": cpu_model(), **one,
+           "sample": (f"the whole {w.rows}x{w.cols} {w.dtype} input, {passes} passes in "
+                      f"{el:.1f} s wall on {threads} threads (float64 two-pass max-subtract, "
+                      "libm exp/log" + (", minus the target element" if tg is not None else "")
+                      + (", over the first axis of a transposed copy" if op == "dim" else "")
+                      + ")")}
+    return rec, (ref, lse)
+
+
+def check_gpu_output(w, gpu_out: np.ndarray, reference: tuple) -> None:
+    """Hold the GPU output of the timed steps against the oracle's first pass
+    (the parity bar: 2e-6 fp32, 1e-5 bf16, times max(1, |value|), and for
+    log-probabilities also |LSE|; non-finite values exactly)."""
+    ref, lse = reference
+    tol = 1e-5 if w.dtype == "bf16" else 2e-6
+    fin = np.isfinite(ref)
+    exact = np.array_equal(gpu_out[~fin], ref[~fin].astype(np.float32), equal_nan=True)
+    scale = np.maximum(1.0, np.abs(ref[fin]))
+    if lse is not None:  # logp carries the LSE's error: scale by the LSE too
+        scale = np.maximum(scale, np.abs(lse[fin]))
+    err = np.abs(gpu_out[fin] - ref[fin]) / (tol * scale)
+    log(f"GPU output vs oracle: max |err|/tol = {err.max(initial=0):.3f}, non-finite match {exact}")
 
 
 def main() -> int:
@@ -575,8 +586,17 @@ def main() -> int:
     try:
         log(f"timing config {args.config} ({args.op}): {args.steps} steps after "
             f"{'at least 50 ms of' if args.warmup is None else args.warmup} warmup")
+        # The forward ops' CPU baseline runs first, while the GPU is idle; its
+        # reference checks the timed steps' output afterwards. (The backward
+        # baselines need the timed run's inputs and run after it.)
+        w0, reference = None, None
+        early = not args.no_cpu_baseline and args.op in ("lse", "logprob", "dim")
+        if early:
+            w0 = workloads.make(args.config)
+            log("timing the float64 oracle on the host cores")
+            cpu_rec, reference = cpu_baseline(w0, args.cpu_seconds, args.op)
         r = time_config(torch, B, handle, args.config, args.steps, args.warmup, args.rotate,
-                        args.op, args.graph)
+                        args.op, args.graph, w=w0)
         w = r["w"]
         traffic = recorded_traffic(args.config) if args.op == "lse" else None
         floor = launch_floor_us(torch, B, handle)
@@ -658,13 +678,12 @@ def main() -> int:
                     f.write(json.dumps(rec) + "\n")
                     if cfg != args.config:
                         del rc
-        if not args.no_cpu_baseline:
+        if early:
+            check_gpu_output(w, r["out"].cpu().numpy().astype(np.float64), reference)
+            line["cpu_baseline"] = cpu_rec
+        elif not args.no_cpu_baseline:
             log("timing the float64 oracle on the host cores")
-            gpu_out = r["out"].cpu().numpy().astype(np.float64)
-            if args.op in ("backward", "logprob_backward"):
-                line["cpu_baseline"] = cpu_baseline_backward(w, r, args.cpu_seconds)
-            else:
-                line["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds, args.op)
+            line["cpu_baseline"] = cpu_baseline_backward(w, r, args.cpu_seconds)
         else:
             line["cpu_baseline"] = None
         print(json.dumps(line), flush=True)
