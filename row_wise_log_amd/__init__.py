@@ -58,18 +58,25 @@ def logsumexp_dim(x, dim, keepdim: bool = False, handle_=None):
 
     from .binding import LSE_DTYPE_BF16, LSE_DTYPE_F32, lse_forward_dim
 
+    if x.dim() == 0:
+        raise ValueError("x must have at least one axis")
+    nd = x.dim()
+    raw = list(dim) if isinstance(dim, (tuple, list)) else [dim]
+    if not raw:
+        raise ValueError("dim must name at least one axis")
+    for d in raw:
+        if not -nd <= d < nd:
+            raise IndexError(f"dim {d} is out of range for a {nd}-D tensor")
+    dims = sorted(d % nd for d in raw)
+    if len(set(dims)) != len(dims):
+        raise ValueError(f"dim {tuple(raw)} names an axis more than once")
+    if dims != list(range(dims[0], dims[-1] + 1)):
+        raise NotImplementedError("the reduced axes must be adjacent")
     codes = {torch.float32: LSE_DTYPE_F32, torch.bfloat16: LSE_DTYPE_BF16}
     if x.dtype not in codes:
         raise TypeError(f"unsupported dtype {x.dtype}: fp32 or bf16")
     if not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous GPU tensor")
-    if x.dim() == 0:
-        raise ValueError("x must have at least one axis")
-    dims = sorted({d % x.dim() for d in (dim if isinstance(dim, (tuple, list)) else (dim,))})
-    if not dims:
-        raise ValueError("dim must name at least one axis")
-    if dims != list(range(dims[0], dims[-1] + 1)):
-        raise NotImplementedError("the reduced axes must be adjacent")
     d0, d1 = dims[0], dims[-1]
     shape = list(x.shape)
     outer = 1

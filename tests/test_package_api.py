@@ -60,3 +60,18 @@ def test_bench_refuses_more_than_one_gpu():
     assert proc.returncode == 2
     msg = json.loads(proc.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_logsumexp_dim_checks_its_axes():
+    """Axes are checked as torch.logsumexp checks them, before anything
+    touches a device: out of range, repeated, or not adjacent."""
+    torch = pytest.importorskip("torch")
+    import row_wise_log_amd as R
+    x = torch.zeros(2, 3, 4)
+    for bad, err in ((3, IndexError), (-4, IndexError), ((0, 5), IndexError),
+                     ((1, 1), ValueError), ((0, -3), ValueError), ((), ValueError),
+                     ((0, 2), NotImplementedError)):
+        with pytest.raises(err):
+            R.logsumexp_dim(x, bad)
+    with pytest.raises(ValueError):        # valid axes, but a CPU tensor
+        R.logsumexp_dim(x, (1, 2))
