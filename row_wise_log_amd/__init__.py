@@ -19,16 +19,26 @@ from .binding import (LseError, lse_create, lse_destroy, lse_forward, lse_plan, 
                       lse_set_schedule, lse_set_tuning, lse_status_string, lse_token_logprob,
                       load)
 
-_handles: dict[int, int] = {}
+_handles: dict[tuple[int, int], int] = {}
 
 
-def handle(device: int) -> int:
-    """A library handle for `device`, created once per process."""
-    h = _handles.get(device)
+def handle(device: int, stream: int = 0) -> int:
+    """A library handle for `device` and the stream handle `stream`, created
+    once per process. A handle's workspace (split rows, split non-last-axis
+    tiles) must not serve two streams at once, so each stream gets its own;
+    calls on one stream are ordered, so they can share one."""
+    key = (device, int(stream))
+    h = _handles.get(key)
     if h is None:
         h = lse_create(device)
-        _handles[device] = h
+        _handles[key] = h
     return h
+
+
+def _device_stream(x) -> tuple[int, int]:
+    import torch
+
+    return x.device.index or 0, torch.cuda.current_stream(x.device).cuda_stream
 
 
 def _check_input(x):
@@ -90,8 +100,8 @@ def logsumexp_dim(x, dim, keepdim: bool = False, handle_=None):
         inner *= s_
     kept = shape[:d0] + ([1] * (d1 - d0 + 1) if keepdim else []) + shape[d1 + 1:]
     out = torch.empty(kept, dtype=torch.float32, device=x.device)
-    h = handle_ if handle_ is not None else handle(x.device.index or 0)
-    stream = torch.cuda.current_stream(x.device).cuda_stream
+    dev, stream = _device_stream(x)
+    h = handle_ if handle_ is not None else handle(dev, stream)
     lse_forward_dim(h, x.data_ptr(), codes[x.dtype], outer, n, inner, out.data_ptr(), stream)
     return out
 
@@ -105,8 +115,8 @@ def logsumexp(x, out=None, handle_=None):
         out = torch.empty(rows, dtype=torch.float32, device=x.device)
     elif out.dtype != torch.float32 or out.shape != (rows,) or not out.is_contiguous():
         raise ValueError("out must be a contiguous fp32 tensor of shape (rows,)")
-    h = handle_ if handle_ is not None else handle(x.device.index or 0)
-    stream = torch.cuda.current_stream(x.device).cuda_stream
+    dev, stream = _device_stream(x)
+    h = handle_ if handle_ is not None else handle(dev, stream)
     lse_forward(h, x.data_ptr(), code, rows, cols, stride, out.data_ptr(), stream)
     return out
 
@@ -124,8 +134,8 @@ def token_logprob(x, targets, return_lse=False, handle_=None):
         raise ValueError("targets must be on the same device as x")
     logp = torch.empty(rows, dtype=torch.float32, device=x.device)
     lse = torch.empty(rows, dtype=torch.float32, device=x.device) if return_lse else None
-    h = handle_ if handle_ is not None else handle(x.device.index or 0)
-    stream = torch.cuda.current_stream(x.device).cuda_stream
+    dev, stream = _device_stream(x)
+    h = handle_ if handle_ is not None else handle(dev, stream)
     lse_token_logprob(h, x.data_ptr(), code, rows, cols, stride, targets.data_ptr(),
                       logp.data_ptr(), lse.data_ptr() if lse is not None else None, stream)
     return (logp, lse) if return_lse else logp
@@ -151,8 +161,8 @@ def _autograd_function():
             code, rows, cols, stride = _check_input(x)
             g = grad_out.to(torch.float32).contiguous()
             grad = torch.empty((rows, cols), dtype=x.dtype, device=x.device)
-            h = handle(x.device.index or 0)
-            stream = torch.cuda.current_stream(x.device).cuda_stream
+            dev, stream = _device_stream(x)
+            h = handle(dev, stream)
             lse_backward(h, x.data_ptr(), code, rows, cols, stride, out.data_ptr(), g.data_ptr(),
                          grad.data_ptr(), cols, stream)
             return grad
@@ -191,8 +201,8 @@ def _token_autograd_function():
                                  "on x's device")
             logp = torch.empty(rows, dtype=torch.float32, device=x.device)
             lse = torch.empty(rows, dtype=torch.float32, device=x.device)
-            h = handle(x.device.index or 0)
-            stream = torch.cuda.current_stream(x.device).cuda_stream
+            dev, stream = _device_stream(x)
+            h = handle(dev, stream)
             lse_token_logprob(h, x.data_ptr(), code, rows, cols, stride, targets.data_ptr(),
                               logp.data_ptr(), lse.data_ptr(), stream)
             ctx.save_for_backward(x, targets, lse)
@@ -204,8 +214,8 @@ def _token_autograd_function():
             code, rows, cols, stride = _check_input(x)
             g = grad_logp.to(torch.float32).contiguous()
             grad = torch.empty((rows, cols), dtype=x.dtype, device=x.device)
-            h = handle(x.device.index or 0)
-            stream = torch.cuda.current_stream(x.device).cuda_stream
+            dev, stream = _device_stream(x)
+            h = handle(dev, stream)
             lse_token_logprob_backward(h, x.data_ptr(), code, rows, cols, stride,
                                        targets.data_ptr(), lse.data_ptr(), g.data_ptr(),
                                        grad.data_ptr(), cols, stream)

@@ -9,7 +9,9 @@ and a split LSE over a non-last axis); it is replayed several times with new
 inputs written by eager work in between, and every replay is compared bit for
 bit with the same calls made eagerly. A second test runs split-row and split
 non-last-axis calls on two handles on two streams at once (one handle per
-stream, as the header asks) and compares every result with a serial run.
+stream, as the header asks) and compares every result with a serial run; a
+third does the same through the torch-level functions, which keep one handle
+per (device, stream).
 """
 import numpy as np
 import pytest
@@ -158,3 +160,35 @@ def test_two_handles_on_two_streams(torch_gpu):
         torch.cuda.synchronize()
         B.lse_destroy(ha)
         B.lse_destroy(hb)
+
+
+def test_package_calls_on_two_streams(torch_gpu):
+    """The torch-level functions keep one library handle per (device,
+    stream), so calls issued on two streams at once never share a split
+    workspace: split-row and split non-last-axis shapes, alternated between
+    two streams with no synchronisation between them, give exactly the
+    results of the same calls made one at a time."""
+    import row_wise_log_amd as R
+    torch = torch_gpu
+    rng = np.random.default_rng(21)
+    xs = [torch.from_numpy(rng.normal(0, 3, size=(8, 300_000)).astype(np.float32)).cuda()
+          for _ in range(4)]                            # few long rows: the split-row schedule
+    ds = [torch.from_numpy(rng.normal(0, 3, size=(20_000, 64)).astype(np.float32)).cuda()
+          for _ in range(4)]                            # a tall [n, inner]: split over n
+    torch.cuda.synchronize()
+    want = [R.logsumexp(x) for x in xs] + [R.logsumexp_dim(d, 0) for d in ds]
+    torch.cuda.synchronize()
+    want = [_bits(torch, w) for w in want]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        note(f"package calls on two streams, repeat {rep}")
+        got = []
+        for i in range(4):
+            with torch.cuda.stream(s1 if i % 2 == 0 else s2):
+                got.append(R.logsumexp(xs[i]))
+        for i in range(4):
+            with torch.cuda.stream(s2 if i % 2 == 0 else s1):
+                got.append(R.logsumexp_dim(ds[i], 0))
+        torch.cuda.synchronize()
+        for k, (g, w) in enumerate(zip(got, want)):
+            assert np.array_equal(_bits(torch, g), w), (rep, k)
