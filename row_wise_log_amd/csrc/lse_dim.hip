@@ -163,8 +163,10 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
             const int64_t qcv = (tile0 + tlm) * gw + c;
             const bool live = q < ent && qcv < ncv;
             // This lane's parts in batches of 8 loads issued together; each
-            // batch raises the running maximum and rescales the sum once.
-            float pm = -kInf, ps = 0.0f;
+            // batch raises the running maximum and rescales the sum (and its
+            // compensation) once.
+            float pm = -kInf;
+            CSum cps;
             if (live) {
                 const unsigned long long* e0 = wp + tlm * ent + q;
                 for (int p0 = l; p0 < parts; p0 += 8 * L) {
@@ -183,23 +185,24 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
 #pragma unroll
                     for (int i = 0; i < 8; ++i) m2 = max3f(m2, bm[i], m2);
                     const float c2 = base2_ref(m2);
-                    ps *= exp2_hw(base2_ref(pm) - c2);
+                    const float r = exp2_hw(base2_ref(pm) - c2);
+                    cps.s *= r;
+                    cps.e *= r;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        ps = __builtin_fmaf(bs[i], exp2_hw(base2_ref(bm[i]) - c2), ps);
+                    for (int i = 0; i < 8; ++i) cps.add(bs[i] * exp2_hw(base2_ref(bm[i]) - c2));
                     pm = m2;
                 }
             }
             lds_m[t] = pm;
-            lds_s[t] = ps;
+            lds_s[t] = cps.total();
             __syncthreads();
             const int g0 = t - l;  // the entry's first lane
             float m = -kInf;
             for (int i = 0; i < L; ++i) m = max3f(m, lds_m[g0 + i], m);
             const float cm = base2_ref(m);
-            float sum = 0.0f;
-            for (int i = 0; i < L; ++i)
-                sum = __builtin_fmaf(lds_s[g0 + i], exp2_hw(base2_ref(lds_m[g0 + i]) - cm), sum);
+            CSum cs;
+            for (int i = 0; i < L; ++i) cs.add(lds_s[g0 + i] * exp2_hw(base2_ref(lds_m[g0 + i]) - cm));
+            const float sum = cs.total();
             const bool slow = live && needs_natural_units(m, sum);
             const int64_t qo = live ? qcv / cvs : 0;
             const int64_t qi = qcv - qo * cvs;
@@ -241,11 +244,12 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
         float m = -kInf;
         for (int r = 0; r < rw; ++r) m = max3f(m, lds_m[(r * gw + c) * K + k], m);
         const float cm = base2_ref(m);
-        float s = 0.0f;
+        CSum cs;
         for (int r = 0; r < rw; ++r) {
             const int i = (r * gw + c) * K + k;
-            s = __builtin_fmaf(lds_s[i], exp2_hw(base2_ref(lds_m[i]) - cm), s);
+            cs.add(lds_s[i] * exp2_hw(base2_ref(lds_m[i]) - cm));
         }
+        const float s = cs.total();
         const int64_t qcv = (tile0 + tl) * gw + c;
         if (qcv >= ncv) continue;
         if constexpr (SPLIT) {

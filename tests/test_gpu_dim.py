@@ -167,3 +167,32 @@ def test_package_keepdim_and_adjacent_axes(torch_gpu):
     assert abs(float(R.logsumexp_dim(one, 0)) - float(torch.logsumexp(one.double().cpu(), 0))) < 2e-5
     with pytest.raises(NotImplementedError):
         R.logsumexp_dim(xt, (0, 2))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_trailing_reference_columns(torch_gpu, handle, dtype):
+    """Columns whose elements lie up to 22 below one maximum near 0.3. Where
+    a lane's reference trails the maximum (long columns) its sum reaches
+    2^31, which the shared finish handles; where every lane holds one
+    element (n = 64 over 3 columns), the merge adds one partial near 1 and
+    63 of 5.7e-8, each under half an ulp of the total, which only a
+    compensated sum keeps (a plain one lost 1.7e-6). The result stays within
+    1e-6 of the oracle, split and unsplit, vector and single-column paths."""
+    rng = np.random.default_rng(5)
+    for n, inner in ((4096, 64), (300, 40), (64, 3)):
+        cols = []
+        for d in (8.0, 16.68, 21.5, 22.1):
+            c = np.full(n, 0.3 - d) + 0.01 * rng.normal(size=n)
+            c[n // 2 + 1] = 0.3
+            cols.append(c)
+        v = np.tile(np.asarray(cols).T, (1, -(-inner // len(cols))))[:, :inner]
+        v = v.astype(np.float32).reshape(1, n, inner)
+        x3 = workloads.f32_to_bf16_bits(v) if dtype == "bf16" else v
+        ref = oracle_mod.lse_dim(x3, dtype)
+        for parts in (0, 1, 3):
+            for front in (0, 1):
+                note(f"trailing reference columns {dtype} n={n} inner={inner} parts={parts} front={front}")
+                got = gpu_dim(torch_gpu, handle, x3, dtype, front=front, parts=parts)
+                err = np.abs(got.astype(np.float64) - ref)
+                assert np.all(err <= 1e-6 * np.maximum(1.0, np.abs(ref))), (n, inner, parts, front,
+                                                                            float(err.max()))
