@@ -3,7 +3,8 @@
 Each case draws a dtype, a row count, a row length (spread over magnitudes,
 1 to 400000, sometimes 0), a row padding, a misaligned start, a forced or
 automatic schedule and sometimes a block / unroll / parts tuning within the
-documented sets, plus rows of special values; lse_forward and
+documented sets, plus rows of special values and dominated rows (one
+maximum over many terms near half an fp32 ulp of the total); lse_forward and
 lse_token_logprob (targets in and out of range) are compared with the
 float64 oracle. A second sweep does the same for lse_forward_dim over random
 [outer, n, inner] with forced or planned splits. The seeds are fixed, so every
@@ -55,8 +56,21 @@ def log_int(rng, lo, hi):
     return int(min(hi, max(lo, v)))
 
 
+def dominated(rng, n):
+    """n values with one maximum and the rest d = 14 to 22.5 below it, each
+    term e^-d near or under half an fp32 ulp of the total: sums that drop
+    small terms, and lazy references far below the maximum, show here."""
+    base, d = rng.normal(0.0, 1.0), rng.uniform(14.0, 22.5)
+    v = base - d + 0.01 * rng.normal(size=n)
+    v[rng.integers(n)] = base
+    return v
+
+
 def make_rows(rng, rows, width, dtype, scale):
     v = rng.normal(0.0, scale, size=(rows, width)).astype(np.float32)
+    if rows >= 1 and width > 0 and rng.random() < 0.5:
+        for r in rng.integers(rows, size=min(rows, 3)):
+            v[r] = dominated(rng, width)                   # one maximum over many tiny terms
     if rows >= 4 and width > 0 and rng.random() < 0.5:
         r = rng.integers(rows, size=4)
         v[r[0]] = -np.inf                                  # a row of -inf
@@ -138,6 +152,10 @@ def test_random_dims(torch_gpu, handle, block):
         parts = int(rng.choice([0, 0, 1, 2, 5, 64]))
         x = make_rows(rng, outer * n, inner, dtype, float(rng.choice([0.5, 3.0, 30.0])))
         x3 = x.reshape(outer, n, inner)
+        if rng.random() < 0.5:                              # the same along the reduced axis
+            o, i = rng.integers(outer), rng.integers(inner)
+            col = dominated(rng, n).astype(np.float32)
+            x3[o, :, i] = workloads.f32_to_bf16_bits(col) if dtype == "bf16" else col
         what = f"dim block {block} case {i}: {dtype} {x3.shape} front={front} parts={parts}"
         note(what)
         got = gpu_dim(torch_gpu, handle, x3, dtype, front, parts)
