@@ -93,7 +93,11 @@ lse_status_t lse_create(lse_handle_t *out, int device);
 
 /*
  * out[r] = LSE(x[r, 0:cols]) for r in [0, rows), enqueued on `stream`
- * (NULL means the null stream of the handle's device).
+ * (NULL means the null stream of the handle's device): the paper's fused
+ * single-pass LSE (§3.1) over the last axis (§2.1), special values as above.
+ * Accuracy: |out[r] - LSE| <= 2e-6 * max(1, |LSE|) for fp32 input and
+ * 1e-5 * max(1, |LSE|) for bf16 input, against the exact LSE of the decoded
+ * elements; the paper reports FuseLSE's error against FP64 in §4.1.
  *   x          device pointer to element (0, 0); aligned to its element size.
  *   dtype      LSE_DTYPE_F32 or LSE_DTYPE_BF16.
  *   rows       >= 0; rows == 0 is a no-op (x and out may be NULL).
