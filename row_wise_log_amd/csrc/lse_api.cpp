@@ -36,8 +36,17 @@ constexpr int kRegsMaxElems = 1024;    // ...or up to 1024 single elements (unal
 // loses where the 64-lane reductions need more wavefronts to hide them.
 constexpr int kWavesPerCUNarrow = 8;
 constexpr int kWavesPerCUWide = 16;
-constexpr int64_t kSplitMinRowBytes = 256 << 10;  // shorter rows stream faster unsplit
-constexpr int64_t kSplitPartBytes = 128 << 10;    // target bytes per split part
+// Few long rows (LSE_SCHED_SPLIT_ROW). Rows longer than 64 KiB are split
+// when there are fewer of them than 5/8 of the CUs (3/8 for rows under
+// 256 KiB); from there on one 512-thread workgroup per row streams faster, as
+// it does for rows of up to 64 KiB at any count. A split row gets the
+// wavefronts that give each lane one batch of four 16-byte loads, at most its
+// share of 4 wavefronts per CU: many small workgroups for short inputs
+// (launch-latency bound), about 4 wavefronts per CU once the input is large.
+// Measured against 27 forced plans on 1 to 224 rows of 64 KiB to 4 MiB (bf16
+// and fp32): on average within 1 % of the fastest, at most 13 % from it.
+constexpr int64_t kSplitMinRowBytes = 64 << 10;
+constexpr int kSplitWavesPerCU = 4;
 // lse_forward_dim: column groups per workgroup (the other 256 / 32 = 8 lanes
 // of each column group take consecutive j), doubled where there are columns
 // enough for two 64-group tiles per CU. Measured on [n, inner] of
@@ -52,6 +61,12 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int pow2_at_least(int64_t v) {
     int p = 1;
     while (p < v) p <<= 1;
+    return p;
+}
+
+int64_t pow2_at_most(int64_t v) {  // v >= 1
+    int64_t p = 1;
+    while (p * 2 <= v) p <<= 1;
     return p;
 }
 
@@ -97,7 +112,8 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
         const int64_t row_bytes = cols * esize;
         if (regs_vec || (regs_scalar && (!aligned16 || vec_units == 0)))
             sched = LSE_SCHED_ROWS_PER_WAVE;
-        else if (rows < n_cu && row_bytes >= kSplitMinRowBytes)
+        else if (row_bytes > kSplitMinRowBytes &&
+                 rows * 8 < static_cast<int64_t>(n_cu) * (row_bytes >= 4 * kSplitMinRowBytes ? 5 : 3))
             sched = LSE_SCHED_SPLIT_ROW;  // few long rows: one workgroup per row would idle CUs
         else
             sched = LSE_SCHED_ROW_PER_WG;
@@ -161,19 +177,22 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
         p->grid = rows;
         return LSE_OK;
     }
-    // LSE_SCHED_SPLIT_ROW: parts of about kSplitPartBytes, at least 2, at most
-    // LSE_SPLIT_MAX_PARTS, and no more than ~8 workgroups per CU in total.
-    p->block = tune.block ? tune.block : 512;
+    // LSE_SCHED_SPLIT_ROW: w wavefronts per row, the fewer of those that give
+    // each lane one batch (4 vectors) and the row's share of kSplitWavesPerCU
+    // per CU, at least 2; as up to LSE_SPLIT_MAX_PARTS parts of 64 threads,
+    // then wider workgroups (at most 512 threads). The last part to finish
+    // merges the row's pairs one per thread, so parts never exceed the block.
+    const int64_t r = rows < LSE_SPLIT_MAX_ROWS ? rows : LSE_SPLIT_MAX_ROWS;
+    const int64_t w_one = pow2_at_least(ceil_div(nvec > 0 ? nvec : 1, 4 * 64));
+    const int64_t w_share = pow2_at_most(std::max<int64_t>(1, kSplitWavesPerCU * int64_t{n_cu} / r));
+    const int64_t w = std::max<int64_t>(2, std::min(w_one, w_share));
+    int64_t parts = std::min<int64_t>(w, LSE_SPLIT_MAX_PARTS);
+    const int64_t wide = std::min<int64_t>(512, 64 * (w / parts));
+    p->block = tune.block ? tune.block : static_cast<int32_t>(wide);
     p->unroll = tune.unroll ? tune.unroll : 4;
-    int64_t parts = tune.parts;
-    if (!parts) {
-        const int64_t r = rows < LSE_SPLIT_MAX_ROWS ? rows : LSE_SPLIT_MAX_ROWS;
-        parts = ceil_div(cols * esize, kSplitPartBytes);
-        const int64_t cap = ceil_div(8 * static_cast<int64_t>(n_cu), r);
-        if (parts > cap) parts = cap;
-        if (parts < 2) parts = 2;
-    }
+    if (tune.parts) parts = tune.parts;
     if (parts > LSE_SPLIT_MAX_PARTS) parts = LSE_SPLIT_MAX_PARTS;
+    if (parts > p->block) parts = p->block;
     p->parts = static_cast<int32_t>(parts);
     const int64_t batch_rows = rows < LSE_SPLIT_MAX_ROWS ? rows : LSE_SPLIT_MAX_ROWS;
     p->grid = batch_rows * parts;  // per launch; rows beyond LSE_SPLIT_MAX_ROWS take more launches

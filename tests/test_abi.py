@@ -195,8 +195,8 @@ def plan(dtype, rows, cols, stride=None, addr=0, n_cu=256, schedule=0):
 
 
 def test_plan_for_the_five_workloads():
-    p1 = plan(F32, 64, 32000)
-    assert p1["schedule"] == B.LSE_SCHED_ROW_PER_WG and p1["grid"] == 64 and p1["block"] == 512
+    p1 = plan(F32, 64, 32000)                             # 64 rows: split, 16 parts each
+    assert p1["schedule"] == B.LSE_SCHED_SPLIT_ROW and p1["grid"] == 1024 and p1["block"] == 64
     p2 = plan(BF16, 512, 128256)
     assert p2["schedule"] == B.LSE_SCHED_ROW_PER_WG and p2["grid"] == 512
     assert (p2["block"], p2["unroll"]) == (512, 4)        # two rows per CU
@@ -257,21 +257,36 @@ def test_plan_streaming_block_follows_row_length():
     assert plan(F32, 100000, 1 << 16)["block"] == 256
     assert plan(BF16, 100000, 4096)["block"] == 64      # 8 KiB rows
     assert plan(BF16, 100000, 8192)["block"] == 128
-    assert plan(F32, 100, 1 << 16)["block"] == 512      # fewer rows than CUs
+    assert plan(F32, 200, 1 << 16)["block"] == 512      # fewer rows than CUs
+    assert plan(F32, 100, 1 << 14)["block"] == 512      # 64 KiB rows are not split
     assert plan(F32, 512, 1 << 16)["block"] == 512      # at most two rows per CU
     assert plan(F32, 513, 1 << 16)["block"] == 256
 
 
 def test_plan_long_rows_and_few_rows():
-    # few long rows split into ~128 KiB parts; otherwise one workgroup per row
-    p = plan(F32, 8, 1 << 20)
-    assert p["schedule"] == B.LSE_SCHED_SPLIT_ROW and p["parts"] == 32 and p["grid"] == 256
-    assert p["workspace_bytes"] == 8 * 32 * 8 + 8 * 4
-    assert plan(F32, 1, 1 << 28)["parts"] == B.LSE_SPLIT_MAX_PARTS
-    assert plan(F32, 255, 1 << 16)["schedule"] == B.LSE_SCHED_SPLIT_ROW
-    assert plan(F32, 255, 1 << 16)["parts"] == 2
-    assert plan(F32, 256, 1 << 16)["schedule"] == B.LSE_SCHED_ROW_PER_WG
-    assert plan(F32, 8, (1 << 16) - 4)["schedule"] == B.LSE_SCHED_ROW_PER_WG
+    # Fewer rows than 5/8 of the CUs, longer than 64 KiB: split, with the
+    # wavefronts for one batch (4 vectors) per lane, at most the row's share of
+    # 4 per CU; up to 64 parts of 64 threads, then wider workgroups.
+    p = plan(F32, 8, 1 << 20)             # 4 MiB rows: share 128 wavefronts each
+    assert p["schedule"] == B.LSE_SCHED_SPLIT_ROW and p["parts"] == 64 and p["block"] == 128
+    assert p["grid"] == 512 and p["workspace_bytes"] == 8 * 64 * 8 + 8 * 4
+    p = plan(BF16, 1, 128256)             # one vocabulary row: 64 one-batch parts
+    assert (p["schedule"], p["parts"], p["block"], p["grid"]) == (B.LSE_SCHED_SPLIT_ROW, 64, 64, 64)
+    p = plan(BF16, 32, 128256)            # share 32 wavefronts per row
+    assert (p["parts"], p["block"], p["grid"]) == (32, 64, 1024)
+    p = plan(F32, 64, 32000)              # 125 KiB rows, share 16
+    assert (p["schedule"], p["parts"], p["block"]) == (B.LSE_SCHED_SPLIT_ROW, 16, 64)
+    p = plan(F32, 1, 1 << 28)
+    assert p["parts"] == B.LSE_SPLIT_MAX_PARTS and p["block"] == 512
+    assert plan(F32, 159, 1 << 16)["schedule"] == B.LSE_SCHED_SPLIT_ROW
+    assert plan(F32, 159, 1 << 16)["parts"] == 4
+    assert plan(F32, 160, 1 << 16)["schedule"] == B.LSE_SCHED_ROW_PER_WG
+    assert plan(F32, 160, 1 << 16)["block"] == 512
+    assert plan(F32, 8, (1 << 14) + 4)["schedule"] == B.LSE_SCHED_SPLIT_ROW
+    assert plan(F32, 8, 1 << 14)["schedule"] == B.LSE_SCHED_ROW_PER_WG   # 64 KiB rows
+    assert plan(F32, 95, 1 << 15)["schedule"] == B.LSE_SCHED_SPLIT_ROW   # 128 KiB rows: 3/8
+    assert plan(F32, 96, 1 << 15)["schedule"] == B.LSE_SCHED_ROW_PER_WG
+    assert plan(F32, 96, 1 << 16)["schedule"] == B.LSE_SCHED_SPLIT_ROW   # 256 KiB rows: 5/8
     # unaligned long rows stream with a head peel
     assert plan(BF16, 4, 5001, 5001)["schedule"] == B.LSE_SCHED_ROW_PER_WG
     assert plan(BF16, 4, 500001, 500001)["schedule"] == B.LSE_SCHED_SPLIT_ROW
@@ -343,11 +358,13 @@ def test_plan_invariants(dtype, rows, cols, pad, mis, n_cu, schedule):
         assert p["grid"] == -(-min(waves, n_cu * (8 if g <= 4 else 16)) // 4)
     elif p["schedule"] == B.LSE_SCHED_ROW_PER_WG:
         assert p["grid"] == rows and p["unroll"] in (4, 8) and p["vector_loads"] == 1
-        assert schedule == B.LSE_SCHED_ROW_PER_WG or not (schedule == 0 and rows < n_cu and
-                                                           cols * esize >= (256 << 10))
+        few = 8 * rows < (5 if cols * esize >= (256 << 10) else 3) * n_cu
+        assert schedule == B.LSE_SCHED_ROW_PER_WG or not (schedule == 0 and few and
+                                                           cols * esize > (64 << 10))
     else:
         batch = min(rows, B.LSE_SPLIT_MAX_ROWS)
         assert 2 <= p["parts"] <= B.LSE_SPLIT_MAX_PARTS
+        assert p["parts"] <= p["block"]  # the last part merges the pairs one per thread
         assert p["grid"] == batch * p["parts"] and p["unroll"] in (4, 8)
         assert p["workspace_bytes"] == batch * p["parts"] * 8 + batch * 4
     if schedule == B.LSE_SCHED_SPLIT_ROW and cols > 0:
