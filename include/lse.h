@@ -238,7 +238,9 @@ lse_status_t lse_set_schedule(lse_handle_t h, lse_schedule_t s);
 /* Tuning overrides, for measurement. Streaming schedules: threads per
  * workgroup `block` (64, 128, 256, 512 or 1024), 16-byte loads per lane per
  * batch `unroll` (4 or 8), SPLIT_ROW workgroups per row `parts` (1..64;
- * lse_forward_dim takes it as its workgroups per tile along n).
+ * lse_forward uses at most `block` of them, as the last part merges the
+ * pairs one per thread; lse_forward_dim takes it as its workgroups per tile
+ * along n).
  * ROWS_PER_WAVE: at most `waves_per_cu` wavefronts per compute unit in the
  * grid (1..1024; the wavefronts loop over the rest) and `lanes_per_row` lanes
  * sharing a row (a power of two up to 64; ignored where no kernel instance

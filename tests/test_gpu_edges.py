@@ -229,6 +229,36 @@ def test_largest_row(torch_gpu, handle):
     del x
 
 
+# (dtype, rows, cols, layout, expected automatic plan: block, parts)
+FEW_LONG_ROWS = [
+    ("bf16", 1, 128256, "contiguous", 64, 64),     # one batch per lane: 64 parts of 64 threads
+    ("bf16", 3, 128257, "misaligned", 64, 64),     # head peel in part 0, tail in the last part
+    ("f32", 8, 1 << 20, "contiguous", 128, 64),    # 128 wavefronts per row: wider workgroups
+    ("f32", 1, 1 << 22, "padded", 512, 64),        # the widest split workgroup
+    ("bf16", 95, 65539, "padded", 64, 8),          # 128 KiB rows just under 3/8 of the CUs
+    ("bf16", 40, 262144, "misaligned", 64, 16),    # 512 KiB rows, 25 wavefronts' share each
+    ("f32", 64, 32000, "contiguous", 64, 16),      # the small fp32 vocabulary workload
+]
+
+
+@pytest.mark.parametrize("dtype,rows,cols,layout,block,parts", FEW_LONG_ROWS)
+def test_few_long_rows_automatic_split(torch_gpu, handle, oracle, dtype, rows, cols, layout, block,
+                                       parts):
+    """The automatic plans for few long rows: the split the planner picks for
+    the shape (checked against the expected block and part count) matches the
+    oracle, with special rows mixed in and misaligned or padded rows."""
+    x, front = make_rows(dtype, rows, cols, layout, seed=rows * 31 + cols)
+    code = B.LSE_DTYPE_BF16 if dtype == "bf16" else B.LSE_DTYPE_F32
+    esize = 2 if dtype == "bf16" else 4
+    stride = x.strides[0] // x.itemsize if rows > 1 else cols
+    p = B.lse_plan(code, rows, cols, stride, front * esize, 256, 0)
+    assert (p["schedule"], p["block"], p["parts"]) == (B.LSE_SCHED_SPLIT_ROW, block, parts), p
+    ref = oracle.lse(x, dtype, threads=8)
+    note(f"few long rows {dtype} {rows}x{cols} {layout}: split {block}x{parts}")
+    got = gpu_lse(torch_gpu, handle, x, dtype, "auto", pad_front=front)
+    compare(got, ref, dtype, f"few long rows {dtype} {rows}x{cols} {layout}")
+
+
 @pytest.mark.parametrize("dtype,rows,cols", [("f32", 64, 32000), ("bf16", 7, 300_001)])
 def test_split_alternating_inputs(torch_gpu, handle, oracle, dtype, rows, cols):
     """Back-to-back split-row calls alternate two inputs that differ by +5 in
