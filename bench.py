@@ -385,6 +385,44 @@ def warm_us_per_call(torch, B, handle, cfg: int, calls: int = 1000) -> float:
     return event_mean_us(torch, call, 50, calls, stream)
 
 
+# Few-row shapes beside the headline: the first rows of the headline input
+# (a decode step's batch of vocabulary rows) and the small fp32 workload.
+SMALL_SHAPES = [("bf16", 1), ("bf16", 8), ("bf16", 32)]
+
+
+def small_shapes_us(torch, B, handle, w2, calls: int = 1000) -> dict:
+    """Microseconds per call of back-to-back lse_forward calls on the first 1,
+    8 and 32 rows of the headline input (bf16 [r, 128256]), each call on
+    another of enough copies to exceed the Infinity Cache twice, so every call
+    reads HBM; with the plan the library picks for each. Returns the records
+    and each shape's output of its last call (for the oracle check)."""
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    res, outs = {}, {}
+    for dtype, rows in SMALL_SHAPES:
+        x = w2.x[:rows]
+        host = torch.from_numpy(np.ascontiguousarray(x).view(np.int16))
+        nbytes = x.nbytes
+        rotate = -(-2 * CACHE_BYTES // nbytes) + 1
+        big = torch.empty((rotate, rows, w2.cols), dtype=torch.int16, device="cuda")
+        big[:] = host.to("cuda")
+        out = torch.empty(rows, dtype=torch.float32, device="cuda")
+        base, step_bytes = big.data_ptr(), nbytes
+
+        def call(i, rows=rows):
+            B.lse_forward(handle, base + (i % rotate) * step_bytes, B.LSE_DTYPE_BF16, rows, w2.cols,
+                          w2.cols, out.data_ptr(), sh)
+
+        for i in range(200):
+            call(i)
+        us = event_mean_us(torch, call, 200, calls, stream)
+        plan = B.lse_plan(B.LSE_DTYPE_BF16, rows, w2.cols, w2.cols, base, 256, 0)
+        res[f"{dtype} [{rows}, {w2.cols}]"] = {"us_per_call": round(us, 2), "plan": plan_name(plan)}
+        outs[rows] = out.cpu().numpy().astype(np.float64)
+        del big
+    return res, outs
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -601,6 +639,10 @@ def main() -> int:
         traffic = recorded_traffic(args.config) if args.op == "lse" else None
         floor = launch_floor_us(torch, B, handle)
         log(f"launch floor (lse_forward on one element, back to back): {floor:.2f} us per call")
+        small = small_out = None
+        if args.op == "lse" and args.config == 2 and not args.graph:
+            small, small_out = small_shapes_us(torch, B, handle, w)
+            log(f"few-row shapes: {small}")
         line = {
             "metric": {"lse": METRIC, "logprob": METRIC_LOGPROB, "backward": METRIC_BACKWARD,
                        "logprob_backward": METRIC_TOKEN_BACKWARD,
@@ -680,12 +722,18 @@ def main() -> int:
                         del rc
         if early:
             check_gpu_output(w, r["out"].cpu().numpy().astype(np.float64), reference)
+            if small_out:  # the few-row shapes are the headline input's first rows
+                for rows, got in small_out.items():
+                    log(f"first {rows} rows:")
+                    check_gpu_output(w, got, (reference[0][:rows], None))
             line["cpu_baseline"] = cpu_rec
         elif not args.no_cpu_baseline:
             log("timing the float64 oracle on the host cores")
             line["cpu_baseline"] = cpu_baseline_backward(w, r, args.cpu_seconds)
         else:
             line["cpu_baseline"] = None
+        if small is not None:
+            line["small_shapes"] = small
         print(json.dumps(line), flush=True)
     finally:
         torch.cuda.synchronize()

@@ -63,6 +63,11 @@ def test_default_workload_line():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["value"] > 0 and cb["cores"] >= 1
     assert isinstance(cb["sample"], str) and cb["sample"]
+    # microseconds per call on few rows of the same input, with their plans
+    small = d["small_shapes"]
+    assert set(small) == {"bf16 [1, 128256]", "bf16 [8, 128256]", "bf16 [32, 128256]"}
+    for rec in small.values():
+        assert 0 < rec["us_per_call"] < 1000 and rec["plan"].startswith("split_row")
 
 
 @pytest.mark.parametrize("args", [["--config", "1", "--graph"], ["--config", "1", "--op", "backward"],
