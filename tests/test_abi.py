@@ -259,7 +259,11 @@ def test_plan_streaming_block_follows_row_length():
     assert plan(BF16, 100000, 8192)["block"] == 128
     assert plan(F32, 200, 1 << 16)["block"] == 512      # fewer rows than CUs
     assert plan(F32, 100, 1 << 14)["block"] == 512      # 64 KiB rows are not split
-    assert plan(F32, 512, 1 << 16)["block"] == 512      # at most two rows per CU
+    assert plan(F32, 223, 1 << 16)["block"] == 512
+    assert plan(F32, 224, 1 << 16)["block"] == 256      # one or two rows per CU
+    assert plan(F32, 479, 1 << 16)["block"] == 256
+    assert plan(F32, 480, 1 << 16)["block"] == 512      # (nearly) two rows on every CU
+    assert plan(F32, 512, 1 << 16)["block"] == 512
     assert plan(F32, 513, 1 << 16)["block"] == 256
 
 
