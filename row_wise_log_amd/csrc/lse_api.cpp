@@ -37,9 +37,12 @@ constexpr int kRegsMaxElems = 1024;    // ...or up to 1024 single elements (unal
 constexpr int kWavesPerCUNarrow = 8;
 constexpr int kWavesPerCUWide = 16;
 // Few long rows (LSE_SCHED_SPLIT_ROW). Rows longer than 64 KiB are split
-// when there are fewer of them than 5/8 of the CUs (3/8 for rows under
-// 256 KiB); from there on one 512-thread workgroup per row streams faster, as
-// it does for rows of up to 64 KiB at any count. A split row gets the
+// when there are at most half as many of them as CUs (fewer than 3/8 for rows
+// under 256 KiB), so that each row's share of the budget below is at least
+// the 8 wavefronts of a 512-thread workgroup; with more rows one 512-thread
+// workgroup per row streams faster (measured at steady state: 150 rows of
+// 256 KiB and 1 MiB, 9.4 and 27.2 us against 11.7 and 34.8 us split), as it
+// does for rows of up to 64 KiB at any count. A split row gets the
 // wavefronts that give each lane one batch of four 16-byte loads, at most its
 // share of 4 wavefronts per CU: many small workgroups for short inputs
 // (launch-latency bound), about 4 wavefronts per CU once the input is large.
@@ -113,7 +116,7 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
         if (regs_vec || (regs_scalar && (!aligned16 || vec_units == 0)))
             sched = LSE_SCHED_ROWS_PER_WAVE;
         else if (row_bytes > kSplitMinRowBytes &&
-                 rows * 8 < static_cast<int64_t>(n_cu) * (row_bytes >= 4 * kSplitMinRowBytes ? 5 : 3))
+                 (row_bytes >= 4 * kSplitMinRowBytes ? rows * 2 <= n_cu : rows * 8 < 3 * int64_t{n_cu}))
             sched = LSE_SCHED_SPLIT_ROW;  // few long rows: one workgroup per row would idle CUs
         else
             sched = LSE_SCHED_ROW_PER_WG;

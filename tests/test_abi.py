@@ -268,7 +268,8 @@ def test_plan_streaming_block_follows_row_length():
 
 
 def test_plan_long_rows_and_few_rows():
-    # Fewer rows than 5/8 of the CUs, longer than 64 KiB: split, with the
+    # At most half as many rows as CUs (under 256 KiB: fewer than 3/8),
+    # longer than 64 KiB: split, with the
     # wavefronts for one batch (4 vectors) per lane, at most the row's share of
     # 4 per CU; up to 64 parts of 64 threads, then wider workgroups.
     p = plan(F32, 8, 1 << 20)             # 4 MiB rows: share 128 wavefronts each
@@ -282,15 +283,15 @@ def test_plan_long_rows_and_few_rows():
     assert (p["schedule"], p["parts"], p["block"]) == (B.LSE_SCHED_SPLIT_ROW, 16, 64)
     p = plan(F32, 1, 1 << 28)
     assert p["parts"] == B.LSE_SPLIT_MAX_PARTS and p["block"] == 512
-    assert plan(F32, 159, 1 << 16)["schedule"] == B.LSE_SCHED_SPLIT_ROW
-    assert plan(F32, 159, 1 << 16)["parts"] == 4
-    assert plan(F32, 160, 1 << 16)["schedule"] == B.LSE_SCHED_ROW_PER_WG
-    assert plan(F32, 160, 1 << 16)["block"] == 512
+    assert plan(F32, 128, 1 << 16)["schedule"] == B.LSE_SCHED_SPLIT_ROW
+    assert plan(F32, 128, 1 << 16)["parts"] == 8
+    assert plan(F32, 129, 1 << 16)["schedule"] == B.LSE_SCHED_ROW_PER_WG
+    assert plan(F32, 129, 1 << 16)["block"] == 512
     assert plan(F32, 8, (1 << 14) + 4)["schedule"] == B.LSE_SCHED_SPLIT_ROW
     assert plan(F32, 8, 1 << 14)["schedule"] == B.LSE_SCHED_ROW_PER_WG   # 64 KiB rows
     assert plan(F32, 95, 1 << 15)["schedule"] == B.LSE_SCHED_SPLIT_ROW   # 128 KiB rows: 3/8
     assert plan(F32, 96, 1 << 15)["schedule"] == B.LSE_SCHED_ROW_PER_WG
-    assert plan(F32, 96, 1 << 16)["schedule"] == B.LSE_SCHED_SPLIT_ROW   # 256 KiB rows: 5/8
+    assert plan(F32, 96, 1 << 16)["schedule"] == B.LSE_SCHED_SPLIT_ROW   # 256 KiB rows: 1/2
     # unaligned long rows stream with a head peel
     assert plan(BF16, 4, 5001, 5001)["schedule"] == B.LSE_SCHED_ROW_PER_WG
     assert plan(BF16, 4, 500001, 500001)["schedule"] == B.LSE_SCHED_SPLIT_ROW
@@ -362,7 +363,7 @@ def test_plan_invariants(dtype, rows, cols, pad, mis, n_cu, schedule):
         assert p["grid"] == -(-min(waves, n_cu * (8 if g <= 4 else 16)) // 4)
     elif p["schedule"] == B.LSE_SCHED_ROW_PER_WG:
         assert p["grid"] == rows and p["unroll"] in (4, 8) and p["vector_loads"] == 1
-        few = 8 * rows < (5 if cols * esize >= (256 << 10) else 3) * n_cu
+        few = 2 * rows <= n_cu if cols * esize >= (256 << 10) else 8 * rows < 3 * n_cu
         assert schedule == B.LSE_SCHED_ROW_PER_WG or not (schedule == 0 and few and
                                                            cols * esize > (64 << 10))
     else:
