@@ -44,14 +44,11 @@ constexpr int kWavesPerCUWide = 16;
 // 256 KiB and 1 MiB, 9.4 and 27.2 us against 11.7 and 34.8 us split), as it
 // does for rows of up to 64 KiB at any count. A split row gets the
 // wavefronts that give each lane one batch of four 16-byte loads, at most its
-// share of 4 wavefronts per CU: many small workgroups for short inputs
+// share of 4 wavefronts per CU (rounded up): many small workgroups for short inputs
 // (launch-latency bound), about 4 wavefronts per CU once the input is large.
-// Short sweeps against 27 forced plans (1 to 224 rows of 64 KiB to 4 MiB,
-// bf16 and fp32) put it within 1 % of the fastest on average; at steady
-// state it beats the previous rule (512-thread parts of ~128 KiB) by 1.16x
-// on random shapes, up to 1.8x on small inputs, and trails the fastest plan
-// by up to 20 % on some inputs of 50 MB and more, where more wavefronts per
-// row would pay.
+// At steady state it beats the previous rule (512-thread parts of ~128 KiB)
+// by 1.17x on random shapes, up to 1.8x on small inputs, and loses 5-9 % on
+// some inputs of 200 MB and more with 129 to 223 rows.
 constexpr int64_t kSplitMinRowBytes = 64 << 10;
 constexpr int kSplitWavesPerCU = 4;
 // lse_forward_dim: column groups per workgroup (the other 256 / 32 = 8 lanes
@@ -68,12 +65,6 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int pow2_at_least(int64_t v) {
     int p = 1;
     while (p < v) p <<= 1;
-    return p;
-}
-
-int64_t pow2_at_most(int64_t v) {  // v >= 1
-    int64_t p = 1;
-    while (p * 2 <= v) p <<= 1;
     return p;
 }
 
@@ -191,12 +182,14 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
     }
     // LSE_SCHED_SPLIT_ROW: w wavefronts per row, the fewer of those that give
     // each lane one batch (4 vectors) and the row's share of kSplitWavesPerCU
-    // per CU, at least 2; as up to LSE_SPLIT_MAX_PARTS parts of 64 threads,
+    // per CU (rounded up to a power of two), at least 2; as up to LSE_SPLIT_MAX_PARTS parts of 64 threads,
     // then wider workgroups (at most 512 threads). The last part to finish
     // merges the row's pairs one per thread, so parts never exceed the block.
     const int64_t r = rows < LSE_SPLIT_MAX_ROWS ? rows : LSE_SPLIT_MAX_ROWS;
     const int64_t w_one = pow2_at_least(ceil_div(nvec > 0 ? nvec : 1, 4 * 64));
-    const int64_t w_share = pow2_at_most(std::max<int64_t>(1, kSplitWavesPerCU * int64_t{n_cu} / r));
+    // the share rounds up: rounded down, 40 or 75 rows got only 2.3-2.6
+    // wavefronts per CU and ran 22 % slower than with 32 and 16 parts
+    const int64_t w_share = pow2_at_least(ceil_div(kSplitWavesPerCU * int64_t{n_cu}, r));
     const int64_t w = std::max<int64_t>(2, std::min(w_one, w_share));
     int64_t parts = std::min<int64_t>(w, LSE_SPLIT_MAX_PARTS);
     const int64_t wide = std::min<int64_t>(512, 64 * (w / parts));

@@ -235,8 +235,8 @@ FEW_LONG_ROWS = [
     ("bf16", 3, 128257, "misaligned", 64, 64),     # head peel in part 0, tail in the last part
     ("f32", 8, 1 << 20, "contiguous", 128, 64),    # 128 wavefronts per row: wider workgroups
     ("f32", 1, 1 << 22, "padded", 512, 64),        # the widest split workgroup
-    ("bf16", 95, 65539, "padded", 64, 8),          # 128 KiB rows just under 3/8 of the CUs
-    ("bf16", 40, 262144, "misaligned", 64, 16),    # 512 KiB rows, 25 wavefronts' share each
+    ("bf16", 95, 65539, "padded", 64, 16),         # 128 KiB rows just under 3/8 of the CUs
+    ("bf16", 40, 262144, "misaligned", 64, 32),    # 512 KiB rows, a share of 26 wavefronts, 32
     ("f32", 64, 32000, "contiguous", 64, 16),      # the small fp32 vocabulary workload
 ]
 
