@@ -282,7 +282,7 @@ def test_plan_long_rows_and_few_rows():
     # the share rounds up to a power of two: 40 rows -> 26 -> 32, 75 -> 14 -> 16
     assert (plan(BF16, 40, 1810534)["parts"], plan(BF16, 40, 1810534)["block"]) == (32, 64)
     assert (plan(BF16, 75, 383639)["parts"], plan(BF16, 75, 383639)["block"]) == (16, 64)
-    assert plan(F32, 3, 292775)["parts"] == 64 and plan(F32, 3, 292775)["block"] == 256
+    assert plan(F32, 3, 292775)["parts"] == 64 and plan(F32, 3, 292775)["block"] == 512
     p = plan(F32, 64, 32000)              # 125 KiB rows, share 16
     assert (p["schedule"], p["parts"], p["block"]) == (B.LSE_SCHED_SPLIT_ROW, 16, 64)
     p = plan(F32, 1, 1 << 28)
