@@ -51,6 +51,11 @@ constexpr int kWavesPerCUWide = 16;
 // some inputs of 200 MB and more with 129 to 223 rows.
 constexpr int64_t kSplitMinRowBytes = 64 << 10;
 constexpr int kSplitWavesPerCU = 4;
+// Just over one row per CU (up to 5/4), one workgroup per row leaves most CUs
+// one row and some two; rows of 1 MiB and more then split into four parts of
+// 256 threads (measured at steady state: 257, 288 and 320 rows of 1 MiB,
+// 6-9 % faster; rows of 256 KiB gain nothing).
+constexpr int64_t kSplitQuarterRowBytes = 1 << 20;
 // lse_forward_dim: column groups per workgroup (the other 256 / 32 = 8 lanes
 // of each column group take consecutive j), doubled where there are columns
 // enough for two 64-group tiles per CU. Measured on [n, inner] of
@@ -113,6 +118,8 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
         else if (row_bytes > kSplitMinRowBytes &&
                  (row_bytes >= 4 * kSplitMinRowBytes ? rows * 2 <= n_cu : rows * 8 < 3 * int64_t{n_cu}))
             sched = LSE_SCHED_SPLIT_ROW;  // few long rows: one workgroup per row would idle CUs
+        else if (row_bytes >= kSplitQuarterRowBytes && rows > n_cu && rows * 4 <= 5 * int64_t{n_cu})
+            sched = LSE_SCHED_SPLIT_ROW;  // just over one row per CU: quarters even the CUs out
         else
             sched = LSE_SCHED_ROW_PER_WG;
     }
@@ -182,9 +189,10 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
     }
     // LSE_SCHED_SPLIT_ROW: w wavefronts per row, the fewer of those that give
     // each lane one batch (4 vectors) and the row's share of kSplitWavesPerCU
-    // per CU (rounded up to a power of two), at least 2; as up to LSE_SPLIT_MAX_PARTS parts of 64 threads,
-    // then wider workgroups (at most 512 threads). The last part to finish
-    // merges the row's pairs one per thread, so parts never exceed the block.
+    // per CU (rounded up to a power of two), at least 2; as up to
+    // LSE_SPLIT_MAX_PARTS parts of 64 threads, then wider workgroups (at most
+    // 512 threads). The last part to finish merges the row's pairs one per
+    // thread, so parts never exceed the block.
     const int64_t r = rows < LSE_SPLIT_MAX_ROWS ? rows : LSE_SPLIT_MAX_ROWS;
     const int64_t w_one = pow2_at_least(ceil_div(nvec > 0 ? nvec : 1, 4 * 64));
     // the share rounds up: rounded down, 40 or 75 rows got only 2.3-2.6
@@ -192,7 +200,11 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
     const int64_t w_share = pow2_at_least(ceil_div(kSplitWavesPerCU * int64_t{n_cu}, r));
     const int64_t w = std::max<int64_t>(2, std::min(w_one, w_share));
     int64_t parts = std::min<int64_t>(w, LSE_SPLIT_MAX_PARTS);
-    const int64_t wide = std::min<int64_t>(512, 64 * (w / parts));
+    int64_t wide = std::min<int64_t>(512, 64 * (w / parts));
+    if (rows > n_cu && rows * 4 <= 5 * int64_t{n_cu}) {  // just over one row per CU: quarters
+        parts = 4;
+        wide = 256;
+    }
     p->block = tune.block ? tune.block : static_cast<int32_t>(wide);
     p->unroll = tune.unroll ? tune.unroll : 4;
     if (tune.parts) parts = tune.parts;

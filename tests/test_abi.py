@@ -296,6 +296,13 @@ def test_plan_long_rows_and_few_rows():
     assert plan(F32, 95, 1 << 15)["schedule"] == B.LSE_SCHED_SPLIT_ROW   # 128 KiB rows: 3/8
     assert plan(F32, 96, 1 << 15)["schedule"] == B.LSE_SCHED_ROW_PER_WG
     assert plan(F32, 96, 1 << 16)["schedule"] == B.LSE_SCHED_SPLIT_ROW   # 256 KiB rows: 1/2
+    # just over one row per CU (up to 5/4), rows of 1 MiB and more: quarters of 256 threads
+    p = plan(F32, 257, 1 << 18)
+    assert (p["schedule"], p["parts"], p["block"]) == (B.LSE_SCHED_SPLIT_ROW, 4, 256)
+    assert plan(F32, 320, 1 << 18)["parts"] == 4
+    assert plan(F32, 321, 1 << 18)["schedule"] == B.LSE_SCHED_ROW_PER_WG
+    assert plan(F32, 256, 1 << 18)["schedule"] == B.LSE_SCHED_ROW_PER_WG
+    assert plan(F32, 300, (1 << 18) - 4)["schedule"] == B.LSE_SCHED_ROW_PER_WG   # under 1 MiB
     # unaligned long rows stream with a head peel
     assert plan(BF16, 4, 5001, 5001)["schedule"] == B.LSE_SCHED_ROW_PER_WG
     assert plan(BF16, 4, 500001, 500001)["schedule"] == B.LSE_SCHED_SPLIT_ROW
@@ -368,8 +375,9 @@ def test_plan_invariants(dtype, rows, cols, pad, mis, n_cu, schedule):
     elif p["schedule"] == B.LSE_SCHED_ROW_PER_WG:
         assert p["grid"] == rows and p["unroll"] in (4, 8) and p["vector_loads"] == 1
         few = 2 * rows <= n_cu if cols * esize >= (256 << 10) else 8 * rows < 3 * n_cu
-        assert schedule == B.LSE_SCHED_ROW_PER_WG or not (schedule == 0 and few and
-                                                           cols * esize > (64 << 10))
+        quarters = n_cu < rows <= 5 * n_cu // 4 and cols * esize >= (1 << 20)
+        assert schedule == B.LSE_SCHED_ROW_PER_WG or not (schedule == 0 and (quarters or (
+            few and cols * esize > (64 << 10))))
     else:
         batch = min(rows, B.LSE_SPLIT_MAX_ROWS)
         assert 2 <= p["parts"] <= B.LSE_SPLIT_MAX_PARTS
