@@ -12,6 +12,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
@@ -48,10 +50,7 @@ def build_control(quiet: bool = True) -> Path:
     return build(CONTROL_LIBRARY, quiet=quiet, sources=CONTROL_SOURCES)
 
 
-def build(output: Path = LIBRARY, extra: list[str] | None = None, quiet: bool = True,
-          sources: list[Path] | None = None) -> Path:
-    tmp = output.with_name(output.name + f".tmp{os.getpid()}")
-    proc = subprocess.run(command(tmp, extra, sources), capture_output=True, text=True)
+def _report(proc: subprocess.CompletedProcess, quiet: bool) -> None:
     if proc.returncode != 0:
         sys.stderr.write(proc.stdout + proc.stderr)
         raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
@@ -61,6 +60,28 @@ def build(output: Path = LIBRARY, extra: list[str] | None = None, quiet: bool = 
         msg = "\n".join(l for l in (proc.stdout + proc.stderr).splitlines() if noise not in l)
         if msg.strip():
             sys.stderr.write(msg + "\n")
+
+
+def build(output: Path = LIBRARY, extra: list[str] | None = None, quiet: bool = True,
+          sources: list[Path] | None = None) -> Path:
+    """Compile each source to an object in parallel (one hipcc per source),
+    then link the shared library; the result replaces `output` atomically."""
+    sources = list(sources or SOURCES)
+    tmp = output.with_name(output.name + f".tmp{os.getpid()}")
+    with tempfile.TemporaryDirectory(prefix="lse_build_") as d:
+        objs = [Path(d) / f"{i}_{s.stem}.o" for i, s in enumerate(sources)]
+        base = command(tmp, extra, sources)
+        # the compile line: the common flags, -c, one source, its object
+        flags = [a for a in base[:base.index("-x")] if a != "-shared"]
+        jobs = [flags + ["-c", "-x", "hip", str(s), "-o", str(o)] for s, o in zip(sources, objs)]
+        workers = max(1, min(len(jobs), len(os.sched_getaffinity(0))))
+        with ThreadPoolExecutor(workers) as ex:
+            procs = list(ex.map(lambda c: subprocess.run(c, capture_output=True, text=True), jobs))
+        for proc in procs:
+            _report(proc, quiet)
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs),
+                "-o", str(tmp)]
+        _report(subprocess.run(link, capture_output=True, text=True), quiet)
     os.replace(tmp, output)
     return output
 

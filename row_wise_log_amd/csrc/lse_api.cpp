@@ -111,17 +111,22 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
     const bool regs_scalar = cols <= kRegsMaxElems;
 
     int sched = schedule;
+    bool quarters = false;  // the automatic split of just over one long row per CU
     if (sched == LSE_SCHED_AUTO) {
         const int64_t row_bytes = cols * esize;
-        if (regs_vec || (regs_scalar && (!aligned16 || vec_units == 0)))
+        if (regs_vec || (regs_scalar && (!aligned16 || vec_units == 0))) {
             sched = LSE_SCHED_ROWS_PER_WAVE;
-        else if (row_bytes > kSplitMinRowBytes &&
-                 (row_bytes >= 4 * kSplitMinRowBytes ? rows * 2 <= n_cu : rows * 8 < 3 * int64_t{n_cu}))
+        } else if (row_bytes > kSplitMinRowBytes &&
+                   (row_bytes >= 4 * kSplitMinRowBytes ? rows * 2 <= n_cu
+                                                       : rows * 8 < 3 * int64_t{n_cu})) {
             sched = LSE_SCHED_SPLIT_ROW;  // few long rows: one workgroup per row would idle CUs
-        else if (row_bytes >= kSplitQuarterRowBytes && rows > n_cu && rows * 4 <= 5 * int64_t{n_cu})
+        } else if (row_bytes >= kSplitQuarterRowBytes && rows > n_cu &&
+                   rows * 4 <= 5 * int64_t{n_cu}) {
             sched = LSE_SCHED_SPLIT_ROW;  // just over one row per CU: quarters even the CUs out
-        else
+            quarters = true;
+        } else {
             sched = LSE_SCHED_ROW_PER_WG;
+        }
     }
     // Rows longer than registers hold go to the streaming schedule.
     if (sched == LSE_SCHED_ROWS_PER_WAVE && !regs_vec && !regs_scalar) sched = LSE_SCHED_ROW_PER_WG;
@@ -201,7 +206,7 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
     const int64_t w = std::max<int64_t>(2, std::min(w_one, w_share));
     int64_t parts = std::min<int64_t>(w, LSE_SPLIT_MAX_PARTS);
     int64_t wide = std::min<int64_t>(512, 64 * (w / parts));
-    if (rows > n_cu && rows * 4 <= 5 * int64_t{n_cu}) {  // just over one row per CU: quarters
+    if (quarters) {  // chosen above for rows of 1 MiB and more, n_cu < rows <= 5/4 n_cu
         parts = 4;
         wide = 256;
     }
@@ -394,24 +399,33 @@ lse_status_t lse_set_tuning(lse_handle_t h, int32_t block, int32_t unroll, int32
 
 }  // extern "C"
 
-namespace {
+namespace lse {
 
-// Plan and launch one call; the arguments were checked by the caller. With
+// Plan and launch one forward call (lse_forward, lse_token_logprob and the
+// no-allocation entry point); the arguments were checked by the caller. With
 // targets set, the kernels also write logp (and write out only if it is not
 // NULL).
-lse_status_t run(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows, int64_t cols,
-                 int64_t row_stride, float* out, const int64_t* targets, float* logp,
-                 hipStream_t stream) {
+lse_status_t run_forward(const ForwardContext& c, const void* x, lse_dtype_t dtype, int64_t rows,
+                         int64_t cols, int64_t row_stride, float* out, const int64_t* targets,
+                         float* logp, hipStream_t stream) {
     lse_plan_t p;
     lse_status_t st = make_plan(dtype, rows, cols, row_stride, reinterpret_cast<uint64_t>(x),
-                                h->n_cu, h->schedule,
-                                Tuning{h->block, h->unroll, h->parts, h->waves_per_cu,
-                                       h->lanes_per_row},
+                                c.n_cu, c.schedule,
+                                Tuning{c.block, c.unroll, c.parts, c.waves_per_cu, c.lanes_per_row},
                                 &p);
     if (st != LSE_OK) return st;
+    // The split schedule's pairs and counters of one launch must fit the
+    // workspace; launches take at most LSE_SPLIT_MAX_ROWS rows, so a plan
+    // never needs more than LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS pairs and
+    // LSE_SPLIT_MAX_ROWS counters.
+    if (p.schedule == LSE_SCHED_SPLIT_ROW) {
+        const int64_t batch = rows < LSE_SPLIT_MAX_ROWS ? rows : LSE_SPLIT_MAX_ROWS;
+        if (batch * p.parts > c.pair_capacity || batch > c.counter_capacity)
+            return LSE_ERR_INVALID_ARG;
+    }
 
     const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
-    lse::LaunchArgs a{};
+    LaunchArgs a{};
     a.schedule = p.schedule;
     a.bf16 = dtype == LSE_DTYPE_BF16;
     a.block = p.block;
@@ -429,13 +443,13 @@ lse_status_t run(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,
     a.out = out;
     a.targets = targets;
     a.logp = logp;
-    a.ws_pairs = h->ws_pairs;
-    a.counters = h->counters;
+    a.ws_pairs = c.ws_pairs;
+    a.counters = c.counters;
     a.stream = stream;
 
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess) return LSE_ERR_HIP;
-    if (prev != h->device && hipSetDevice(h->device) != hipSuccess) return LSE_ERR_HIP;
+    if (prev != c.device && hipSetDevice(c.device) != hipSuccess) return LSE_ERR_HIP;
 
     hipError_t err = hipSuccess;
     if (p.schedule == LSE_SCHED_SPLIT_ROW) {
@@ -443,20 +457,50 @@ lse_status_t run(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,
         // row batches on the same stream (each launch resets its counters).
         for (int64_t r0 = 0; r0 < rows && err == hipSuccess; r0 += LSE_SPLIT_MAX_ROWS) {
             const int64_t n = rows - r0 < LSE_SPLIT_MAX_ROWS ? rows - r0 : LSE_SPLIT_MAX_ROWS;
-            lse::LaunchArgs b = a;
+            LaunchArgs b = a;
             b.x = a.x + r0 * a.stride_bytes;
             b.out = a.out ? a.out + r0 : nullptr;
             b.targets = a.targets ? a.targets + r0 : nullptr;
             b.logp = a.logp ? a.logp + r0 : nullptr;
             b.rows = n;
             b.grid = n * p.parts;
-            err = lse::launch(b);
+            err = launch(b);
         }
     } else {
-        err = lse::launch(a);
+        err = launch(a);
     }
-    if (prev != h->device) (void)hipSetDevice(prev);
+    if (prev != c.device) (void)hipSetDevice(prev);
     return err == hipSuccess ? LSE_OK : LSE_ERR_HIP;
+}
+
+lse_status_t check_forward(const void* x, lse_dtype_t dtype, int64_t rows, int64_t cols,
+                           int64_t row_stride, const float* out) {
+    lse_status_t st = check_sizes(dtype, rows, cols, row_stride, reinterpret_cast<uint64_t>(x));
+    if (st != LSE_OK || rows == 0) return st;
+    if (out == nullptr || (cols > 0 && x == nullptr)) return LSE_ERR_INVALID_ARG;
+    if (reinterpret_cast<uint64_t>(out) % 4 != 0) return LSE_ERR_INVALID_ARG;
+    return LSE_OK;
+}
+
+}  // namespace lse
+
+namespace {
+
+lse::ForwardContext context_of(lse_handle_t h) {
+    lse::ForwardContext c{};
+    c.device = h->device;
+    c.n_cu = h->n_cu;
+    c.schedule = h->schedule;
+    c.block = h->block;
+    c.unroll = h->unroll;
+    c.parts = h->parts;
+    c.waves_per_cu = h->waves_per_cu;
+    c.lanes_per_row = h->lanes_per_row;
+    c.ws_pairs = h->ws_pairs;
+    c.counters = h->counters;
+    c.pair_capacity = int64_t{LSE_SPLIT_MAX_ROWS} * LSE_SPLIT_MAX_PARTS;
+    c.counter_capacity = LSE_SPLIT_MAX_ROWS;
+    return c;
 }
 
 }  // namespace
@@ -465,14 +509,12 @@ extern "C" {
 
 lse_status_t lse_forward(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,
                          int64_t cols, int64_t row_stride, float* out, hipStream_t stream) {
-    const uint64_t x_addr = reinterpret_cast<uint64_t>(x);
-    lse_status_t st = check_sizes(dtype, rows, cols, row_stride, x_addr);
+    lse_status_t st = lse::check_forward(x, dtype, rows, cols, row_stride, out);
     if (st != LSE_OK) return st;
-    if (rows == 0) return h == nullptr ? LSE_ERR_INVALID_ARG : LSE_OK;
-    if (out == nullptr || (cols > 0 && x == nullptr)) return LSE_ERR_INVALID_ARG;
-    if (reinterpret_cast<uint64_t>(out) % 4 != 0) return LSE_ERR_INVALID_ARG;
     if (h == nullptr) return LSE_ERR_INVALID_ARG;
-    return run(h, x, dtype, rows, cols, row_stride, out, nullptr, nullptr, stream);
+    if (rows == 0) return LSE_OK;
+    return lse::run_forward(context_of(h), x, dtype, rows, cols, row_stride, out, nullptr, nullptr,
+                            stream);
 }
 
 }  // extern "C"
@@ -631,7 +673,8 @@ lse_status_t lse_token_logprob(lse_handle_t h, const void* x, lse_dtype_t dtype,
         reinterpret_cast<uint64_t>(lse_out) % 4 != 0)
         return LSE_ERR_INVALID_ARG;
     if (h == nullptr) return LSE_ERR_INVALID_ARG;
-    return run(h, x, dtype, rows, cols, row_stride, lse_out, targets, logp, stream);
+    return lse::run_forward(context_of(h), x, dtype, rows, cols, row_stride, lse_out, targets,
+                            logp, stream);
 }
 
 }  // extern "C"

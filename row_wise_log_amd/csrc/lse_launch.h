@@ -1,9 +1,12 @@
 // lse_launch.h - the interface between the host planner (lse_api.cpp) and the
-// kernel dispatch (lse_kernels.hip). Host-only types; no device code.
+// kernel dispatch (lse_kernels.hip, lse_backward.hip, lse_dim.hip, lse_noalloc.hip).
+// Host-only types; no device code.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
+
+#include "lse.h"
 
 namespace lse {
 
@@ -42,6 +45,31 @@ struct LaunchArgs {
 
 // Launches the kernel the plan names; returns hipGetLastError() after it.
 hipError_t launch(const LaunchArgs& a);
+
+// What a forward call needs besides its operands: the device, its CU count,
+// the schedule and tuning overrides (0 = the planner's choice), and the split
+// schedule's workspace with its capacity (pairs of 8 bytes; counters
+// kCounterWords words apart, zero between calls). A handle provides them, or
+// the no-allocation entry point its per-device scratch.
+struct ForwardContext {
+    int device;
+    int n_cu;
+    int schedule;
+    int block, unroll, parts, waves_per_cu, lanes_per_row;
+    unsigned* ws_pairs;
+    unsigned* counters;
+    int64_t pair_capacity;
+    int64_t counter_capacity;
+};
+
+// Argument checks shared by the forward entry points (no HIP call).
+lse_status_t check_forward(const void* x, lse_dtype_t dtype, int64_t rows, int64_t cols,
+                           int64_t row_stride, const float* out);
+
+// Plan and launch one forward call on `stream` (lse_api.cpp).
+lse_status_t run_forward(const ForwardContext& c, const void* x, lse_dtype_t dtype, int64_t rows,
+                         int64_t cols, int64_t row_stride, float* out, const int64_t* targets,
+                         float* logp, hipStream_t stream);
 
 // The backward pass, grad_x = grad_out * exp(x - lse) (lse_backward.hip).
 struct GradArgs {

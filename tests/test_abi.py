@@ -303,6 +303,13 @@ def test_plan_long_rows_and_few_rows():
     assert plan(F32, 321, 1 << 18)["schedule"] == B.LSE_SCHED_ROW_PER_WG
     assert plan(F32, 256, 1 << 18)["schedule"] == B.LSE_SCHED_ROW_PER_WG
     assert plan(F32, 300, (1 << 18) - 4)["schedule"] == B.LSE_SCHED_ROW_PER_WG   # under 1 MiB
+    # the quarters belong to the automatic choice only: a forced split in the
+    # same band of rows keeps the general rule (the rows' share of 4 wavefronts
+    # per CU: 4 parts of 64 threads), for short rows and long ones alike
+    p = plan(F32, 300, 1 << 14, schedule=3)
+    assert (p["schedule"], p["parts"], p["block"]) == (B.LSE_SCHED_SPLIT_ROW, 4, 64)
+    p = plan(F32, 300, 1 << 18, schedule=3)
+    assert (p["schedule"], p["parts"], p["block"]) == (B.LSE_SCHED_SPLIT_ROW, 4, 64)
     # unaligned long rows stream with a head peel
     assert plan(BF16, 4, 5001, 5001)["schedule"] == B.LSE_SCHED_ROW_PER_WG
     assert plan(BF16, 4, 500001, 500001)["schedule"] == B.LSE_SCHED_SPLIT_ROW

@@ -238,6 +238,8 @@ FEW_LONG_ROWS = [
     ("bf16", 95, 65539, "padded", 64, 16),         # 128 KiB rows just under 3/8 of the CUs
     ("bf16", 40, 262144, "misaligned", 64, 32),    # 512 KiB rows, a share of 26 wavefronts, 32
     ("f32", 64, 32000, "contiguous", 64, 16),      # the small fp32 vocabulary workload
+    ("bf16", 257, 524288, "padded", 256, 4),       # just over one 1 MiB row per CU: quarters
+    ("f32", 320, 262144, "misaligned", 256, 4),    # 5/4 rows per CU, the band's upper end
 ]
 
 
