@@ -224,6 +224,32 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void *x, lse_dtype_t dtype,
                              int64_t outer, int64_t n, int64_t inner, float *out,
                              hipStream_t stream);
 
+/*
+ * lse_forward without a handle and without allocating, for callers that
+ * cannot call hipMalloc: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid device allocation. Same operation, arguments (minus
+ * the handle), accuracy, special values and stream semantics as lse_forward,
+ * on the current device (`stream` must belong to it), with the planner's
+ * automatic schedule (lse_set_schedule / lse_set_tuning do not apply).
+ *
+ * Scratch. The split-row schedule's (max, sum) pairs and arrival counters
+ * live in a fixed device array of 768 KiB that each GPU the library runs on
+ * holds until the process ends (room for LSE_SPLIT_MAX_ROWS rows of
+ * LSE_SPLIT_MAX_PARTS pairs per launch; longer inputs go in several launches,
+ * so every shape fits, and a plan that did not would be rejected with
+ * INVALID_ARG before any launch). The first call on a device looks the array
+ * up and enqueues one small kernel on `stream` that zeroes the counters (again
+ * on later calls while that kernel was only captured, not run); lse_create on
+ * a device does the same set-up. Every call on a GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (other streams, threads or graph
+ * replays running at the same time) race and give wrong results.
+ * No hipMalloc, hipFree or allocating library call; no synchronisation.
+ * Errors: as lse_forward (no handle error); NO_DEVICE (no current device, or
+ * not gfx950); HIP.
+ */
+lse_status_t lse_forward_noalloc(const void *x, lse_dtype_t dtype, int64_t rows, int64_t cols,
+                                 int64_t row_stride, float *out, hipStream_t stream);
+
 /* Release the handle and its workspace. NULL is allowed and returns LSE_OK.
  * The caller must ensure no work using the handle is still pending. */
 lse_status_t lse_destroy(lse_handle_t h);

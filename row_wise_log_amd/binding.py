@@ -33,7 +33,8 @@ LSE_SPLIT_MAX_PARTS = 64
 
 EXPORTS = ["lse_create", "lse_forward", "lse_forward_dim", "lse_token_logprob", "lse_backward",
            "lse_token_logprob_backward",
-           "lse_destroy", "lse_status_string", "lse_set_schedule", "lse_set_tuning", "lse_plan"]
+           "lse_destroy", "lse_status_string", "lse_set_schedule", "lse_set_tuning", "lse_plan",
+           "lse_forward_noalloc"]
 
 
 class LseError(RuntimeError):
@@ -70,6 +71,7 @@ def load(path: Path | str = LIBRARY) -> ctypes.CDLL:
     sig = {
         "lse_create": (i32, [ctypes.POINTER(vp), ctypes.c_int]),
         "lse_forward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp]),
+        "lse_forward_noalloc": (i32, [vp, i32, i64, i64, i64, vp, vp]),
         "lse_token_logprob": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]),
         "lse_backward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, i64, vp]),
         "lse_token_logprob_backward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, vp]),
@@ -115,6 +117,17 @@ def lse_forward(handle: int, x_ptr: int, dtype: int, rows: int, cols: int, row_s
                 out_ptr: int, stream: int | None = None) -> None:
     _check(load().lse_forward(handle, x_ptr, dtype, rows, cols, row_stride, out_ptr, stream),
            "lse_forward")
+
+
+def lse_forward_noalloc(x_ptr: int, dtype: int, rows: int, cols: int, row_stride: int,
+                        out_ptr: int, stream: int | None = None) -> None:
+    _check(load().lse_forward_noalloc(x_ptr, dtype, rows, cols, row_stride, out_ptr, stream),
+           "lse_forward_noalloc")
+
+
+def lse_forward_noalloc_status(x_ptr, dtype, rows, cols, row_stride, out_ptr, stream=None) -> int:
+    """lse_forward_noalloc returning the raw status instead of raising (for argument tests)."""
+    return load().lse_forward_noalloc(x_ptr, dtype, rows, cols, row_stride, out_ptr, stream)
 
 
 def lse_forward_status(handle, x_ptr, dtype, rows, cols, row_stride, out_ptr, stream=None) -> int:

@@ -344,6 +344,10 @@ lse_status_t lse_create(lse_handle_t* out, int device) {
             h->counters = reinterpret_cast<unsigned*>(static_cast<char*>(mem) + pair_bytes);
             h->dim_pairs = reinterpret_cast<unsigned*>(static_cast<char*>(mem) + pair_bytes +
                                                        count_bytes);
+            // The device's scratch for lse_forward_noalloc is set up here too
+            // when it can be (its entry point retries and reports otherwise).
+            if (lse::noalloc_prepare(device, nullptr, nullptr, nullptr) != LSE_OK)
+                (void)hipGetLastError();
             if (hipMemset(h->counters, 0, count_bytes) != hipSuccess ||
                 hipDeviceSynchronize() != hipSuccess)
                 st = LSE_ERR_HIP;

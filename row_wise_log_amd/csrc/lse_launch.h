@@ -71,6 +71,11 @@ lse_status_t run_forward(const ForwardContext& c, const void* x, lse_dtype_t dty
                          int64_t cols, int64_t row_stride, float* out, const int64_t* targets,
                          float* logp, hipStream_t stream);
 
+// The no-allocation entry point's per-device scratch (lse_noalloc.hip): look
+// up the current device's copy (once) and clear its arrival counters on
+// `stream` unless a launch already did. ptr and n_cu may be NULL.
+lse_status_t noalloc_prepare(int device, hipStream_t stream, unsigned char** ptr, int* n_cu);
+
 // The backward pass, grad_x = grad_out * exp(x - lse) (lse_backward.hip).
 struct GradArgs {
     bool bf16;

@@ -100,6 +100,35 @@ def test_forward_argument_checks(lib, args, status):
 
 
 @pytest.mark.parametrize("args, status", [
+    # (x, dtype, rows, cols, row_stride, out): lse_forward_noalloc checks the
+    # same arguments before any HIP call and needs no handle
+    ((16, 7, 4, 4, 4, 16), B.LSE_ERR_UNSUPPORTED_DTYPE),
+    ((16, F32, -1, 4, 4, 16), B.LSE_ERR_INVALID_ARG),
+    ((16, F32, 4, 1 << 31, 1 << 31, 16), B.LSE_ERR_INVALID_ARG),
+    ((16, F32, 4, 8, 7, 16), B.LSE_ERR_INVALID_ARG),           # stride < cols
+    ((17, BF16, 4, 4, 4, 16), B.LSE_ERR_INVALID_ARG),          # x not 2-byte aligned
+    ((None, F32, 4, 4, 4, 16), B.LSE_ERR_INVALID_ARG),         # NULL x with work
+    ((16, F32, 4, 4, 4, None), B.LSE_ERR_INVALID_ARG),         # NULL out
+    ((16, F32, 4, 4, 4, 18), B.LSE_ERR_INVALID_ARG),           # out not 4-byte aligned
+    ((None, F32, 0, 4, 4, None), B.LSE_OK),                    # rows = 0: nothing to do
+])
+def test_forward_noalloc_argument_checks(lib, args, status):
+    x, dtype, rows, cols, stride, out = args
+    assert B.lse_forward_noalloc_status(x, dtype, rows, cols, stride, out) == status
+
+
+def test_forward_noalloc_without_device_reports_no_device(lib):
+    try:
+        h = B.lse_create(0)
+    except B.LseError:
+        pass
+    else:
+        B.lse_destroy(h)
+        pytest.skip("a GPU is present")
+    assert B.lse_forward_noalloc_status(16, F32, 4, 4, 4, 16) == B.LSE_ERR_NO_DEVICE
+
+
+@pytest.mark.parametrize("args, status", [
     # (x, dtype, rows, cols, row_stride, targets, logp, lse_out) with a NULL handle
     ((16, 7, 4, 4, 4, 64, 16, None), B.LSE_ERR_UNSUPPORTED_DTYPE),
     ((16, F32, -1, 4, 4, 64, 16, None), B.LSE_ERR_INVALID_ARG),
