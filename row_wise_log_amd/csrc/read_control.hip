@@ -32,6 +32,18 @@
 // of the same size: src[0:bytes] copied to dst with the same chunks, loads and
 // pipeline, non-temporal 16-byte stores. src and dst 16-byte aligned and not
 // overlapping; the same return codes.
+//
+//   int lse_control_rows(const void* x, int64_t bytes, int64_t grid, int store,
+//                        unsigned* out, hipStream_t stream)
+//
+// The measuring stick for many 64-byte rows (16 fp32), read with the register-
+// rows schedule's pattern: `grid` workgroups of 256 threads, 4 lanes per row,
+// 4 KiB per wavefront per iteration, grid-stride over iterations. bytes: a
+// multiple of 4096. store != 0 writes the XOR of each row's 16 words to
+// out[row] (bytes / 64 words), one 256-byte store per wavefront per iteration
+// as the LSE kernel writes its results: the read + write control. store == 0
+// writes one word per wavefront (out: grid * 4 words): the read-only control
+// with the same geometry.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -157,6 +169,81 @@ __global__ __launch_bounds__(BLOCK) void copy_chunks(const u32x4* __restrict__ s
         __builtin_nontemporal_store(__builtin_nontemporal_load(src + v0 + i), dst + v0 + i);
 }
 
+// The row control: the memory pattern of the register-rows LSE schedule on
+// 64-byte rows (4 lanes per row, 16 rows per wavefront per round, 4 rounds:
+// 4 KiB per wavefront per iteration, iterations wave, wave + nwaves, ... with
+// the next iteration's loads in flight while one is consumed). Each row's 16
+// words are XORed into one word. With STORE, every iteration writes its 64
+// rows' words to out[row] through LDS, lane l storing row it*64 + l (one
+// 256-byte store per wavefront per iteration, as the LSE kernel writes its
+// results); without, each wavefront writes the XOR of all its rows to
+// out[wave] once at the end. Workgroups of 256 threads.
+template <bool STORE>
+__global__ __launch_bounds__(256) void rows64_chunks(const u32x4* __restrict__ x, int64_t iters,
+                                                      unsigned* __restrict__ out) {
+    __shared__ unsigned stage[4][64];
+    const int lane = threadIdx.x & 63;
+    unsigned* st = stage[threadIdx.x >> 6];
+    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+    const int64_t last = iters - 1;
+    unsigned acc = 0;
+    auto load = [&](u32x4* r, int64_t it) {
+        // an opaque zero computed from acc keeps these loads after the
+        // consumption of the registers they overwrite (as in read_chunks)
+        unsigned z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z) : "v"(acc));
+        const u32x4* q = x + it * 256 + lane + z;  // round k: vectors it*256 + k*64 + lane
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r[k] = __builtin_nontemporal_load(q + k * 64);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto consume = [&](const u32x4* r, int64_t it) {
+        unsigned v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = xor4(r[k]);
+            v[k] ^= __shfl_xor(v[k], 1, 64);
+            v[k] ^= __shfl_xor(v[k], 2, 64);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc ^= v[k];
+        if constexpr (STORE) {
+            // lane 4j of round k holds row k*16 + j of the iteration
+            __builtin_amdgcn_wave_barrier();
+            if ((lane & 3) == 0) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) st[k * 16 + (lane >> 2)] = v[k];
+            }
+            __builtin_amdgcn_wave_barrier();
+            out[it * 64 + lane] = st[lane];
+        }
+    };
+    if (wave <= last) {
+        u32x4 a[4], b[4];
+        int64_t it = wave;
+        load(a, it);
+        while (true) {
+            int64_t next = it + nwaves;
+            load(b, next < last ? next : last);
+            consume(a, it);
+            it = next;
+            if (it > last) break;
+            next = it + nwaves;
+            load(a, next < last ? next : last);
+            consume(b, it);
+            it = next;
+            if (it > last) break;
+        }
+    }
+    if constexpr (!STORE) {
+        // every lane of a row's group holds the same words: XOR across groups
+#pragma unroll
+        for (int off = 4; off < 64; off <<= 1) acc ^= __shfl_xor(acc, off, 64);
+        if (lane == 0) out[wave] = acc;
+    }
+}
+
 template <int BLOCK>
 int launch(const void* x, int64_t nvec, int64_t chunks, unsigned* out, hipStream_t stream) {
     hipLaunchKernelGGL(read_chunks<BLOCK>, dim3(static_cast<unsigned>(chunks)), dim3(BLOCK), 0,
@@ -208,4 +295,19 @@ extern "C" int lse_control_copy(const void* src, void* dst, int64_t bytes, int64
         case 1024: return launch_copy<1024>(src, dst, nvec, chunks, stream);
         default: return 1;
     }
+}
+
+extern "C" int lse_control_rows(const void* x, int64_t bytes, int64_t grid, int store,
+                                unsigned* out, hipStream_t stream) {
+    if (bytes < 0 || bytes % 4096 != 0 || grid < 1 || grid > 0x7FFFFFFF) return 1;
+    if (x == nullptr || out == nullptr || reinterpret_cast<uintptr_t>(x) % 16 != 0) return 1;
+    if (reinterpret_cast<uintptr_t>(out) % 4 != 0) return 1;
+    const int64_t iters = bytes / 4096;
+    if (store)
+        hipLaunchKernelGGL(rows64_chunks<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                           stream, static_cast<const u32x4*>(x), iters, out);
+    else
+        hipLaunchKernelGGL(rows64_chunks<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                           stream, static_cast<const u32x4*>(x), iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
 }

@@ -2,7 +2,10 @@
 
 The read control reads a byte range once, with the streaming LSE schedule's
 loads and pipeline, and keeps only the XOR of each chunk's 32-bit words; the
-copy control reads a range and writes it to another buffer the same way.
+copy control reads a range and writes it to another buffer the same way; the
+row control reads 64-byte rows with the register-rows schedule's pattern and
+optionally writes one word per row (the read + write stick for many short
+rows).
 bench.py times them on the same buffers and launch geometry as an LSE launch
 (read) or a backward launch (copy), which shows how far each kernel sits from
 plainly moving the same bytes on the same device. They are measurement
@@ -32,6 +35,8 @@ def load(path: Path | str = LIBRARY) -> ctypes.CDLL:
     lib.lse_control_read.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp]
     lib.lse_control_copy.restype = ctypes.c_int
     lib.lse_control_copy.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp]
+    lib.lse_control_rows.restype = ctypes.c_int
+    lib.lse_control_rows.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp]
     _lib = lib
     return lib
 
@@ -56,3 +61,15 @@ def lse_control_copy(src: int, dst: int, nbytes: int, chunks: int, block: int, s
                          f"block={block})")
     if rc != 0:
         raise RuntimeError(f"lse_control_copy: launch failed ({rc})")
+
+
+def lse_control_rows(x: int, nbytes: int, grid: int, store: bool, out: int, stream: int) -> None:
+    """Read x[0:nbytes] as 64-byte rows with the register-rows LSE pattern
+    (`grid` workgroups of 256 threads); with store, write each row's XOR to
+    out[row] (nbytes / 64 words), else one XOR per wavefront to out[wave]
+    (grid * 4 words). x 16-byte aligned, nbytes a multiple of 4096."""
+    rc = load().lse_control_rows(x, nbytes, grid, 1 if store else 0, out, stream)
+    if rc == 1:
+        raise ValueError(f"lse_control_rows: invalid argument (bytes={nbytes}, grid={grid})")
+    if rc != 0:
+        raise RuntimeError(f"lse_control_rows: launch failed ({rc})")

@@ -160,3 +160,44 @@ def test_copy_moves_every_byte(torch_gpu, block):
             out = dst.cpu().numpy().view(np.uint32)
             assert np.array_equal(out[guard:guard + 4 * nvec], data), (block, nvec, chunks)
             assert np.all(out[:guard] == 0x5A5A5A5A) and np.all(out[guard + 4 * nvec:] == 0x5A5A5A5A)
+
+
+@pytest.mark.parametrize("args", [
+    dict(nbytes=4095, grid=1),          # not whole 4 KiB iterations
+    dict(nbytes=-4096, grid=1),
+    dict(nbytes=4096, grid=0),
+])
+def test_rows_argument_checks_on_host(args):
+    with pytest.raises(ValueError):
+        RC.lse_control_rows(16, args["nbytes"], args["grid"], True, 16, 0)
+    with pytest.raises(ValueError):
+        RC.lse_control_rows(0, 4096, 1, True, 16, 0)          # NULL x
+    with pytest.raises(ValueError):
+        RC.lse_control_rows(8, 4096, 1, True, 16, 0)          # x not 16-byte aligned
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("iters,grid", [(1, 1), (7, 2), (1000, 3), (4096, 512)])
+def test_rows_control_reads_every_row(torch_gpu, iters, grid):
+    """The row control's per-row XOR (store) and per-wavefront XOR (no store)
+    against numpy: every 64-byte row read, every row's word stored."""
+    torch = torch_gpu
+    rng = np.random.default_rng(iters)
+    words = rng.integers(0, 2 ** 32, size=iters * 1024, dtype=np.uint32)
+    x = torch.from_numpy(words.view(np.int32)).cuda()
+    rows = iters * 64
+    per_row = np.bitwise_xor.reduce(words.reshape(rows, 16), axis=1)
+    out = torch.full((rows,), -1, dtype=torch.int32, device="cuda")
+    RC.lse_control_rows(x.data_ptr(), words.nbytes, grid, True, out.data_ptr(),
+                        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), per_row)
+    nwaves = grid * 4
+    out = torch.full((nwaves,), -1, dtype=torch.int32, device="cuda")
+    RC.lse_control_rows(x.data_ptr(), words.nbytes, grid, False, out.data_ptr(),
+                        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    want = np.zeros(nwaves, dtype=np.uint32)
+    for it in range(iters):  # iteration it (64 rows) belongs to wavefront it % nwaves
+        want[it % nwaves] ^= np.bitwise_xor.reduce(per_row[it * 64:(it + 1) * 64])
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want)
