@@ -240,50 +240,92 @@ __device__ __forceinline__ void fold_tile(const RegTile<D, VPL, VEC, ROUNDS>& t,
 
 // Store one iteration's RW staged results: lane l writes row it*RW + l, so
 // consecutive lanes write consecutive words. `out` may be NULL (TOK only).
-template <int RW, bool FAST, bool TOK>
+template <int RW, bool FAST, bool TOK, bool NT>
 __device__ __forceinline__ void store_stage(const float* stage, const float* stage_lp, int64_t it,
                                             int64_t rows, float* out, float* logp) {
-    __builtin_amdgcn_wave_barrier();
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < (RW + 63) / 64; ++i) {
         const int slot = lane + 64 * i;
         const int64_t r = it * RW + slot;
         if ((RW % 64 == 0 || slot < RW) && (FAST || r < rows)) {
-            if (!TOK || out != nullptr) out[r] = stage[slot];
-            if constexpr (TOK) logp[r] = stage_lp[slot];
+            if constexpr (NT) {
+                if (!TOK || out != nullptr) __builtin_nontemporal_store(stage[slot], out + r);
+                if constexpr (TOK) __builtin_nontemporal_store(stage_lp[slot], logp + r);
+            } else {
+                if (!TOK || out != nullptr) out[r] = stage[slot];
+                if constexpr (TOK) logp[r] = stage_lp[slot];
+            }
         }
     }
-    __builtin_amdgcn_wave_barrier();
 }
+
+// Where a wavefront's iterations hold at least 64 rows (rows of up to 64
+// bytes), the results are not stored iteration by iteration: each
+// wavefront keeps the results of up to F iterations in its LDS slots and
+// stores them together (non-temporal), so the output stream reaches memory
+// in bursts instead of one 256-byte store between every two 4 KiB reads.
+// Measured on fp32 [16777216, 16]: a read + write kernel of this geometry
+// took 186.7 us storing every iteration and 174.4 us flushing 64 iterations
+// at a time (the same reads alone: 154.8 us). F fills 64 KiB of LDS per
+// 256-thread workgroup (two workgroups per CU).
+template <int RW, bool TOK>
+struct Deferral {
+    static constexpr bool kOn = RW >= 64;
+    static constexpr int kF = kOn ? 4096 / (RW * (TOK ? 2 : 1)) : 1;
+};
 
 // The wavefront's loop over iterations wave, wave + nwaves, ...: the next
 // iteration's tile is loaded (into the other buffer) before this one is folded.
+// `stage` (and, with TOK, `stage_lp`) are this wavefront's F * RW LDS slots.
 template <DType D, int G, int VPL, bool VEC, bool TAIL, bool FAST, int ROUNDS, bool TOK>
 __device__ __forceinline__ void fold_rows(const RegRows& rr, float* out, float* logp, int64_t wave,
-                                          int64_t nwaves) {
+                                          int64_t nwaves, float* stage, float* stage_lp) {
     constexpr int RW = (64 / G) * ROUNDS;
-    __shared__ float stage_all[4][RW];                  // per-wavefront output staging (4 per block)
-    __shared__ float stage_lp_all[TOK ? 4 : 1][TOK ? RW : 1];
-    float* stage = stage_all[threadIdx.x >> 6];
-    float* stage_lp = stage_lp_all[TOK ? threadIdx.x >> 6 : 0];
+    constexpr bool DEFER = Deferral<RW, TOK>::kOn;
+    constexpr int F = Deferral<RW, TOK>::kF;
     RegTile<D, VPL, VEC, ROUNDS> ta, tb;
     int64_t it = wave;
     if (it > rr.last_it) return;
+    int slot = 0;             // DEFER: iterations staged so far
+    int64_t first_it = it;    // DEFER: the iteration in slot 0
+    // Store the staged slots: slot j holds iteration first_it + j * nwaves.
+    auto flush = [&]() {
+        __builtin_amdgcn_wave_barrier();
+        for (int j = 0; j < slot; ++j)
+            store_stage<RW, FAST, TOK, true>(stage + j * RW, stage_lp + (TOK ? j * RW : 0),
+                                             first_it + j * nwaves, rr.rows, out, logp);
+        __builtin_amdgcn_wave_barrier();
+        slot = 0;
+    };
+    auto fold_store = [&](const RegTile<D, VPL, VEC, ROUNDS>& t, int64_t cur) {
+        if constexpr (DEFER) {
+            if (slot == 0) first_it = cur;
+            fold_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS, TOK>(t, rr, stage + slot * RW,
+                                                               stage_lp + (TOK ? slot * RW : 0));
+            if (++slot == F) flush();
+        } else {
+            fold_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS, TOK>(t, rr, stage, stage_lp);
+            __builtin_amdgcn_wave_barrier();
+            store_stage<RW, FAST, TOK, false>(stage, stage_lp, cur, rr.rows, out, logp);
+            __builtin_amdgcn_wave_barrier();
+        }
+    };
     load_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS, TOK>(ta, rr, it);
     while (true) {
         int64_t next = it + nwaves;
         load_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS, TOK>(tb, rr, next < rr.last_it ? next : rr.last_it);
-        fold_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS, TOK>(ta, rr, stage, stage_lp);
-        store_stage<RW, FAST, TOK>(stage, stage_lp, it, rr.rows, out, logp);
+        fold_store(ta, it);
         it = next;
         if (it > rr.last_it) break;
         next = it + nwaves;
         load_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS, TOK>(ta, rr, next < rr.last_it ? next : rr.last_it);
-        fold_tile<D, G, VPL, VEC, TAIL, FAST, ROUNDS, TOK>(tb, rr, stage, stage_lp);
-        store_stage<RW, FAST, TOK>(stage, stage_lp, it, rr.rows, out, logp);
+        fold_store(tb, it);
         it = next;
         if (it > rr.last_it) break;
+    }
+    if constexpr (DEFER) {
+        if (slot > 0) flush();
     }
 }
 
@@ -297,6 +339,12 @@ __global__ __launch_bounds__(256) void rows_in_registers(const char* __restrict_
     constexpr int K = VEC ? Elem<D>::kPerVec : 1;
     constexpr int UB = VEC ? 16 : Elem<D>::kBytes;
     constexpr int RW = (64 / G) * ROUNDS;
+    constexpr int F = Deferral<RW, TOK>::kF;
+    // per-wavefront output staging (4 wavefronts per block), F iterations each
+    __shared__ float stage_all[4][F * RW];
+    __shared__ float stage_lp_all[TOK ? 4 : 1][TOK ? F * RW : 1];
+    float* stage = stage_all[threadIdx.x >> 6];
+    float* stage_lp = stage_lp_all[TOK ? threadIdx.x >> 6 : 0];
     const int lane = threadIdx.x & 63;
     const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
     const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
@@ -321,9 +369,11 @@ __global__ __launch_bounds__(256) void rows_in_registers(const char* __restrict_
     rr.tail = static_cast<int>(cols - rr.units * K);
     rr.lane_off = rr.sub * stride_bytes + rr.g * UB;
     if (rr.units == G * VPL && rows % RW == 0)
-        fold_rows<D, G, VPL, VEC, TAIL, true, ROUNDS, TOK>(rr, out, logp, wave, nwaves);
+        fold_rows<D, G, VPL, VEC, TAIL, true, ROUNDS, TOK>(rr, out, logp, wave, nwaves, stage,
+                                                           stage_lp);
     else
-        fold_rows<D, G, VPL, VEC, TAIL, false, ROUNDS, TOK>(rr, out, logp, wave, nwaves);
+        fold_rows<D, G, VPL, VEC, TAIL, false, ROUNDS, TOK>(rr, out, logp, wave, nwaves, stage,
+                                                            stage_lp);
 }
 
 // ---------------------------------------------------------------------------

@@ -40,8 +40,8 @@
 // rows schedule's pattern: `grid` workgroups of 256 threads, 4 lanes per row,
 // 4 KiB per wavefront per iteration, grid-stride over iterations. bytes: a
 // multiple of 4096. store != 0 writes the XOR of each row's 16 words to
-// out[row] (bytes / 64 words), one 256-byte store per wavefront per iteration
-// as the LSE kernel writes its results: the read + write control. store == 0
+// out[row] (bytes / 64 words), staged in LDS and stored 64 iterations at a
+// time as the LSE kernel writes its results: the read + write control. store == 0
 // writes one word per wavefront (out: grid * 4 words): the read-only control
 // with the same geometry.
 #include <hip/hip_runtime.h>
@@ -173,21 +173,34 @@ __global__ __launch_bounds__(BLOCK) void copy_chunks(const u32x4* __restrict__ s
 // 64-byte rows (4 lanes per row, 16 rows per wavefront per round, 4 rounds:
 // 4 KiB per wavefront per iteration, iterations wave, wave + nwaves, ... with
 // the next iteration's loads in flight while one is consumed). Each row's 16
-// words are XORed into one word. With STORE, every iteration writes its 64
-// rows' words to out[row] through LDS, lane l storing row it*64 + l (one
-// 256-byte store per wavefront per iteration, as the LSE kernel writes its
-// results); without, each wavefront writes the XOR of all its rows to
-// out[wave] once at the end. Workgroups of 256 threads.
+// words are XORed into one word. With STORE, the words go out as the LSE
+// kernel writes its results: each wavefront stages 64 iterations' words (64
+// per iteration, row it*64 + l in slot l) in LDS and then stores them with
+// non-temporal 256-byte stores, lane l storing row it*64 + l; without, each
+// wavefront writes the XOR of all its rows to out[wave] once at the end.
+// Workgroups of 256 threads.
+constexpr int kRowsFlush = 64;  // iterations staged per wavefront between stores
+
 template <bool STORE>
 __global__ __launch_bounds__(256) void rows64_chunks(const u32x4* __restrict__ x, int64_t iters,
                                                       unsigned* __restrict__ out) {
-    __shared__ unsigned stage[4][64];
+    __shared__ unsigned stage[4][STORE ? kRowsFlush * 64 : 1];
     const int lane = threadIdx.x & 63;
     unsigned* st = stage[threadIdx.x >> 6];
     const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
     const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
     const int64_t last = iters - 1;
     unsigned acc = 0;
+    int slot = 0;
+    int64_t first_it = wave;
+    auto flush = [&]() {
+        __builtin_amdgcn_wave_barrier();
+        for (int j = 0; j < slot; ++j)
+            __builtin_nontemporal_store(st[j * 64 + lane],
+                                        out + (first_it + static_cast<int64_t>(j) * nwaves) * 64 + lane);
+        __builtin_amdgcn_wave_barrier();
+        slot = 0;
+    };
     auto load = [&](u32x4* r, int64_t it) {
         // an opaque zero computed from acc keeps these loads after the
         // consumption of the registers they overwrite (as in read_chunks)
@@ -205,18 +218,16 @@ __global__ __launch_bounds__(256) void rows64_chunks(const u32x4* __restrict__ x
             v[k] = xor4(r[k]);
             v[k] ^= __shfl_xor(v[k], 1, 64);
             v[k] ^= __shfl_xor(v[k], 2, 64);
+            acc ^= v[k];
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc ^= v[k];
         if constexpr (STORE) {
             // lane 4j of round k holds row k*16 + j of the iteration
-            __builtin_amdgcn_wave_barrier();
+            if (slot == 0) first_it = it;
             if ((lane & 3) == 0) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) st[k * 16 + (lane >> 2)] = v[k];
+                for (int k = 0; k < 4; ++k) st[slot * 64 + k * 16 + (lane >> 2)] = v[k];
             }
-            __builtin_amdgcn_wave_barrier();
-            out[it * 64 + lane] = st[lane];
+            if (++slot == kRowsFlush) flush();
         }
     };
     if (wave <= last) {
@@ -235,6 +246,7 @@ __global__ __launch_bounds__(256) void rows64_chunks(const u32x4* __restrict__ x
             it = next;
             if (it > last) break;
         }
+        if (STORE && slot > 0) flush();
     }
     if constexpr (!STORE) {
         // every lane of a row's group holds the same words: XOR across groups
