@@ -1,6 +1,6 @@
 """Benchmark of the row-wise log-sum-exp on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--only]
 
 One step is one lse_forward call over the whole workload: every row's
 log-sum-exp in one pass. The headline workload is bf16 [512, 128256] (the
@@ -14,8 +14,16 @@ Prints ONE JSON line with the metric, the per-launch roofline of the kernel
 against the 8 TB/s HBM peak), the same-bytes read-only control kernel timed
 the same way with the same launch geometry (roofline.read_control: how fast
 this device reads those bytes when nothing else is done with them), and the
-float64 CPU oracle's rate on the same workload as a baseline. --all also times the other four workloads and writes
-their lines to --all-out.
+float64 CPU oracle's rate on the same workload as a baseline. For the forward
+LSE the line also carries the other four workloads (`configs`), each timed
+the same way beside its own control and checked against the oracle on every
+row; --only leaves them out.
+
+Before a workload's W warmup steps the GPU is brought to its steady state by
+at least 50 ms of the control kernel's launches on the same input (which are
+also the control's own timing): on a GPU that was idle, launch times move for
+the first ~20 ms of continuous work, and a run with few warmup steps would
+otherwise time that transient.
 """
 from __future__ import annotations
 
@@ -44,8 +52,10 @@ METRIC_TOKEN_BACKWARD = ("token log-prob backward input GB/s (x, int64 targets, 
 HBM_PEAK_GBS = 8000.0
 CACHE_BYTES = 256 << 20
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.txt"
+# What decides the bytes a launch moves: the kernels and the planner that picks
+# the kernel instance and its grid.
 KERNEL_SOURCES = [ROOT / "row_wise_log_amd" / "csrc" / n
-                  for n in ("lse_kernels.hip", "lse_device.h")]
+                  for n in ("lse_kernels.hip", "lse_device.h", "lse_api.cpp", "lse_launch.h")]
 
 
 def log(msg: str) -> None:
@@ -84,44 +94,54 @@ def plan_name(plan: dict) -> str:
     return f"{s}(block={plan['block']},unroll={plan['unroll']},parts={plan['parts']},grid={plan['grid']})"
 
 
-def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int | None,
-                op: str = "lse", graph: bool = False, w=None):
+def time_config(torch, B, handle, cfg: int, steps: int, warmup: int | None, rotate: int | None,
+                op: str = "lse", graph: bool = False, w=None, extras: bool = True):
+    """Time K steps of `op` on workload cfg after W warmup steps, with the
+    control kernel of the same bytes timed first (its launches also bring the
+    GPU to its steady state). extras: also the median of single calls and the
+    graph-replayed figure."""
     w = w if w is not None else workloads.make(cfg)
     rows, cols = w.rows, w.cols
     esize = 2 if w.dtype == "bf16" else 4
     in_bytes = rows * cols * esize
     out_bytes = rows * 4
-    targets = None
-    bwd = None
-    if op in ("backward", "logprob_backward"):
-        # the forward value comes from the float64 oracle (rounded to fp32), so
-        # the check of the timed output never feeds the GPU's own results back
-        import oracle
-        lse32 = oracle.lse(w.x, w.dtype, threads=len(os.sched_getaffinity(0))).astype(np.float32)
-        g = np.random.default_rng(7).normal(0, 1, size=rows).astype(np.float32)
-        bwd = {"lse": torch.from_numpy(lse32).to("cuda"), "g": torch.from_numpy(g).to("cuda"),
-               "grad": torch.empty(rows * cols, dtype=torch.int16 if w.dtype == "bf16"
-                                   else torch.float32, device="cuda"),
-               "lse_host": lse32, "g_host": g}
-        out_bytes += rows * cols * esize  # grad_x
-        in_bytes += rows * 8              # lse and grad_out
-        if op == "logprob_backward":
-            bwd["targets_host"] = workloads.targets(cfg)
-            bwd["targets"] = torch.from_numpy(bwd["targets_host"]).to("cuda")
-            in_bytes += rows * 8          # int64 targets
-    if op == "logprob":
-        targets = torch.from_numpy(workloads.targets(cfg)).to("cuda")
-        in_bytes += rows * 8  # one int64 target per row
     dtype_code = B.LSE_DTYPE_BF16 if w.dtype == "bf16" else B.LSE_DTYPE_F32
     if rotate is None:
         rotate = max(1, -(-2 * CACHE_BYTES // in_bytes) + 1)
     host = torch.from_numpy(w.x.view(np.int16) if w.dtype == "bf16" else w.x)
     bufs = [host.to("cuda") for _ in range(rotate)]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    targets = None
+    bwd = None
+    if op == "logprob":
+        targets = torch.from_numpy(workloads.targets(cfg)).to("cuda")
+        in_bytes += rows * 8  # one int64 target per row
+    if op in ("backward", "logprob_backward"):
+        # the forward value comes from the library's own forward pass on the
+        # device (untimed), as in a training step; the oracle only checks
+        lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+        g = np.random.default_rng(7).normal(0, 1, size=rows).astype(np.float32)
+        bwd = {"lse": lse, "g": torch.from_numpy(g).to("cuda"),
+               "grad": torch.empty(rows * cols, dtype=torch.int16 if w.dtype == "bf16"
+                                   else torch.float32, device="cuda"),
+               "g_host": g}
+        if op == "logprob_backward":
+            bwd["targets_host"] = workloads.targets(cfg)
+            bwd["targets"] = torch.from_numpy(bwd["targets_host"]).to("cuda")
+            logp = torch.empty(rows, dtype=torch.float32, device="cuda")
+            B.lse_token_logprob(handle, bufs[0].data_ptr(), dtype_code, rows, cols, cols,
+                                bwd["targets"].data_ptr(), logp.data_ptr(), lse.data_ptr(), sh)
+            in_bytes += rows * 8          # int64 targets
+        else:
+            B.lse_forward(handle, bufs[0].data_ptr(), dtype_code, rows, cols, cols, lse.data_ptr(), sh)
+        torch.cuda.synchronize()
+        bwd["lse_host"] = lse.cpu().numpy()
+        out_bytes += rows * cols * esize  # grad_x
+        in_bytes += rows * 8              # lse and grad_out
     out = torch.empty(cols if op == "dim" else rows, dtype=torch.float32, device="cuda")
     if op == "dim":
         out_bytes = cols * 4
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
     plan = B.lse_plan(dtype_code, rows, cols, cols, bufs[0].data_ptr(), 256, 0)
 
     def step(i, sh=sh):
@@ -143,6 +163,23 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
         else:
             B.lse_token_logprob(handle, bufs[i % rotate].data_ptr(), dtype_code, rows, cols, cols,
                                 targets.data_ptr(), out.data_ptr(), None, sh)
+
+    # The control first: at least PREHEAT_SECONDS of its launches (untimed),
+    # then K timed ones; the LSE's warmup steps follow at once.
+    nbytes = rows * cols * esize
+    extra_controls = {}
+    if op in ("lse", "logprob", "dim"):
+        control = time_read_control(torch, bufs, nbytes, plan, steps, stream)
+        if op == "lse" and plan["schedule"] == B.LSE_SCHED_ROWS_PER_WAVE and cols == 16 \
+                and nbytes % 4096 == 0 and plan["lanes_per_row"] == 4:
+            # many 64-byte rows: the same geometry with and without one word
+            # written per row (the read + write stick the output stream needs)
+            for store in (True, False):
+                key = "read_write_control" if store else "read_control_same_geometry"
+                extra_controls[key] = time_rows_control(torch, bufs, nbytes, int(plan["grid"]),
+                                                        store, steps, stream)
+    else:
+        control = time_copy_control(torch, bufs, nbytes, steps, stream)
 
     warmup = run_warmup(torch, step, warmup, stream)
     # The timed region: K back-to-back launches between a synchronize on each
@@ -180,22 +217,19 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int, rotate: int
     del g
 
     ms_step = wall / steps * 1e3
-    median_us = median_single_call_us(torch, step, warmup + steps, stream)
-    graph_us = graph_us_per_call(torch, step, warmup + steps + 60)
-    control = None
-    if op in ("lse", "logprob", "dim"):
-        control = time_read_control(torch, bufs, rows * cols * esize, plan, steps, warmup, stream)
-        control["frac_of_read_control"] = round(control["launch_us_mean"] / (mean_launch * 1e3), 4)
-    else:
-        control = time_copy_control(torch, bufs, rows * cols * esize, steps, warmup, stream)
-        control["frac_of_copy_control"] = round(control["launch_us_mean"] / (mean_launch * 1e3), 4)
+    median_us = median_single_call_us(torch, step, warmup + steps, stream) if extras else None
+    graph_us = graph_us_per_call(torch, step, warmup + steps + 60) if extras else None
+    key = "frac_of_read_control" if op in ("lse", "logprob", "dim") else "frac_of_copy_control"
+    control[key] = round(control["launch_us_mean"] / (mean_launch * 1e3), 4)
+    for c in extra_controls.values():
+        c["frac_of_control"] = round(c["launch_us_mean"] / (mean_launch * 1e3), 4)
     return {
         "w": w, "plan": plan, "rotate": rotate, "in_bytes": in_bytes, "out_bytes": out_bytes,
         "ms_per_step": ms_step, "launch_ms_mean": mean_launch,
         "value_gbs": in_bytes / (ms_step * 1e-3) / 1e9,
         "achieved_gbs": (in_bytes + out_bytes) / (mean_launch * 1e-3) / 1e9,
-        "out": out, "op": op, "bwd": bwd, "control": control, "median_us": median_us,
-        "graph_us": graph_us, "warmup": warmup,
+        "out": out, "op": op, "bwd": bwd, "control": control, "extra_controls": extra_controls,
+        "median_us": median_us, "graph_us": graph_us, "warmup": warmup,
     }
 
 
@@ -283,13 +317,28 @@ def median_single_call_us(torch, step, first: int, stream, calls: int = 60, skip
     return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs[skip:]]))
 
 
-def time_read_control(torch, bufs, nbytes: int, plan: dict, steps: int, warmup: int,
-                      stream) -> dict:
+PREHEAT_SECONDS = 0.05
+
+
+def time_control(torch, step, steps: int, stream) -> float:
+    """Untimed launches of a control `step` for at least PREHEAT_SECONDS of
+    back-to-back GPU work (the GPU's steady state, and the control's own
+    warmup), then the mean microseconds per launch of K timed ones."""
+    for i in range(5):
+        step(i)
+    per = max(event_mean_us(torch, step, 5, 5, stream) * 1e-6, 1e-6)
+    n = int(np.ceil(PREHEAT_SECONDS / per))
+    for i in range(10, 10 + n):
+        step(i)
+    return event_mean_us(torch, step, 10 + n, steps, stream)
+
+
+def time_read_control(torch, bufs, nbytes: int, plan: dict, steps: int, stream) -> dict:
     """The read-only control kernel over the same input copies, in the same
     rotation, with the LSE plan's workgroup count and size: one XOR per chunk
     of the input, so the time is that of reading the bytes and nothing else.
     Timed like the LSE launches (one event pair around K back-to-back
-    launches)."""
+    launches), after at least PREHEAT_SECONDS of its launches."""
     from row_wise_log_amd import read_control as RC
     grid, block = int(plan["grid"]), int(plan["block"])
     out = torch.empty(grid, dtype=torch.int32, device="cuda")
@@ -298,14 +347,35 @@ def time_read_control(torch, bufs, nbytes: int, plan: dict, steps: int, warmup: 
     def step(i):
         RC.lse_control_read(bufs[i % len(bufs)].data_ptr(), nbytes, grid, block, out.data_ptr(), sh)
 
-    for i in range(warmup):
-        step(i)
-    us = event_mean_us(torch, step, warmup, steps, stream)
+    us = time_control(torch, step, steps, stream)
     return {"kernel": "read_chunks (XOR of each chunk's words)", "grid": grid, "block": block,
             "launch_us_mean": round(us, 2), "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
-def time_copy_control(torch, bufs, nbytes: int, steps: int, warmup: int, stream) -> dict:
+def time_rows_control(torch, bufs, nbytes: int, grid: int, store: bool, steps: int,
+                      stream) -> dict:
+    """The row control on 64-byte rows with the register-rows LSE launch's
+    grid: reads every row with that kernel's pattern and, with store, writes
+    one 4-byte word per row with the same stores (staged in LDS, 64
+    iterations at a time): the bytes the LSE launch moves, with no
+    arithmetic."""
+    from row_wise_log_amd import read_control as RC
+    rows = nbytes // 64
+    out = torch.empty(rows if store else grid * 4, dtype=torch.int32, device="cuda")
+    sh = stream.cuda_stream
+
+    def step(i):
+        RC.lse_control_rows(bufs[i % len(bufs)].data_ptr(), nbytes, grid, store, out.data_ptr(), sh)
+
+    us = time_control(torch, step, steps, stream)
+    moved = nbytes + (rows * 4 if store else 0)
+    return {"kernel": "rows64_chunks (XOR of each 64-byte row" +
+                      (", one word stored per row)" if store else ", no stores)"),
+            "grid": grid, "block": 256, "launch_us_mean": round(us, 2),
+            "GBs": round(moved / (us * 1e-6) / 1e9, 1)}
+
+
+def time_copy_control(torch, bufs, nbytes: int, steps: int, stream) -> dict:
     """The copy control kernel from the same input copies, in the same
     rotation, into a buffer of grad_x's size (its own, so the backward's
     output stays for the oracle check): x's bytes read and written once, one
@@ -319,9 +389,7 @@ def time_copy_control(torch, bufs, nbytes: int, steps: int, warmup: int, stream)
     def step(i):
         RC.lse_control_copy(bufs[i % len(bufs)].data_ptr(), dst.data_ptr(), nbytes, grid, block, sh)
 
-    for i in range(warmup):
-        step(i)
-    us = event_mean_us(torch, step, warmup, steps, stream)
+    us = time_control(torch, step, steps, stream)
     del dst
     return {"kernel": "copy_chunks (x copied to a buffer of grad_x's size)", "grid": grid, "block": block,
             "launch_us_mean": round(us, 2), "GBs_read_plus_written": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
@@ -340,7 +408,7 @@ def sweep_read_control(torch, cfg: int, steps: int, warmup: int) -> list:
     for grid in (256, 512, 1024, 2048, 4096, 8192, 16384):
         for block in (256, 512, 1024):
             c = time_read_control(torch, bufs, nbytes, {"grid": grid, "block": block}, steps,
-                                  warmup, stream)
+                                  stream)
             rec = {"control_sweep": cfg, "grid": grid, "block": block,
                    "launch_us_mean": c["launch_us_mean"], "GBs": c["GBs"]}
             log(json.dumps(rec))
@@ -487,10 +555,13 @@ def cpu_baseline_backward(w, r, seconds: float = 10.0) -> dict:
             t_ = t_ + (2.0 ** -8 + 1e-6) * (np.abs(np.where(np.isfinite(ref), ref, 0.0)) + t_)
         tol = t_[fin]
     err = np.abs(got[fin] - ref[fin]) / tol
+    exact = bool(np.array_equal(got[~fin], ref[~fin], equal_nan=True))
     log(f"GPU gradient vs oracle ({n} rows): max |err|/tol = {err.max(initial=0):.3f}, "
-        f"non-finite match {np.array_equal(got[~fin], ref[~fin], equal_nan=True)}")
+        f"non-finite match {exact}")
     return {"value": round(x.nbytes * passes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
+            "gpu_check": {"max_err_over_tol": round(float(err.max(initial=0)), 4),
+                          "nonfinite_exact": exact, "rows_checked": int(n)},
             "sample": (f"the first {n} of {w.rows} rows ({x.nbytes} input bytes), {passes} passes "
                        f"in {el:.1f} s wall on {threads} threads (float64 "
                        + ("g * exp(x - lse)" if tg is None else "g * ([j == t] - exp(x - lse))")
@@ -564,6 +635,76 @@ def check_gpu_output(w, gpu_out: np.ndarray, reference: tuple) -> None:
         scale = np.maximum(scale, np.abs(lse[fin]))
     err = np.abs(gpu_out[fin] - ref[fin]) / (tol * scale)
     log(f"GPU output vs oracle: max |err|/tol = {err.max(initial=0):.3f}, non-finite match {exact}")
+    return {"max_err_over_tol": round(float(err.max(initial=0)), 4), "nonfinite_exact": bool(exact),
+            "rows_checked": int(len(ref))}
+
+
+def oracle_reference(w, op: str = "lse") -> tuple:
+    """The float64 oracle over every row of the workload, on all host cores
+    (the checker of the timed steps' output; not timed as a baseline)."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    return oracle.lse(w.x, w.dtype, threads=threads), None
+
+
+def torch_context(torch, w, steps: int) -> dict:
+    """The pages' own comparison on this input: torch.logsumexp and torch.sum
+    over the last axis of the same device tensor (the paper's section 1 sets
+    one against the other; its Figure 1 profiles the former's sub-kernels at
+    this shape), mean microseconds per call over K calls cycling through
+    copies larger than the Infinity Cache. Context only: never on the
+    library's path."""
+    host = torch.from_numpy(w.x.view(np.int16))
+    nb = w.x.nbytes
+    rotate = max(1, -(-2 * CACHE_BYTES // nb) + 1)
+    bufs = [host.to("cuda").view(torch.bfloat16) if w.dtype == "bf16" else host.to("cuda")
+            for _ in range(rotate)]
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in (("torch.logsumexp", lambda t: torch.logsumexp(t, dim=1)),
+                     ("torch.sum", lambda t: torch.sum(t, dim=1))):
+        def call(i, fn=fn):
+            fn(bufs[i % rotate])
+        for i in range(10):
+            call(i)
+        res[name + "_us"] = round(event_mean_us(torch, call, 10, max(steps, 20), stream), 2)
+    del bufs
+    res["note"] = (f"on the same {w.dtype} device tensor, dim=1, torch {torch.__version__}; "
+                   "the pages report 1.95 ms against 0.31 ms on another GPU (context only)")
+    return res
+
+
+def versions(torch) -> dict:
+    rocm = "unknown"
+    try:
+        rocm = Path("/opt/rocm/.info/version").read_text().strip()
+    except OSError:
+        pass
+    return {"numpy": np.__version__, "torch": torch.__version__,
+            "hip": getattr(torch.version, "hip", None), "rocm": rocm}
+
+
+def config_record(r: dict, check: dict | None, traffic: float | None) -> dict:
+    """The compact record of one forward workload for the `configs` key."""
+    w = r["w"]
+    us = r["launch_ms_mean"] * 1e3
+    rec = {"workload": f"config{w.spec.cfg} {w.spec.name}: {w.spec.recipe}",
+           "rows": w.rows, "cols": w.cols, "input_dtype": w.dtype,
+           "plan": plan_name(r["plan"]),
+           "us_per_launch": round(us, 2),
+           "us_per_call_wall": round(r["ms_per_step"] * 1e3, 2),
+           "input_GBs_wall": round(r["value_gbs"], 1),
+           "rows_per_s": round(w.rows / (r["ms_per_step"] * 1e-3), 1),
+           "algorithmic_bytes_per_launch": r["in_bytes"] + r["out_bytes"],
+           "achieved_GBs": round(r["achieved_gbs"], 1),
+           "frac_of_hbm_peak": round(r["achieved_gbs"] / HBM_PEAK_GBS, 4),
+           "traffic": traffic,
+           "read_control": r["control"],
+           "warmup": r["warmup"]}
+    rec.update(r["extra_controls"])
+    if check is not None:
+        rec.update(check)
+    return rec
 
 
 def main() -> int:
@@ -572,20 +713,27 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warmup steps (default: at least 40 steps and at least 50 ms of "
-                         "back-to-back GPU work, so that the timed steps run at the steady state)")
+                         "back-to-back GPU work); the control kernel's launches run before them")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--rotate", type=int, default=None,
                     help="input copies cycled through (default: enough to exceed 2x the 256 MiB cache)")
-    ap.add_argument("--all", action="store_true", help="also time the other four workloads")
-    ap.add_argument("--all-out", default="bench_all.jsonl")
+    ap.add_argument("--only", action="store_true",
+                    help="time only the --config workload (the forward LSE line otherwise also "
+                         "carries the other four workloads under `configs`)")
+    ap.add_argument("--no-small-shapes", action="store_true",
+                    help="leave out the few-row shapes of the headline input (counter runs that "
+                         "select the headline kernel by name)")
+    ap.add_argument("--no-torch-context", action="store_true",
+                    help="leave out torch.logsumexp / torch.sum on the headline tensor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--op", choices=["lse", "logprob", "backward", "logprob_backward", "dim"],
                     default="lse",
                     help="lse: lse_forward (the headline); logprob: lse_token_logprob with one "
                          "seeded int64 target per row; backward: lse_backward (reads x, writes "
-                         "grad_x); logprob_backward: lse_token_logprob_backward (the same, with "
-                         "the targets); dim: lse_forward_dim over the workload's first axis")
+                         "grad_x) on the forward pass's own LSE; logprob_backward: "
+                         "lse_token_logprob_backward (the same, with the targets); dim: "
+                         "lse_forward_dim over the workload's first axis")
     ap.add_argument("--graph", action="store_true",
                     help="capture the K timed steps into one HIP graph and time one replay of it "
                          "(the same K full calls on the same rotating inputs; default: K eager "
@@ -640,7 +788,7 @@ def main() -> int:
         floor = launch_floor_us(torch, B, handle)
         log(f"launch floor (lse_forward on one element, back to back): {floor:.2f} us per call")
         small = small_out = None
-        if args.op == "lse" and args.config == 2 and not args.graph:
+        if args.op == "lse" and args.config == 2 and not args.graph and not args.no_small_shapes:
             small, small_out = small_shapes_us(torch, B, handle, w)
             log(f"few-row shapes: {small}")
         line = {
@@ -672,6 +820,9 @@ def main() -> int:
                 "graph_us_per_call": round(r["graph_us"], 2),
                 "timed_as": "one HIP graph replay of the K steps" if args.graph
                             else "K eager launches",
+                "preheat": "at least 50 ms of the control kernel's launches on the same input "
+                           "right before the warmup steps",
+                "input_sha256": workloads.sha256(w.x),
             },
             "roofline": {
                 "bound": "hbm",
@@ -685,47 +836,26 @@ def main() -> int:
                 "algorithmic_bytes_per_launch": r["in_bytes"] + r["out_bytes"],
                 ("read_control" if args.op in ("lse", "logprob", "dim") else "copy_control"):
                     r["control"],
+                **r["extra_controls"],
             },
+            "versions": versions(torch),
         }
+        if args.op == "lse" and args.config == 2 and not args.no_torch_context:
+            ctx = torch_context(torch, w, args.steps)
+            ctx["speedup_of_lse_forward_over_torch_logsumexp"] = round(
+                ctx["torch.logsumexp_us"] / (r["launch_ms_mean"] * 1e3), 2)
+            line["torch_context"] = ctx
+            log(f"torch context: {ctx}")
         if args.control_sweep:
             sweep_read_control(torch, args.config, args.steps, r["warmup"])
-        if args.all:
-            Path(args.all_out).parent.mkdir(parents=True, exist_ok=True)
-            with open(args.all_out, "w") as f:
-                for cfg in [1, 2, 3, 4, 5]:
-                    log(f"timing config {cfg}")
-                    rc = r if cfg == args.config else time_config(
-                        torch, B, handle, cfg, args.steps, args.warmup, None, args.op, args.graph)
-                    rec = {"config": cfg, "op": args.op, "workload": rc["w"].spec.name,
-                           "plan": plan_name(rc["plan"]) if args.op in ("lse", "logprob")
-                           else f"lse_{args.op}",
-                           "input_GBs": round(rc["value_gbs"], 1),
-                           "pct_hbm_peak": round(100 * rc["value_gbs"] / HBM_PEAK_GBS, 2),
-                           "us_per_call": round(rc["ms_per_step"] * 1e3, 2),
-                           "launch_us_mean": round(rc["launch_ms_mean"] * 1e3, 2),
-                           "launch_us_median_single_calls": round(rc["median_us"], 2),
-                           "graph_us_per_call": round(rc["graph_us"], 2),
-                           "achieved_GBs_per_launch": round(rc["achieved_gbs"], 1),
-                           "rows_per_s": round(rc["w"].rows / (rc["ms_per_step"] * 1e-3), 1),
-                           "launch_floor_us": round(floor, 2)}
-                    if "frac_of_read_control" in rc["control"]:
-                        rec["read_control_us"] = rc["control"]["launch_us_mean"]
-                        rec["frac_of_read_control"] = rc["control"]["frac_of_read_control"]
-                    else:
-                        rec["copy_control_us"] = rc["control"]["launch_us_mean"]
-                        rec["frac_of_copy_control"] = rc["control"]["frac_of_copy_control"]
-                    if args.op == "lse" and rc["in_bytes"] <= CACHE_BYTES // 4:
-                        rec["us_per_call_warm"] = round(warm_us_per_call(torch, B, handle, cfg), 2)
-                    log(json.dumps(rec))
-                    f.write(json.dumps(rec) + "\n")
-                    if cfg != args.config:
-                        del rc
         if early:
-            check_gpu_output(w, r["out"].cpu().numpy().astype(np.float64), reference)
+            chk = check_gpu_output(w, r["out"].cpu().numpy().astype(np.float64), reference)
+            line.update(chk)
             if small_out:  # the few-row shapes are the headline input's first rows
                 for rows, got in small_out.items():
                     log(f"first {rows} rows:")
-                    check_gpu_output(w, got, (reference[0][:rows], None))
+                    small[f"bf16 [{rows}, {w.cols}]"].update(
+                        check_gpu_output(w, got, (reference[0][:rows], None)))
             line["cpu_baseline"] = cpu_rec
         elif not args.no_cpu_baseline:
             log("timing the float64 oracle on the host cores")
@@ -734,6 +864,26 @@ def main() -> int:
             line["cpu_baseline"] = None
         if small is not None:
             line["small_shapes"] = small
+        del r
+        if args.op == "lse" and not args.only:
+            # The other four workloads: each timed the same way (its control
+            # first, then W warmup and K timed steps) and checked on every row.
+            others = {}
+            for cfg in [c for c in (1, 2, 3, 4, 5) if c != args.config]:
+                wc = workloads.make(cfg)
+                log(f"timing config {cfg}")
+                rc = time_config(torch, B, handle, cfg, args.steps, args.warmup, None, "lse",
+                                 args.graph, w=wc, extras=False)
+                ref = oracle_reference(wc)
+                chk = check_gpu_output(wc, rc["out"].cpu().numpy().astype(np.float64), ref)
+                rec = config_record(rc, chk, recorded_traffic(cfg))
+                if cfg == 1:
+                    rec["us_per_call_warm"] = round(warm_us_per_call(torch, B, handle, cfg), 2)
+                log(json.dumps(rec))
+                others[str(cfg)] = rec
+                del rc, wc, ref
+                torch.cuda.empty_cache()
+            line["configs"] = others
         print(json.dumps(line), flush=True)
     finally:
         torch.cuda.synchronize()

@@ -53,11 +53,16 @@ def check_common(d: dict, steps: int) -> None:
 
 def test_default_workload_line():
     """The headline workload (bf16 [512, 128256]) with a short timed region,
-    the float64 oracle's baseline included."""
-    d = run_bench("--steps", "50", "--warmup", "10", "--cpu-seconds", "1")
-    check_common(d, 50)
+    the float64 oracle's baseline included, and the other four workloads,
+    each checked on every row against the oracle."""
+    d = run_bench("--steps", "20", "--warmup", "5", "--cpu-seconds", "1")
+    check_common(d, 20)
     assert d["config"]["rows"] == 512 and d["config"]["cols"] == 128256
     assert d["config"]["input_dtype"] == "bf16" and d["dtype"] == "f32"
+    assert len(d["config"]["input_sha256"]) == 64
+    assert {"numpy", "torch", "hip", "rocm"} <= set(d["versions"])
+    assert d["max_err_over_tol"] <= 1.0 and d["nonfinite_exact"] is True
+    assert d["rows_checked"] == 512
     ctl = d["roofline"]["read_control"]
     assert ctl["launch_us_mean"] > 0 and 0 < ctl["frac_of_read_control"] < 2
     cb = d["cpu_baseline"]
@@ -68,12 +73,28 @@ def test_default_workload_line():
     assert set(small) == {"bf16 [1, 128256]", "bf16 [8, 128256]", "bf16 [32, 128256]"}
     for rec in small.values():
         assert 0 < rec["us_per_call"] < 1000 and rec["plan"].startswith("split_row")
+        assert rec["max_err_over_tol"] <= 1.0
+    ctx = d["torch_context"]
+    assert ctx["torch.logsumexp_us"] > 0 and ctx["torch.sum_us"] > 0
+    # the other four workloads, every row checked
+    assert set(d["configs"]) == {"1", "3", "4", "5"}
+    sizes = {"1": (64, 32000), "3": (4096, 262144), "4": (65536, 4096), "5": (1 << 24, 16)}
+    for k, rec in d["configs"].items():
+        assert (rec["rows"], rec["cols"]) == sizes[k]
+        assert rec["rows_checked"] == rec["rows"]
+        assert rec["max_err_over_tol"] <= 1.0 and rec["nonfinite_exact"] is True
+        assert rec["us_per_launch"] > 0 and rec["read_control"]["launch_us_mean"] > 0
+        assert rec["frac_of_hbm_peak"] == pytest.approx(
+            rec["algorithmic_bytes_per_launch"] / (rec["us_per_launch"] * 1e-6) / 8e12, rel=5e-3)
+    rw = d["configs"]["5"]["read_write_control"]
+    assert rw["launch_us_mean"] > 0 and 0 < rw["frac_of_control"] < 2
+    assert d["configs"]["5"]["read_control_same_geometry"]["launch_us_mean"] > 0
 
 
 @pytest.mark.parametrize("args", [["--config", "1", "--graph"], ["--config", "1", "--op", "backward"],
                                   ["--config", "1", "--op", "logprob"], ["--config", "1", "--op", "dim"]])
 def test_other_modes(args):
-    d = run_bench(*args, "--steps", "30", "--warmup", "5", "--no-cpu-baseline")
+    d = run_bench(*args, "--steps", "30", "--warmup", "5", "--no-cpu-baseline", "--only")
     check_common(d, 30)
     assert d["cpu_baseline"] is None
     r = d["roofline"]
