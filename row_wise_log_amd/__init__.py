@@ -11,28 +11,110 @@ memory and the current stream; the computation is the HIP library's
 ``lse_token_logprob`` / ``lse_token_logprob_backward`` (see include/lse.h);
 ``token_logprob_autograd(x, t)`` is the token log-probability with its
 gradient. The library is loaded on first use
-and a missing library is an error, never a fallback.
+and a missing library is an error, never a fallback. The helpers keep one
+library handle per (device, stream); ``prepare(stream)`` makes it ahead of a
+HIP graph capture on that stream (none can be made during one), and
+``release()`` frees handles.
 """
 from __future__ import annotations
 
-from .binding import (LseError, lse_create, lse_destroy, lse_forward, lse_plan,  # noqa: F401
-                      lse_set_schedule, lse_set_tuning, lse_status_string, lse_token_logprob,
-                      load)
+from collections import OrderedDict
 
-_handles: dict[tuple[int, int], int] = {}
+from .binding import (LseError, lse_create, lse_destroy, lse_forward,  # noqa: F401
+                      lse_forward_noalloc, lse_plan, lse_set_schedule, lse_set_tuning,
+                      lse_status_string, lse_token_logprob, load)
+
+# Library handles of the torch helpers, one per (device, stream): a handle's
+# split workspace must not serve two streams at once, and calls on one stream
+# are ordered, so they can share one. Handles are created outside graph
+# capture only (lse_create allocates and synchronises). At most
+# MAX_HANDLES_PER_DEVICE unpinned handles are kept per device, the least
+# recently used one released beyond that (after a device synchronisation);
+# handles made by prepare(), or used while a stream was being captured (a
+# captured graph keeps their workspace addresses), are pinned and live until
+# release().
+MAX_HANDLES_PER_DEVICE = 8
+_handles: OrderedDict[tuple[int, int], int] = OrderedDict()
+_pinned: set[tuple[int, int]] = set()
+
+
+def _capturing() -> bool:
+    import torch
+
+    return torch.cuda.is_current_stream_capturing()
+
+
+def _evict(device: int) -> None:
+    import torch
+
+    loose = [k for k in _handles if k[0] == device and k not in _pinned]
+    if len(loose) < MAX_HANDLES_PER_DEVICE:
+        return
+    torch.cuda.synchronize(device)  # no work may still use the handle
+    for key in loose[:len(loose) - MAX_HANDLES_PER_DEVICE + 1]:
+        lse_destroy(_handles.pop(key))
 
 
 def handle(device: int, stream: int = 0) -> int:
-    """A library handle for `device` and the stream handle `stream`, created
-    once per process. A handle's workspace (split rows, split non-last-axis
-    tiles) must not serve two streams at once, so each stream gets its own;
-    calls on one stream are ordered, so they can share one."""
+    """The library handle for `device` and the stream handle `stream`. Made
+    on first use, outside graph capture; under capture a stream with no
+    handle yet is an error (call prepare() for it before capturing)."""
     key = (device, int(stream))
     h = _handles.get(key)
+    capturing = _capturing()
     if h is None:
+        if capturing:
+            raise RuntimeError(
+                "row_wise_log_amd: no library handle for this stream, and one cannot be made "
+                "while the stream is being captured (lse_create allocates and synchronises); "
+                "call row_wise_log_amd.prepare(stream) before the capture")
+        _evict(device)
         h = lse_create(device)
         _handles[key] = h
+    else:
+        _handles.move_to_end(key)
+    if capturing:
+        _pinned.add(key)
     return h
+
+
+def prepare(stream=None, device: int | None = None) -> int:
+    """Make (outside graph capture) and pin the handle that the helpers use
+    on `stream` (a torch.cuda.Stream or a raw stream handle; default the
+    current stream of `device`, default the current device). Call it before
+    capturing helpers into a HIP graph on that stream. Returns the handle."""
+    import torch
+
+    if _capturing():
+        raise RuntimeError("row_wise_log_amd.prepare() must run outside graph capture")
+    if device is None:
+        device = stream.device.index if isinstance(stream, torch.cuda.Stream) else \
+            torch.cuda.current_device()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    raw = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+    h = handle(device, raw)
+    _pinned.add((device, raw))
+    return h
+
+
+def release(stream=None, device: int | None = None) -> None:
+    """Release the helpers' handles (pinned ones included): the one of
+    `stream` if given, else every handle of `device`, else all. Synchronises
+    the devices concerned first; graphs captured with those handles must not
+    be replayed afterwards."""
+    import torch
+
+    if stream is not None:
+        raw = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+        keys = [k for k in _handles if k[1] == raw and (device is None or k[0] == device)]
+    else:
+        keys = [k for k in _handles if device is None or k[0] == device]
+    for d in sorted({k[0] for k in keys}):
+        torch.cuda.synchronize(d)
+    for k in keys:
+        _pinned.discard(k)
+        lse_destroy(_handles.pop(k))
 
 
 def _device_stream(x) -> tuple[int, int]:

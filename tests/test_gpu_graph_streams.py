@@ -192,3 +192,71 @@ def test_package_calls_on_two_streams(torch_gpu):
         torch.cuda.synchronize()
         for k, (g, w) in enumerate(zip(got, want)):
             assert np.array_equal(_bits(torch, g), w), (rep, k)
+
+
+def test_package_helpers_captured_on_a_fresh_stream(torch_gpu):
+    """The torch-level helpers inside torch.cuda.graph on a new stream: with
+    no handle prepared for it, the helper raises a clear error before any HIP
+    call (a handle cannot be made while capturing); after prepare(stream) the
+    captured logsumexp / token_logprob / logsumexp_autograd forward replay
+    correctly, four times, with new inputs written eagerly in between."""
+    torch = torch_gpu
+    import row_wise_log_amd as lib
+    rng = np.random.default_rng(5)
+    x = torch.empty(24, 90_000, device="cuda")                       # split rows (fp32)
+    xb = torch.empty(600, 128256, dtype=torch.bfloat16, device="cuda")  # a workgroup per row
+    t = torch.from_numpy(rng.integers(0, 128256, size=600)).to("cuda")
+    lib.logsumexp(torch.zeros(2, 8, device="cuda"))  # code objects loaded eagerly elsewhere
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    note("package helpers: capture without prepare must raise")
+    g0 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g0, stream=s):
+        with pytest.raises(RuntimeError, match="prepare"):
+            lib.logsumexp(x)
+        _ = x.sum(dim=1)  # the capture ends with ordinary work in it
+    del g0
+    lib.prepare(s)
+    g = torch.cuda.CUDAGraph()
+    note("package helpers: capture after prepare")
+    with torch.cuda.graph(g, stream=s):
+        out_a = lib.logsumexp(x)
+        lp, lse_b = lib.token_logprob(xb, t, return_lse=True)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        va = rng.normal(0, 3, size=(24, 90_000)).astype(np.float32)
+        vb = rng.normal(0, 2, size=(600, 128256)).astype(np.float32)
+        x.copy_(torch.from_numpy(va))
+        xb.copy_(torch.from_numpy(vb).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        bits = xb.view(torch.int16).cpu().numpy().view(np.uint16)
+        compare(out_a.cpu().numpy(), oracle_mod.lse(va, "f32", threads=8), "f32",
+                f"captured logsumexp replay {rep}")
+        ref_b = oracle_mod.lse(bits, "bf16", threads=8)
+        compare(lse_b.cpu().numpy(), ref_b, "bf16", f"captured token_logprob lse replay {rep}")
+        ref_lp = oracle_mod.token_logprob(bits, t.cpu().numpy(), "bf16", threads=8)
+        got_lp = lp.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got_lp - ref_lp) <= 1e-5 * np.maximum(1.0, np.abs(ref_b))), rep
+    del g
+    lib.release(s)
+
+
+def test_package_handle_cache_is_bounded(torch_gpu):
+    """Eager helper calls on more streams than the cache keeps: at most
+    MAX_HANDLES_PER_DEVICE unpinned handles stay per device, and every call
+    still computes the right result."""
+    torch = torch_gpu
+    import row_wise_log_amd as lib
+    x = torch.full((3, 1000), 2.0, device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(lib.MAX_HANDLES_PER_DEVICE + 4)]
+    for st in streams:
+        with torch.cuda.stream(st):
+            out = lib.logsumexp(x)
+        st.synchronize()
+        assert np.allclose(out.cpu().numpy(), 2.0 + np.log(1000.0), rtol=2e-6)
+        loose = [k for k in lib._handles if k[0] == 0 and k not in lib._pinned]
+        assert len(loose) <= lib.MAX_HANDLES_PER_DEVICE
+    for st in streams:
+        lib.release(st)
