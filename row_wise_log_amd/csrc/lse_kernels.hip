@@ -533,12 +533,19 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
     Merged b = block_merge<BLOCK>(a.m, a.c, acc_sum(a), pairs);
 
     if constexpr (SPLIT) {
-        // Publish this part's pair, then count the part in. The pair is
-        // written with agent-scope (sc1) stores, which are coherent across
-        // the XCDs' L2s; waiting for them to complete before the counter add
-        // orders them before it. The last part to arrive reads the pairs
-        // with agent-scope loads after its add returns. No L2-wide writeback
-        // or invalidate is needed, as every access involved is agent-scope.
+        // Publish this part's pair, then count the part in. What this relies
+        // on is the gfx942/gfx950 memory model for agent scope: atomic loads
+        // and stores at agent scope are issued with the sc1 bit and access
+        // the point of coherence of all the device's L2s, and atomic
+        // read-modify-writes at agent scope are coherent across them; a
+        // wave's s_waitcnt vmcnt(0) completes its earlier stores before any
+        // later memory instruction issues. So the pair (sc1 stores) is at the
+        // point of coherence before the counter add is performed, and the
+        // last part, whose sc1 loads issue only after its add has returned
+        // (the barrier below orders them after it), reads every part's pair.
+        // This is the release / acquire sequence the compiler emits at agent
+        // scope minus the L2 writeback and invalidate, which only non-atomic
+        // accesses need (none is used for the pairs).
         if (tid == 0) {
             unsigned* slot = ws_pairs + 2 * (row * nparts + part);
             __hip_atomic_store(slot, __float_as_uint(b.m), __ATOMIC_RELAXED,
