@@ -16,7 +16,8 @@ log-probability's backward pass g[r] * ([j == t_r] - exp(x[r, j] - lse[r]));
 ``lse_dim(x3, dtype)`` reduces the middle axis of an [outer, n, inner] array
 (torch.logsumexp over a non-last axis) by moving that axis last and calling
 the row oracle.
-bf16 inputs are passed as uint16 bit patterns.
+bf16 inputs are passed as uint16 bit patterns; fp16 inputs as float16 arrays or
+their uint16 bit patterns with dtype "f16".
 """
 from __future__ import annotations
 
@@ -31,7 +32,7 @@ HERE = Path(__file__).resolve().parent
 SOURCE = HERE / "lse_oracle.c"
 LIBRARY = HERE / "liblse_oracle.so"
 
-DTYPES = {"f32": 0, "bf16": 1}
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
 
 
 def build(source: Path = SOURCE, output: Path = LIBRARY) -> Path:
@@ -118,8 +119,10 @@ class Oracle:
     def _prepare(x: np.ndarray, dtype: str | None):
         x = np.asarray(x)
         if dtype is None:
-            dtype = "bf16" if x.dtype == np.uint16 else "f32"
-        want = np.uint16 if dtype == "bf16" else np.float32
+            dtype = {np.dtype(np.uint16): "bf16", np.dtype(np.float16): "f16"}.get(x.dtype, "f32")
+        if dtype == "f16" and x.dtype == np.float16:
+            x = x.view(np.uint16)  # fp16 is passed as its bit patterns
+        want = np.float32 if dtype == "f32" else np.uint16
         if x.dtype != want:
             raise TypeError(f"dtype {dtype} needs a {np.dtype(want)} array, got {x.dtype}")
         if x.ndim != 2:
@@ -148,22 +151,11 @@ class Oracle:
     def lse(self, x: np.ndarray, dtype: str | None = None, threads: int = 1) -> np.ndarray:
         """Row-wise LSE of a 2-D array in float64.
 
-        ``x`` is float32 (dtype "f32") or uint16 bf16 bits (dtype "bf16"). Any
-        row stride is accepted as long as the last axis is contiguous.
+        ``x`` is float32 (dtype "f32"), uint16 bf16 bits (dtype "bf16"), or
+        float16 / uint16 fp16 bits (dtype "f16"; a float16 array implies it).
+        Any row stride is accepted as long as the last axis is contiguous.
         """
-        x = np.asarray(x)
-        if dtype is None:
-            dtype = "bf16" if x.dtype == np.uint16 else "f32"
-        want = np.uint16 if dtype == "bf16" else np.float32
-        if x.dtype != want:
-            raise TypeError(f"dtype {dtype} needs a {np.dtype(want)} array, got {x.dtype}")
-        if x.ndim != 2:
-            raise ValueError("x must be 2-D")
-        rows, cols = x.shape
-        if (cols > 1 and x.strides[1] != x.itemsize) or \
-                (rows > 1 and (x.strides[0] < cols * x.itemsize or x.strides[0] % x.itemsize)):
-            x = np.ascontiguousarray(x)
-        stride = x.strides[0] // x.itemsize if rows > 1 else cols
+        x, dtype, rows, cols, stride = self._prepare(x, dtype)
         out = np.full(rows, np.nan, dtype=np.float64)  # rows left unwritten stay NaN
         rc = self._fn(x.ctypes.data if x.size else None, DTYPES[dtype], rows, cols,
                       stride, out.ctypes.data, int(threads))

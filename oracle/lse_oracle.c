@@ -23,7 +23,12 @@
  *     m = max_j x_j,   s = sum_j exp(x_j - m)  (in ascending j),
  *     out = m + log(s).
  * Elements are widened exactly to double: fp32 directly, bf16 by placing its
- * 16 bits in the high half of an fp32 word. Nothing is flushed to zero.
+ * 16 bits in the high half of an fp32 word, fp16 (IEEE binary16) from its
+ * fields (sign, 5-bit exponent with bias 15, 10-bit fraction; exponent 0
+ * is zero or subnormal, fraction * 2^-24; exponent 31 is inf or NaN).
+ * Nothing is flushed to zero. The 16-bit inputs follow the paper's
+ * reduced-bit FuseLSE16 (§4.3, Figure 5), read as FuseLSE over 16-bit data;
+ * the arithmetic here stays float64.
  *
  * Special cases (the paper lists edge-case handling in its Table 3 without
  * the cells; these follow torch.logsumexp, which it replaces as a drop-in):
@@ -66,7 +71,23 @@
 #include <stdint.h>
 #include <string.h>
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2 };
+
+/* IEEE binary16 bits to double, from the format's definition. */
+static double half_to_double(uint16_t h)
+{
+    const int sign = h >> 15;
+    const int e = (h >> 10) & 0x1F;
+    const int frac = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)frac, -24);                   /* zero, subnormal */
+    else if (e == 31)
+        v = frac ? NAN : INFINITY;                      /* inf, NaN */
+    else
+        v = ldexp((double)(1024 + frac), e - 25);       /* (1 + frac/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
 
 /* Exact widening of the element at `index` (in elements from x) to double. */
 static double load_elem(const void *x, int dtype, int64_t index)
@@ -75,6 +96,10 @@ static double load_elem(const void *x, int dtype, int64_t index)
         float f;
         memcpy(&f, (const char *)x + 4 * index, 4);
         return (double)f;
+    } else if (dtype == ORACLE_F16) {
+        uint16_t h;
+        memcpy(&h, (const char *)x + 2 * index, 2);
+        return half_to_double(h);
     } else {
         uint16_t h;
         uint32_t w;
@@ -188,7 +213,7 @@ static int run_all(const void *x, int dtype, int64_t rows, int64_t cols, int64_t
     int64_t per;
     int t, started = 0;
 
-    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16)
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F16)
         return -1;
     if (rows < 0 || cols < 0 || (rows > 1 && row_stride < cols))
         return -1;

@@ -40,6 +40,11 @@ def _bf16_value(bits: int) -> float:
     return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
 
 
+def _f16_value(bits: int) -> float:
+    """Decode an IEEE half bit pattern with struct's binary16 format."""
+    return struct.unpack("<e", struct.pack("<H", int(bits) & 0xFFFF))[0]
+
+
 def brute_lse(values) -> float:
     """log(sum exp(v)) by exact summation; only for |v| small enough not to overflow."""
     vals = [float(v) for v in values]
@@ -157,6 +162,68 @@ def pin_special_values(orc):
     _close(got[3], 1.0 + LN2, 1e-15, "bf16 [1, 1]")
 
 
+# --- fp16 inputs (the 16-bit reading of the paper's FuseLSE16, §4.3) ----------
+
+def pin_f16_every_pattern(orc):
+    """All 65536 fp16 bit patterns as one-element rows: the LSE of a single
+    element is the element, so every decoded value is checked exactly against
+    struct's binary16 decoding (NaN patterns give NaN, +-inf themselves)."""
+    bits = np.arange(1 << 16, dtype=np.uint16).reshape(-1, 1)
+    got = orc.lse(bits, "f16")
+    for b in range(1 << 16):
+        want = _f16_value(b)
+        if math.isnan(want):
+            assert math.isnan(got[b]), f"f16 pattern {b:#06x}: want NaN, got {got[b]!r}"
+        else:
+            assert got[b] == want, f"f16 pattern {b:#06x}: want {want!r}, got {got[b]!r}"
+
+
+def pin_f16_rows(orc):
+    """fp16 rows (strided, random finite patterns with |x| <= 50, and special
+    rows) against log(fsum(exp)) of struct-decoded values; constant rows
+    c + ln N; and the token log-probability and softmax gradient of fp16 rows
+    against the same brute force."""
+    rng = np.random.default_rng(21)
+    for cols in (1, 3, 8, 17, 64):
+        for stride in (cols, cols + 5):
+            bits = rng.integers(0, 1 << 16, size=(6, stride), dtype=np.uint32).astype(np.uint16)
+            vals = [[_f16_value(b) for b in row] for row in bits]
+            for r in range(bits.shape[0]):
+                for j in range(stride):
+                    if not math.isfinite(vals[r][j]) or abs(vals[r][j]) > 50:
+                        bits[r, j] = 0x3C00 if j % 2 else 0xCD00  # 1.0 or -20.0
+            view = bits[:, :cols]
+            got = orc.lse(view, "f16")
+            for r in range(view.shape[0]):
+                want = brute_lse([_f16_value(b) for b in view[r]])
+                _close(got[r], want, 1e-14, f"f16 brute cols={cols} r={r}")
+            t = rng.integers(0, cols, size=view.shape[0])
+            got = orc.token_logprob(view, t, "f16")
+            for r in range(view.shape[0]):
+                v = [_f16_value(b) for b in view[r]]
+                bl = brute_lse(v)
+                _close(got[r], v[t[r]] - bl, 1e-14 * max(1.0, abs(bl)) / max(1.0, abs(v[t[r]] - bl)),
+                       f"f16 logprob cols={cols} r={r}")
+    for c, h in ((1.0, 0x3C00), (-20.0, 0xCD00), (65504.0, 0x7BFF), (2.0 ** -24, 0x0001)):
+        for n in (1, 7, 1000):
+            row = np.full((1, n), h, dtype=np.uint16)
+            _close(orc.lse(row, "f16")[0], c + math.log(n), 4e-16, f"f16 const c={c} N={n}")
+    # specials: 0x7C00 = +inf, 0xFC00 = -inf, 0x7E00 = NaN
+    b = np.array([[0xFC00, 0xFC00], [0x7C00, 0x3C00], [0x7E00, 0x3C00], [0x3C00, 0x3C00]],
+                 dtype=np.uint16)
+    got = orc.lse(b, "f16")
+    assert got[0] == -np.inf and got[1] == np.inf and np.isnan(got[2]), f"f16 specials {got}"
+    _close(got[3], 1.0 + LN2, 1e-15, "f16 [1, 1]")
+    # the softmax gradient of fp16 rows: exp(x - lse) with struct-decoded x
+    bits = np.array([[0x3C00, 0xBC00, 0x4000, 0x0000, 0x0001]], dtype=np.uint16)
+    v = [_f16_value(b) for b in bits[0]]
+    lse32 = np.array([brute_lse(v)], dtype=np.float32)
+    got = orc.softmax_grad(bits, lse32, np.array([2.0], np.float32), "f16")
+    for j in range(5):
+        want = 2.0 * math.exp(v[j] - float(lse32[0]))
+        assert abs(got[0, j] - want) <= 1e-15 * max(1.0, want), f"f16 grad j={j}"
+
+
 # --- invariants --------------------------------------------------------------
 
 def pin_shift_invariance(orc):
@@ -207,7 +274,7 @@ def pin_thread_count_invariance(orc):
 def pin_argument_checks(orc):
     out = np.empty(4)
     x = np.zeros((4, 4), np.float32)
-    assert orc.raw(x.ctypes.data, 2, 4, 4, 4, out.ctypes.data) == -1, "bad dtype accepted"
+    assert orc.raw(x.ctypes.data, 3, 4, 4, 4, out.ctypes.data) == -1, "bad dtype accepted"
     assert orc.raw(x.ctypes.data, 0, -1, 4, 4, out.ctypes.data) == -1, "rows < 0 accepted"
     assert orc.raw(x.ctypes.data, 0, 4, -1, 4, out.ctypes.data) == -1, "cols < 0 accepted"
     assert orc.raw(x.ctypes.data, 0, 4, 4, 3, out.ctypes.data) == -1, "stride < cols accepted"
@@ -571,4 +638,6 @@ CHEAP_PINS = [
     pin_grad_constant_rows,
     pin_grad_brute_force_bf16,
     pin_grad_special_values,
+    pin_f16_every_pattern,
+    pin_f16_rows,
 ]

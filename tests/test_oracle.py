@@ -251,3 +251,24 @@ def test_oracle_matches_decimal_arithmetic_bf16(oracle, bits):
             assert got[i] == want
         else:
             assert abs(got[i] - want) <= 1e-13 * max(1.0, abs(want)), (bits[i], got[i], want)
+
+
+@settings(max_examples=200, deadline=None)
+@given(bits=st.lists(st.lists(st.integers(0, 0xFFFF).filter(
+    lambda b: (b & 0x7C00) != 0x7C00 or b == 0xFC00), min_size=1, max_size=40),
+    min_size=1, max_size=4))
+def test_oracle_matches_decimal_arithmetic_f16(oracle, bits):
+    """Every finite fp16 pattern (and -inf), decoded by numpy's float16, against
+    the decimal reference."""
+    width = max(len(r) for r in bits)
+    x = np.full((len(bits), width), 0xFC00, dtype=np.uint16)
+    for i, r in enumerate(bits):
+        x[i, :len(r)] = r
+    got = oracle.lse(x, "f16")
+    vals = x.view(np.float16).astype(np.float64)
+    for i in range(len(bits)):
+        want = decimal_lse([float(v) for v in vals[i]])
+        if math.isinf(want):
+            assert got[i] == want
+        else:
+            assert abs(got[i] - want) <= 1e-13 * max(1.0, abs(want)), (bits[i], got[i], want)

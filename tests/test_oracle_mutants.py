@@ -24,6 +24,13 @@ MUTANTS = {
     "min_not_max": ("if (v > m)", "if (v < m)"),
     "bf16_shift_15": ("w = (uint32_t)h << 16;", "w = (uint32_t)h << 15;"),
     "bf16_low_half": ("w = (uint32_t)h << 16;", "w = (uint32_t)h;"),
+    "f16_bias_14": ("v = ldexp((double)(1024 + frac), e - 25);",
+                    "v = ldexp((double)(1024 + frac), e - 24);"),
+    "f16_no_implicit_one": ("v = ldexp((double)(1024 + frac), e - 25);",
+                            "v = ldexp((double)frac, e - 25);"),
+    "f16_subnormal_scale": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
+    "f16_sign_dropped": ("return sign ? -v : v;", "return (sign && 0) ? -v : v;"),
+    "f16_decoded_as_bf16": ("} else if (dtype == ORACLE_F16) {", "} else if (dtype == -1) {"),
     "f32_wrong_width": ("(const char *)x + 4 * index", "(const char *)x + 2 * index"),
     "row_start_uses_cols": ("jb->out[r] = lse_one_row(jb->x, jb->dtype, r * jb->row_stride",
                             "jb->out[r] = lse_one_row(jb->x, jb->dtype, r * jb->cols"),
