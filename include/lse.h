@@ -48,11 +48,15 @@ extern "C" {
 
 typedef struct lse_handle_s *lse_handle_t;
 
-/* Element type of x. bf16 is decoded exactly (its 16 bits become the high
- * half of an fp32 word) and accumulated in fp32, like fp32 input. */
+/* Element type of x. The 16-bit types are decoded exactly to fp32 (bf16's
+ * 16 bits become the high half of an fp32 word; every IEEE half value,
+ * subnormals included, is an fp32 value) and accumulated in fp32, like fp32
+ * input. A 16-bit input halves the bytes read, the lever behind the paper's
+ * reduced-bit FuseLSE16 (§4.3, Figure 5); the arithmetic stays fp32. */
 typedef enum {
     LSE_DTYPE_F32 = 0,
-    LSE_DTYPE_BF16 = 1
+    LSE_DTYPE_BF16 = 1,
+    LSE_DTYPE_F16 = 2
 } lse_dtype_t;
 
 typedef enum {
@@ -96,10 +100,10 @@ lse_status_t lse_create(lse_handle_t *out, int device);
  * (NULL means the null stream of the handle's device): the paper's fused
  * single-pass LSE (§3.1) over the last axis (§2.1), special values as above.
  * Accuracy: |out[r] - LSE| <= 2e-6 * max(1, |LSE|) for fp32 input and
- * 1e-5 * max(1, |LSE|) for bf16 input, against the exact LSE of the decoded
- * elements; the paper reports FuseLSE's error against FP64 in §4.1.
+ * 1e-5 * max(1, |LSE|) for bf16 and fp16 input, against the exact LSE of the
+ * decoded elements; the paper reports FuseLSE's error against FP64 in §4.1.
  *   x          device pointer to element (0, 0); aligned to its element size.
- *   dtype      LSE_DTYPE_F32 or LSE_DTYPE_BF16.
+ *   dtype      LSE_DTYPE_F32, LSE_DTYPE_BF16 or LSE_DTYPE_F16.
  *   rows       >= 0; rows == 0 is a no-op (x and out may be NULL).
  *   cols       >= 0, < 2^31; cols == 0 writes -inf to every out[r].
  *   row_stride elements between consecutive row starts; >= cols when
@@ -152,7 +156,8 @@ lse_status_t lse_token_logprob(lse_handle_t h, const void *x, lse_dtype_t dtype,
  * the row's softmax scaled by the incoming gradient; backward support is
  * one of the properties the paper tabulates for its kernels (Table 3). One
  * streaming pass: x is read once and grad_x written once, in x's element
- * type (bf16 results are rounded to nearest even from fp32 arithmetic).
+ * type (bf16 and fp16 results are rounded to nearest even from fp32
+ * arithmetic).
  *   x, dtype, rows, cols, row_stride   as for lse_forward.
  *   lse        device pointer to rows fp32 values, normally lse_forward's
  *              output for the same x (any values are accepted: the formula is

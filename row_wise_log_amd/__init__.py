@@ -1,7 +1,7 @@
 """Row-wise log-sum-exp on MI355X (gfx950): a C-ABI HIP library and its binding.
 
-``logsumexp(x)`` returns log(sum(exp(x), dim=-1)) in fp32 for a 2-D fp32 or
-bf16 CUDA/HIP tensor whose last axis is contiguous; ``logsumexp_autograd(x)``
+``logsumexp(x)`` returns log(sum(exp(x), dim=-1)) in fp32 for a 2-D fp32,
+bf16 or fp16 CUDA/HIP tensor whose last axis is contiguous; ``logsumexp_autograd(x)``
 is the same value with a gradient (the library's backward pass, grad_out *
 exp(x - lse), in x's dtype); ``logsumexp_dim(x, d)`` reduces any axis of a
 contiguous tensor; ``token_logprob(x, t)`` returns x[r, t[r]] -
@@ -123,18 +123,23 @@ def _device_stream(x) -> tuple[int, int]:
     return x.device.index or 0, torch.cuda.current_stream(x.device).cuda_stream
 
 
+def _dtype_codes(torch) -> dict:
+    from .binding import LSE_DTYPE_BF16, LSE_DTYPE_F16, LSE_DTYPE_F32
+
+    return {torch.float32: LSE_DTYPE_F32, torch.bfloat16: LSE_DTYPE_BF16,
+            torch.float16: LSE_DTYPE_F16}
+
+
 def _check_input(x):
     import torch
-
-    from .binding import LSE_DTYPE_BF16, LSE_DTYPE_F32
 
     if x.dim() != 2:
         raise ValueError("x must be 2-D (rows, cols)")
     if not x.is_cuda:
         raise ValueError("x must be a GPU tensor")
-    codes = {torch.float32: LSE_DTYPE_F32, torch.bfloat16: LSE_DTYPE_BF16}
+    codes = _dtype_codes(torch)
     if x.dtype not in codes:
-        raise TypeError(f"unsupported dtype {x.dtype}: fp32 or bf16")
+        raise TypeError(f"unsupported dtype {x.dtype}: fp32, bf16 or fp16")
     rows, cols = x.shape
     if cols > 1 and x.stride(1) != 1:
         raise ValueError("the last axis must be contiguous")
@@ -142,13 +147,13 @@ def _check_input(x):
 
 
 def logsumexp_dim(x, dim, keepdim: bool = False, handle_=None):
-    """LSE over axis `dim` of a contiguous fp32/bf16 GPU tensor of any rank, as
+    """LSE over axis `dim` of a contiguous fp32/bf16/fp16 GPU tensor of any rank, as
     fp32 (torch.logsumexp(x, dim, keepdim) semantics). `dim` may also be a
     tuple of adjacent axes, which a contiguous tensor holds as one axis; other
     tuples raise NotImplementedError."""
     import torch
 
-    from .binding import LSE_DTYPE_BF16, LSE_DTYPE_F32, lse_forward_dim
+    from .binding import lse_forward_dim
 
     if x.dim() == 0:
         raise ValueError("x must have at least one axis")
@@ -164,9 +169,9 @@ def logsumexp_dim(x, dim, keepdim: bool = False, handle_=None):
         raise ValueError(f"dim {tuple(raw)} names an axis more than once")
     if dims != list(range(dims[0], dims[-1] + 1)):
         raise NotImplementedError("the reduced axes must be adjacent")
-    codes = {torch.float32: LSE_DTYPE_F32, torch.bfloat16: LSE_DTYPE_BF16}
+    codes = _dtype_codes(torch)
     if x.dtype not in codes:
-        raise TypeError(f"unsupported dtype {x.dtype}: fp32 or bf16")
+        raise TypeError(f"unsupported dtype {x.dtype}: fp32, bf16 or fp16")
     if not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous GPU tensor")
     d0, d1 = dims[0], dims[-1]
@@ -189,7 +194,7 @@ def logsumexp_dim(x, dim, keepdim: bool = False, handle_=None):
 
 
 def logsumexp(x, out=None, handle_=None):
-    """LSE over the last axis of a 2-D fp32/bf16 GPU tensor, as fp32[rows]."""
+    """LSE over the last axis of a 2-D fp32/bf16/fp16 GPU tensor, as fp32[rows]."""
     import torch
 
     code, rows, cols, stride = _check_input(x)
@@ -204,7 +209,7 @@ def logsumexp(x, out=None, handle_=None):
 
 
 def token_logprob(x, targets, return_lse=False, handle_=None):
-    """x[r, targets[r]] - LSE(x[r, :]) for a 2-D fp32/bf16 GPU tensor and an
+    """x[r, targets[r]] - LSE(x[r, :]) for a 2-D fp32/bf16/fp16 GPU tensor and an
     int64 GPU tensor of rows targets, as fp32[rows] (and the LSE, if asked).
     A target outside [0, cols) gives NaN."""
     import torch
@@ -256,7 +261,7 @@ _LSE_FN = None
 
 
 def logsumexp_autograd(x):
-    """LSE over the last axis of a 2-D fp32/bf16 GPU tensor, as fp32[rows],
+    """LSE over the last axis of a 2-D fp32/bf16/fp16 GPU tensor, as fp32[rows],
     differentiable: the gradient with respect to x is grad_out[r] *
     exp(x[r, j] - lse[r]) (the row's softmax scaled by the incoming gradient),
     computed by the library's lse_backward and returned in x's dtype."""
@@ -310,7 +315,7 @@ _TOK_FN = None
 
 
 def token_logprob_autograd(x, targets):
-    """x[r, targets[r]] - LSE(x[r, :]) for a 2-D fp32/bf16 GPU tensor, as
+    """x[r, targets[r]] - LSE(x[r, :]) for a 2-D fp32/bf16/fp16 GPU tensor, as
     fp32[rows], differentiable with respect to x: the gradient is
     grad_logp[r] * ([j == t] - exp(x[r, j] - lse[r])), computed by the
     library's lse_token_logprob_backward in x's dtype (NaN rows for targets

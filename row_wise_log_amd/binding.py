@@ -14,6 +14,7 @@ LIBRARY = Path(__file__).resolve().parent / "liblse_amd.so"
 
 LSE_DTYPE_F32 = 0
 LSE_DTYPE_BF16 = 1
+LSE_DTYPE_F16 = 2
 
 LSE_OK = 0
 LSE_ERR_INVALID_ARG = 1

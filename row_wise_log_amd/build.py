@@ -21,8 +21,9 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIBRARY = PKG / "liblse_amd.so"
-SOURCES = [CSRC / "lse_kernels.hip", CSRC / "lse_backward.hip", CSRC / "lse_dim.hip",
-           CSRC / "lse_noalloc.hip", CSRC / "lse_api.cpp"]
+SOURCES = [CSRC / "lse_kernels_f32.hip", CSRC / "lse_kernels_bf16.hip",
+           CSRC / "lse_kernels_f16.hip", CSRC / "lse_kernels.hip", CSRC / "lse_backward.hip",
+           CSRC / "lse_dim.hip", CSRC / "lse_noalloc.hip", CSRC / "lse_api.cpp"]
 ARCH = "gfx950"
 # The read-only control kernel that bench.py times beside the LSE kernels; its
 # own library, so nothing on the LSE path can reach it.

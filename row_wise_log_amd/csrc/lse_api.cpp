@@ -67,6 +67,12 @@ constexpr int kDimGroups = 32;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+bool valid_dtype(lse_dtype_t d) {
+    return d == LSE_DTYPE_F32 || d == LSE_DTYPE_BF16 || d == LSE_DTYPE_F16;
+}
+
+int elem_bytes(lse_dtype_t d) { return d == LSE_DTYPE_F32 ? 4 : 2; }
+
 int pow2_at_least(int64_t v) {
     int p = 1;
     while (p < v) p <<= 1;
@@ -87,11 +93,11 @@ bool regs_instance(int g, int vpl, bool vec) {
 
 lse_status_t check_sizes(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t row_stride,
                          uint64_t x_addr) {
-    if (dtype != LSE_DTYPE_F32 && dtype != LSE_DTYPE_BF16) return LSE_ERR_UNSUPPORTED_DTYPE;
+    if (!valid_dtype(dtype)) return LSE_ERR_UNSUPPORTED_DTYPE;
     if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return LSE_ERR_INVALID_ARG;
     if (rows > 1 && (row_stride < cols || row_stride > (INT64_MAX / 4) / rows))
         return LSE_ERR_INVALID_ARG;
-    const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
+    const int esize = elem_bytes(dtype);
     if (rows > 0 && cols > 0 && x_addr % esize != 0) return LSE_ERR_INVALID_ARG;
     return LSE_OK;
 }
@@ -101,7 +107,7 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
     std::memset(p, 0, sizeof(*p));
     if (rows == 0) return LSE_OK;
 
-    const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
+    const int esize = elem_bytes(dtype);
     const int k = 16 / esize;
     const int64_t stride_bytes = (rows > 1 ? row_stride : cols) * esize;
     const bool aligned16 = x_addr % 16 == 0 && (rows == 1 || stride_bytes % 16 == 0);
@@ -182,7 +188,7 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
         if (rows <= 2 * cu) {
             block = (rows * 8 >= 7 * cu && rows * 8 < 15 * cu) ? 256 : 512;
         } else {
-            const int64_t per = nvec / (dtype == LSE_DTYPE_BF16 ? 8 : 4);
+            const int64_t per = nvec / (16 / esize);
             block = 64;
             while (block < 256 && 2 * block <= per) block *= 2;
         }
@@ -236,7 +242,7 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
 lse_status_t make_grad_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t row_stride,
                             int64_t grad_row_stride, uint64_t x_addr, uint64_t g_addr, int n_cu,
                             lse::GradArgs* a) {
-    const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
+    const int esize = elem_bytes(dtype);
     const int k = 16 / esize;
     const int64_t xs = (rows > 1 ? row_stride : cols) * esize;
     const int64_t gs = (rows > 1 ? grad_row_stride : cols) * esize;
@@ -248,7 +254,7 @@ lse_status_t make_grad_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64
     const int64_t units = aligned ? cols / k : peel ? (cols - (k - 1)) / k : cols;
     const int64_t ub = vec ? 16 : esize;
     constexpr int64_t kBatch = 256 * 4;
-    a->bf16 = dtype == LSE_DTYPE_BF16;
+    a->dtype = dtype;
     a->vector_units = vec;
     a->peel = peel;
     a->rows = rows;
@@ -428,10 +434,10 @@ lse_status_t run_forward(const ForwardContext& c, const void* x, lse_dtype_t dty
             return LSE_ERR_INVALID_ARG;
     }
 
-    const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
+    const int esize = elem_bytes(dtype);
     LaunchArgs a{};
     a.schedule = p.schedule;
-    a.bf16 = dtype == LSE_DTYPE_BF16;
+    a.dtype = dtype;
     a.block = p.block;
     a.grid = p.grid;
     a.vector_loads = p.vector_loads != 0;
@@ -534,7 +540,7 @@ lse_status_t run_backward(lse_handle_t h, const void* x, lse_dtype_t dtype, int6
     const uint64_t x_addr = reinterpret_cast<uint64_t>(x);
     lse_status_t st = check_sizes(dtype, rows, cols, row_stride, x_addr);
     if (st != LSE_OK) return st;
-    const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
+    const int esize = elem_bytes(dtype);
     if (rows > 1 && (grad_row_stride < cols || grad_row_stride > (INT64_MAX / 4) / rows))
         return LSE_ERR_INVALID_ARG;
     if (rows == 0 || cols == 0) return h == nullptr ? LSE_ERR_INVALID_ARG : LSE_OK;
@@ -589,8 +595,8 @@ lse_status_t lse_token_logprob_backward(lse_handle_t h, const void* x, lse_dtype
 
 lse_status_t lse_forward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t outer,
                              int64_t n, int64_t inner, float* out, hipStream_t stream) {
-    if (dtype != LSE_DTYPE_F32 && dtype != LSE_DTYPE_BF16) return LSE_ERR_UNSUPPORTED_DTYPE;
-    const int esize = dtype == LSE_DTYPE_BF16 ? 2 : 4;
+    if (!valid_dtype(dtype)) return LSE_ERR_UNSUPPORTED_DTYPE;
+    const int esize = elem_bytes(dtype);
     if (outer < 0 || n < 0 || inner < 0 || n > kMaxDim) return LSE_ERR_INVALID_ARG;
     constexpr int64_t kMaxOut = int64_t{1} << 40;
     if (inner > 0 && outer > kMaxOut / inner) return LSE_ERR_INVALID_ARG;
@@ -607,7 +613,7 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, i
     const int k = 16 / esize;
     const bool vec = inner % k == 0 && x_addr % 16 == 0;
     lse::DimArgs a{};
-    a.bf16 = dtype == LSE_DTYPE_BF16;
+    a.dtype = dtype;
     a.vector_cols = vec;
     a.x = static_cast<const char*>(x);
     a.n = n;

@@ -64,6 +64,14 @@ __device__ __forceinline__ u32x4 grad_vec(u32x4 w, float lse, float g, int tk) {
     if constexpr (D == DType::F32) {
         r = u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
                   __float_as_uint(o[3])};
+    } else if constexpr (D == DType::F16) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        unsigned p[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            p[k] = __builtin_bit_cast(unsigned,
+                                      __builtin_convertvector(f2{o[2 * k], o[2 * k + 1]}, half2_t));
+        r = u32x4{p[0], p[1], p[2], p[3]};
     } else {
         typedef float f2 __attribute__((ext_vector_type(2)));
         typedef __bf16 b2 __attribute__((ext_vector_type(2)));
@@ -81,12 +89,21 @@ __device__ __forceinline__ float grad_scalar(float x, float lse, float g) {
     return g * exp2_hw((x - lse) * kLog2e);
 }
 
+// fp32 to the bits of a 16-bit element, rounded to nearest even.
+template <DType D>
+__device__ __forceinline__ unsigned short float_to_half_bits(float v) {
+    if constexpr (D == DType::BF16)
+        return __builtin_bit_cast(unsigned short, static_cast<__bf16>(v));
+    else
+        return __builtin_bit_cast(unsigned short, static_cast<_Float16>(v));
+}
+
 template <DType D>
 __device__ __forceinline__ void store_scalar(char* p, float v) {
     if constexpr (D == DType::F32) {
         *reinterpret_cast<float*>(p) = v;
     } else {
-        *reinterpret_cast<__bf16*>(p) = static_cast<__bf16>(v);
+        *reinterpret_cast<unsigned short*>(p) = float_to_half_bits<D>(v);
     }
 }
 
@@ -219,8 +236,7 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
             } else if constexpr (D == DType::F32) {
                 t.e[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xo, 0, 2));
             } else {
-                t.e[u] = __uint_as_float(
-                    static_cast<unsigned>(__builtin_amdgcn_raw_buffer_load_b16(xr, xo, 0, 2)) << 16);
+                t.e[u] = half_to_float<D>(__builtin_amdgcn_raw_buffer_load_b16(xr, xo, 0, 2));
             }
             int64_t tt = t0;
             if constexpr (!ONE_ROW) {
@@ -246,8 +262,8 @@ __global__ __launch_bounds__(BLOCK) void lse_grad(const char* __restrict__ x, in
                 if constexpr (D == DType::F32)
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), gr, t.go[u], 0, 2);
                 else
-                    __builtin_amdgcn_raw_buffer_store_b16(
-                        __builtin_bit_cast(unsigned short, static_cast<__bf16>(v)), gr, t.go[u], 0, 2);
+                    __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits<D>(v), gr, t.go[u], 0,
+                                                          2);
             }
         }
     };
@@ -335,7 +351,12 @@ hipError_t launch_grad_d(const GradArgs& a) {
 
 hipError_t launch_grad(const GradArgs& a) {
     if (a.grid <= 0) return hipSuccess;
-    return a.bf16 ? launch_grad_d<DType::BF16>(a) : launch_grad_d<DType::F32>(a);
+    switch (a.dtype) {
+        case LSE_DTYPE_F32: return launch_grad_d<DType::F32>(a);
+        case LSE_DTYPE_BF16: return launch_grad_d<DType::BF16>(a);
+        case LSE_DTYPE_F16: return launch_grad_d<DType::F16>(a);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace lse

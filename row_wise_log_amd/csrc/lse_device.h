@@ -47,7 +47,7 @@ constexpr float kInf = __builtin_inff();
 // maxima (not waited on).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-enum class DType : int { F32 = 0, BF16 = 1 };
+enum class DType : int { F32 = 0, BF16 = 1, F16 = 2 };
 
 template <DType D> struct Elem;
 template <> struct Elem<DType::F32> {
@@ -59,6 +59,11 @@ template <> struct Elem<DType::BF16> {
     static constexpr int kBytes = 2;
     static constexpr int kPerVec = 8;
     static constexpr unsigned kNegInfWord = 0xFF80FF80u;  // two bf16 -inf
+};
+template <> struct Elem<DType::F16> {
+    static constexpr int kBytes = 2;
+    static constexpr int kPerVec = 8;
+    static constexpr unsigned kNegInfWord = 0xFC00FC00u;  // two fp16 -inf
 };
 
 // ---- arithmetic primitives -------------------------------------------------
@@ -93,8 +98,30 @@ __device__ __forceinline__ bool is_nan(float v) {
 
 // ---- element decoding ------------------------------------------------------
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// One 16-bit element (its bits in the low half of `bits`) to fp32, exactly:
+// bf16's 16 bits become the high half of an fp32 word; fp16 converts with
+// v_cvt_f32_f16 (every fp16 value, subnormals included, is an fp32 value).
+template <DType D>
+__device__ __forceinline__ float half_to_float(unsigned bits) {
+    if constexpr (D == DType::BF16)
+        return __uint_as_float(bits << 16);
+    else
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(bits)));
+}
+
+// The 16-bit element in the high (hi) or low half of a 32-bit word, as fp32.
+template <DType D>
+__device__ __forceinline__ float word_half_to_float(unsigned word, bool hi) {
+    if constexpr (D == DType::BF16)
+        return __uint_as_float(hi ? (word & 0xFFFF0000u) : (word << 16));
+    else
+        return half_to_float<D>(hi ? word >> 16 : word & 0xFFFFu);
+}
+
 // One 16-byte word vector to fp32 values, in memory order. bf16 is exact: its
-// 16 bits become the high half of an fp32 word.
+// 16 bits become the high half of an fp32 word; fp16 is exact by conversion.
 template <DType D>
 __device__ __forceinline__ void decode(const u32x4 w, float* f) {
     if constexpr (D == DType::F32) {
@@ -102,6 +129,14 @@ __device__ __forceinline__ void decode(const u32x4 w, float* f) {
         f[1] = __uint_as_float(w.y);
         f[2] = __uint_as_float(w.z);
         f[3] = __uint_as_float(w.w);
+    } else if constexpr (D == DType::F16) {
+        const unsigned ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const half2_t h = __builtin_bit_cast(half2_t, ws[k]);
+            f[2 * k] = static_cast<float>(h.x);
+            f[2 * k + 1] = static_cast<float>(h.y);
+        }
     } else {
         f[0] = __uint_as_float(w.x << 16);
         f[1] = __uint_as_float(w.x & 0xFFFF0000u);
@@ -120,7 +155,7 @@ __device__ __forceinline__ float load_scalar(const char* p) {
         return __builtin_nontemporal_load(reinterpret_cast<const float*>(p));
     } else {
         unsigned short h = __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p));
-        return __uint_as_float(static_cast<unsigned>(h) << 16);
+        return half_to_float<D>(h);
     }
 }
 

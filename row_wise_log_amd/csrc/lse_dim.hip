@@ -323,9 +323,18 @@ hipError_t launch_cols_d(const DimArgs& a) {
 
 hipError_t launch_cols(const DimArgs& a) {
     if (a.grid <= 0) return hipSuccess;
-    if (a.bf16) return a.vector_cols ? launch_cols_d<DType::BF16, true>(a)
-                                     : launch_cols_d<DType::BF16, false>(a);
-    return a.vector_cols ? launch_cols_d<DType::F32, true>(a) : launch_cols_d<DType::F32, false>(a);
+    switch (a.dtype) {
+        case LSE_DTYPE_F32:
+            return a.vector_cols ? launch_cols_d<DType::F32, true>(a)
+                                 : launch_cols_d<DType::F32, false>(a);
+        case LSE_DTYPE_BF16:
+            return a.vector_cols ? launch_cols_d<DType::BF16, true>(a)
+                                 : launch_cols_d<DType::BF16, false>(a);
+        case LSE_DTYPE_F16:
+            return a.vector_cols ? launch_cols_d<DType::F16, true>(a)
+                                 : launch_cols_d<DType::F16, false>(a);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace lse

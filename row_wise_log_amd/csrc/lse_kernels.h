@@ -1,5 +1,7 @@
-// lse_kernels.hip - the row-wise log-sum-exp kernels for gfx950 and their
-// launch dispatch.
+// lse_kernels.h - the row-wise log-sum-exp kernels for gfx950 and their
+// launch dispatch per element type. Each element type's instances are built in
+// a translation unit of their own (lse_kernels_f32.hip, lse_kernels_bf16.hip,
+// lse_kernels_f16.hip); lse_kernels.hip holds the entry of the dispatch.
 //
 // One pass over the input, one fp32 scalar out per row: the single-pass fused
 // LSE of "Speeding up Log-Sum-Exp: Kernel Fusion at the Memory Wall, Integer
@@ -26,6 +28,8 @@
 //                     (m, s) pair to a workspace, and the last workgroup of
 //                     a row to arrive (an agent-scope counter) merges the P
 //                     pairs in part order and resets the counter.
+#pragma once
+
 #include "lse_device.h"
 #include "lse_launch.h"
 
@@ -590,7 +594,7 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
             if constexpr (D == DType::F32)
                 x_t = __uint_as_float(t_word);
             else
-                x_t = __uint_as_float(t_hi ? (t_word & 0xFFFF0000u) : (t_word << 16));
+                x_t = word_half_to_float<D>(t_word, t_hi);
             logp[row] = t_ok ? x_t - r : __builtin_nanf("");
         }
     }
@@ -619,7 +623,7 @@ hipError_t launch_regs(const LaunchArgs& a) {
     // More rounds in flight when each lane's share of a row is small.
     constexpr int ROUNDS = VPL == 1 ? 4 : (VPL == 2 ? 2 : 1);
     if (a.rows_per_wave != (64 / G) * ROUNDS) return hipErrorInvalidConfiguration;
-    const int k = VEC ? (a.bf16 ? 8 : 4) : 1;
+    const int k = VEC ? (a.dtype == LSE_DTYPE_F32 ? 4 : 8) : 1;
     const bool tail = a.cols % k != 0;
     if (tail) return launch_regs_tok<D, G, VPL, VEC, VEC, ROUNDS>(a);
     return launch_regs_tok<D, G, VPL, VEC, false, ROUNDS>(a);
@@ -685,6 +689,9 @@ hipError_t launch_stream_cfg(const LaunchArgs& a) {
     return hipErrorInvalidConfiguration;
 }
 
+}  // namespace
+
+// The launch of one plan for element type D (instantiated per element type).
 template <DType D>
 hipError_t launch_dtype(const LaunchArgs& a) {
     switch (a.schedule) {
@@ -696,13 +703,6 @@ hipError_t launch_dtype(const LaunchArgs& a) {
             return launch_stream_cfg<D, true>(a);
     }
     return hipErrorInvalidConfiguration;
-}
-
-}  // namespace
-
-hipError_t launch(const LaunchArgs& a) {
-    if (a.grid <= 0) return hipSuccess;
-    return a.bf16 ? launch_dtype<DType::BF16>(a) : launch_dtype<DType::F32>(a);
 }
 
 }  // namespace lse

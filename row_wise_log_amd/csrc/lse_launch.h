@@ -21,7 +21,7 @@ constexpr int kCounterWords = 64;
 struct LaunchArgs {
     // what to run
     int schedule;
-    bool bf16;
+    int dtype;             // an lse_dtype_t
     int block;
     int64_t grid;
     bool vector_loads;
@@ -78,7 +78,7 @@ lse_status_t noalloc_prepare(int device, hipStream_t stream, unsigned char** ptr
 
 // The backward pass, grad_x = grad_out * exp(x - lse) (lse_backward.hip).
 struct GradArgs {
-    bool bf16;
+    int dtype;             // an lse_dtype_t
     bool vector_units;     // 16-byte units (rows 16-byte aligned, or peel below)
     bool peel;             // each row's units start at its first 16-byte boundary
     int64_t grid;
@@ -102,7 +102,7 @@ hipError_t launch_grad(const GradArgs& a);
 // parts > 1 the last workgroup of each tile to arrive merges the parts' pairs
 // from ws_pairs in the same launch.
 struct DimArgs {
-    bool bf16;
+    int dtype;             // an lse_dtype_t
     bool vector_cols;      // 16-byte groups of columns (inner % K == 0, x 16-byte aligned)
     int64_t grid;
     int parts;             // workgroups per tile along the reduced axis (<= 1024)

@@ -12,9 +12,9 @@ import numpy as np
 
 from row_wise_log_amd import binding as B
 
-TOL = {"f32": 2e-6, "bf16": 1e-5}
-DTYPE_CODE = {"f32": B.LSE_DTYPE_F32, "bf16": B.LSE_DTYPE_BF16}
-ESIZE = {"f32": 4, "bf16": 2}
+TOL = {"f32": 2e-6, "bf16": 1e-5, "f16": 1e-5}
+DTYPE_CODE = {"f32": B.LSE_DTYPE_F32, "bf16": B.LSE_DTYPE_BF16, "f16": B.LSE_DTYPE_F16}
+ESIZE = {"f32": 4, "bf16": 2, "f16": 2}
 SCHEDULES = ["auto", "rows_per_wave", "row_per_wg", "split_row"]
 
 
@@ -138,6 +138,22 @@ def compare_logp(got: np.ndarray, ref: np.ndarray, ref_lse: np.ndarray, dtype: s
     return float(ratio.max())
 
 
+# One rounding of a 16-bit output from fp32 arithmetic: relative (2^-8 for
+# bf16's 8 significant bits, 2^-11 for fp16's 11, plus 1e-6 for the fp32 value's
+# own error) and absolute (fp16's subnormal spacing 2^-24 halved; bf16 has
+# fp32's exponent range and needs none).
+OUT_ROUND = {"bf16": (2.0 ** -8 + 1e-6, 0.0), "f16": (2.0 ** -11 + 1e-6, 2.0 ** -25)}
+
+
+def decode_out(vals: np.ndarray, dtype: str) -> np.ndarray:
+    """Output words (uint16 for the 16-bit types, uint32 for fp32) as float32."""
+    if dtype == "bf16":
+        return (vals.astype(np.uint32) << 16).view(np.float32)
+    if dtype == "f16":
+        return np.ascontiguousarray(vals).view(np.float16).astype(np.float32)
+    return np.ascontiguousarray(vals).view(np.float32)
+
+
 def gpu_backward(torch, handle, x: np.ndarray, lse: np.ndarray, g: np.ndarray, dtype: str,
                  pad_front: int = 0, grad_pad: int = 0, grad_front: int = 0):
     """Run lse_backward on a host array; returns (grad as float32 rows x cols,
@@ -149,9 +165,9 @@ def gpu_backward(torch, handle, x: np.ndarray, lse: np.ndarray, g: np.ndarray, d
     gt = torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to("cuda")
     gstride = cols + grad_pad
     total = grad_front + (rows - 1) * gstride + cols + 64 if rows else 64
-    sentinel = 0x7F7F if dtype == "bf16" else 0x7F7F7F7F
-    store = torch.int16 if dtype == "bf16" else torch.int32
-    buf = torch.full((total,), sentinel if dtype != "bf16" else 0x7F7F, dtype=store, device="cuda")
+    sentinel = 0x7F7F if ESIZE[dtype] == 2 else 0x7F7F7F7F
+    store = torch.int16 if ESIZE[dtype] == 2 else torch.int32
+    buf = torch.full((total,), sentinel, dtype=store, device="cuda")
     esz = ESIZE[dtype]
     B.lse_backward(handle, ptr, DTYPE_CODE[dtype], rows, cols, stride, lt.data_ptr(), gt.data_ptr(),
                    buf.data_ptr() + grad_front * esz, gstride,
@@ -159,8 +175,8 @@ def gpu_backward(torch, handle, x: np.ndarray, lse: np.ndarray, g: np.ndarray, d
     torch.cuda.synchronize()
     host = buf.cpu().numpy()
     del t, lt, gt, buf
-    host = host.view(np.uint16) if dtype == "bf16" else host.view(np.uint32)
-    want_sentinel = np.uint16(0x7F7F) if dtype == "bf16" else np.uint32(0x7F7F7F7F)
+    host = host.view(np.uint16) if ESIZE[dtype] == 2 else host.view(np.uint32)
+    want_sentinel = np.uint16(0x7F7F) if ESIZE[dtype] == 2 else np.uint32(0x7F7F7F7F)
     if gstride == cols:  # the rows are one contiguous block
         n = rows * cols
         untouched = bool(np.all(host[:grad_front] == want_sentinel) and
@@ -172,11 +188,7 @@ def gpu_backward(torch, handle, x: np.ndarray, lse: np.ndarray, g: np.ndarray, d
         mask[idx.ravel()] = True
         untouched = bool(np.all(host[~mask] == want_sentinel))
         vals = host[idx]
-    if dtype == "bf16":
-        out = (vals.astype(np.uint32) << 16).view(np.float32)
-    else:
-        out = np.ascontiguousarray(vals).view(np.float32)
-    return out, untouched
+    return decode_out(vals, dtype), untouched
 
 
 def compare_grad(got: np.ndarray, ref: np.ndarray, d: np.ndarray, g: np.ndarray, dtype: str,
@@ -185,7 +197,8 @@ def compare_grad(got: np.ndarray, ref: np.ndarray, d: np.ndarray, g: np.ndarray,
     |got - ref| <= (rel + 2e-7 |x - lse|) |ref| + 2^-125 max(1, |g|), rel = 4e-7 for
     fp32 output (roundings of x - lse and of the log2(e) scaling, v_exp_f32's ulp, the
     multiply) and 2^-8 + 1e-6 for bf16 output (one rounding to 8 significant bits,
-    at most 2^-8 relative, on top of the fp32 value's error)."""
+    at most 2^-8 relative, on top of the fp32 value's error), 2^-11 + 1e-6 and
+    2^-25 absolute for fp16 output (11 significant bits; subnormal spacing)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, what
@@ -198,10 +211,10 @@ def compare_grad(got: np.ndarray, ref: np.ndarray, d: np.ndarray, g: np.ndarray,
     fin = ~nan & ~inf
     if not fin.any():
         return 0.0
-    rel = 2.0 ** -8 + 1e-6 if dtype == "bf16" else 4e-7
+    rel, absr = OUT_ROUND.get(dtype, (4e-7, 0.0))
     dd = np.where(np.isfinite(d), np.abs(d), 0.0)
     gg = np.broadcast_to(np.maximum(1.0, np.abs(np.asarray(g, np.float64)))[:, None], ref.shape)
-    tol = (rel + 2e-7 * dd[fin]) * np.abs(ref[fin]) + 2.0 ** -125 * gg[fin]
+    tol = (rel + 2e-7 * dd[fin]) * np.abs(ref[fin]) + 2.0 ** -125 * gg[fin] + absr
     err = np.abs(got[fin] - ref[fin])
     assert np.all(np.isfinite(got[fin])), f"{what}: non-finite grad for a finite reference"
     ratio = err / tol
@@ -225,8 +238,8 @@ def gpu_token_backward(torch, handle, x: np.ndarray, targets: np.ndarray, lse: n
     gt = torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to("cuda")
     gstride = cols + grad_pad
     total = grad_front + (rows - 1) * gstride + cols + 64 if rows else 64
-    store = torch.int16 if dtype == "bf16" else torch.int32
-    sentinel = 0x7F7F if dtype == "bf16" else 0x7F7F7F7F
+    store = torch.int16 if ESIZE[dtype] == 2 else torch.int32
+    sentinel = 0x7F7F if ESIZE[dtype] == 2 else 0x7F7F7F7F
     buf = torch.full((total,), sentinel, dtype=store, device="cuda")
     esz = ESIZE[dtype]
     B.lse_token_logprob_backward(handle, ptr, DTYPE_CODE[dtype], rows, cols, stride, tg.data_ptr(),
@@ -235,16 +248,14 @@ def gpu_token_backward(torch, handle, x: np.ndarray, targets: np.ndarray, lse: n
     torch.cuda.synchronize()
     host = buf.cpu().numpy()
     del t, tg, lt, gt, buf
-    host = host.view(np.uint16) if dtype == "bf16" else host.view(np.uint32)
-    want_sentinel = np.uint16(0x7F7F) if dtype == "bf16" else np.uint32(0x7F7F7F7F)
+    host = host.view(np.uint16) if ESIZE[dtype] == 2 else host.view(np.uint32)
+    want_sentinel = np.uint16(0x7F7F) if ESIZE[dtype] == 2 else np.uint32(0x7F7F7F7F)
     mask = np.zeros(total, dtype=bool)
     idx = grad_front + np.arange(rows)[:, None] * gstride + np.arange(cols)[None, :]
     mask[idx.ravel()] = True
     untouched = bool(np.all(host[~mask] == want_sentinel))
     vals = host[idx]
-    out = (vals.astype(np.uint32) << 16).view(np.float32) if dtype == "bf16" else \
-        np.ascontiguousarray(vals).view(np.float32)
-    return out, untouched
+    return decode_out(vals, dtype), untouched
 
 
 def compare_token_grad(got: np.ndarray, ref: np.ndarray, soft: np.ndarray, d: np.ndarray,
@@ -277,8 +288,9 @@ def compare_token_grad(got: np.ndarray, ref: np.ndarray, soft: np.ndarray, d: np
     sp = np.abs(np.where(np.isfinite(soft), soft, 0.0))
     tol = (4e-7 + 2e-7 * dd) * sp + np.where(onehot, 2.0 ** -23 * np.maximum(gg, sp), 0.0) + \
         2.0 ** -125 * np.maximum(1.0, gg)
-    if dtype == "bf16":
-        tol = tol + (2.0 ** -8 + 1e-6) * (np.abs(ref) + tol)
+    if dtype in OUT_ROUND:
+        rel, absr = OUT_ROUND[dtype]
+        tol = tol + rel * (np.abs(ref) + tol) + absr
     assert np.all(np.isfinite(got[fin])), f"{what}: non-finite grad for a finite reference"
     ratio = np.abs(got[fin] - ref[fin]) / tol[fin]
     worst = int(np.argmax(ratio))

@@ -27,14 +27,16 @@ Determinism: rows are drawn in fixed chunks. Chunk i of every workload uses
 ``numpy.random.default_rng(SeedSequence(0, spawn_key=(i,)))``, which is the
 i-th child of seed 0, so any prefix of rows can be regenerated alone and is
 bit-identical to the same rows of the full matrix. bf16 values are stored as
-their uint16 bit patterns, rounded from fp32 to nearest-even.
+their uint16 bit patterns, rounded from fp32 to nearest-even; ``make(...,
+storage="f16")`` stores the same fp32 draws as IEEE half bit patterns instead
+(``storage="f32"`` keeps them unrounded).
 """
 from __future__ import annotations
 
 import hashlib
 import os
 from concurrent.futures import ThreadPoolExecutor
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -49,7 +51,7 @@ _ALLNEG_KEY = 0xFFFF_FFFF
 class Spec:
     cfg: int
     name: str
-    dtype: str  # "f32" or "bf16": the storage type of x
+    dtype: str  # "f32", "bf16" or "f16": the storage type of x
     rows: int
     cols: int
     chunk_rows: int
@@ -78,7 +80,7 @@ SPECS = {
 @dataclass
 class Workload:
     spec: Spec
-    x: np.ndarray          # [rows, cols] float32, or uint16 bf16 bit patterns
+    x: np.ndarray          # [rows, cols] float32, or uint16 bf16 / fp16 bit patterns
     rows: int
     aux: dict = field(default_factory=dict)
 
@@ -105,6 +107,13 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     if nan.any():
         out[nan] = np.uint16(0x7FC0)
     return out
+
+
+def f32_to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE half, nearest-even (numpy's cast), returning
+    uint16 bits; beyond the half range they become +-inf."""
+    with np.errstate(over="ignore"):
+        return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -134,14 +143,14 @@ def _chunk2(rng, n, cols, want_aux):
     off = rng.uniform(-20.0, 20.0, size=n).astype(np.float32)
     z += off[:, None]
     aux = {"offset": off, "spikes": spikes} if want_aux else {}
-    return f32_to_bf16_bits(z), aux
+    return z, aux
 
 
 def _chunk3(rng, n, cols, want_aux):
     x = rng.standard_normal((n, cols), dtype=np.float32)
     x *= np.float32(4.0)
     x[rng.random((n, cols), dtype=np.float32) < np.float32(0.01)] = -np.inf
-    return f32_to_bf16_bits(x), {}
+    return x, {}
 
 
 def _chunk4(rng, n, cols, want_aux):
@@ -168,20 +177,34 @@ def allneg_rows(total_rows: int = 1 << 24) -> np.ndarray:
     return np.sort(sel)
 
 
+_ROUND = {"bf16": f32_to_bf16_bits, "f16": f32_to_f16_bits}
+
+
 def make(cfg: int, rows: int | None = None, aux: bool = False,
-         threads: int | None = None) -> Workload:
+         threads: int | None = None, storage: str | None = None) -> Workload:
     """Return workload ``cfg`` or the prefix of its first ``rows`` rows.
 
     A prefix holds exactly the same values as the same rows of the full
     matrix. ``aux=True`` also returns the generator's own draws (offsets,
     spike columns, sigma, the Dirichlet p and keep mask, the all -inf rows)
     for the tests that check the workloads against their definitions.
+    ``storage`` ("f32", "bf16" or "f16") overrides the stored element type:
+    the same seeded fp32 values, kept or rounded to nearest-even in the other
+    16-bit format (the paper's reduced-bit comparison, §4.3).
     """
     spec = SPECS[cfg]
+    if storage is not None and storage != spec.dtype:
+        if storage not in ("f32", "bf16", "f16"):
+            raise ValueError(f"unknown storage {storage!r}")
+        spec = replace(spec, dtype=storage, name=spec.name.replace(spec.dtype, storage, 1)
+                       .replace("fp32", storage, 1),
+                       recipe=spec.recipe.replace("RNE to bf16", f"stored as {storage}")
+                       if "RNE to bf16" in spec.recipe else spec.recipe + f"; stored as {storage}")
     n = spec.rows if rows is None else int(rows)
     if not 0 <= n <= spec.rows:
         raise ValueError(f"rows must be in [0, {spec.rows}]")
-    store = np.uint16 if spec.dtype == "bf16" else np.float32
+    store = np.float32 if spec.dtype == "f32" else np.uint16
+    rnd = _ROUND.get(spec.dtype)
     x = np.empty((n, spec.cols), dtype=store)
     nchunks = -(-n // spec.chunk_rows)
     auxes: list[dict] = [dict() for _ in range(nchunks)]
@@ -191,7 +214,7 @@ def make(cfg: int, rows: int | None = None, aux: bool = False,
         full = min(spec.chunk_rows, spec.rows - r0)
         xc, ac = _CHUNK[cfg](_rng(i), full, spec.cols, aux)
         take = min(full, n - r0)
-        x[r0:r0 + take] = xc[:take]
+        x[r0:r0 + take] = rnd(xc[:take]) if rnd is not None else xc[:take]
         auxes[i] = {k: v[:take] for k, v in ac.items()}
 
     if threads is None:
@@ -210,7 +233,7 @@ def make(cfg: int, rows: int | None = None, aux: bool = False,
     if cfg == 5:
         neg = allneg_rows(spec.rows)
         neg = neg[neg < n]
-        x[neg] = -np.inf
+        x[neg] = -np.inf if rnd is None else rnd(np.array([-np.inf], dtype=np.float32))[0]
         if aux:
             out_aux["allneg"] = neg
     return Workload(spec=spec, x=x, rows=n, aux=out_aux)
