@@ -86,6 +86,11 @@ def test_default_workload_line():
         assert rec["us_per_launch"] > 0 and rec["read_control"]["launch_us_mean"] > 0
         assert rec["frac_of_hbm_peak"] == pytest.approx(
             rec["algorithmic_bytes_per_launch"] / (rec["us_per_launch"] * 1e-6) / 8e12, rel=5e-3)
+    rb = d["reduced_bit"]
+    for k in ("f32", "bf16", "f16"):
+        assert rb[k]["us_per_launch"] > 0 and rb[k]["max_err_over_tol_own_bits"] <= 1.0
+    assert rb["f32"]["mae_vs_f64_of_fp32_values"] < 1e-5 < rb["f16"]["mae_vs_f64_of_fp32_values"]
+    assert rb["f16"]["mae_vs_f64_of_fp32_values"] < rb["bf16"]["mae_vs_f64_of_fp32_values"]
     rw = d["configs"]["5"]["read_write_control"]
     assert rw["launch_us_mean"] > 0 and 0 < rw["frac_of_control"] < 2
     assert d["configs"]["5"]["read_control_same_geometry"]["launch_us_mean"] > 0
