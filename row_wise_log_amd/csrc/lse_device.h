@@ -449,16 +449,43 @@ struct Merged {
     float m, c, s;
 };
 
+// A compensated sum over each aligned group of G lanes (G a power of two, at
+// most 16): every lane of a group ends with the group's sum `s` and the
+// accumulated rounding error `e` of its adds (TwoSum at every step, as CSum
+// keeps for sequential adds). The patterns pair lanes symmetrically and TwoSum
+// is exact, so every lane of a group holds the same bits.
+template <int G>
+__device__ __forceinline__ void group_csum(float& s, float& e) {
+    auto step = [&](float vs, float ve) {
+        const float sum = s + vs;
+        const float bp = sum - s;
+        const float err = (s - (sum - bp)) + (vs - bp);
+        e = (e + ve) + err;
+        s = sum;
+    };
+    if constexpr (G >= 2) step(dpp_free<kDppXor1>(s), dpp_free<kDppXor1>(e));
+    if constexpr (G >= 4) step(dpp_free<kDppXor2>(s), dpp_free<kDppXor2>(e));
+    if constexpr (G >= 8) step(dpp_free<kDppHalfMirror>(s), dpp_free<kDppHalfMirror>(e));
+    if constexpr (G >= 16) step(dpp_free<kDppMirror>(s), dpp_free<kDppMirror>(e));
+}
+
 // Merge every lane's (m, c, s) into the workgroup's: each wavefront takes its
 // lanes' max and then the sum of their sums rescaled to it (DPP, no LDS);
 // lane 0 posts the wavefront's (max, sum) to `pairs` (2 floats per
-// wavefront); after one barrier every thread folds the pairs in wavefront
-// order, so the result is uniform and the same on every run. Every thread of
-// the block must call it; `pairs` must not be rewritten before all threads
-// have returned (a barrier separates two calls).
+// wavefront); after one barrier lanes 0..NW-1 of every wavefront each take
+// one wavefront's pair and merge them with a DPP tree (maximum, then a
+// compensated sum), lane 0's result broadcast to the whole wavefront, so the
+// result is uniform and the same on every run. A tree of log2(NW) steps
+// instead of NW sequential merges shortens the end of each workgroup, which
+// lies on the launch's critical path: measured with per-wavefront timestamps
+// on workload 2, from the last wavefront's final fold to the store took 0.73
+// us with the sequential merge and 0.61 us with the tree (launch 21.60 ->
+// 21.42 us). Every thread of the block must call it; `pairs` must not be
+// rewritten before all threads have returned (a barrier separates two calls).
 template <int BLOCK>
 __device__ __forceinline__ Merged block_merge(float m, float c, float s, float* pairs) {
     constexpr int NW = BLOCK / 64;
+    static_assert(NW <= 16, "the cross-wave tree spans one DPP row of 16 lanes");
     const float wm = group_reduce<64>(m, OpMax{});
     const float wc = base2_ref(wm);
     const float ws = group_reduce<64>(s * exp2_hw(c - wc), OpSum{});
@@ -466,18 +493,23 @@ __device__ __forceinline__ Merged block_merge(float m, float c, float s, float* 
         return Merged{wm, wc, ws};
     } else {
         const int wave = threadIdx.x >> 6;
-        if ((threadIdx.x & 63) == 0) {
+        const int l = threadIdx.x & 63;
+        if (l == 0) {
             pairs[2 * wave] = wm;
             pairs[2 * wave + 1] = ws;
         }
         __syncthreads();
-        float bm = pairs[0];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) bm = max3f(bm, pairs[2 * w], pairs[2 * w]);
+        // lanes past NW hold the empty pair (-inf, 0), which adds exactly 0
+        const float pm = l < NW ? pairs[2 * l] : -kInf;
+        const float ps = l < NW ? pairs[2 * l + 1] : 0.0f;
+        const float bm = readlane(group_reduce<NW>(pm, OpMax{}), 0);
         const float bc = base2_ref(bm);
+        float ts = ps * exp2_hw(base2_ref(pm) - bc);
+        float te = 0.0f;
+        group_csum<NW>(ts, te);
         CSum bs;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) bs.add(pairs[2 * w + 1] * exp2_hw(base2_ref(pairs[2 * w]) - bc));
+        bs.s = readlane(ts, 0);
+        bs.e = readlane(te, 0);
         return Merged{bm, bc, bs.total()};
     }
 }
