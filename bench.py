@@ -338,7 +338,7 @@ def time_control(torch, step, steps: int, stream) -> float:
     for i in range(5):
         step(i)
     per = max(event_mean_us(torch, step, 5, 5, stream) * 1e-6, 1e-6)
-    n = int(np.ceil(PREHEAT_SECONDS / per))
+    n = int(np.ceil(PREHEAT_SECONDS / per)) if PREHEAT_SECONDS > 0 else 0
     for i in range(10, 10 + n):
         step(i)
     return event_mean_us(torch, step, 10 + n, steps, stream)
@@ -649,12 +649,21 @@ def check_gpu_output(w, gpu_out: np.ndarray, reference: tuple) -> None:
             "rows_checked": int(len(ref))}
 
 
-def oracle_reference(w, op: str = "lse") -> tuple:
-    """The float64 oracle over every row of the workload, on all host cores
-    (the checker of the timed steps' output; not timed as a baseline)."""
+def oracle_reference(w, op: str = "lse"):
+    """The float64 oracle over every output of the workload, on all host
+    cores (the checker of the timed steps' output; not timed as a baseline),
+    as (reference, LSE for the log-probabilities' bar); None for the backward
+    ops, whose outputs the backward baseline checks on the headline only."""
     import oracle
     threads = len(os.sched_getaffinity(0))
-    return oracle.lse(w.x, w.dtype, threads=threads), None
+    if op == "lse":
+        return oracle.lse(w.x, w.dtype, threads=threads), None
+    if op == "logprob":
+        lse = oracle.lse(w.x, w.dtype, threads=threads)
+        return oracle.token_logprob(w.x, workloads.targets(w.spec.cfg), w.dtype, threads=threads), lse
+    if op == "dim":
+        return oracle.lse_dim(w.x.reshape(1, w.rows, w.cols), w.dtype, threads=threads).ravel(), None
+    return None
 
 
 def torch_context(torch, w, steps: int) -> dict:
@@ -731,12 +740,13 @@ def versions(torch) -> dict:
 
 
 def config_record(r: dict, check: dict | None, traffic: float | None) -> dict:
-    """The compact record of one forward workload for the `configs` key."""
+    """The compact record of one workload for the `configs` key."""
     w = r["w"]
     us = r["launch_ms_mean"] * 1e3
+    forward = r["op"] in ("lse", "logprob", "dim")
     rec = {"workload": f"config{w.spec.cfg} {w.spec.name}: {w.spec.recipe}",
-           "rows": w.rows, "cols": w.cols, "input_dtype": w.dtype,
-           "plan": plan_name(r["plan"]),
+           "rows": w.rows, "cols": w.cols, "input_dtype": w.dtype, "op": r["op"],
+           "plan": plan_name(r["plan"]) if r["op"] in ("lse", "logprob") else f"lse_{r['op']}",
            "us_per_launch": round(us, 2),
            "us_per_call_wall": round(r["ms_per_step"] * 1e3, 2),
            "input_GBs_wall": round(r["value_gbs"], 1),
@@ -745,7 +755,7 @@ def config_record(r: dict, check: dict | None, traffic: float | None) -> dict:
            "achieved_GBs": round(r["achieved_gbs"], 1),
            "frac_of_hbm_peak": round(r["achieved_gbs"] / HBM_PEAK_GBS, 4),
            "traffic": traffic,
-           "read_control": r["control"],
+           ("read_control" if forward else "copy_control"): r["control"],
            "warmup": r["warmup"]}
     rec.update(r["extra_controls"])
     if check is not None:
@@ -753,7 +763,155 @@ def config_record(r: dict, check: dict | None, traffic: float | None) -> dict:
     return rec
 
 
+# ---- rocprofv3 summaries (no GPU needed) ------------------------------------
+#
+# The summaries under profiles/ are written by these functions from the CSV
+# files that `rocprofv3 ... --output-format csv -d DIR -o run -- python3
+# bench.py ...` leaves in DIR, so that each one can be regenerated from
+# committed code.
+
+def _csv_rows(directory: str, suffix: str) -> list:
+    import csv
+    rows = []
+    for f in sorted(Path(directory).rglob(f"*{suffix}")):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return rows
+
+
+def short_kernel_name(name: str) -> str:
+    name = name.strip()
+    return name[:name.index("(", name.index(">"))] if ">" in name and "(" in name else name
+
+
+def summarize_trace(directory: str) -> str:
+    """Markdown table of a kernel trace: per kernel, dispatches and the mean,
+    median, min and max duration in microseconds."""
+    groups: dict[tuple, list] = {}
+    for r in _csv_rows(directory, "kernel_trace.csv"):
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+        block = int(r["Workgroup_Size_X"])
+        key = (short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(block, 1), block)
+        groups.setdefault(key, []).append(us)
+    out = ["| kernel | workgroups x threads | dispatches | mean us | median us | min us | max us |",
+           "|---|---|---|---|---|---|---|"]
+    for (name, wgs, block), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(v)
+        out.append(f"| `{name}` | {wgs} x {block} | {len(a)} | {a.mean():.2f} | {np.median(a):.2f} | "
+                   f"{a.min():.2f} | {a.max():.2f} |")
+    return "\n".join(out)
+
+
+def summarize_trace_runs(directory: str, min_len: int = 50) -> str:
+    """Markdown table of the runs in a kernel trace: maximal sequences of
+    consecutive dispatches (in dispatch order) of one kernel and launch shape,
+    at least min_len long, e.g. one workload's warmup and timed steps."""
+    rows = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"]))
+    runs, cur, key0 = [], [], None
+    for r in rows:
+        block = int(r["Workgroup_Size_X"])
+        key = (short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(block, 1), block)
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+        if key != key0 and cur:
+            runs.append((key0, int(cur[0][0]), cur))
+            cur = []
+        key0 = key
+        cur.append((r["Dispatch_Id"], us))
+    if cur:
+        runs.append((key0, int(cur[0][0]), cur))
+    out = ["| first dispatch | kernel | workgroups x threads | dispatches | mean us | mean of the last "
+           "1000 us | median us |", "|---|---|---|---|---|---|---|"]
+    for (name, wgs, block), first, v in runs:
+        if len(v) < min_len:
+            continue
+        a = np.array([u for _, u in v])
+        out.append(f"| {first} | `{name}` | {wgs} x {block} | {len(a)} | {a.mean():.2f} | "
+                   f"{a[-1000:].mean():.2f} | {np.median(a):.2f} |")
+    return "\n".join(out)
+
+
+def counter_means(directory: str) -> dict:
+    """{kernel: {counter: mean value per dispatch}} from a counter collection."""
+    acc: dict[str, dict[str, list]] = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        k = short_kernel_name(r["Kernel_Name"])
+        acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: {c: (float(np.mean(v)), len(v)) for c, v in d.items()} for k, d in acc.items()}
+
+
+def summarize_counters(directory: str) -> str:
+    """Markdown table: per kernel and counter, the mean per dispatch."""
+    out = ["| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
+    for k, d in sorted(counter_means(directory).items()):
+        for c, (m, n) in sorted(d.items()):
+            out.append(f"| `{k}` | {c} | {n} | {m:.6g} |")
+    return "\n".join(out)
+
+
+def plan_kernel_name(plan: dict, dtype: str, cols: int) -> str:
+    """The demangled name of the kernel instance an lse_forward plan launches."""
+    d = {"f32": 0, "bf16": 1, "f16": 2}[dtype]
+    if plan["schedule"] == 1:
+        vpl, g, vec = plan["loads_per_lane"], plan["lanes_per_row"], plan["vector_loads"]
+        rounds = 4 if vpl == 1 else (2 if vpl == 2 else 1)
+        k = (4 if dtype == "f32" else 8) if vec else 1
+        tail = bool(vec) and cols % k != 0
+        return (f"void lse::rows_in_registers<(lse::DType){d}, {g}, {vpl}, {str(bool(vec)).lower()}, "
+                f"{str(tail).lower()}, {rounds}, false>")
+    split = "true" if plan["schedule"] == 3 else "false"
+    return f"void lse::stream_rows<(lse::DType){d}, {plan['block']}, {plan['unroll']}, {split}, false>"
+
+
+def write_traffic(fetch_dir: str, write_dir: str, copy_bytes: int, command: str) -> str:
+    """profiles/traffic.txt from a FETCH_SIZE run and a WRITE_SIZE run of the
+    default forward bench (all five workloads), each counter scaled by
+    known / measured for the three plain device copies of copy_bytes bytes the
+    bench makes first (the copy kernel's dispatches)."""
+    from row_wise_log_amd import binding as B
+    fetch, write = counter_means(fetch_dir), counter_means(write_dir)
+
+    def factor(directory, counter):
+        # the calibration copies are the first three copy-kernel dispatches
+        rows = [r for r in _csv_rows(directory, "counter_collection.csv")
+                if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        if len(rows) < 3:
+            raise SystemExit(f"fewer than three copy-kernel dispatches with {counter}")
+        measured = float(np.mean([float(r["Counter_Value"]) for r in rows[:3]]))
+        return (copy_bytes / 1024.0) / measured
+
+    ff, fw = factor(fetch_dir, "FETCH_SIZE"), factor(write_dir, "WRITE_SIZE")
+    lines = ["# HBM traffic per launch from rocprofv3 counters (read by bench.py for roofline.traffic).",
+             "# FETCH_SIZE / WRITE_SIZE means (KiB per dispatch) scaled by known/measured for the three",
+             f"# plain device copies of {copy_bytes} bytes the bench makes first in the same process.",
+             "# Commands (from the repository root, one counter per run):",
+             f"#   {command.replace('COUNTER', 'FETCH_SIZE')}",
+             f"#   {command.replace('COUNTER', 'WRITE_SIZE')}",
+             "# then: python3 bench.py --write-traffic FETCH_DIR WRITE_DIR --copy-bytes "
+             f"{copy_bytes}",
+             "# bench.py reports roofline.traffic only while kernel_source_hash matches the sources.",
+             f"kernel_source_hash: {kernel_source_hash()}"]
+    for cfg in (1, 2, 3, 4, 5):
+        spec = workloads.SPECS[cfg]
+        esize = 4 if spec.dtype == "f32" else 2
+        plan = B.lse_plan(dtype_code_of(B, spec.dtype), spec.rows, spec.cols, spec.cols, 0, 256, 0)
+        k = plan_kernel_name(plan, spec.dtype, spec.cols)
+        if k not in fetch or k not in write:
+            raise SystemExit(f"config {cfg}: kernel {k} not in the counter runs")
+        fkib, wkib = fetch[k]["FETCH_SIZE"][0], write[k]["WRITE_SIZE"][0]
+        total = fkib * 1024 * ff + wkib * 1024 * fw
+        alg = spec.rows * spec.cols * esize + 4 * spec.rows
+        lines.append(f"# config {cfg}: {k}: FETCH {fkib:.1f} KiB x {ff:.4f}, WRITE {wkib:.1f} KiB x "
+                     f"{fw:.4f}; algorithmic {spec.rows * spec.cols * esize} + {4 * spec.rows} B; "
+                     f"traffic/algorithmic = {total / alg:.4f}")
+        lines.append(f"config{cfg}_bytes_per_launch: {total:.0f}")
+    return "\n".join(lines) + "\n"
+
+
 def main() -> int:
+    global PREHEAT_SECONDS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
@@ -763,6 +921,9 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--rotate", type=int, default=None,
                     help="input copies cycled through (default: enough to exceed 2x the 256 MiB cache)")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the other four workloads for --op logprob, backward, "
+                         "logprob_backward or dim (the forward LSE line carries them by default)")
     ap.add_argument("--only", action="store_true",
                     help="time only the --config workload (the forward LSE line otherwise also "
                          "carries the other four workloads under `configs`)")
@@ -791,7 +952,38 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run three plain device copies of BYTES bytes (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--preheat-seconds", type=float, default=0.05,
+                    help="minimum duration of each workload's untimed control launches before its "
+                         "warmup steps (0 in counter runs, where launches are serialised)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 kernel trace (CSV) and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 counter collection and exit")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.txt from a FETCH_SIZE and a WRITE_SIZE run and exit")
+    ap.add_argument("--copy-bytes", type=int, default=268435456,
+                    help="size of the calibration copies in the counter runs (--write-traffic)")
+    ap.add_argument("--traffic-command", default=(
+        "rocprofv3 --pmc COUNTER --output-format csv -d <dir> -o run -- python3 bench.py "
+        "--no-cpu-baseline --no-torch-context --steps 5 --warmup 1 --preheat-seconds 0 "
+        "--copy-calibration 268435456"))
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        print()
+        print(summarize_trace_runs(args.summarize_trace))
+        return 0
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
+        return 0
+    if args.write_traffic:
+        TRAFFIC_FILE.write_text(write_traffic(*args.write_traffic, args.copy_bytes,
+                                              args.traffic_command))
+        print(TRAFFIC_FILE.read_text())
+        return 0
+
+    PREHEAT_SECONDS = args.preheat_seconds
 
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the row-wise LSE "
@@ -914,19 +1106,22 @@ def main() -> int:
         if small is not None:
             line["small_shapes"] = small
         del r
-        if args.op == "lse" and not args.only:
+        if (args.op == "lse" and not args.only) or args.all:
             # The other four workloads: each timed the same way (its control
-            # first, then W warmup and K timed steps) and checked on every row.
+            # first, then W warmup and K timed steps) and, for the forward
+            # ops, checked on every row.
             others = {}
             for cfg in [c for c in (1, 2, 3, 4, 5) if c != args.config]:
                 wc = workloads.make(cfg)
-                log(f"timing config {cfg}")
-                rc = time_config(torch, B, handle, cfg, args.steps, args.warmup, None, "lse",
+                log(f"timing config {cfg} ({args.op})")
+                rc = time_config(torch, B, handle, cfg, args.steps, args.warmup, None, args.op,
                                  args.graph, w=wc, extras=False)
-                ref = oracle_reference(wc)
-                chk = check_gpu_output(wc, rc["out"].cpu().numpy().astype(np.float64), ref)
-                rec = config_record(rc, chk, recorded_traffic(cfg))
-                if cfg == 1:
+                ref = oracle_reference(wc, args.op)
+                chk = None
+                if ref is not None:
+                    chk = check_gpu_output(wc, rc["out"].cpu().numpy().astype(np.float64), ref)
+                rec = config_record(rc, chk, recorded_traffic(cfg) if args.op == "lse" else None)
+                if cfg == 1 and args.op == "lse":
                     rec["us_per_call_warm"] = round(warm_us_per_call(torch, B, handle, cfg), 2)
                 log(json.dumps(rec))
                 others[str(cfg)] = rec
