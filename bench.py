@@ -65,9 +65,14 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel and planner sources with their comments and blank
+    lines removed: what decides the bytes a launch moves, not its prose."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        h.update(p.read_bytes())
+        text = re.sub(r"/\*.*?\*/", "", p.read_text(), flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 
@@ -763,6 +768,97 @@ def config_record(r: dict, check: dict | None, traffic: float | None) -> dict:
     return rec
 
 
+# ---- plan A/B at the steady state ---------------------------------------------
+
+def parse_plan(spec: str) -> dict:
+    """'auto' or comma-separated key=value with keys schedule (auto,
+    rows_per_wave, row_per_wg, split_row), block, unroll, parts, waves_per_cu,
+    lanes_per_row: a plan forced through lse_set_schedule / lse_set_tuning."""
+    plan = {"schedule": "auto", "block": 0, "unroll": 0, "parts": 0, "waves_per_cu": 0,
+            "lanes_per_row": 0}
+    if spec.strip() != "auto":
+        for item in spec.split(","):
+            k, _, v = item.partition("=")
+            k = k.strip()
+            if k not in plan:
+                raise SystemExit(f"unknown plan key {k!r} in {spec!r}")
+            plan[k] = v.strip() if k == "schedule" else int(v)
+    return plan
+
+
+def plan_ab(torch, B, dtype: str, rows: int, cols: int, plans: list, blocks: int = 4,
+            block_ms: float = 30.0, warm_ms: float = 100.0) -> dict:
+    """Alternate blocks of back-to-back lse_forward launches of each plan on
+    one shape (random N(0, 3^2) rows, rotating copies beyond the Infinity
+    Cache) after warm_ms of launches: each block runs at least block_ms, one
+    event pair around it; the median over the blocks of each plan's mean
+    microseconds per launch. Every plan's output is checked against the
+    float64 oracle."""
+    import oracle
+    rng = np.random.default_rng(rows * 7 + cols)
+    v = rng.normal(0, 3, size=(rows, cols)).astype(np.float32)
+    x = v if dtype == "f32" else (workloads.f32_to_bf16_bits(v) if dtype == "bf16"
+                                   else workloads.f32_to_f16_bits(v))
+    del v
+    ref = oracle.lse(x, dtype, threads=len(os.sched_getaffinity(0)))
+    nbytes = x.nbytes
+    rotate = max(1, -(-2 * CACHE_BYTES // nbytes) + 1)
+    host = torch.from_numpy(x if dtype == "f32" else x.view(np.int16))
+    bufs = [host.to("cuda") for _ in range(rotate)]
+    code = dtype_code_of(B, dtype)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    handles, outs = [], []
+    for pl in plans:
+        h = B.lse_create(0)
+        B.lse_set_schedule(h, pl["schedule"])
+        B.lse_set_tuning(h, pl["block"], pl["unroll"], pl["parts"], pl["waves_per_cu"],
+                         pl["lanes_per_row"])
+        handles.append(h)
+        outs.append(torch.empty(rows, dtype=torch.float32, device="cuda"))
+
+    def step_of(j):
+        h, o = handles[j], outs[j]
+        return lambda i: B.lse_forward(h, bufs[i % rotate].data_ptr(), code, rows, cols, cols,
+                                       o.data_ptr(), sh)
+
+    steps = [step_of(j) for j in range(len(plans))]
+    checks = []
+    for j, st in enumerate(steps):
+        st(0)
+        torch.cuda.synchronize()
+        checks.append(check_gpu_output(type("W", (), {"dtype": dtype})(),
+                                       outs[j].cpu().numpy().astype(np.float64), (ref, None)))
+    per = [max(event_mean_us(torch, st, 0, 10, stream), 0.5) for st in steps]
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < warm_ms * 1e-3:
+        steps[i % len(steps)](i)
+        i += 1
+    means = [[] for _ in plans]
+    for _ in range(blocks):
+        for j, st in enumerate(steps):
+            n = max(20, int(np.ceil(block_ms * 1e3 / per[j])))
+            means[j].append(event_mean_us(torch, st, 0, n, stream))
+    plan_info = []
+    for pl in plans:
+        pi = B.lse_plan(code, rows, cols, cols, bufs[0].data_ptr(), 256, B.SCHEDULES[pl["schedule"]])
+        for k in ("block", "unroll", "parts"):  # the forced tuning overrides the planner's
+            if pl[k] and pi["schedule"] != 1:
+                pi[k] = pl[k]
+        if pl["parts"] and pi["schedule"] == 3:
+            pi["grid"] = min(rows, B.LSE_SPLIT_MAX_ROWS) * pl["parts"]
+        plan_info.append(pi)
+    for h in handles:
+        B.lse_destroy(h)
+    med = [float(np.median(m)) for m in means]
+    return {"dtype": dtype, "rows": rows, "cols": cols, "bytes": nbytes,
+            "plans": [{"forced": pl, "planned": plan_name(pi), "us_median": round(m, 2),
+                       "us_blocks": [round(u, 2) for u in ms], **ck}
+                      for pl, pi, m, ms, ck in zip(plans, plan_info, med, means, checks)],
+            "ratio_b_over_a": round(med[1] / med[0], 4) if len(med) > 1 else None}
+
+
 # ---- rocprofv3 summaries (no GPU needed) ------------------------------------
 #
 # The summaries under profiles/ are written by these functions from the CSV
@@ -955,6 +1051,14 @@ def main() -> int:
     ap.add_argument("--preheat-seconds", type=float, default=0.05,
                     help="minimum duration of each workload's untimed control launches before its "
                          "warmup steps (0 in counter runs, where launches are serialised)")
+    ap.add_argument("--ab", nargs=3, action="append", metavar=("DTYPE", "ROWS", "COLS"),
+                    help="plan A/B on a shape (repeatable): alternate blocks of --plan launches "
+                         "at the steady state and print one JSON line per shape, then exit")
+    ap.add_argument("--plan", action="append", default=None,
+                    help="a plan for --ab: 'auto' or e.g. 'schedule=row_per_wg,block=256' (give two "
+                         "or more; default: auto against row_per_wg)")
+    ap.add_argument("--ab-blocks", type=int, default=4)
+    ap.add_argument("--ab-block-ms", type=float, default=30.0)
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print a markdown summary of a rocprofv3 kernel trace (CSV) and exit")
     ap.add_argument("--summarize-counters", metavar="DIR",
@@ -1006,6 +1110,13 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"calibration: 3 copies of {args.copy_calibration} bytes")
         del src, dst
+    if args.ab:
+        plans = [parse_plan(p_) for p_ in (args.plan or ["auto", "schedule=row_per_wg"])]
+        for dt, rows_, cols_ in args.ab:
+            res = plan_ab(torch, B, dt, int(rows_), int(cols_), plans, args.ab_blocks,
+                          args.ab_block_ms)
+            print(json.dumps(res), flush=True)
+        return 0
     handle = B.lse_create(0)
     try:
         log(f"timing config {args.config} ({args.op}): {args.steps} steps after "

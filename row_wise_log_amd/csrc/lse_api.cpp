@@ -53,8 +53,10 @@ constexpr int64_t kSplitMinRowBytes = 64 << 10;
 constexpr int kSplitWavesPerCU = 4;
 // Just over one row per CU (up to 5/4), one workgroup per row leaves most CUs
 // one row and some two; rows of 1 MiB and more then split into four parts of
-// 256 threads (measured at steady state: 257, 288 and 320 rows of 1 MiB,
-// 6-9 % faster; rows of 256 KiB gain nothing).
+// 256 threads. Measured at steady state with bench.py --ab (257 to 320 rows of
+// 1 and 4 MiB, bf16 and fp32): 5-13 % faster than one 256-thread workgroup
+// per row, 11-23 % faster than 512 threads; rows of 256 KiB split the same
+// way are 1-2 % slower, so they are not split.
 constexpr int64_t kSplitQuarterRowBytes = 1 << 20;
 // lse_forward_dim: column groups per workgroup (the other 256 / 32 = 8 lanes
 // of each column group take consecutive j), doubled where there are columns
