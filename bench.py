@@ -185,7 +185,7 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int | None, rota
     nbytes = rows * cols * esize
     extra_controls = {}
     if op in ("lse", "logprob", "dim"):
-        control = time_read_control(torch, bufs, nbytes, plan, steps, stream)
+        control, control_step = time_read_control(torch, bufs, nbytes, plan, steps, stream)
         if op == "lse" and plan["schedule"] == B.LSE_SCHED_ROWS_PER_WAVE and cols == 16 \
                 and nbytes % 4096 == 0 and plan["lanes_per_row"] == 4:
             # many 64-byte rows: the same geometry with and without one word
@@ -195,15 +195,12 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int | None, rota
                 extra_controls[key] = time_rows_control(torch, bufs, nbytes, int(plan["grid"]),
                                                         store, steps, stream)
     else:
-        control = time_copy_control(torch, bufs, nbytes, steps, stream)
+        control, control_step = time_copy_control(torch, bufs, nbytes, steps, stream)
+    control_step_us = control["launch_us_mean"]
 
     warmup = run_warmup(torch, step, warmup, stream)
     # The timed region: K back-to-back launches between a synchronize on each
-    # side, with one HIP event pair on the launch stream around them. The
-    # wall clock gives the whole-job rate; the events give the mean launch
-    # duration on the GPU (the launches are queued ahead, so host overhead
-    # is hidden and the event interval is the kernels' own time plus the
-    # hardware's inter-dispatch gaps).
+    # side; the wall clock gives the whole-job rate (`value`).
     # With graph=True the K steps are captured into one HIP graph first and
     # the timed region is one replay of it (after one untimed replay).
     g = None
@@ -216,25 +213,40 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int | None, rota
                 step(warmup + i, hs)
         torch.cuda.synchronize()
         g.replay()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(stream)
     if g is not None:
         g.replay()
     else:
         for i in range(steps):
             step(warmup + i)
-    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # The launches' own time on the GPU (`roofline.achieved`): the same K
+    # steps again, with one HIP event pair on the launch stream around them,
+    # queued behind a lead of control launches long enough for the host to
+    # enqueue all K before the first event is reached, so the event interval
+    # is the kernels' back-to-back time (plus the hardware's inter-dispatch
+    # gaps) and not the host's launch rate, which short launches outrun.
+    lead = max(1, int(np.ceil(steps * LEAD_US_PER_STEP / max(control_step_us, 1.0))))
+    for i in range(lead):
+        control_step(i)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(steps):
+            step(warmup + steps + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
     mean_launch = e0.elapsed_time(e1) / steps
     del g
 
     ms_step = wall / steps * 1e3
-    median_us = median_single_call_us(torch, step, warmup + steps, stream) if extras else None
-    graph_us = graph_us_per_call(torch, step, warmup + steps + 60) if extras else None
+    median_us = median_single_call_us(torch, step, warmup + 2 * steps, stream) if extras else None
+    graph_us = graph_us_per_call(torch, step, warmup + 2 * steps + 60) if extras else None
     key = "frac_of_read_control" if op in ("lse", "logprob", "dim") else "frac_of_copy_control"
     control[key] = round(control["launch_us_mean"] / (mean_launch * 1e3), 4)
     for c in extra_controls.values():
@@ -334,19 +346,33 @@ def median_single_call_us(torch, step, first: int, stream, calls: int = 60, skip
 
 
 PREHEAT_SECONDS = 0.05
+# GPU work queued ahead of the event-timed pass, per step: more than the host
+# needs to enqueue one lse_forward call (a few microseconds through ctypes).
+LEAD_US_PER_STEP = 15.0
 
 
 def time_control(torch, step, steps: int, stream) -> float:
     """Untimed launches of a control `step` for at least PREHEAT_SECONDS of
     back-to-back GPU work (the GPU's steady state, and the control's own
-    warmup), then the mean microseconds per launch of K timed ones."""
+    warmup), then the mean microseconds per launch of K timed ones queued
+    right behind them (one HIP event pair)."""
     for i in range(5):
         step(i)
     per = max(event_mean_us(torch, step, 5, 5, stream) * 1e-6, 1e-6)
-    n = int(np.ceil(PREHEAT_SECONDS / per)) if PREHEAT_SECONDS > 0 else 0
+    # the untimed launches also lead the timed ones: enough GPU work for the
+    # host to enqueue all K before the first event is reached
+    n = max(int(np.ceil(PREHEAT_SECONDS / per)) if PREHEAT_SECONDS > 0 else 0,
+            int(np.ceil(steps * LEAD_US_PER_STEP * 1e-6 / per)))
     for i in range(10, 10 + n):
         step(i)
-    return event_mean_us(torch, step, 10 + n, steps, stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(10 + n, 10 + n + steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
 
 
 def time_read_control(torch, bufs, nbytes: int, plan: dict, steps: int, stream) -> dict:
@@ -365,7 +391,7 @@ def time_read_control(torch, bufs, nbytes: int, plan: dict, steps: int, stream) 
 
     us = time_control(torch, step, steps, stream)
     return {"kernel": "read_chunks (XOR of each chunk's words)", "grid": grid, "block": block,
-            "launch_us_mean": round(us, 2), "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+            "launch_us_mean": round(us, 2), "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}, step
 
 
 def time_rows_control(torch, bufs, nbytes: int, grid: int, store: bool, steps: int,
@@ -406,9 +432,8 @@ def time_copy_control(torch, bufs, nbytes: int, steps: int, stream) -> dict:
         RC.lse_control_copy(bufs[i % len(bufs)].data_ptr(), dst.data_ptr(), nbytes, grid, block, sh)
 
     us = time_control(torch, step, steps, stream)
-    del dst
     return {"kernel": "copy_chunks (x copied to a buffer of grad_x's size)", "grid": grid, "block": block,
-            "launch_us_mean": round(us, 2), "GBs_read_plus_written": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}
+            "launch_us_mean": round(us, 2), "GBs_read_plus_written": round(2 * nbytes / (us * 1e-6) / 1e9, 1)}, step
 
 
 def sweep_read_control(torch, cfg: int, steps: int, warmup: int) -> list:
@@ -423,8 +448,8 @@ def sweep_read_control(torch, cfg: int, steps: int, warmup: int) -> list:
     res = []
     for grid in (256, 512, 1024, 2048, 4096, 8192, 16384):
         for block in (256, 512, 1024):
-            c = time_read_control(torch, bufs, nbytes, {"grid": grid, "block": block}, steps,
-                                  stream)
+            c, _ = time_read_control(torch, bufs, nbytes, {"grid": grid, "block": block}, steps,
+                                     stream)
             rec = {"control_sweep": cfg, "grid": grid, "block": block,
                    "launch_us_mean": c["launch_us_mean"], "GBs": c["GBs"]}
             log(json.dumps(rec))

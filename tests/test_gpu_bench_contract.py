@@ -109,3 +109,15 @@ def test_other_modes(args):
         assert r["read_control"]["launch_us_mean"] > 0
     if "--graph" in args:
         assert d["config"]["timed_as"].startswith("one HIP graph")
+
+
+def test_all_workloads_for_another_op():
+    """--all for the token log-probability: the other four workloads under
+    `configs`, each checked against the oracle on every row."""
+    d = run_bench("--config", "1", "--op", "logprob", "--all", "--steps", "10", "--warmup", "2",
+                  "--no-cpu-baseline")
+    check_common(d, 10)
+    assert set(d["configs"]) == {"2", "3", "4", "5"}
+    for rec in d["configs"].values():
+        assert rec["op"] == "logprob" and rec["us_per_launch"] > 0
+        assert rec["rows_checked"] == rec["rows"] and rec["max_err_over_tol"] <= 1.0
