@@ -7,7 +7,7 @@
 // each thread keeping a register accumulator (§3.1): a running maximum and a
 // sum of exponentials, the online form its §2.2 describes. Here a lane keeps
 //
-//     m  a reference: the largest element folded so far, or (fold_lazy) a
+//     m  a reference: the largest element folded so far, or (fold_lazy_vecs) a
 //        value at most 32*ln2 below it (natural units, exact),
 //     c  = fl(clamp(m, -2^30, 2^30) * log2(e)), the base-2 reference,
 //     s  = sum over folded x of 2^(x*log2(e) - c),
@@ -269,8 +269,21 @@ __device__ __forceinline__ void fold(Acc& a, const float* f) {
     a.c = c;
 }
 
-// Fold N values lazily. The batch's terms are first taken against the lane's
-// current reference c, with no maximum computed. That sum is kept when it is
+// Sum of v[0..N) as the same tree sum_exp_of<N> builds (halves of N / 2 and
+// N - N / 2, recursively).
+template <int N>
+__device__ __forceinline__ float tree_sum(const float* v) {
+    if constexpr (N == 1) {
+        return v[0];
+    } else {
+        constexpr int H = N / 2;
+        return tree_sum<H>(v) + tree_sum<N - H>(v + H);
+    }
+}
+
+// Fold a batch of U 16-byte vectors of type D (N = U * K values) lazily. The
+// batch's terms are first taken against the lane's current reference c, with
+// no maximum computed. That sum is kept when it is
 // at most 2^32 and the reference is a finite maximum within +-2^30; otherwise
 // (a new maximum more than 32*ln2 above the reference, an infinity, a NaN, no
 // finite maximum yet, or the clamp in use) the batch is folded again by fold<N>,
@@ -283,10 +296,26 @@ __device__ __forceinline__ void fold(Acc& a, const float* f) {
 // reference is not a finite value within +-2^30 (its first batch, above all)
 // goes to fold<N> directly: its lazy sum would be thrown away. Where each lane
 // folds only one or two batches per row, that halves the exponentials.
-template <int N>
-__device__ __forceinline__ void fold_lazy(Acc& a, const float* f) {
+//
+// The lazy test reads only the accumulator, so it is taken before any vector
+// is decoded: each vector's exponentials start as soon as that vector's load
+// has returned, and the batch's arithmetic overlaps the arrival of its later
+// loads (at a row's end only the last vector's terms remain after the last
+// load). With U and K powers of two, the per-vector sums joined by
+// tree_sum<U> are the tree of sum_exp_of<N> over the decoded batch.
+template <DType D, int U>
+__device__ __forceinline__ void fold_lazy_vecs(Acc& a, const u32x4 (&w)[U]) {
+    constexpr int K = Elem<D>::kPerVec;
+    static_assert((U & (U - 1)) == 0 && (K & (K - 1)) == 0, "the two trees agree for powers of two");
     if (__builtin_fabsf(a.m) <= kClamp) {
-        const float t = sum_exp_of<N>(f, a.c);
+        float tv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float f[K];
+            decode<D>(w[u], f);
+            tv[u] = sum_exp_of<K>(f, a.c);
+        }
+        const float t = tree_sum<U>(tv);
         if (t <= 0x1p32f) {
             const float s = a.s;
             const float sum = s + t;
@@ -296,16 +325,28 @@ __device__ __forceinline__ void fold_lazy(Acc& a, const float* f) {
             return;
         }
     }
-    fold<N>(a, f);
+    // The empty asm makes these words opaque, so that the decodes here are
+    // not merged with the lazy path's and hoisted above its test (which
+    // would wait for every load of the batch before the first exponential).
+    float f[U * K];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        u32x4 v = w[u];
+        asm volatile("" : "+v"(v));
+        decode<D>(v, &f[u * K]);
+    }
+    fold<U * K>(a, f);
 }
 
-// fold_lazy with the lazy sum always taken first and a single branch: for
-// accumulators that fold many small batches (one per column and step in the
-// non-last-axis kernel), where a second branch per fold costs more than the
-// exponentials it saves on an accumulator's first batch.
+// The lazy fold of N decoded values f whose terms against the accumulator's
+// reference, sum_exp_of<N>(f, a.c), the caller has already summed into t:
+// for accumulators that fold many small batches (one per column and step in
+// the non-last-axis kernel), where the terms are computed as their loads
+// return and a second branch per fold would cost more than the exponentials
+// it saves on an accumulator's first batch. t is kept under the lazy rule of
+// fold_lazy_vecs; otherwise the batch is folded again by fold<N>.
 template <int N>
-__device__ __forceinline__ void fold_lazy_flat(Acc& a, const float* f) {
-    const float t = sum_exp_of<N>(f, a.c);
+__device__ __forceinline__ void fold_lazy_terms(Acc& a, const float* f, float t) {
     if (t <= 0x1p32f && __builtin_fabsf(a.m) <= kClamp) {
         const float s = a.s;
         const float sum = s + t;

@@ -10,7 +10,7 @@
 // torch.logsumexp (abstract, §6); this covers the reduction axes other than
 // the last (inner == 1 is lse_forward). Same arithmetic as the row kernels:
 // each element read once, a per-lane (max, exp-sum) accumulator folded lazily
-// (fold_lazy_flat), pairwise merges, one fp32 per output.
+// (fold_lazy_terms), pairwise merges, one fp32 per output.
 //
 // Layout. The reduced elements of one output are inner elements apart, and
 // neighbouring outputs are neighbours in memory. A lane owns K adjacent
@@ -96,8 +96,13 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
         }
         __builtin_amdgcn_sched_barrier(0);
     };
+    // Each column's U steps fold lazily, with the terms taken step by step: a
+    // step's K exponentials depend only on that step's load and the columns'
+    // references, so they start as soon as the load has returned, and the
+    // arithmetic overlaps the later steps' loads. The per-column sums (the
+    // tree of sum_exp_of<U>) and lazy tests follow the last step.
     auto fold_batch = [&](const Batch& b, bool guarded) {
-        float f[U][K];
+        float f[U][K], e[U][K];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if constexpr (VEC)
@@ -108,13 +113,24 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
 #pragma unroll
                 for (int k = 0; k < K; ++k) f[u][k] = -kInf;
             }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                e[u][k] = exp2_hw(__builtin_fmaf(f[u][k], kLog2e, -a[k].c));
+                // Ordered empty asm pins the step's terms here: otherwise the
+                // compiler moves each term next to its column's sum, and the
+                // first column's sum waits for every step's load.
+                asm volatile("" : "+v"(e[u][k]));
+            }
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            float g[U];
+            float g[U], h[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) g[u] = f[u][k];
-            fold_lazy_flat<U>(a[k], g);
+            for (int u = 0; u < U; ++u) {
+                g[u] = f[u][k];
+                h[u] = e[u][k];
+            }
+            fold_lazy_terms<U>(a[k], g, tree_sum<U>(h));
         }
     };
 

@@ -11,7 +11,7 @@
 // non-temporal loads with many bytes in flight per compute unit, and keep the
 // per-element VALU work of the streaming loop to decode, one fma, one
 // v_exp_f32 and one add (the running maximum is only refreshed when a batch
-// outgrows it: fold_lazy).
+// outgrows it: fold_lazy_vecs).
 //
 // Three schedules, picked on the host by shape (lse_api.cpp):
 //
@@ -487,12 +487,7 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto fold_batch = [&](const u32x4 (&w)[U]) {
-        float f[U * K];
-#pragma unroll
-        for (int u = 0; u < U; ++u) decode<D>(w[u], &f[u * K]);
-        fold_lazy<U * K>(a, f);
-    };
+    auto fold_batch = [&](const u32x4 (&w)[U]) { fold_lazy_vecs<D, U>(a, w); };
     auto fold_guarded = [&](const u32x4 (&w)[U]) {
         u32x4 m[U];
 #pragma unroll
