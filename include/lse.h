@@ -86,9 +86,9 @@ typedef enum {
  * Create a handle on HIP device `device` (an index as for hipSetDevice).
  * Queries the compute-unit count, allocates the split-row workspace
  * (LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS (max, sum) pairs plus one
- * counter per row, each in its own 256 bytes, about 0.75 MiB, the counters
- * zeroed) and lse_forward_dim's workspace (LSE_DIM_MAX_PAIRS pairs, 32 MiB),
- * and synchronises once. On success *out receives the handle; on failure
+ * counter per row, each in its own 256 bytes, about 0.75 MiB, all zeroed)
+ * and lse_forward_dim's workspace (LSE_DIM_MAX_PAIRS pairs, 32 MiB), and
+ * synchronises once. On success *out receives the handle; on failure
  * *out is set to NULL.
  * Errors: INVALID_ARG (out NULL, device out of range), NO_DEVICE (no device
  * or not gfx950), ALLOC, HIP.
@@ -243,7 +243,7 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void *x, lse_dtype_t dtype,
  * LSE_SPLIT_MAX_PARTS pairs per launch; longer inputs go in several launches,
  * so every shape fits, and a plan that did not would be rejected with
  * INVALID_ARG before any launch). The first call on a device looks the array
- * up and enqueues one small kernel on `stream` that zeroes the counters (again
+ * up and enqueues one small kernel on `stream` that zeroes it (again
  * on later calls while that kernel was only captured, not run); lse_create on
  * a device does the same set-up. Every call on a GPU shares that GPU's
  * scratch: calls that overlap on one GPU (other streams, threads or graph

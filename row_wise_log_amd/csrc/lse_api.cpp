@@ -18,7 +18,7 @@
 struct lse_handle_s {
     int device;
     int n_cu;
-    unsigned* ws_pairs;  // LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS (max, sum) pairs
+    unsigned* ws_pairs;  // LSE_SPLIT_MAX_ROWS * LSE_SPLIT_MAX_PARTS (max, sum) pairs, zero between calls
     unsigned* counters;  // LSE_SPLIT_MAX_ROWS arrival counters, 256 bytes apart, zero between calls
     unsigned* dim_pairs; // LSE_DIM_MAX_PAIRS (max, sum) pairs for lse_forward_dim's split
     int schedule;        // lse_schedule_t forced for later calls (AUTO = by shape)
@@ -356,7 +356,7 @@ lse_status_t lse_create(lse_handle_t* out, int device) {
             // when it can be (its entry point retries and reports otherwise).
             if (lse::noalloc_prepare(device, nullptr, nullptr, nullptr) != LSE_OK)
                 (void)hipGetLastError();
-            if (hipMemset(h->counters, 0, count_bytes) != hipSuccess ||
+            if (hipMemset(h->ws_pairs, 0, pair_bytes + count_bytes) != hipSuccess ||
                 hipDeviceSynchronize() != hipSuccess)
                 st = LSE_ERR_HIP;
         }

@@ -297,10 +297,13 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
 
     if constexpr (SPLIT) {
         // Count this workgroup in once every lane's pair stores have
-        // completed; the last of the tile's parts to arrive merges them (the
-        // agent-scope protocol of the split-row kernel in lse_kernels.hip:
-        // sc1 stores completed by s_waitcnt vmcnt(0) before the counter add,
-        // sc1 loads issued after the add has returned).
+        // completed; the last of the tile's parts to arrive merges them. In
+        // the gfx942/gfx950 memory model, atomic loads and stores at agent
+        // scope are issued with the sc1 bit and performed at the point of
+        // coherence of all the device's L2s, and atomic read-modify-writes
+        // at agent scope are coherent across them: s_waitcnt vmcnt(0) has
+        // the pairs there before the counter add issues, and the merging
+        // part's loads issue after its add has returned.
         __shared__ int is_last;
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);

@@ -532,45 +532,59 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
     Merged b = block_merge<BLOCK>(a.m, a.c, acc_sum(a), pairs);
 
     if constexpr (SPLIT) {
-        // Publish this part's pair, then count the part in. What this relies
-        // on is the gfx942/gfx950 memory model for agent scope: atomic loads
-        // and stores at agent scope are issued with the sc1 bit and access
-        // the point of coherence of all the device's L2s, and atomic
-        // read-modify-writes at agent scope are coherent across them; a
-        // wave's s_waitcnt vmcnt(0) completes its earlier stores before any
-        // later memory instruction issues. So the pair (sc1 stores) is at the
-        // point of coherence before the counter add is performed, and the
-        // last part, whose sc1 loads issue only after its add has returned
-        // (the barrier below orders them after it), reads every part's pair.
-        // This is the release / acquire sequence the compiler emits at agent
-        // scope minus the L2 writeback and invalidate, which only non-atomic
-        // accesses need (none is used for the pairs).
+        // Merge across the row's parts in the same launch. Each part's
+        // workgroup publishes its (max, sum) as one 64-bit word in the row's
+        // slot for that part and counts itself in on the row's counter; the
+        // part that counts last merges. Slots hold 0 between launches (the
+        // workspace is cleared when it is made, and every launch clears what
+        // it used), and no pair is 0: a sum of 0 goes with a maximum of -inf.
+        //
+        // What this relies on is the gfx942/gfx950 memory model at agent
+        // scope: atomic loads, stores and read-modify-writes at agent scope
+        // are issued with the sc1 bit and performed at the point of
+        // coherence of all the device's L2s, and an aligned 64-bit access is
+        // single-copy atomic. So a slot read at agent scope holds either 0
+        // or the whole pair its part wrote in this launch. The counter only
+        // tells the last part that every part has issued its store, not that
+        // the store has been performed (no part waits for its store before
+        // counting in: that wait was a memory round trip on the critical
+        // path of every split row), so the last part reads each slot until
+        // it is not 0. Each slot is cleared by the lane that read it (or, for
+        // the last part's own slot, by the thread that wrote it), so that in
+        // each slot's modification order the clearing store follows the pair,
+        // as it does for the counter, whose clearing follows the last add.
+        unsigned long long* slots = reinterpret_cast<unsigned long long*>(ws_pairs) + row * nparts;
+        const unsigned long long mine =
+            (static_cast<unsigned long long>(__float_as_uint(b.s)) << 32) | __float_as_uint(b.m);
         if (tid == 0) {
-            unsigned* slot = ws_pairs + 2 * (row * nparts + part);
-            __hip_atomic_store(slot, __float_as_uint(b.m), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(slot + 1, __float_as_uint(b.s), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const unsigned prev = __hip_atomic_fetch_add(counters + row * kCounterWords, 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(slots + part, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned prev = __hip_atomic_fetch_add(counters + row * kCounterWords, 1u,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             is_last = (prev == static_cast<unsigned>(nparts - 1));
         }
         __syncthreads();
         if (!is_last) return;
+        const bool other = tid < nparts && tid != part;
+        unsigned long long v = tid == part ? mine : 0ull;
+        if (other) {
+            // A pair's store was issued before its part counted in, so it
+            // lands within a memory round trip or so; the bound only makes
+            // the wait finite by construction.
+            for (int i = 0; v == 0 && i < kSplitSpinLimit; ++i)
+                v = __hip_atomic_load(slots + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         float pm = -kInf, ps = 0.0f;
         if (tid < nparts) {
-            const unsigned* slot = ws_pairs + 2 * (row * nparts + tid);
-            pm = __uint_as_float(__hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            ps = __uint_as_float(
-                __hip_atomic_load(slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            pm = __uint_as_float(static_cast<unsigned>(v));
+            ps = __uint_as_float(static_cast<unsigned>(v >> 32));
         }
         b = block_merge<BLOCK>(pm, base2_ref(pm), ps, pairs);
-        if (tid == 0)
+        if (other) __hip_atomic_store(slots + tid, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) {
+            __hip_atomic_store(slots + part, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(counters + row * kCounterWords, 0u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 
     float r;

@@ -18,6 +18,10 @@ enum : int { kSchedRowsPerWave = 1, kSchedRowPerWG = 2, kSchedSplitRow = 3 };
 // the counters in one line and 3.0 us with each in its own.
 constexpr int kCounterWords = 64;
 
+// Bound on the merging part's reads of one split-row slot (each a memory
+// round trip); a pair is expected within the first few.
+constexpr int kSplitSpinLimit = 1 << 16;
+
 struct LaunchArgs {
     // what to run
     int schedule;
@@ -38,7 +42,7 @@ struct LaunchArgs {
     float* out;          // LSE per row; may be NULL when targets is set
     const int64_t* targets;  // token log-probabilities: target column per row (NULL: LSE only)
     float* logp;         // x[r, targets[r]] - LSE per row (with targets)
-    unsigned* ws_pairs;  // split-row (max, sum) pairs, 2 words each
+    unsigned* ws_pairs;  // split-row (max, sum) pairs, 2 words each, zero between calls
     unsigned* counters;  // split-row arrival counters, one per row (kCounterWords apart), zero between calls
     hipStream_t stream;
 };
@@ -49,7 +53,7 @@ hipError_t launch(const LaunchArgs& a);
 // What a forward call needs besides its operands: the device, its CU count,
 // the schedule and tuning overrides (0 = the planner's choice), and the split
 // schedule's workspace with its capacity (pairs of 8 bytes; counters
-// kCounterWords words apart, zero between calls). A handle provides them, or
+// kCounterWords words apart; both zero between calls). A handle provides them, or
 // the no-allocation entry point its per-device scratch.
 struct ForwardContext {
     int device;
@@ -72,8 +76,8 @@ lse_status_t run_forward(const ForwardContext& c, const void* x, lse_dtype_t dty
                          float* logp, hipStream_t stream);
 
 // The no-allocation entry point's per-device scratch (lse_noalloc.hip): look
-// up the current device's copy (once) and clear its arrival counters on
-// `stream` unless a launch already did. ptr and n_cu may be NULL.
+// up the current device's copy (once) and clear its pairs and arrival
+// counters on `stream` unless a launch already did. ptr and n_cu may be NULL.
 lse_status_t noalloc_prepare(int device, hipStream_t stream, unsigned char** ptr, int* n_cu);
 
 // The backward pass, grad_x = grad_out * exp(x - lse) (lse_backward.hip).

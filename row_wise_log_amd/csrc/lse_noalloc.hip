@@ -11,10 +11,10 @@
 // which in host code is only a host-side stand-in.
 //
 // Every call on one GPU shares that GPU's scratch, which keeps the last call's
-// contents. The arrival counters must be zero when a launch starts: they are
-// cleared once per device by a small fill kernel on the first call's stream
-// (again on later calls while the clearing launch was only captured into a
-// graph), and every split launch leaves them zero. Calls that overlap on one
+// contents. The pairs and arrival counters must be zero when a launch starts:
+// they are cleared once per device by a small fill kernel on the first call's
+// stream (again on later calls while the clearing launch was only captured
+// into a graph), and every split launch leaves what it used zero. Calls that overlap on one
 // GPU (two streams, two threads, two graphs replayed at once) race on the
 // scratch and give wrong results; serialise them.
 #include <hip/hip_runtime.h>
@@ -43,7 +43,7 @@ constexpr int kMaxDevices = 64;
 
 struct DeviceScratch {
     bool ready = false;     // address and CU count known
-    bool cleared = false;   // counters zeroed by a launch that ran (not only captured)
+    bool cleared = false;   // pairs and counters zeroed by a launch that ran (not only captured)
     unsigned char* ptr = nullptr;  // this device's copy of `scratch`
     int n_cu = 0;
 };
@@ -79,8 +79,8 @@ lse_status_t set_up(int device, DeviceScratch& d) {
 
 namespace lse {
 
-// Set up the scratch of the current device `device` and clear its counters
-// on `stream` if no launch has cleared them yet. Called by lse_create (with
+// Set up the scratch of the current device `device` and clear it on
+// `stream` if no launch has cleared it yet. Called by lse_create (with
 // the null stream, which it then synchronises) and by the entry point.
 lse_status_t noalloc_prepare(int device, hipStream_t stream, unsigned char** ptr, int* n_cu) {
     if (device < 0 || device >= kMaxDevices) return LSE_ERR_NO_DEVICE;
@@ -89,8 +89,8 @@ lse_status_t noalloc_prepare(int device, hipStream_t stream, unsigned char** ptr
     lse_status_t st = set_up(device, d);
     if (st != LSE_OK) return st;
     if (!d.cleared) {
-        unsigned* counters = reinterpret_cast<unsigned*>(d.ptr + kPairBytes);
-        hipLaunchKernelGGL(zero_words, dim3(64), dim3(256), 0, stream, counters, kCounterWordsAll);
+        hipLaunchKernelGGL(zero_words, dim3(64), dim3(256), 0, stream,
+                           reinterpret_cast<unsigned*>(d.ptr), kScratchBytes / 4);
         if (hipGetLastError() != hipSuccess) return LSE_ERR_HIP;
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
