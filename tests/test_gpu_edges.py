@@ -295,3 +295,37 @@ def test_split_alternating_inputs(torch_gpu, handle, oracle, dtype, rows, cols):
             assert np.array_equal(o[i].view(np.uint32), o[i % 2].view(np.uint32)), (sched, i)
         compare(o[0], refs[0], dtype, f"alternating a {sched}")
         compare(o[1], refs[1], dtype, f"alternating b {sched}")
+
+
+def test_split_alternating_part_counts(torch_gpu, handle, oracle):
+    """Back-to-back split-row calls on one handle whose plans cut rows into
+    different numbers of parts, so that each call's (row, part) slots overlap
+    the previous call's at other offsets: every call must leave the slots it
+    used clear for the next, whatever its layout. Each output must equal the
+    first of its shape bit for bit and match the oracle."""
+    torch = torch_gpu
+    shapes = [("f32", 64, 32000), ("bf16", 8, 128256), ("f32", 3, 300_001), ("bf16", 40, 70_000)]
+    devs, refs, codes, plans = [], [], [], []
+    for k, (dtype, rows, cols) in enumerate(shapes):
+        v = np.random.default_rng(40 + k).normal(0, 3, size=(rows, cols)).astype(np.float32)
+        x = workloads.f32_to_bf16_bits(v) if dtype == "bf16" else v
+        refs.append(oracle.lse(x, dtype, threads=8))
+        devs.append(torch.from_numpy(x.view(np.int16) if dtype == "bf16" else x).to("cuda"))
+        codes.append(B.LSE_DTYPE_BF16 if dtype == "bf16" else B.LSE_DTYPE_F32)
+        plans.append(B.lse_plan(codes[-1], rows, cols, cols, devs[-1].data_ptr(), 256, 0))
+    assert all(p["schedule"] == 3 for p in plans), plans
+    assert len({p["parts"] for p in plans}) > 1, plans
+    calls = 120
+    outs = [torch.empty((calls // len(shapes), rows), device="cuda") for _, rows, _ in shapes]
+    stream = torch.cuda.current_stream().cuda_stream
+    note(f"split alternating part counts {[p['parts'] for p in plans]}")
+    for i in range(calls):
+        k = i % len(shapes)
+        _, rows, cols = shapes[k]
+        B.lse_forward(handle, devs[k].data_ptr(), codes[k], rows, cols, cols,
+                      outs[k][i // len(shapes)].data_ptr(), stream)
+    torch.cuda.synchronize()
+    for k, (dtype, rows, cols) in enumerate(shapes):
+        o = outs[k].cpu().numpy()
+        assert np.all(o.view(np.uint32) == o[0].view(np.uint32)), (dtype, rows, cols)
+        compare(o[0], refs[k], dtype, f"alternating parts {dtype} {rows}x{cols}")

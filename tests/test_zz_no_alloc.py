@@ -90,3 +90,36 @@ def test_noalloc_alternating_split_inputs(torch_gpu, oracle):
     got = outs.cpu().numpy()
     for i in range(calls):
         compare(got[i], refs[i % 2], "f32", f"noalloc alternating call {i}")
+
+
+def test_noalloc_alternating_part_counts(torch_gpu, oracle):
+    """Split-row calls through the shared scratch whose plans cut rows into
+    16, 64 and 32 parts, back to back: each call's (row, part) slots overlap
+    the previous call's at other offsets, so each must leave what it used
+    clear. Every output equals the first of its shape bit for bit and
+    matches the oracle."""
+    torch = torch_gpu
+    shapes = [(64, 32000), (8, 128256), (40, 70_000)]
+    devs, refs, parts = [], [], []
+    for k, (rows, cols) in enumerate(shapes):
+        x = np.random.default_rng(60 + k).normal(0, 3, size=(rows, cols)).astype(np.float32)
+        refs.append(oracle.lse(x, "f32", threads=8))
+        devs.append(torch.from_numpy(x).to("cuda"))
+        plan = B.lse_plan(B.LSE_DTYPE_F32, rows, cols, cols, devs[-1].data_ptr(), 256, 0)
+        assert plan["schedule"] == B.LSE_SCHED_SPLIT_ROW
+        parts.append(plan["parts"])
+    assert len(set(parts)) == len(shapes), parts
+    calls = 90
+    outs = [torch.empty((calls // len(shapes), rows), device="cuda") for rows, _ in shapes]
+    stream = torch.cuda.current_stream().cuda_stream
+    note(f"noalloc alternating part counts {parts}")
+    for i in range(calls):
+        k = i % len(shapes)
+        rows, cols = shapes[k]
+        B.lse_forward_noalloc(devs[k].data_ptr(), B.LSE_DTYPE_F32, rows, cols, cols,
+                              outs[k][i // len(shapes)].data_ptr(), stream)
+    torch.cuda.synchronize()
+    for k, (rows, cols) in enumerate(shapes):
+        o = outs[k].cpu().numpy()
+        assert np.all(o.view(np.uint32) == o[0].view(np.uint32)), (rows, cols)
+        compare(o[0], refs[k], "f32", f"noalloc alternating parts {rows}x{cols}")
