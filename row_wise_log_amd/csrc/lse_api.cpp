@@ -54,9 +54,9 @@ constexpr int kSplitWavesPerCU = 4;
 // Just over one row per CU (up to 5/4), one workgroup per row leaves most CUs
 // one row and some two; rows of 1 MiB and more then split into four parts of
 // 256 threads. Measured at steady state with bench.py --ab (257 to 320 rows of
-// 1 and 4 MiB, bf16 and fp32): 5-13 % faster than one 256-thread workgroup
-// per row, 11-23 % faster than 512 threads; rows of 256 KiB split the same
-// way are 1-2 % slower, so they are not split.
+// 1 and 4 MiB, bf16 and fp32): 5-15 % faster than one 256-thread workgroup
+// per row, 10-23 % faster than 512 threads; rows of 256 KiB split the same
+// way gain nothing or are 2 % slower, so they are not split.
 constexpr int64_t kSplitQuarterRowBytes = 1 << 20;
 // lse_forward_dim: column groups per workgroup (the other 256 / 32 = 8 lanes
 // of each column group take consecutive j), doubled where there are columns
