@@ -953,6 +953,41 @@ def summarize_trace_runs(directory: str, min_len: int = 50) -> str:
     return "\n".join(out)
 
 
+CONTROL_KERNELS = ("read_chunks", "copy_chunks", "rows64_chunks")
+
+
+def summarize_event_passes(directory: str, steps: int = 1000) -> str:
+    """Markdown table of the event-timed passes in a kernel trace of bench.py.
+    bench.py runs a workload's warmup and wall-clock launches, then a lead of
+    control launches, then the event-timed launches of the same kernel: so a
+    run of a library kernel whose previous run is a control kernel and whose
+    run before that is the same kernel and launch shape is an event pass, and
+    its first `steps` dispatches are the timed launches. Reported with the
+    mean of the control's lead run."""
+    rows = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"]))
+    runs, cur, key0 = [], [], None
+    for r in rows:
+        block = int(r["Workgroup_Size_X"])
+        key = (short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(block, 1), block)
+        if key != key0 and cur:
+            runs.append((key0, cur))
+            cur = []
+        key0 = key
+        cur.append((int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
+    if cur:
+        runs.append((key0, cur))
+    out = ["| first dispatch | kernel | workgroups x threads | timed dispatches | mean us | min us | max us | "
+           "control lead before it: dispatches, mean us |", "|---|---|---|---|---|---|---|---|"]
+    for (k2, _), (k1, lead), (key, v) in zip(runs, runs[1:], runs[2:]):
+        if k2 != key or "lse::" not in key[0] or not any(c in k1[0] for c in CONTROL_KERNELS):
+            continue
+        a = np.array([u for _, u in v[:steps]])
+        c = np.array([u for _, u in lead])
+        out.append(f"| {v[0][0]} | `{key[0]}` | {key[1]} x {key[2]} | {len(a)} | {a.mean():.2f} | "
+                   f"{a.min():.2f} | {a.max():.2f} | {len(c)}, {c.mean():.2f} |")
+    return "\n".join(out)
+
+
 def counter_means(directory: str) -> dict:
     """{kernel: {counter: mean value per dispatch}} from a counter collection."""
     acc: dict[str, dict[str, list]] = {}
@@ -1085,7 +1120,9 @@ def main() -> int:
     ap.add_argument("--ab-blocks", type=int, default=4)
     ap.add_argument("--ab-block-ms", type=float, default=30.0)
     ap.add_argument("--summarize-trace", metavar="DIR",
-                    help="print a markdown summary of a rocprofv3 kernel trace (CSV) and exit")
+                    help="print a markdown summary of a rocprofv3 kernel trace (CSV) and exit: per "
+                         "kernel, per run of consecutive dispatches, and the event-timed passes "
+                         "(their first --steps dispatches)")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="print a markdown summary of a rocprofv3 counter collection and exit")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -1102,6 +1139,8 @@ def main() -> int:
         print(summarize_trace(args.summarize_trace))
         print()
         print(summarize_trace_runs(args.summarize_trace))
+        print()
+        print(summarize_event_passes(args.summarize_trace, args.steps))
         return 0
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))

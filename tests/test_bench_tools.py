@@ -122,3 +122,29 @@ def test_parse_plan():
     assert (p["schedule"], p["block"], p["parts"], p["unroll"]) == ("split_row", 256, 4, 0)
     with pytest.raises(SystemExit):
         bench.parse_plan("blocks=256")
+
+
+def test_event_passes_are_the_runs_after_a_control_lead(tmp_path):
+    """An event pass is a library kernel's run whose previous run is a control
+    (the lead) and whose run before that is the same kernel and shape (its
+    warmup and wall-clock pass); only its first `steps` dispatches count."""
+    ctl = "void (anonymous namespace)::read_chunks<512>(unsigned int const*, long, long, unsigned int*)"
+    other = ("void lse::stream_rows<(lse::DType)0, 64, 4, true, false>(char const*, long, long, "
+             "float*, int, unsigned int*, unsigned int*, long const*, float*)")
+    rows, t, did = [], 0, 0
+    # control (its own timed run), LSE warmup + wall pass, control lead, LSE event
+    # pass + 60 single calls (slower), then another kernel after a control run
+    # (not an event pass: no earlier run of it)
+    for n, name, dur in ((100, ctl, 21_000), (300, HEADLINE, 22_000), (50, ctl, 21_000),
+                         (1000, HEADLINE, 21_500), (60, HEADLINE, 30_000), (80, ctl, 5_000),
+                         (1200, other, 5_000)):
+        for _ in range(n):
+            did += 1
+            rows.append({"Dispatch_Id": did, "Kernel_Name": name, "Start_Timestamp": t,
+                         "End_Timestamp": t + dur, "Workgroup_Size_X": 512,
+                         "Grid_Size_X": 512 * 512})
+            t += dur + 100
+    write_csv(tmp_path / "host" / "1" / "run_kernel_trace.csv", TRACE_COLS, rows)
+    table = bench.summarize_event_passes(str(tmp_path), steps=1000).splitlines()
+    assert len(table) == 3, table
+    assert "| 451 |" in table[2] and "| 1000 | 21.50 |" in table[2] and "| 50, 21.00 |" in table[2]
