@@ -14,7 +14,8 @@ padded and misaligned x and gradient rows (rows misaligned alike in x and
 grad_x take the peeled 16-byte path, the others the element path).
 
 LSE_SWEEP_SEED=k (default 0) shifts every seed by 1000 k, for a wider sweep
-run by hand; the default cases are the ones the suite always runs.
+run by hand; a list or range ("1-12", "3,5") runs each shift in the same
+process. The default cases are the ones the suite always runs.
 """
 import os
 
@@ -31,7 +32,17 @@ from row_wise_log_amd import binding as B
 pytestmark = pytest.mark.gpu
 
 MAX_ELEMS = 3_000_000  # keeps each case's oracle call short
-SEED = 1000 * int(os.environ.get("LSE_SWEEP_SEED", "0"))
+
+
+def _shifts(spec: str) -> list:
+    out = []
+    for part in spec.split(","):
+        a, _, b = part.partition("-")
+        out.extend(range(int(a), int(b or a) + 1))
+    return out
+
+
+SEEDS = [1000 * k for k in _shifts(os.environ.get("LSE_SWEEP_SEED", "0"))]
 
 
 @pytest.fixture(scope="module")
@@ -100,9 +111,10 @@ def row_cases(seed, n):
         yield i, dtype, rows, cols, pad, front, sched, tuning, scale, rng
 
 
+@pytest.mark.parametrize("seed", SEEDS)
 @pytest.mark.parametrize("block", range(8))
-def test_random_rows(torch_gpu, handle, oracle, block):
-    for i, dtype, rows, cols, pad, front, sched, tuning, scale, rng in row_cases(SEED + 100 + block, 50):
+def test_random_rows(torch_gpu, handle, oracle, seed, block):
+    for i, dtype, rows, cols, pad, front, sched, tuning, scale, rng in row_cases(seed + 100 + block, 50):
         full = make_rows(rng, rows, cols + pad, dtype, scale)
         x = full[:, :cols]
         what = (f"block {block} case {i}: {dtype} rows={rows} cols={cols} pad={pad} front={front} "
@@ -137,9 +149,10 @@ def gpu_dim(torch, handle, x3, dtype, front, parts):
     return out.cpu().numpy()[: outer * inner]
 
 
+@pytest.mark.parametrize("seed", SEEDS)
 @pytest.mark.parametrize("block", range(6))
-def test_random_dims(torch_gpu, handle, block):
-    rng = np.random.default_rng(SEED + 200 + block)
+def test_random_dims(torch_gpu, handle, seed, block):
+    rng = np.random.default_rng(seed + 200 + block)
     for i in range(30):
         dtype = ["f32", "bf16"][rng.integers(2)]
         outer, n, inner = log_int(rng, 1, 64), log_int(rng, 1, 60_000), log_int(rng, 1, 5000)
@@ -162,9 +175,10 @@ def test_random_dims(torch_gpu, handle, block):
         compare(got, oracle_mod.lse_dim(x3, dtype, threads=8).ravel(), dtype, what)
 
 
+@pytest.mark.parametrize("seed", SEEDS)
 @pytest.mark.parametrize("block", range(4))
-def test_random_backward(torch_gpu, handle, oracle, block):
-    rng = np.random.default_rng(SEED + 300 + block)
+def test_random_backward(torch_gpu, handle, oracle, seed, block):
+    rng = np.random.default_rng(seed + 300 + block)
     for i in range(30):
         dtype = ["f32", "bf16"][rng.integers(2)]
         cols = log_int(rng, 1, 300_000)
@@ -192,11 +206,12 @@ def test_random_backward(torch_gpu, handle, oracle, block):
         compare_grad(got, ref, d, g, dtype, what)
 
 
+@pytest.mark.parametrize("seed", SEEDS)
 @pytest.mark.parametrize("block", range(3))
-def test_random_token_backward(torch_gpu, handle, oracle, block):
+def test_random_token_backward(torch_gpu, handle, oracle, seed, block):
     """The token log-probability's backward on random shapes and layouts, with
     targets drawn in range and just outside it (rows of NaN)."""
-    rng = np.random.default_rng(SEED + 400 + block)
+    rng = np.random.default_rng(seed + 400 + block)
     for i in range(25):
         dtype = ["f32", "bf16"][rng.integers(2)]
         cols = log_int(rng, 1, 300_000)
