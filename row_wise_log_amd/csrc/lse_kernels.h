@@ -25,9 +25,10 @@
 //                     workgroup merges the lanes' pairs.
 //  stream_rows<SPLIT> too few rows to fill the GPU. Each row is cut into P
 //                     parts, one workgroup each; every part writes its
-//                     (m, s) pair to a workspace, and the last workgroup of
-//                     a row to arrive (an agent-scope counter) merges the P
-//                     pairs in part order and resets the counter.
+//                     (m, s) pair to a workspace slot, and the last
+//                     workgroup of a row to arrive (an agent-scope counter)
+//                     merges the P pairs in part order and clears the slots
+//                     and the counter.
 #pragma once
 
 #include "lse_device.h"
