@@ -962,8 +962,10 @@ def summarize_event_passes(directory: str, steps: int = 1000) -> str:
     control launches, then the event-timed launches of the same kernel: so a
     run of a library kernel whose previous run is a control kernel and whose
     run before that is the same kernel and launch shape is an event pass, and
-    its first `steps` dispatches are the timed launches. Reported with the
-    mean of the control's lead run."""
+    its first `steps` dispatches are the timed launches. Reported with their
+    span (first start to last end, per dispatch: the interval an event pair
+    around them measures, gaps included) and the mean of the control's lead
+    run."""
     rows = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"]))
     runs, cur, key0 = [], [], None
     for r in rows:
@@ -973,18 +975,23 @@ def summarize_event_passes(directory: str, steps: int = 1000) -> str:
             runs.append((key0, cur))
             cur = []
         key0 = key
-        cur.append((int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
+        cur.append((int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3,
+                    int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
     if cur:
         runs.append((key0, cur))
     out = ["| first dispatch | kernel | workgroups x threads | timed dispatches | mean us | min us | max us | "
-           "control lead before it: dispatches, mean us |", "|---|---|---|---|---|---|---|---|"]
+           "span per dispatch us | control lead before it: dispatches, mean us |",
+           "|---|---|---|---|---|---|---|---|---|"]
     for (k2, _), (k1, lead), (key, v) in zip(runs, runs[1:], runs[2:]):
         if k2 != key or "lse::" not in key[0] or not any(c in k1[0] for c in CONTROL_KERNELS):
             continue
-        a = np.array([u for _, u in v[:steps]])
-        c = np.array([u for _, u in lead])
+        timed = v[:steps]
+        a = np.array([e[1] for e in timed])
+        c = np.array([e[1] for e in lead])
+        # first start to last end over the dispatches: what an event pair around them measures
+        span = (timed[-1][3] - timed[0][2]) * 1e-3 / len(timed)
         out.append(f"| {v[0][0]} | `{key[0]}` | {key[1]} x {key[2]} | {len(a)} | {a.mean():.2f} | "
-                   f"{a.min():.2f} | {a.max():.2f} | {len(c)}, {c.mean():.2f} |")
+                   f"{a.min():.2f} | {a.max():.2f} | {span:.2f} | {len(c)}, {c.mean():.2f} |")
     return "\n".join(out)
 
 

@@ -570,9 +570,12 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
         if (other) {
             // A pair's store was issued before its part counted in, so it
             // lands within a memory round trip or so; the bound only makes
-            // the wait finite by construction.
+            // the wait finite by construction. A slot still empty after it
+            // (which the protocol rules out) makes the row's result NaN
+            // rather than a silently wrong number.
             for (int i = 0; v == 0 && i < kSplitSpinLimit; ++i)
                 v = __hip_atomic_load(slots + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (v == 0) v = 0x7FC000007FC00000ull;  // (NaN, NaN)
         }
         float pm = -kInf, ps = 0.0f;
         if (tid < nparts) {

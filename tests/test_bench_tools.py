@@ -148,3 +148,5 @@ def test_event_passes_are_the_runs_after_a_control_lead(tmp_path):
     table = bench.summarize_event_passes(str(tmp_path), steps=1000).splitlines()
     assert len(table) == 3, table
     assert "| 451 |" in table[2] and "| 1000 | 21.50 |" in table[2] and "| 50, 21.00 |" in table[2]
+    # span: 1000 dispatches of 21.5 us with 0.1 us between them
+    assert "| 21.60 |" in table[2]
