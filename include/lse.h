@@ -28,9 +28,9 @@
  * the call. A handle owns a small device workspace for the split-row
  * schedule; calls that share one handle must not run concurrently (use one
  * handle per stream). The compute entry points allocate nothing, never
- * synchronise and enqueue no memset (the split schedules' arrival counters
- * are reset by the kernels that use them), so they may be captured into a
- * HIP graph and the graph replayed.
+ * synchronise and enqueue no memset (the split schedules' pair slots and
+ * arrival counters are cleared by the kernels that use them), so they may be
+ * captured into a HIP graph and the graph replayed.
  *
  * Errors. Every entry point returns an lse_status_t; nothing aborts. The
  * arguments of lse_forward are checked on the host before any HIP call, in
