@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
                                                 int64_t inner, int64_t ncv, int gw, int64_t tile0,
                                                 float* __restrict__ out, int parts,
                                                 unsigned* __restrict__ ws_pairs,
-                                                unsigned* __restrict__ counters) {
+                                                unsigned* __restrict__ counters, int xcd_runs) {
     constexpr int K = VEC ? Elem<D>::kPerVec : 1;
     constexpr int EB = Elem<D>::kBytes;
     __shared__ float lds_m[256 * K];
@@ -47,22 +47,55 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
     const int col = t % gw;
     const int jr = t / gw;               // this lane's step within a load
     const bool active = jr < rw;         // lanes past rw * gw hold nothing
-    const int64_t tl = blockIdx.x / parts;
-    const int part = static_cast<int>(blockIdx.x - tl * parts);
+    // Workgroups go to the XCDs in turn (b mod 8), and each XCD has its own
+    // L2. When a tile's pieces of a row do not start on 128-byte lines (the
+    // one-column path, or a row pitch or base that is not a multiple of 128
+    // bytes), neighbouring tiles share lines, and spread over the XCDs each
+    // such line is fetched once per XCD that needs it. With xcd_runs (the
+    // host's choice for those layouts) each XCD takes a contiguous run of the
+    // launch's (tile, part) pairs instead, so that neighbours share an L2.
+    // (32-bit arithmetic: the grid is below 2^31 workgroups, and a 64-bit
+    // division here delayed every workgroup's first loads.)
+    unsigned wgi = blockIdx.x;
+    if (xcd_runs) {
+        const unsigned b = blockIdx.x, q = gridDim.x / 8, r = gridDim.x % 8, xcd = b % 8;
+        wgi = xcd * q + (xcd < r ? xcd : r) + b / 8;
+    }
+    const unsigned tlu = wgi / static_cast<unsigned>(parts);
+    const int64_t tl = tlu;
+    const int part = static_cast<int>(wgi - tlu * static_cast<unsigned>(parts));
+    // The index arithmetic is 32-bit wherever the sizes allow (n < 2^31 by the
+    // entry point's contract; column groups below 2^32 unless the array is
+    // larger than that): 64-bit divisions, one per lane for the column, took
+    // about a thousand instructions before the first load.
     const int64_t cvs = VEC ? inner / K : inner;  // column groups per outer slice
     const int64_t cv_raw = (tile0 + tl) * gw + col;
     const int64_t cv = cv_raw < ncv ? cv_raw : ncv - 1;  // past the end: read a real column
-    const int64_t o = cv / cvs;
-    const int64_t iv = cv - o * cvs;
+    int64_t o, iv;
+    if (ncv <= 0xFFFFFFFFll) {
+        const unsigned c = static_cast<unsigned>(cv), cs = static_cast<unsigned>(cvs);
+        const unsigned oo = c / cs;
+        o = oo;
+        iv = c - oo * cs;
+    } else {
+        o = cv / cvs;
+        iv = cv - o * cvs;
+    }
     const char* base = x + (o * n * inner + iv * K) * EB;  // element (o, 0, iv*K)
     const int64_t jstride = inner * EB;
 
-    // This part's j range; the lane takes j = pj0 + jr + s * rw for steps s.
-    const int64_t pj0 = n * part / parts;
-    const int64_t pj1 = n * (part + 1) / parts;
-    const int64_t len = pj1 - pj0;
-    const int64_t full_steps = len / rw;             // every lane's j is in range
-    const int64_t steps = (len + rw - 1) / rw;       // the last may be partial
+    // This part's j range, [n * part / parts, n * (part + 1) / parts), in
+    // 32-bit terms: with n = q * parts + r, n * p / parts = q * p + r * p / parts
+    // (r * p < parts^2 <= 2^20). The lane takes j = pj0 + jr + s * rw.
+    const unsigned nu = static_cast<unsigned>(n), pu = static_cast<unsigned>(parts);
+    const unsigned qn = nu / pu, rn = nu - qn * pu;
+    const unsigned partu = static_cast<unsigned>(part);
+    const int64_t pj0 = qn * partu + rn * partu / pu;
+    const int64_t pj1 = qn * (partu + 1) + rn * (partu + 1) / pu;
+    const unsigned lenu = static_cast<unsigned>(pj1 - pj0);
+    const int64_t len = lenu;
+    const int64_t full_steps = lenu / static_cast<unsigned>(rw);   // every lane's j is in range
+    const int64_t steps = (lenu + rw - 1) / static_cast<unsigned>(rw);  // the last may be partial
     const int64_t nfull = full_steps / U;            // whole batches of U steps
     const int64_t rem = steps - nfull * U;           // steps in the guarded batch
 
@@ -330,11 +363,12 @@ hipError_t launch_cols_d(const DimArgs& a) {
     constexpr int U = 4;
     if (a.parts == 1)
         hipLaunchKernelGGL((lse_cols<D, VEC, U, false>), dim3(a.grid), dim3(256), 0, a.stream, a.x,
-                           a.n, a.inner, a.ncv, a.gw, a.tile0, a.out, 1, a.ws_pairs, a.counters);
+                           a.n, a.inner, a.ncv, a.gw, a.tile0, a.out, 1, a.ws_pairs, a.counters,
+                           a.xcd_runs ? 1 : 0);
     else
         hipLaunchKernelGGL((lse_cols<D, VEC, U, true>), dim3(a.grid), dim3(256), 0, a.stream, a.x,
                            a.n, a.inner, a.ncv, a.gw, a.tile0, a.out, a.parts, a.ws_pairs,
-                           a.counters);
+                           a.counters, a.xcd_runs ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -119,6 +119,7 @@ struct DimArgs {
     unsigned* ws_pairs;    // tiles * gw * K * parts (max, sum) pairs of one launch
     unsigned* counters;    // one arrival counter per tile of a launch (kCounterWords apart),
                            // zero between calls
+    bool xcd_runs;         // give each XCD a contiguous run of workgroups (see lse_cols)
     hipStream_t stream;
 };
 
