@@ -449,14 +449,14 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
     };
 
     Acc a = acc_empty();
-    if (part == 0 && tid < head) {
-        float f = load_scalar<D>(rp + tid * EB);
-        fold<1>(a, &f);
-    }
-    if (part == nparts - 1 && tid < tail) {
-        float f = load_scalar<D>(rp + (head + nvec * K + tid) * EB);
-        fold<1>(a, &f);
-    }
+    // The head and tail elements of a row that is not 16-byte aligned: loaded
+    // here, before the batches, but folded only after them, so their memory
+    // round trip overlaps the stream instead of preceding it.
+    float ends[2] = {-kInf, -kInf};
+    const bool has_head = part == 0 && head > 0;  // uniform
+    const bool has_tail = part == nparts - 1 && tail > 0;
+    if (has_head && tid < head) ends[0] = load_scalar<D>(rp + tid * EB);
+    if (has_tail && tid < tail) ends[1] = load_scalar<D>(rp + (head + nvec * K + tid) * EB);
 
     // Batches of U vectors per lane: nfull whole batches, then one guarded
     // batch holding the last rem < U * BLOCK vectors. Software-pipelined:
@@ -528,6 +528,8 @@ __global__ __launch_bounds__(BLOCK) void stream_rows(const char* __restrict__ x,
         }
     }
     if (TOK && nfull < 3) fetch_target();
+
+    if (has_head || has_tail) fold<2>(a, ends);
 
     // Merge the lanes (one barrier), then across parts for a split row.
     Merged b = block_merge<BLOCK>(a.m, a.c, acc_sum(a), pairs);
