@@ -184,11 +184,17 @@ lse_status_t make_plan(lse_dtype_t dtype, int64_t rows, int64_t cols, int64_t ro
         // two rows and others one and 256 threads stream 5-16 % faster
         // (measured at steady state on 224 to 448 rows of 256 KiB and 1 MiB;
         // at 160 and 200 rows 512 threads are 9-12 % faster, from 480 rows to
-        // twice the CUs the two agree).
+        // twice the CUs the two agree). From 15/8 rows per CU, rows of up to
+        // 100 KiB also take 256 threads, so that each lane keeps several
+        // batches: measured on 480 and 512 rows, 3-4 % faster at 64 and 98
+        // KiB (bf16 [512, 50257]: 11.47 -> 11.04 us), while at 128 KiB 512
+        // threads were 3-5 % faster and from 160 KiB the two agree within 2 %.
         int block = 256;
         const int64_t cu = n_cu;
         if (rows <= 2 * cu) {
-            block = (rows * 8 >= 7 * cu && rows * 8 < 15 * cu) ? 256 : 512;
+            const bool band = rows * 8 >= 7 * cu && rows * 8 < 15 * cu;
+            const bool short_rows = rows * 8 >= 15 * cu && cols * esize <= (100 << 10);
+            block = band || short_rows ? 256 : 512;
         } else {
             const int64_t per = nvec / (16 / esize);
             block = 64;
