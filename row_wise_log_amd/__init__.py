@@ -18,6 +18,7 @@ HIP graph capture on that stream (none can be made during one), and
 """
 from __future__ import annotations
 
+import threading
 from collections import OrderedDict
 
 from .binding import (LseError, lse_create, lse_destroy, lse_forward,  # noqa: F401
@@ -36,6 +37,10 @@ from .binding import (LseError, lse_create, lse_destroy, lse_forward,  # noqa: F
 MAX_HANDLES_PER_DEVICE = 8
 _handles: OrderedDict[tuple[int, int], int] = OrderedDict()
 _pinned: set[tuple[int, int]] = set()
+# Guards _handles and _pinned: helpers called from several host threads (one
+# stream each) must neither make two handles for one key nor evict a handle
+# another thread has just looked up.
+_lock = threading.RLock()
 
 
 def _capturing() -> bool:
@@ -60,22 +65,23 @@ def handle(device: int, stream: int = 0) -> int:
     on first use, outside graph capture; under capture a stream with no
     handle yet is an error (call prepare() for it before capturing)."""
     key = (device, int(stream))
-    h = _handles.get(key)
     capturing = _capturing()
-    if h is None:
+    with _lock:
+        h = _handles.get(key)
+        if h is None:
+            if capturing:
+                raise RuntimeError(
+                    "row_wise_log_amd: no library handle for this stream, and one cannot be made "
+                    "while the stream is being captured (lse_create allocates and synchronises); "
+                    "call row_wise_log_amd.prepare(stream) before the capture")
+            _evict(device)
+            h = lse_create(device)
+            _handles[key] = h
+        else:
+            _handles.move_to_end(key)
         if capturing:
-            raise RuntimeError(
-                "row_wise_log_amd: no library handle for this stream, and one cannot be made "
-                "while the stream is being captured (lse_create allocates and synchronises); "
-                "call row_wise_log_amd.prepare(stream) before the capture")
-        _evict(device)
-        h = lse_create(device)
-        _handles[key] = h
-    else:
-        _handles.move_to_end(key)
-    if capturing:
-        _pinned.add(key)
-    return h
+            _pinned.add(key)
+        return h
 
 
 def prepare(stream=None, device: int | None = None) -> int:
@@ -93,9 +99,10 @@ def prepare(stream=None, device: int | None = None) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(device)
     raw = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
-    h = handle(device, raw)
-    _pinned.add((device, raw))
-    return h
+    with _lock:
+        h = handle(device, raw)
+        _pinned.add((device, raw))
+        return h
 
 
 def release(stream=None, device: int | None = None) -> None:
@@ -105,16 +112,17 @@ def release(stream=None, device: int | None = None) -> None:
     be replayed afterwards."""
     import torch
 
-    if stream is not None:
-        raw = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
-        keys = [k for k in _handles if k[1] == raw and (device is None or k[0] == device)]
-    else:
-        keys = [k for k in _handles if device is None or k[0] == device]
-    for d in sorted({k[0] for k in keys}):
-        torch.cuda.synchronize(d)
-    for k in keys:
-        _pinned.discard(k)
-        lse_destroy(_handles.pop(k))
+    with _lock:
+        if stream is not None:
+            raw = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+            keys = [k for k in _handles if k[1] == raw and (device is None or k[0] == device)]
+        else:
+            keys = [k for k in _handles if device is None or k[0] == device]
+        for d in sorted({k[0] for k in keys}):
+            torch.cuda.synchronize(d)
+        for k in keys:
+            _pinned.discard(k)
+            lse_destroy(_handles.pop(k))
 
 
 def _device_stream(x) -> tuple[int, int]:

@@ -260,3 +260,44 @@ def test_package_handle_cache_is_bounded(torch_gpu):
         assert len(loose) <= lib.MAX_HANDLES_PER_DEVICE
     for st in streams:
         lib.release(st)
+
+
+def test_package_helpers_from_several_host_threads(torch_gpu):
+    """Helper calls from four host threads, each on its own stream, all at
+    once: every stream gets exactly one handle, no two streams share one, and
+    every result matches the oracle."""
+    import threading
+
+    torch = torch_gpu
+    import row_wise_log_amd as lib
+    rng = np.random.default_rng(77)
+    vals = [rng.normal(0, 3, size=(40, 70_000)).astype(np.float32) for _ in range(4)]
+    xs = [torch.from_numpy(v).to("cuda") for v in vals]
+    streams = [torch.cuda.Stream() for _ in vals]
+    outs, errors = [None] * len(vals), []
+    start = threading.Barrier(len(vals))
+
+    def work(i):
+        try:
+            start.wait()
+            with torch.cuda.stream(streams[i]):
+                for _ in range(20):
+                    outs[i] = lib.logsumexp(xs[i])
+            streams[i].synchronize()
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(vals))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    keys = [(0, st.cuda_stream) for st in streams]
+    assert all(k in lib._handles for k in keys)
+    assert len({lib._handles[k] for k in keys}) == len(keys)
+    for i, v in enumerate(vals):
+        compare(outs[i].cpu().numpy(), oracle_mod.lse(v, "f32", threads=8), "f32",
+                f"host thread {i}")
+    for st in streams:
+        lib.release(st)
