@@ -106,6 +106,25 @@ def test_config4_particle_rows_brute(oracle, prefixes):
     assert np.percentile(np.abs(got - pred), 90) < 0.2
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_full_length_rows_brute_force(oracle, prefixes, cfg):
+    """Whole rows of the long-row workloads (32000, 128256 and 262144
+    elements) against log(fsum(exp(x))): every element decoded on its own
+    (struct for bf16), summed exactly, no maximum subtracted. A term dropped,
+    doubled or taken from the wrong place moves a row of N elements by about
+    1/N relative, far above the bar; the oracle's own ascending double sum is
+    within sqrt(N) ulps of the exact one."""
+    w = prefixes[cfg]
+    got = oracle.lse(w.x, w.dtype, threads=4)
+    for r in sorted({0, w.rows // 2, w.rows - 1}):
+        if w.dtype == "bf16":
+            vals = [oracle_pins._bf16_value(b) for b in w.x[r].tolist()]
+        else:
+            vals = w.x[r].astype(np.float64).tolist()
+        want = oracle_pins.brute_lse(vals)
+        assert abs(got[r] - want) <= 1e-12 * max(1.0, abs(want)), (cfg, r, got[r], want)
+
+
 def test_config2_spike_bound(oracle, prefixes):
     """Eight spike columns equal to bf16(o_i + 15) are the row maximum, so
     LSE_i >= spike + ln 8 and LSE_i <= spike + ln 8 + ln(1 + (N - 8) e^(next - spike) / 8)."""
