@@ -230,6 +230,36 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void *x, lse_dtype_t dtype,
                              hipStream_t stream);
 
 /*
+ * The backward pass of lse_forward_dim over the middle axis of a contiguous
+ * [outer, n, inner] array:
+ *
+ *     grad_x[(o*n + j)*inner + i] = grad_out[o*inner + i]
+ *                                   * exp(x[(o*n + j)*inner + i] - lse[o*inner + i]),
+ *
+ * the gradient of out = LSE over j with respect to x (along j, each column's
+ * softmax scaled by its incoming gradient): the backward support the paper
+ * lists for its kernels (Table 3), for the torch.logsumexp drop-in (abstract,
+ * §6) over any axis. lse_backward is the last-axis case (inner == 1 calls it).
+ *   x, dtype, outer, n, inner   as for lse_forward_dim.
+ *   lse        device pointer to outer * inner fp32 values, normally
+ *              lse_forward_dim's output; 4-byte aligned.
+ *   grad_out   device pointer to outer * inner fp32 incoming gradients,
+ *              4-byte aligned.
+ *   grad_x     device pointer to an array of x's layout and element type
+ *              (16-bit results rounded to nearest even), aligned to its
+ *              element size; must not overlap x, lse or grad_out.
+ * As in lse_backward, the formula is applied as written in fp32 arithmetic
+ * (any lse is accepted; IEEE special values). One streaming pass: x read
+ * once, grad_x written once, nothing else written; no workspace, no
+ * allocation, no synchronisation.
+ * Errors: UNSUPPORTED_DTYPE; INVALID_ARG (sizes, NULL or misaligned pointers
+ * with work to do, NULL handle); HIP.
+ */
+lse_status_t lse_backward_dim(lse_handle_t h, const void *x, lse_dtype_t dtype,
+                              int64_t outer, int64_t n, int64_t inner, const float *lse,
+                              const float *grad_out, void *grad_x, hipStream_t stream);
+
+/*
  * lse_forward without a handle and without allocating, for callers that
  * cannot call hipMalloc: code under HIP graph capture, tight serving loops,
  * harnesses that forbid device allocation. Same operation, arguments (minus

@@ -212,3 +212,27 @@ def lse_dim(x3: np.ndarray, dtype: str | None = None, threads: int = 1) -> np.nd
     rows = np.ascontiguousarray(np.transpose(x3, (0, 2, 1))).reshape(outer * inner, n)
     return default().lse(rows, dtype, threads).reshape(outer, inner)
 
+
+
+def lse_dim_grad(x3: np.ndarray, lse2, grad_out2, dtype: str | None = None,
+                 threads: int = 1) -> np.ndarray:
+    """The backward of lse_dim: grad[o, j, i] = grad_out[o, i] * exp(x[o, j, i] - lse[o, i])
+    in float64 for an [outer, n, inner] array, with lse and grad_out [outer, inner]
+    (fp32 values as the GPU receives them).
+
+    The plain definition: the row oracle's softmax_grad (whose formula is pinned by
+    finite differences) over a different axis. The reduced axis is moved last (a
+    transposed copy), each (o, i) is one row with its own lse and grad_out, and the
+    result is moved back. The paper lists backward support for its kernels (Table 3)
+    and offers them as drop-in replacements for torch.logsumexp over any axis
+    (abstract, §6).
+    """
+    x3 = np.asarray(x3)
+    if x3.ndim != 3:
+        raise ValueError("x3 must be 3-D [outer, n, inner]")
+    outer, n, inner = x3.shape
+    lse2 = np.asarray(lse2, dtype=np.float32).reshape(outer * inner)
+    g2 = np.asarray(grad_out2, dtype=np.float32).reshape(outer * inner)
+    rows = np.ascontiguousarray(np.transpose(x3, (0, 2, 1))).reshape(outer * inner, n)
+    g = default().softmax_grad(rows, lse2, g2, dtype, threads=threads)
+    return np.ascontiguousarray(np.transpose(g.reshape(outer, inner, n), (0, 2, 1)))

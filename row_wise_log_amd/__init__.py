@@ -4,10 +4,12 @@
 bf16 or fp16 CUDA/HIP tensor whose last axis is contiguous; ``logsumexp_autograd(x)``
 is the same value with a gradient (the library's backward pass, grad_out *
 exp(x - lse), in x's dtype); ``logsumexp_dim(x, d)`` reduces any axis of a
-contiguous tensor; ``token_logprob(x, t)`` returns x[r, t[r]] -
-logsumexp(x)[r] from the same single pass. PyTorch only provides the device
-memory and the current stream; the computation is the HIP library's
-``lse_forward`` / ``lse_backward`` / ``lse_forward_dim`` /
+contiguous tensor (``logsumexp_dim_autograd`` with its gradient);
+``token_logprob(x, t)`` returns x[r, t[r]] - logsumexp(x)[r] from the same
+single pass. The plain helpers turn into their autograd variants when x
+requires a gradient. PyTorch only provides the device memory and the current
+stream; the computation is the HIP library's ``lse_forward`` /
+``lse_backward`` / ``lse_forward_dim`` / ``lse_backward_dim`` /
 ``lse_token_logprob`` / ``lse_token_logprob_backward`` (see include/lse.h);
 ``token_logprob_autograd(x, t)`` is the token log-probability with its
 gradient. The library is loaded on first use
@@ -154,14 +156,10 @@ def _check_input(x):
     return codes[x.dtype], rows, cols, (x.stride(0) if rows > 1 else cols)
 
 
-def logsumexp_dim(x, dim, keepdim: bool = False, handle_=None):
-    """LSE over axis `dim` of a contiguous fp32/bf16/fp16 GPU tensor of any rank, as
-    fp32 (torch.logsumexp(x, dim, keepdim) semantics). `dim` may also be a
-    tuple of adjacent axes, which a contiguous tensor holds as one axis; other
-    tuples raise NotImplementedError."""
+def _dim_geometry(x, dim, keepdim: bool):
+    """(outer, n, inner, output shape) of torch.logsumexp(x, dim, keepdim) for a
+    contiguous tensor: the reduced axes (one, or a tuple of adjacent ones) form n."""
     import torch
-
-    from .binding import lse_forward_dim
 
     if x.dim() == 0:
         raise ValueError("x must have at least one axis")
@@ -194,17 +192,92 @@ def logsumexp_dim(x, dim, keepdim: bool = False, handle_=None):
     for s_ in shape[d1 + 1:]:
         inner *= s_
     kept = shape[:d0] + ([1] * (d1 - d0 + 1) if keepdim else []) + shape[d1 + 1:]
+    return outer, n, inner, kept
+
+
+def logsumexp_dim(x, dim, keepdim: bool = False, handle_=None):
+    """LSE over axis `dim` of a contiguous fp32/bf16/fp16 GPU tensor of any rank, as
+    fp32 (torch.logsumexp(x, dim, keepdim) semantics). `dim` may also be a
+    tuple of adjacent axes, which a contiguous tensor holds as one axis; other
+    tuples raise NotImplementedError. When x requires a gradient (and grad mode
+    is on) this is logsumexp_dim_autograd: the same value, differentiable
+    through the library's backward pass."""
+    import torch
+
+    from .binding import lse_forward_dim
+
+    if _needs_grad(torch, x) and handle_ is None:
+        return logsumexp_dim_autograd(x, dim, keepdim)
+    outer, n, inner, kept = _dim_geometry(x, dim, keepdim)
     out = torch.empty(kept, dtype=torch.float32, device=x.device)
     dev, stream = _device_stream(x)
     h = handle_ if handle_ is not None else handle(dev, stream)
-    lse_forward_dim(h, x.data_ptr(), codes[x.dtype], outer, n, inner, out.data_ptr(), stream)
+    lse_forward_dim(h, x.data_ptr(), _dtype_codes(torch)[x.dtype], outer, n, inner,
+                    out.data_ptr(), stream)
     return out
 
 
-def logsumexp(x, out=None, handle_=None):
-    """LSE over the last axis of a 2-D fp32/bf16/fp16 GPU tensor, as fp32[rows]."""
+def _dim_autograd_function():
     import torch
 
+    from .binding import lse_backward_dim
+
+    class _LogSumExpDim(torch.autograd.Function):
+        """LSE over any axis with the library's backward pass (lse_backward_dim)."""
+
+        @staticmethod
+        def forward(ctx, x, dim, keepdim):
+            out = logsumexp_dim(x, dim, keepdim)
+            ctx.save_for_backward(x, out)
+            ctx.geometry = _dim_geometry(x, dim, keepdim)[:3]
+            return out
+
+        @staticmethod
+        def backward(ctx, grad_out):
+            x, out = ctx.saved_tensors
+            outer, n, inner = ctx.geometry
+            g = grad_out.to(torch.float32).contiguous()
+            lse = out.contiguous()
+            grad = torch.empty_like(x)
+            dev, stream = _device_stream(x)
+            h = handle(dev, stream)
+            lse_backward_dim(h, x.data_ptr(), _dtype_codes(torch)[x.dtype], outer, n, inner,
+                             lse.data_ptr(), g.data_ptr(), grad.data_ptr(), stream)
+            return grad, None, None
+
+    return _LogSumExpDim
+
+
+_LSE_DIM_FN = None
+
+
+def logsumexp_dim_autograd(x, dim, keepdim: bool = False):
+    """logsumexp_dim with a gradient: with respect to x it is grad_out *
+    exp(x - lse) broadcast along the reduced axes (each column's softmax along
+    them, scaled by its incoming gradient), computed by the library's
+    lse_backward_dim and returned in x's dtype."""
+    global _LSE_DIM_FN
+    if _LSE_DIM_FN is None:
+        _LSE_DIM_FN = _dim_autograd_function()
+    return _LSE_DIM_FN.apply(x, dim, keepdim)
+
+
+def _needs_grad(torch, x) -> bool:
+    return x.requires_grad and torch.is_grad_enabled()
+
+
+def logsumexp(x, out=None, handle_=None):
+    """LSE over the last axis of a 2-D fp32/bf16/fp16 GPU tensor, as fp32[rows].
+    When x requires a gradient (and grad mode is on) this is logsumexp_autograd,
+    as torch.logsumexp would be differentiable; with out= that raises, as torch's
+    out= variants do."""
+    import torch
+
+    if _needs_grad(torch, x):
+        if out is not None:
+            raise RuntimeError("logsumexp(): out= does not support automatic differentiation, "
+                               "and x requires grad")
+        return logsumexp_autograd(x)
     code, rows, cols, stride = _check_input(x)
     if out is None:
         out = torch.empty(rows, dtype=torch.float32, device=x.device)
@@ -219,9 +292,16 @@ def logsumexp(x, out=None, handle_=None):
 def token_logprob(x, targets, return_lse=False, handle_=None):
     """x[r, targets[r]] - LSE(x[r, :]) for a 2-D fp32/bf16/fp16 GPU tensor and an
     int64 GPU tensor of rows targets, as fp32[rows] (and the LSE, if asked).
-    A target outside [0, cols) gives NaN."""
+    A target outside [0, cols) gives NaN. When x requires a gradient (and grad
+    mode is on) this is token_logprob_autograd (which returns logp only, so
+    return_lse=True raises there)."""
     import torch
 
+    if _needs_grad(torch, x) and handle_ is None:
+        if return_lse:
+            raise RuntimeError("token_logprob(): return_lse=True is not differentiable; use "
+                               "token_logprob_autograd for the gradient")
+        return token_logprob_autograd(x, targets)
     code, rows, cols, stride = _check_input(x)
     if targets.dtype != torch.int64 or targets.shape != (rows,) or not targets.is_contiguous():
         raise ValueError("targets must be a contiguous int64 tensor of shape (rows,)")

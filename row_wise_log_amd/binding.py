@@ -33,7 +33,7 @@ LSE_SPLIT_MAX_ROWS = 1024
 LSE_SPLIT_MAX_PARTS = 64
 
 EXPORTS = ["lse_create", "lse_forward", "lse_forward_dim", "lse_token_logprob", "lse_backward",
-           "lse_token_logprob_backward",
+           "lse_token_logprob_backward", "lse_backward_dim",
            "lse_destroy", "lse_status_string", "lse_set_schedule", "lse_set_tuning", "lse_plan",
            "lse_forward_noalloc"]
 
@@ -77,6 +77,7 @@ def load(path: Path | str = LIBRARY) -> ctypes.CDLL:
         "lse_backward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, i64, vp]),
         "lse_token_logprob_backward": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, vp]),
         "lse_forward_dim": (i32, [vp, vp, i32, i64, i64, i64, vp, vp]),
+        "lse_backward_dim": (i32, [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]),
         "lse_destroy": (i32, [vp]),
         "lse_status_string": (ctypes.c_char_p, [i32]),
         "lse_set_schedule": (i32, [vp, i32]),
@@ -192,6 +193,20 @@ def lse_forward_dim(handle: int, x_ptr: int, dtype: int, outer: int, n: int, inn
 def lse_forward_dim_status(handle, x_ptr, dtype, outer, n, inner, out_ptr, stream=None) -> int:
     """lse_forward_dim returning the raw status instead of raising (for argument tests)."""
     return load().lse_forward_dim(handle, x_ptr, dtype, outer, n, inner, out_ptr, stream)
+
+
+def lse_backward_dim(handle: int, x_ptr: int, dtype: int, outer: int, n: int, inner: int,
+                     lse_ptr: int, grad_out_ptr: int, grad_x_ptr: int,
+                     stream: int | None = None) -> None:
+    _check(load().lse_backward_dim(handle, x_ptr, dtype, outer, n, inner, lse_ptr, grad_out_ptr,
+                                   grad_x_ptr, stream), "lse_backward_dim")
+
+
+def lse_backward_dim_status(handle, x_ptr, dtype, outer, n, inner, lse_ptr, grad_out_ptr,
+                            grad_x_ptr, stream=None) -> int:
+    """lse_backward_dim returning the raw status instead of raising (for argument tests)."""
+    return load().lse_backward_dim(handle, x_ptr, dtype, outer, n, inner, lse_ptr, grad_out_ptr,
+                                   grad_x_ptr, stream)
 
 
 def lse_set_schedule(handle: int, schedule: int | str) -> None:

@@ -693,6 +693,79 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, i
     return err == hipSuccess ? LSE_OK : LSE_ERR_HIP;
 }
 
+lse_status_t lse_backward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t outer,
+                              int64_t n, int64_t inner, const float* lse, const float* grad_out,
+                              void* grad_x, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return LSE_ERR_UNSUPPORTED_DTYPE;
+    const int esize = elem_bytes(dtype);
+    if (outer < 0 || n < 0 || inner < 0 || n > kMaxDim) return LSE_ERR_INVALID_ARG;
+    constexpr int64_t kMaxOut = int64_t{1} << 40;
+    if (inner > 0 && outer > kMaxOut / inner) return LSE_ERR_INVALID_ARG;
+    const int64_t nout = outer * inner;
+    if (nout > 0 && n > (INT64_MAX / esize) / nout) return LSE_ERR_INVALID_ARG;
+    if (nout == 0 || n == 0) return h == nullptr ? LSE_ERR_INVALID_ARG : LSE_OK;
+    if (x == nullptr || lse == nullptr || grad_out == nullptr || grad_x == nullptr)
+        return LSE_ERR_INVALID_ARG;
+    const uint64_t x_addr = reinterpret_cast<uint64_t>(x);
+    const uint64_t g_addr = reinterpret_cast<uint64_t>(grad_x);
+    if (x_addr % esize != 0 || g_addr % esize != 0 ||
+        reinterpret_cast<uint64_t>(lse) % 4 != 0 || reinterpret_cast<uint64_t>(grad_out) % 4 != 0)
+        return LSE_ERR_INVALID_ARG;
+    if (h == nullptr) return LSE_ERR_INVALID_ARG;
+    // inner == 1: rows of n elements with one (lse, grad_out) pair each
+    if (inner == 1)
+        return lse_backward(h, x, dtype, outer, n, n, lse, grad_out, grad_x, n, stream);
+
+    const int k = 16 / esize;
+    const bool vec = inner % k == 0 && x_addr % 16 == 0 && g_addr % 16 == 0;
+    lse::DimGradArgs a{};
+    a.dtype = dtype;
+    a.vector_cols = vec;
+    a.x = static_cast<const char*>(x);
+    a.n = n;
+    a.inner = inner;
+    a.ncv = vec ? nout / k : nout;
+    a.lse = lse;
+    a.grad_out = grad_out;
+    a.grad_x = static_cast<char*>(grad_x);
+    a.stream = stream;
+    // The forward's tiles (column groups per workgroup, XCD runs where tiles
+    // share cache lines); n is split until there are about two workgroups
+    // per CU, each lane keeping at least 16 steps of j (nothing is merged).
+    const int64_t cvs = vec ? inner / k : inner;
+    a.gw = static_cast<int>(cvs >= 2 * kDimGroups &&
+                                    ceil_div(a.ncv, 2 * kDimGroups) >= 2 * int64_t{h->n_cu}
+                                ? 2 * kDimGroups
+                                : std::min<int64_t>(kDimGroups, cvs));
+    a.xcd_runs = !vec || (int64_t{a.gw} * 16) % 128 != 0 || (inner * esize) % 128 != 0 ||
+                 x_addr % 128 != 0 || g_addr % 128 != 0;
+    const int64_t rw = 256 / a.gw;
+    const int64_t tiles = ceil_div(a.ncv, a.gw);
+    int64_t parts = h->parts;
+    if (parts == 0) {
+        parts = 1;
+        const int64_t want = 2 * int64_t{h->n_cu};
+        if (tiles < want)
+            parts = std::min<int64_t>({ceil_div(want, tiles), int64_t{1024},
+                                       std::max<int64_t>(1, n / (16 * rw))});
+    }
+    parts = std::min<int64_t>(parts, int64_t{1024});
+    a.parts = static_cast<int>(parts);
+    const int64_t batch = std::min<int64_t>(tiles, (int64_t{1} << 30) / parts);
+
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return LSE_ERR_HIP;
+    if (prev != h->device && hipSetDevice(h->device) != hipSuccess) return LSE_ERR_HIP;
+    hipError_t err = hipSuccess;
+    for (int64_t t0 = 0; t0 < tiles && err == hipSuccess; t0 += batch) {
+        a.tile0 = t0;
+        a.grid = std::min<int64_t>(batch, tiles - t0) * parts;
+        err = lse::launch_grad_cols(a);
+    }
+    if (prev != h->device) (void)hipSetDevice(prev);
+    return err == hipSuccess ? LSE_OK : LSE_ERR_HIP;
+}
+
 lse_status_t lse_token_logprob(lse_handle_t h, const void* x, lse_dtype_t dtype, int64_t rows,
                                int64_t cols, int64_t row_stride, const int64_t* targets,
                                float* logp, float* lse_out, hipStream_t stream) {

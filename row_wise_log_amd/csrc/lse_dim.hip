@@ -356,6 +356,161 @@ __global__ __launch_bounds__(256) void lse_cols(const char* __restrict__ x, int6
     }
 }
 
+// ---------------------------------------------------------------------------
+// The backward pass over the middle axis,
+//
+//     grad_x[(o*n + j)*inner + i] = grad_out[o*inner + i]
+//                                   * exp(x[(o*n + j)*inner + i] - lse[o*inner + i]),
+//
+// the gradient of lse_forward_dim's output with respect to x: along j, each
+// column's softmax scaled by that column's incoming gradient (the backward
+// support the paper lists for its kernels, Table 3, for the torch.logsumexp
+// drop-in of the abstract and section 6, whose dim may be any axis). The
+// same tiles as lse_cols: a lane owns K adjacent columns (one 16-byte group,
+// x and grad_x 16-byte aligned and inner a multiple of K) or one column,
+// reads their lse and grad_out once, and walks its part's j with one load
+// and one store per step; nothing is merged, so the parts are independent.
+// Per element: subtract, scale by log2 e, v_exp_f32, multiply, as the
+// row-wise backward pass. Loads past the part's end reload its last row (in
+// bounds) and their stores are skipped; lanes past the last column store
+// nothing.
+template <DType D>
+__device__ __forceinline__ u32x4 pack_out(const float* o) {
+    if constexpr (D == DType::F32) {
+        return u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                     __float_as_uint(o[3])};
+    } else {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        unsigned p[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if constexpr (D == DType::F16) {
+                p[k] = __builtin_bit_cast(unsigned,
+                                          __builtin_convertvector(f2{o[2 * k], o[2 * k + 1]}, half2_t));
+            } else {
+                typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+                p[k] = __builtin_bit_cast(unsigned,
+                                          __builtin_convertvector(f2{o[2 * k], o[2 * k + 1]}, b2));
+            }
+        }
+        return u32x4{p[0], p[1], p[2], p[3]};
+    }
+}
+
+template <DType D>
+__device__ __forceinline__ void store_elem(char* p, float v) {
+    if constexpr (D == DType::F32) {
+        __builtin_nontemporal_store(v, reinterpret_cast<float*>(p));
+    } else if constexpr (D == DType::BF16) {
+        __builtin_nontemporal_store(__builtin_bit_cast(unsigned short, static_cast<__bf16>(v)),
+                                    reinterpret_cast<unsigned short*>(p));
+    } else {
+        __builtin_nontemporal_store(__builtin_bit_cast(unsigned short, static_cast<_Float16>(v)),
+                                    reinterpret_cast<unsigned short*>(p));
+    }
+}
+
+template <DType D, bool VEC, int U>
+__global__ __launch_bounds__(256) void lse_grad_cols(const char* __restrict__ x, int64_t n,
+                                                     int64_t inner, int64_t ncv, int gw,
+                                                     int64_t tile0, int parts,
+                                                     const float* __restrict__ lse,
+                                                     const float* __restrict__ gout,
+                                                     char* __restrict__ gx, int xcd_runs) {
+    constexpr int K = VEC ? Elem<D>::kPerVec : 1;
+    constexpr int EB = Elem<D>::kBytes;
+    const int t = threadIdx.x;
+    const int rw = 256 / gw;
+    const int col = t % gw;
+    const int jr = t / gw;
+    unsigned wgi = blockIdx.x;  // as in lse_cols: XCD runs where tiles share lines
+    if (xcd_runs) {
+        const unsigned b = blockIdx.x, q = gridDim.x / 8, r = gridDim.x % 8, xcd = b % 8;
+        wgi = xcd * q + (xcd < r ? xcd : r) + b / 8;
+    }
+    const unsigned tlu = wgi / static_cast<unsigned>(parts);
+    const int part = static_cast<int>(wgi - tlu * static_cast<unsigned>(parts));
+    const int64_t cvs = VEC ? inner / K : inner;
+    const int64_t cv_raw = (tile0 + static_cast<int64_t>(tlu)) * gw + col;
+    const bool live = jr < rw && cv_raw < ncv;
+    const int64_t cv = cv_raw < ncv ? cv_raw : ncv - 1;
+    int64_t o, iv;
+    if (ncv <= 0xFFFFFFFFll) {
+        const unsigned c = static_cast<unsigned>(cv), cs = static_cast<unsigned>(cvs);
+        const unsigned oo = c / cs;
+        o = oo;
+        iv = c - oo * cs;
+    } else {
+        o = cv / cvs;
+        iv = cv - o * cvs;
+    }
+    const int64_t off0 = o * n * inner + iv * K;  // element (o, 0, iv*K)
+    const char* xb = x + off0 * EB;
+    char* gb = gx + off0 * EB;
+    const int64_t jstride = inner * EB;
+    float L[K], G[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        L[k] = lse[o * inner + iv * K + k];
+        G[k] = gout[o * inner + iv * K + k];
+    }
+    // this part's j range, as in lse_cols
+    const unsigned nu = static_cast<unsigned>(n), pu = static_cast<unsigned>(parts);
+    const unsigned qn = nu / pu, rn = nu - qn * pu;
+    const unsigned partu = static_cast<unsigned>(part);
+    const int64_t pj0 = qn * partu + rn * partu / pu;
+    const int64_t pj1 = qn * (partu + 1) + rn * (partu + 1) / pu;
+    if (pj1 <= pj0) return;  // uniform: the part is empty
+    const int64_t steps = (pj1 - pj0 + rw - 1) / rw;
+    const int64_t nb = (steps + U - 1) / U;
+
+    struct Batch {
+        u32x4 w[VEC ? U : 1];
+        float e[VEC ? 1 : U];
+    };
+    auto load = [&](Batch& bt, int64_t kb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = pj0 + jr + (kb * U + u) * rw;
+            const char* p = xb + (j < pj1 ? j : pj1 - 1) * jstride;
+            if constexpr (VEC)
+                bt.w[u] = load_vec(reinterpret_cast<const u32x4*>(p));
+            else
+                bt.e[u] = load_scalar<D>(p);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto process = [&](const Batch& bt, int64_t kb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = pj0 + jr + (kb * U + u) * rw;
+            char* q = gb + j * jstride;
+            if constexpr (VEC) {
+                float f[K], r[K];
+                decode<D>(bt.w[u], f);
+#pragma unroll
+                for (int k = 0; k < K; ++k) r[k] = G[k] * exp2_hw((f[k] - L[k]) * kLog2e);
+                if (live && j < pj1)
+                    __builtin_nontemporal_store(pack_out<D>(r), reinterpret_cast<u32x4*>(q));
+            } else {
+                const float r = G[0] * exp2_hw((bt.e[u] - L[0]) * kLog2e);
+                if (live && j < pj1) store_elem<D>(q, r);
+            }
+        }
+    };
+    // two batches in flight: the next is loaded before one is computed and stored
+    Batch ba, bb;
+    load(ba, 0);
+    for (int64_t kb = 0; kb < nb; kb += 2) {
+        if (kb + 1 < nb) load(bb, kb + 1);
+        process(ba, kb);
+        if (kb + 1 < nb) {
+            if (kb + 2 < nb) load(ba, kb + 2);
+            process(bb, kb + 1);
+        }
+    }
+}
+
 namespace {
 
 template <DType D, bool VEC>
@@ -373,6 +528,30 @@ hipError_t launch_cols_d(const DimArgs& a) {
 }
 
 }  // namespace
+
+template <DType D, bool VEC>
+hipError_t launch_grad_cols_d(const DimGradArgs& a) {
+    hipLaunchKernelGGL((lse_grad_cols<D, VEC, 4>), dim3(a.grid), dim3(256), 0, a.stream, a.x, a.n,
+                       a.inner, a.ncv, a.gw, a.tile0, a.parts, a.lse, a.grad_out, a.grad_x,
+                       a.xcd_runs ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_cols(const DimGradArgs& a) {
+    if (a.grid <= 0) return hipSuccess;
+    switch (a.dtype) {
+        case LSE_DTYPE_F32:
+            return a.vector_cols ? launch_grad_cols_d<DType::F32, true>(a)
+                                 : launch_grad_cols_d<DType::F32, false>(a);
+        case LSE_DTYPE_BF16:
+            return a.vector_cols ? launch_grad_cols_d<DType::BF16, true>(a)
+                                 : launch_grad_cols_d<DType::BF16, false>(a);
+        case LSE_DTYPE_F16:
+            return a.vector_cols ? launch_grad_cols_d<DType::F16, true>(a)
+                                 : launch_grad_cols_d<DType::F16, false>(a);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_cols(const DimArgs& a) {
     if (a.grid <= 0) return hipSuccess;

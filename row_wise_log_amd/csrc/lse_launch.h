@@ -125,4 +125,25 @@ struct DimArgs {
 
 hipError_t launch_cols(const DimArgs& a);
 
+// The backward pass over the middle axis (lse_dim.hip): the same tiles as
+// DimArgs, parts along n independent (nothing to merge).
+struct DimGradArgs {
+    int dtype;             // an lse_dtype_t
+    bool vector_cols;      // 16-byte groups of columns (inner % K == 0, x and grad_x 16-byte aligned)
+    int64_t grid;
+    int parts;             // workgroups per tile along n
+    int gw;                // column groups per tile
+    const char* x;
+    int64_t n, inner;
+    int64_t ncv;           // column groups in all
+    int64_t tile0;
+    const float* lse;      // [outer, inner] fp32
+    const float* grad_out; // [outer, inner] fp32
+    char* grad_x;          // x's layout and element type
+    bool xcd_runs;
+    hipStream_t stream;
+};
+
+hipError_t launch_grad_cols(const DimGradArgs& a);
+
 }  // namespace lse

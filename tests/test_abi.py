@@ -206,6 +206,29 @@ def test_forward_dim_argument_checks(lib, args, status):
     assert B.lse_forward_dim_status(None, *args) == status
 
 
+@pytest.mark.parametrize("args, status", [
+    # (x, dtype, outer, n, inner, lse, grad_out, grad_x) with a NULL handle
+    ((16, 7, 2, 3, 4, 16, 16, 16), B.LSE_ERR_UNSUPPORTED_DTYPE),
+    ((16, F32, -1, 3, 4, 16, 16, 16), B.LSE_ERR_INVALID_ARG),
+    ((16, F32, 2, -3, 4, 16, 16, 16), B.LSE_ERR_INVALID_ARG),
+    ((16, F32, 2, 3, -4, 16, 16, 16), B.LSE_ERR_INVALID_ARG),
+    ((16, F32, 2, 1 << 31, 4, 16, 16, 16), B.LSE_ERR_INVALID_ARG),       # n too large
+    ((16, F32, 1 << 21, 3, 1 << 20, 16, 16, 16), B.LSE_ERR_INVALID_ARG),  # outer * inner > 2^40
+    ((18, F32, 2, 3, 4, 16, 16, 16), B.LSE_ERR_INVALID_ARG),             # x misaligned
+    ((16, BF16, 2, 3, 4, 16, 16, 17), B.LSE_ERR_INVALID_ARG),            # grad_x misaligned
+    ((16, F32, 2, 3, 4, 18, 16, 16), B.LSE_ERR_INVALID_ARG),             # lse misaligned
+    ((16, F32, 2, 3, 4, 16, 18, 16), B.LSE_ERR_INVALID_ARG),             # grad_out misaligned
+    ((None, F32, 2, 3, 4, 16, 16, 16), B.LSE_ERR_INVALID_ARG),           # NULL x with work
+    ((16, F32, 2, 3, 4, None, 16, 16), B.LSE_ERR_INVALID_ARG),           # NULL lse
+    ((16, F32, 2, 3, 4, 16, None, 16), B.LSE_ERR_INVALID_ARG),           # NULL grad_out
+    ((16, F32, 2, 3, 4, 16, 16, None), B.LSE_ERR_INVALID_ARG),           # NULL grad_x
+    ((16, F32, 2, 3, 4, 16, 16, 16), B.LSE_ERR_INVALID_ARG),             # all fine but the handle
+    ((None, F32, 2, 0, 4, None, None, None), B.LSE_ERR_INVALID_ARG),     # nothing to do still needs a handle
+])
+def test_backward_dim_argument_checks(lib, args, status):
+    assert B.lse_backward_dim_status(None, *args) == status
+
+
 def test_forward_accepts_stride_below_cols_for_one_row(lib):
     # one row: row_stride is ignored, so only the handle is wrong
     assert B.lse_forward_status(None, 16, F32, 1, 8, 0, 16) == B.LSE_ERR_INVALID_ARG

@@ -205,6 +205,68 @@ def test_lse_dim_against_scipy_and_brute_force(oracle):
     assert np.all(orc_mod.lse_dim(np.zeros((2, 0, 3), np.float32), "f32") == -np.inf)
 
 
+def test_lse_dim_grad_pins(oracle):
+    """The middle-axis gradient oracle: (1) element by element against an
+    explicit triple loop of g[o, i] * exp(x[o, j, i] - lse[o, i]) (math.exp,
+    distinct values everywhere, so a transposed or shifted axis fails);
+    (2) central finite differences of the brute-force (fsum) LSE of each
+    column, weighted by g; (3) the column sums g * exp(LSE - lse32);
+    (4) bf16 decoding and special values (NaN, -inf entries, an -inf column)."""
+    import oracle as orc_mod
+    rng = np.random.default_rng(31)
+    # (1) explicit loop, with lse and g that are not the forward's
+    x = rng.uniform(-3, 3, size=(2, 5, 3)).astype(np.float32)
+    lse = rng.uniform(-1, 1, size=(2, 3)).astype(np.float32)
+    g = rng.uniform(0.5, 2, size=(2, 3)).astype(np.float32)
+    got = orc_mod.lse_dim_grad(x, lse, g, "f32")
+    assert got.shape == x.shape
+    for o in range(2):
+        for j in range(5):
+            for i in range(3):
+                want = float(g[o, i]) * math.exp(float(x[o, j, i]) - float(lse[o, i]))
+                assert abs(got[o, j, i] - want) <= 1e-14 * abs(want), (o, j, i)
+    # (2) finite differences of sum_{o,i} g[o,i] * LSE(x)[o,i] with the fp32 LSE
+    x = rng.uniform(-2, 2, size=(2, 4, 3)).astype(np.float64)
+    g = rng.uniform(0.5, 2, size=(2, 3)).astype(np.float32)
+    lse_exact = np.array([[oracle_pins.brute_lse(x[o, :, i]) for i in range(3)] for o in range(2)])
+    got = orc_mod.lse_dim_grad(x.astype(np.float32), lse_exact.astype(np.float32), g, "f32")
+    h = 1e-5
+    for o in range(2):
+        for j in range(4):
+            for i in range(3):
+                up, dn = x[o, :, i].copy(), x[o, :, i].copy()
+                up[j] += h
+                dn[j] -= h
+                fd = float(g[o, i]) * (oracle_pins.brute_lse(up) - oracle_pins.brute_lse(dn)) / (2 * h)
+                # the float32 inputs and lse differ from the float64 ones by < 1e-7 relative
+                assert abs(got[o, j, i] - fd) <= 1e-6 * max(1.0, abs(fd)), (o, j, i, got[o, j, i], fd)
+    # (3) column sums
+    x = rng.normal(0, 3, size=(3, 50, 7)).astype(np.float32)
+    lse32 = orc_mod.lse_dim(x, "f32").astype(np.float32)
+    g = rng.normal(0, 1, size=(3, 7)).astype(np.float32)
+    got = orc_mod.lse_dim_grad(x, lse32, g, "f32")
+    exact = orc_mod.lse_dim(x, "f32")
+    want = g.astype(np.float64) * np.exp(exact - lse32.astype(np.float64))
+    assert np.all(np.abs(got.sum(axis=1) - want) <= 1e-12 * np.maximum(1.0, np.abs(want)))
+    # (4) bf16 decoding, NaN and -inf entries, a column of -inf
+    bits = workloads.f32_to_bf16_bits(rng.normal(0, 2, size=(1, 6, 4)).astype(np.float32))
+    bits[0, 1, 0] = 0xFF80  # -inf entry
+    bits[0, 2, 1] = 0x7FC0  # NaN entry
+    bits[0, :, 3] = 0xFF80  # a column of -inf
+    vals = workloads.bf16_bits_to_f32(bits).astype(np.float64)
+    lse = np.zeros((1, 4), np.float32)
+    lse[0, 3] = -np.inf
+    g = np.ones((1, 4), np.float32)
+    got = orc_mod.lse_dim_grad(bits, lse, g, "bf16")
+    assert got[0, 1, 0] == 0.0
+    assert np.isnan(got[0, 2, 1]) and np.isfinite(np.delete(got[0, :, 1], 2)).all()
+    assert np.isnan(got[0, :, 3]).all()  # exp(-inf - (-inf)) is exp(NaN)
+    mask = np.ones_like(vals, dtype=bool)
+    mask[0, 1, 0] = mask[0, 2, 1] = False
+    mask[0, :, 3] = False
+    assert np.all(np.abs(got[mask] - np.exp(vals[mask])) <= 1e-14 * np.exp(vals[mask]))
+
+
 
 # --- the oracle against 50-digit decimal arithmetic (hypothesis) ------------
 
