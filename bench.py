@@ -45,6 +45,8 @@ import workloads  # noqa: E402
 METRIC = "LSE input GB/s (% of HBM peak) at [512,128256] bf16; µs/call small shapes"
 METRIC_LOGPROB = "token log-prob input GB/s (x plus int64 targets) at the workload's shape"
 METRIC_DIM = "LSE over the first axis input GB/s (outer 1, n rows, inner cols) at the workload's shape"
+METRIC_DIM_BACKWARD = ("LSE backward over the first axis input GB/s (x, lse, grad_out read; "
+                       "grad_x written) at the workload's shape")
 METRIC_BACKWARD = ("LSE backward input GB/s (x, lse, grad_out read; grad_x written) at the "
                    "workload's shape")
 METRIC_TOKEN_BACKWARD = ("token log-prob backward input GB/s (x, int64 targets, lse, grad_logp "
@@ -155,13 +157,32 @@ def time_config(torch, B, handle, cfg: int, steps: int, warmup: int | None, rota
         bwd["lse_host"] = lse.cpu().numpy()
         out_bytes += rows * cols * esize  # grad_x
         in_bytes += rows * 8              # lse and grad_out
+    if op == "dim_backward":
+        # the workload's [rows, cols] array as [1, rows, cols], reduced over
+        # its rows: lse from the library's own forward pass over that axis on
+        # the device (untimed), one seeded incoming gradient per column
+        lse = torch.empty(cols, dtype=torch.float32, device="cuda")
+        B.lse_forward_dim(handle, bufs[0].data_ptr(), dtype_code, 1, rows, cols, lse.data_ptr(), sh)
+        g = np.random.default_rng(7).normal(0, 1, size=cols).astype(np.float32)
+        bwd = {"lse": lse, "g": torch.from_numpy(g).to("cuda"), "dim": True,
+               "grad": torch.empty(rows * cols, dtype=torch.float32 if w.dtype == "f32"
+                                   else torch.int16, device="cuda"),
+               "g_host": g}
+        torch.cuda.synchronize()
+        bwd["lse_host"] = lse.cpu().numpy()
+        in_bytes += cols * 8              # lse and grad_out
+        out_bytes = rows * cols * esize   # grad_x
     out = torch.empty(cols if op == "dim" else rows, dtype=torch.float32, device="cuda")
     if op == "dim":
         out_bytes = cols * 4
     plan = B.lse_plan(dtype_code, rows, cols, cols, bufs[0].data_ptr(), 256, 0)
 
     def step(i, sh=sh):
-        if op == "dim":
+        if op == "dim_backward":
+            B.lse_backward_dim(handle, bufs[i % rotate].data_ptr(), dtype_code, 1, rows, cols,
+                               bwd["lse"].data_ptr(), bwd["g"].data_ptr(), bwd["grad"].data_ptr(),
+                               sh)
+        elif op == "dim":
             B.lse_forward_dim(handle, bufs[i % rotate].data_ptr(), dtype_code, 1, rows, cols,
                               out.data_ptr(), sh)
         elif bwd is not None and "targets" in bwd:
@@ -606,6 +627,51 @@ def cpu_baseline_backward(w, r, seconds: float = 10.0) -> dict:
                        f"in {el:.1f} s wall on {threads} threads (float64 "
                        + ("g * exp(x - lse)" if tg is None else "g * ([j == t] - exp(x - lse))")
                        + ")")}
+
+
+def cpu_baseline_dim_backward(w, r, seconds: float = 10.0) -> dict:
+    """The float64 oracle's backward pass over the rows axis (lse_dim_grad on
+    the [1, rows, cols] array) on the host cores, over a bounded sample of
+    columns (at most 256 MB of input); its first pass also checks the GPU
+    gradient of those columns, at the row-wise backward pass's bar."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    esize = w.x.itemsize
+    c = max(1, min(w.cols, (256 << 20) // (w.rows * esize)))
+    x3 = w.x[:, :c].reshape(1, w.rows, c)
+    lse32, g = r["bwd"]["lse_host"][:c], r["bwd"]["g_host"][:c]
+    passes, ref = 0, None
+    t0 = time.perf_counter()
+    while True:
+        out = oracle.lse_dim_grad(x3, lse32, g, w.dtype, threads=threads)
+        if ref is None:
+            ref = out[0]
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or passes >= 1000:
+            break
+    raw = r["bwd"]["grad"].cpu().numpy().reshape(w.rows, w.cols)[:, :c]
+    got = ((raw.view(np.uint16).astype(np.uint32) << 16).view(np.float32) if w.dtype == "bf16"
+           else raw).astype(np.float64)
+    fin = np.isfinite(ref)
+    rel = 2.0 ** -8 + 1e-6 if w.dtype == "bf16" else 4e-7
+    xv = (workloads.bf16_bits_to_f32(x3[0]) if w.dtype == "bf16" else x3[0]).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        d = np.abs(xv - lse32.astype(np.float64)[None, :])
+    gg = np.broadcast_to(np.maximum(1.0, np.abs(g.astype(np.float64)))[None, :], ref.shape)
+    tol = (rel + 2e-7 * np.where(np.isfinite(d), d, 0.0)[fin]) * np.abs(ref[fin]) + \
+        2.0 ** -125 * gg[fin]
+    err = np.abs(got[fin] - ref[fin]) / tol
+    exact = bool(np.array_equal(got[~fin], ref[~fin], equal_nan=True))
+    log(f"GPU gradient vs oracle ({c} columns): max |err|/tol = {err.max(initial=0):.3f}, "
+        f"non-finite match {exact}")
+    return {"value": round(x3.nbytes * passes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "gpu_check": {"max_err_over_tol": round(float(err.max(initial=0)), 4),
+                          "nonfinite_exact": exact, "columns_checked": int(c)},
+            "sample": (f"the first {c} columns of the {w.rows}x{w.cols} {w.dtype} input "
+                       f"({x3.nbytes} bytes), {passes} passes in {el:.1f} s wall on {threads} "
+                       "threads (float64 grad_out * exp(x - lse) over a transposed copy)")}
 
 
 def cpu_baseline(w, seconds: float = 10.0, op: str = "lse") -> tuple:
@@ -1097,7 +1163,8 @@ def main() -> int:
                     help="leave out torch.logsumexp / torch.sum on the headline tensor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--op", choices=["lse", "logprob", "backward", "logprob_backward", "dim"],
+    ap.add_argument("--op", choices=["lse", "logprob", "backward", "logprob_backward", "dim",
+                                     "dim_backward"],
                     default="lse",
                     help="lse: lse_forward (the headline); logprob: lse_token_logprob with one "
                          "seeded int64 target per row; backward: lse_backward (reads x, writes "
@@ -1214,7 +1281,7 @@ def main() -> int:
         line = {
             "metric": {"lse": METRIC, "logprob": METRIC_LOGPROB, "backward": METRIC_BACKWARD,
                        "logprob_backward": METRIC_TOKEN_BACKWARD,
-                       "dim": METRIC_DIM}[args.op],
+                       "dim": METRIC_DIM, "dim_backward": METRIC_DIM_BACKWARD}[args.op],
             "value": round(r["value_gbs"], 1),
             "unit": "GB/s",
             "n_gpus": 1,
@@ -1282,7 +1349,9 @@ def main() -> int:
             line["cpu_baseline"] = cpu_rec
         elif not args.no_cpu_baseline:
             log("timing the float64 oracle on the host cores")
-            line["cpu_baseline"] = cpu_baseline_backward(w, r, args.cpu_seconds)
+            line["cpu_baseline"] = (cpu_baseline_dim_backward(w, r, args.cpu_seconds)
+                                    if args.op == "dim_backward"
+                                    else cpu_baseline_backward(w, r, args.cpu_seconds))
         else:
             line["cpu_baseline"] = None
         if small is not None:
