@@ -454,7 +454,8 @@ __global__ __launch_bounds__(256) void lse_grad_cols(const char* __restrict__ x,
         L[k] = lse[o * inner + iv * K + k];
         G[k] = gout[o * inner + iv * K + k];
     }
-    // this part's j range, as in lse_cols
+    // this part's j range, as in lse_cols (32-bit: rn * (part + 1) < parts^2
+    // <= 2^32 for the at most 65536 parts the planner gives a tile)
     const unsigned nu = static_cast<unsigned>(n), pu = static_cast<unsigned>(parts);
     const unsigned qn = nu / pu, rn = nu - qn * pu;
     const unsigned partu = static_cast<unsigned>(part);

@@ -131,7 +131,7 @@ struct DimGradArgs {
     int dtype;             // an lse_dtype_t
     bool vector_cols;      // 16-byte groups of columns (inner % K == 0, x and grad_x 16-byte aligned)
     int64_t grid;
-    int parts;             // workgroups per tile along n
+    int parts;             // workgroups per tile along n (<= 65536)
     int gw;                // column groups per tile
     const char* x;
     int64_t n, inner;

@@ -200,6 +200,18 @@ def test_workload2_first_axis_full_size(torch_gpu, handle):
     check(got, x3, lse2, g2, "bf16", "workload 2 axis 0")
 
 
+def test_short_rows_in_one_batch_parts(torch_gpu, handle):
+    """Rows of 16 fp32 over a long axis (a tile spans whole rows, so n is cut
+    into parts of one batch per lane, up to 65536 of them): 2^20 rows, every
+    element against the oracle."""
+    x = make((1, 1 << 20, 16), "f32", seed=22)
+    lse2, g2 = lse_and_grads(x, "f32", seed=23)
+    note("dim backward 2^20 rows of 16 fp32")
+    got, untouched = gpu_dim_grad(torch_gpu, handle, x, lse2, g2, "f32")
+    assert untouched
+    check(got, x, lse2, g2, "f32", "rows of 16")
+
+
 def test_package_autograd_every_axis(torch_gpu):
     """logsumexp_dim_autograd, and logsumexp_dim on a tensor that requires a
     gradient, against torch.logsumexp's float64 autograd on the CPU for every
