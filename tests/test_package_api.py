@@ -75,3 +75,23 @@ def test_logsumexp_dim_checks_its_axes():
             R.logsumexp_dim(x, bad)
     with pytest.raises(ValueError):        # valid axes, but a CPU tensor
         R.logsumexp_dim(x, (1, 2))
+
+
+def test_gradient_paths_refuse_what_they_cannot_differentiate():
+    """With an input that requires a gradient (grad mode on), the plain helpers
+    take their autograd variants; out= and return_lse=True, which those cannot
+    serve, raise instead of silently dropping the gradient (before any device
+    call)."""
+    x = torch.zeros(4, 8, requires_grad=True)
+    with pytest.raises(RuntimeError, match="out="):
+        R.logsumexp(x, out=torch.empty(4))
+    with pytest.raises(RuntimeError, match="return_lse"):
+        R.token_logprob(x, torch.zeros(4, dtype=torch.int64), return_lse=True)
+    # the autograd variants check their inputs like the plain helpers
+    with pytest.raises(ValueError, match="GPU"):
+        R.logsumexp(x)
+    with pytest.raises(ValueError, match="contiguous GPU"):
+        R.logsumexp_dim(torch.zeros(2, 3, 4, requires_grad=True), 1)
+    with torch.no_grad():  # grad mode off: the plain path and its own checks
+        with pytest.raises(ValueError, match="GPU"):
+            R.logsumexp(x, out=torch.empty(4))
