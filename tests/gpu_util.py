@@ -10,6 +10,8 @@ import sys
 
 import numpy as np
 
+import oracle as oracle_mod
+import workloads
 from row_wise_log_amd import binding as B
 
 TOL = {"f32": 2e-6, "bf16": 1e-5, "f16": 1e-5}
@@ -297,3 +299,56 @@ def compare_token_grad(got: np.ndarray, ref: np.ndarray, soft: np.ndarray, d: np
     assert ratio[worst] <= 1.0, (f"{what}: element {np.argwhere(fin)[worst].tolist()} got "
                                  f"{got[fin][worst]!r} want {ref[fin][worst]!r} ({ratio[worst]:.2f} x tol)")
     return float(ratio.max())
+
+
+def decoded_dim(x, dtype):
+    """An [outer, n, inner] array of any input type as float64 values."""
+    if dtype == "bf16":
+        return workloads.bf16_bits_to_f32(x).astype(np.float64)
+    if dtype == "f16":
+        return x.view(np.float16).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def gpu_dim_grad(torch, handle, x3, lse2, g2, dtype, front=0, gfront=0, parts=0):
+    """lse_backward_dim on a host array with x and grad_x `front` / `gfront`
+    elements into their buffers; returns (grad as float32 [outer, n, inner],
+    untouched: every element of grad_x's buffer outside the array kept its
+    sentinel)."""
+    outer, n, inner = x3.shape
+    esz = ESIZE[dtype]
+    store = np.int16 if esz == 2 else np.int32
+    flat = np.zeros(front + x3.size, dtype=x3.dtype)
+    flat[front:] = x3.ravel()
+    xt = torch.from_numpy(flat.view(store)).to("cuda")
+    lt = torch.from_numpy(np.ascontiguousarray(lse2, dtype=np.float32).ravel()).to("cuda")
+    gt = torch.from_numpy(np.ascontiguousarray(g2, dtype=np.float32).ravel()).to("cuda")
+    sentinel = 0x7F7F if esz == 2 else 0x7F7F7F7F
+    tstore = torch.int16 if esz == 2 else torch.int32
+    buf = torch.full((gfront + x3.size + 64,), sentinel, dtype=tstore, device="cuda")
+    B.lse_set_tuning(handle, 0, 0, parts, 0, 0)
+    try:
+        B.lse_backward_dim(handle, xt.data_ptr() + front * esz, DTYPE_CODE[dtype], outer, n, inner,
+                           lt.data_ptr(), gt.data_ptr(), buf.data_ptr() + gfront * esz,
+                           torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    finally:
+        B.lse_set_tuning(handle, 0, 0, 0, 0, 0)
+    host = buf.cpu().numpy()
+    del xt, lt, gt, buf
+    host = host.view(np.uint16) if esz == 2 else host.view(np.uint32)
+    want = np.uint16(0x7F7F) if esz == 2 else np.uint32(0x7F7F7F7F)
+    untouched = bool(np.all(host[:gfront] == want) and np.all(host[gfront + x3.size:] == want))
+    vals = host[gfront:gfront + x3.size]
+    return decode_out(vals, dtype).reshape(x3.shape), untouched
+
+
+def compare_dim_grad(got, x3, lse2, g2, dtype, what):
+    """compare_grad on the moved axis: each (o, i) column is one row of n."""
+    outer, n, inner = x3.shape
+    ref = oracle_mod.lse_dim_grad(x3, lse2, g2, dtype, threads=8)
+    rows = lambda a: np.ascontiguousarray(np.transpose(a, (0, 2, 1))).reshape(outer * inner, n)
+    with np.errstate(invalid="ignore"):
+        d = decoded_dim(x3, dtype) - np.asarray(lse2, np.float64).reshape(outer, 1, inner)
+    return compare_grad(rows(got), rows(ref), rows(d), np.asarray(g2, np.float32).ravel(), dtype,
+                        what)

@@ -11,7 +11,8 @@ float64 oracle. A second sweep does the same for lse_forward_dim over random
 run checks the same cases; each case is printed before it runs. A third
 sweep runs lse_backward and lse_token_logprob_backward on random shapes with
 padded and misaligned x and gradient rows (rows misaligned alike in x and
-grad_x take the peeled 16-byte path, the others the element path).
+grad_x take the peeled 16-byte path, the others the element path), and
+lse_backward_dim on random [outer, n, inner].
 
 LSE_SWEEP_SEED=k (default 0) shifts every seed by 1000 k, for a wider sweep
 run by hand; a list or range ("1-12", "3,5") runs each shift in the same
@@ -24,9 +25,9 @@ import pytest
 
 import oracle as oracle_mod
 import workloads
-from gpu_util import (DTYPE_CODE, SCHEDULES, compare, compare_grad, compare_logp,
-                      compare_token_grad, gpu_backward, gpu_lse, gpu_token_backward,
-                      gpu_token_logprob, note)
+from gpu_util import (DTYPE_CODE, SCHEDULES, compare, compare_dim_grad, compare_grad,
+                      compare_logp, compare_token_grad, gpu_backward, gpu_dim_grad, gpu_lse,
+                      gpu_token_backward, gpu_token_logprob, note)
 from row_wise_log_amd import binding as B
 
 pytestmark = pytest.mark.gpu
@@ -173,6 +174,38 @@ def test_random_dims(torch_gpu, handle, seed, block):
         note(what)
         got = gpu_dim(torch_gpu, handle, x3, dtype, front, parts)
         compare(got, oracle_mod.lse_dim(x3, dtype, threads=8).ravel(), dtype, what)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+@pytest.mark.parametrize("block", range(3))
+def test_random_dim_backward(torch_gpu, handle, seed, block):
+    """lse_backward_dim on random [outer, n, inner] (the 16-byte and element
+    paths, short rows cut into one-batch parts, forced splits), with x and
+    grad_x sometimes misaligned, against the oracle; nothing outside grad_x
+    is written."""
+    rng = np.random.default_rng(seed + 500 + block)
+    for i in range(20):
+        dtype = ["f32", "bf16", "f16"][rng.integers(3)]
+        outer, n, inner = log_int(rng, 1, 32), log_int(rng, 1, 60_000), log_int(rng, 1, 5000)
+        while outer * n * inner > MAX_ELEMS // 2:
+            if n > 1:
+                n //= 2
+            else:
+                inner = max(1, inner // 2)
+        front, gfront = int(rng.choice([0, 0, 1])), int(rng.choice([0, 0, 1]))
+        parts = int(rng.choice([0, 0, 0, 1, 2, 7, 64]))
+        v = rng.normal(0, float(rng.choice([0.5, 3.0, 30.0])), size=(outer, n, inner))
+        v = v.astype(np.float32)
+        x3 = (workloads.f32_to_bf16_bits(v) if dtype == "bf16" else
+              workloads.f32_to_f16_bits(v) if dtype == "f16" else v)
+        lse2 = oracle_mod.lse_dim(x3, dtype, threads=8).astype(np.float32)
+        g2 = rng.normal(0, 2, size=(outer, inner)).astype(np.float32)
+        what = (f"dim backward block {block} case {i}: {dtype} {x3.shape} front={front} "
+                f"grad_front={gfront} parts={parts}")
+        note(what)
+        got, untouched = gpu_dim_grad(torch_gpu, handle, x3, lse2, g2, dtype, front, gfront, parts)
+        assert untouched, what + ": bytes outside grad_x were written"
+        compare_dim_grad(got, x3, lse2, g2, dtype, what)
 
 
 @pytest.mark.parametrize("seed", SEEDS)
