@@ -206,7 +206,10 @@ def logsumexp_dim(x, dim, keepdim: bool = False, handle_=None):
 
     from .binding import lse_forward_dim
 
-    if _needs_grad(torch, x) and handle_ is None:
+    if _needs_grad(torch, x):
+        if handle_ is not None:
+            raise RuntimeError("logsumexp_dim(): handle_ does not support automatic "
+                               "differentiation, and x requires grad")
         return logsumexp_dim_autograd(x, dim, keepdim)
     outer, n, inner, kept = _dim_geometry(x, dim, keepdim)
     out = torch.empty(kept, dtype=torch.float32, device=x.device)
@@ -274,9 +277,9 @@ def logsumexp(x, out=None, handle_=None):
     import torch
 
     if _needs_grad(torch, x):
-        if out is not None:
-            raise RuntimeError("logsumexp(): out= does not support automatic differentiation, "
-                               "and x requires grad")
+        if out is not None or handle_ is not None:
+            raise RuntimeError("logsumexp(): out= and handle_ do not support automatic "
+                               "differentiation, and x requires grad")
         return logsumexp_autograd(x)
     code, rows, cols, stride = _check_input(x)
     if out is None:
@@ -297,10 +300,11 @@ def token_logprob(x, targets, return_lse=False, handle_=None):
     return_lse=True raises there)."""
     import torch
 
-    if _needs_grad(torch, x) and handle_ is None:
-        if return_lse:
-            raise RuntimeError("token_logprob(): return_lse=True is not differentiable; use "
-                               "token_logprob_autograd for the gradient")
+    if _needs_grad(torch, x):
+        if return_lse or handle_ is not None:
+            raise RuntimeError("token_logprob(): return_lse=True and handle_ do not support "
+                               "automatic differentiation; use token_logprob_autograd for the "
+                               "gradient")
         return token_logprob_autograd(x, targets)
     code, rows, cols, stride = _check_input(x)
     if targets.dtype != torch.int64 or targets.shape != (rows,) or not targets.is_contiguous():

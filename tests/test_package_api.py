@@ -92,6 +92,11 @@ def test_gradient_paths_refuse_what_they_cannot_differentiate():
         R.logsumexp(x)
     with pytest.raises(ValueError, match="contiguous GPU"):
         R.logsumexp_dim(torch.zeros(2, 3, 4, requires_grad=True), 1)
+    for call in (lambda: R.logsumexp(x, handle_=1),
+                 lambda: R.logsumexp_dim(torch.zeros(2, 3, requires_grad=True), 0, handle_=1),
+                 lambda: R.token_logprob(x, torch.zeros(4, dtype=torch.int64), handle_=1)):
+        with pytest.raises(RuntimeError, match="handle_"):
+            call()
     with torch.no_grad():  # grad mode off: the plain path and its own checks
         with pytest.raises(ValueError, match="GPU"):
             R.logsumexp(x, out=torch.empty(4))
