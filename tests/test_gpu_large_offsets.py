@@ -10,6 +10,9 @@ reduction over arrays of 6 to 9 GB (an MI355X holds 288 GB).
   path) and 2^29 + 3 (fp32, element path): all columns zero except 64
   sampled ones, so every untouched output must be ln n; the sampled columns
   against the oracle.
+* lse_backward_dim over [1, 65536, 40000] bf16 (5.2 GB): every gradient of
+  the zero columns must be exactly 2^-16; the sampled columns against the
+  oracle; nothing written past grad_x.
 """
 import math
 
@@ -121,3 +124,47 @@ def test_dim_over_large_arrays(torch_gpu, handle, dtype, n, inner):
     ref = oracle_mod.lse(np.ascontiguousarray(hv.T), dtype)   # each sampled column is a row of n
     compare(out[idx].cpu().numpy(), ref, dtype, f"dim {dtype} sampled columns")
     del x, out
+
+
+def test_dim_backward_over_a_large_array(torch_gpu, handle):
+    """lse_backward_dim over [1, 65536, 40000] bf16 (2.6 G elements, 5.2 GB;
+    byte offsets past 2^32 on the 16-byte path): x = 0 except a few sampled
+    columns, so every other column's gradient is exactly g / n = 2^-16 (for
+    g = 1 and lse = fl(ln 65536)); the sampled columns are checked against
+    the oracle, and the 16 KiB guard after grad_x stays untouched."""
+    torch = torch_gpu
+    n, inner = 65536, 40000
+    note(f"large dim backward bf16 n={n} inner={inner}: {n * inner * 2 / 1e9:.1f} GB")
+    x = torch.zeros((n, inner), dtype=torch.int16, device="cuda")
+    rng = np.random.default_rng(7)
+    cols = np.unique(np.concatenate([rng.integers(0, inner, size=20), [0, inner - 1]]))
+    vals = rng.normal(0, 3, size=(n, len(cols))).astype(np.float32)
+    hv = workloads.f32_to_bf16_bits(vals)
+    idx = torch.from_numpy(cols).cuda()
+    x[:, idx] = torch.from_numpy(hv.view(np.int16)).cuda()
+    lse = np.full(inner, math.log(n), dtype=np.float32)
+    lse[cols] = oracle_mod.lse(np.ascontiguousarray(hv.T), "bf16").astype(np.float32)
+    g = np.ones(inner, dtype=np.float32)
+    g[cols] = rng.normal(0, 2, size=len(cols)).astype(np.float32)
+    lt, gt = torch.from_numpy(lse).cuda(), torch.from_numpy(g).cuda()
+    guard = 8192
+    grad = torch.full((n * inner + guard,), 0x7F7F, dtype=torch.int16, device="cuda")
+    B.lse_backward_dim(handle, x.data_ptr(), DTYPE_CODE["bf16"], 1, n, inner, lt.data_ptr(),
+                       gt.data_ptr(), grad.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert bool((grad[n * inner:] == 0x7F7F).all()), "the guard after grad_x was written"
+    gv = grad[: n * inner].view(n, inner)
+    mask = torch.ones(inner, dtype=torch.bool, device="cuda")
+    mask[idx] = False
+    want = np.array([2.0 ** -16], dtype=np.float32)
+    want_bits = int(workloads.f32_to_bf16_bits(want)[0])
+    bad = int((gv[:, mask] != want_bits).sum())
+    assert bad == 0, f"{bad} elements of the constant columns differ from 2^-16"
+    got = gv[:, idx].cpu().numpy().view(np.uint16)
+    got = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = oracle_mod.softmax_grad(np.ascontiguousarray(hv.T), lse[cols], g[cols], "bf16").T
+    rel = 2.0 ** -8 + 1e-6
+    d = np.abs(workloads.bf16_bits_to_f32(hv).astype(np.float64) - lse[cols][None, :])
+    tol = (rel + 2e-7 * d) * np.abs(ref) + 2.0 ** -125 * np.maximum(1.0, np.abs(g[cols]))[None, :]
+    assert np.all(np.abs(got - ref) <= tol), "sampled columns differ from the oracle"
+    del x, grad, gv
