@@ -1,11 +1,12 @@
 """The entry points under HIP graph capture and on concurrent streams.
 
-lse_forward, lse_token_logprob, lse_backward and lse_forward_dim allocate
-nothing and synchronise nothing, and the split schedules' arrival counters
-are reset by the kernels themselves, so a caller may capture the calls into a
-graph and replay it. One graph holds every schedule (register rows, a
-workgroup per row, split rows, the token log-probability, the backward pass
-and a split LSE over a non-last axis); it is replayed several times with new
+lse_forward, lse_token_logprob, lse_backward, lse_forward_dim and
+lse_backward_dim allocate nothing and synchronise nothing, and the split
+schedules' arrival counters are reset by the kernels themselves, so a caller
+may capture the calls into a graph and replay it. One graph holds every
+schedule (register rows, a workgroup per row, split rows, the token
+log-probability, the backward pass, a split LSE over a non-last axis and two
+backward passes over it); it is replayed several times with new
 inputs written by eager work in between, and every replay is compared bit for
 bit with the same calls made eagerly. A second test runs split-row and split
 non-last-axis calls on two handles on two streams at once (one handle per
@@ -50,6 +51,10 @@ class Calls:
         self.targets = torch.from_numpy(rng.integers(0, 128256, size=64)).to(dev)
         self.lse_d = torch.empty(37, device=dev)
         self.g_d = torch.from_numpy(rng.normal(0, 1, size=37).astype(np.float32)).to(dev)
+        # lse and grad_out of x["e"] and x["c"] over their first axis (the dim backward)
+        self.lse_e, self.lse_c = torch.empty(256, device=dev), torch.empty(100, device=dev)
+        self.g_e = torch.from_numpy(rng.normal(0, 1, size=256).astype(np.float32)).to(dev)
+        self.g_c = torch.from_numpy(rng.normal(0, 1, size=100).astype(np.float32)).to(dev)
         self.h = B.lse_create(0)
         self.h_split = B.lse_create(0)
         B.lse_set_schedule(self.h_split, "split_row")
@@ -60,15 +65,22 @@ class Calls:
         for k, (r, c, dt) in self.shapes.items():
             v = self.rng.normal(0, 3, size=(r, c)).astype(np.float32)
             self.x[k].copy_(torch.from_numpy(v).to(dt))
+        s = torch.cuda.current_stream().cuda_stream
         B.lse_forward(self.h, self.x["d"].data_ptr(), B.LSE_DTYPE_F32, 37, 5000, 5000,
-                      self.lse_d.data_ptr(), torch.cuda.current_stream().cuda_stream)
+                      self.lse_d.data_ptr(), s)
+        B.lse_forward_dim(self.h, self.x["e"].data_ptr(), B.LSE_DTYPE_F32, 1, 50_000, 256,
+                          self.lse_e.data_ptr(), s)
+        B.lse_forward_dim(self.h, self.x["c"].data_ptr(), B.LSE_DTYPE_F32, 1, 10_000, 100,
+                          self.lse_c.data_ptr(), s)
 
     def outputs(self):
         torch = self.torch
         return {"a": torch.empty(64, device="cuda"), "b": torch.empty(8, device="cuda"),
                 "c": torch.empty(10_000, device="cuda"), "lp": torch.empty(64, device="cuda"),
                 "lse_a": torch.empty(64, device="cuda"),
-                "grad": torch.empty(37, 5000, device="cuda"), "dim": torch.empty(256, device="cuda")}
+                "grad": torch.empty(37, 5000, device="cuda"), "dim": torch.empty(256, device="cuda"),
+                "dgrad_e": torch.empty(50_000, 256, device="cuda"),
+                "dgrad_c": torch.empty(10_000, 100, device="cuda")}
 
     def run(self, o):
         s = self.torch.cuda.current_stream().cuda_stream
@@ -86,6 +98,11 @@ class Calls:
         # 50000 x 256 over the first axis: 2 tiles of 32 column groups, j split
         B.lse_forward_dim(self.h, x["e"].data_ptr(), B.LSE_DTYPE_F32, 1, 50_000, 256,
                           o["dim"].data_ptr(), s)
+        # the backward over the first axis: split tiles, and short rows in one-batch parts
+        B.lse_backward_dim(self.h, x["e"].data_ptr(), B.LSE_DTYPE_F32, 1, 50_000, 256,
+                           self.lse_e.data_ptr(), self.g_e.data_ptr(), o["dgrad_e"].data_ptr(), s)
+        B.lse_backward_dim(self.h, x["c"].data_ptr(), B.LSE_DTYPE_F32, 1, 10_000, 100,
+                           self.lse_c.data_ptr(), self.g_c.data_ptr(), o["dgrad_c"].data_ptr(), s)
 
     def close(self):
         self.torch.cuda.synchronize()
