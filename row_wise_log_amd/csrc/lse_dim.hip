@@ -26,6 +26,9 @@
 // write their (max, sum) pairs to the handle's workspace; the last of a
 // tile's P workgroups to arrive (an agent-scope counter per tile) merges the
 // tile's pairs in the same launch and resets the counter.
+//
+// The file also holds the backward pass over the same axis (lse_grad_cols,
+// below): the same tiles, one load and one store per step, nothing merged.
 #include "lse_device.h"
 #include "lse_launch.h"
 
