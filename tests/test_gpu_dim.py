@@ -3,8 +3,10 @@ float64 oracle (the reduced axis moved last, then the row oracle).
 
 Shapes [outer, n, inner] with vector and single-column paths, the split of
 n across workgroups (forced and planned, in batches of tiles), special and
-huge-magnitude columns, n == 0, inner == 1 (the row path), a misaligned base,
-two workloads reduced over their first axis at full size, and the package's
+huge-magnitude columns (also in narrow tiles, whose lanes share columns in
+the end-of-workgroup merge), n == 0, inner == 1 (the row path), a misaligned
+base, two workloads and [1, 1000000, inner] arrays of one or two column groups
+reduced over their first axis at full size, and the package's
 torch-tensor entry against torch.logsumexp in float64.
 """
 import numpy as np
@@ -110,6 +112,43 @@ def test_special_and_huge_columns(torch_gpu, handle):
             note(f"dim special columns dtype={dtype} parts={parts}")
             compare(gpu_dim(torch_gpu, handle, x, dtype, parts=parts).ravel(), ref.ravel(), dtype,
                     f"special {dtype} parts={parts}")
+
+
+@pytest.mark.parametrize("dtype,inner", [("f32", 4), ("f32", 8), ("bf16", 8), ("bf16", 16),
+                                         ("f32", 3), ("bf16", 5)])
+def test_special_values_in_narrow_tiles(torch_gpu, handle, dtype, inner):
+    """Rows of one or two 16-byte groups (or a few single columns): each
+    workgroup reads 32 to 256 steps of j at once, and several lanes share a
+    column in the end-of-workgroup merge. Special columns as above, split and
+    unsplit, with and without a misaligned base."""
+    rng = np.random.default_rng(inner)
+    v = rng.normal(0, 2, size=(2, 5000, inner)).astype(np.float32)
+    v[0, :, 0] = -np.inf
+    v[0, 4321, 1] = np.nan
+    v[1, 4999, 0] = np.inf
+    v[1, :2500, 1] = -np.inf
+    v[1, 17, 2] = 2.0e9
+    v[0, 0, 2] = 60.0
+    v[0, 4999, inner - 1] = 60.0
+    x = workloads.f32_to_bf16_bits(v) if dtype == "bf16" else v
+    ref = oracle_mod.lse_dim(x, dtype, threads=8)
+    for parts in (0, 1, 3):
+        for front in (0, 1):
+            note(f"dim narrow special dtype={dtype} inner={inner} parts={parts} front={front}")
+            compare(gpu_dim(torch_gpu, handle, x, dtype, parts=parts, front=front).ravel(),
+                    ref.ravel(), dtype, f"narrow special {dtype} inner={inner} parts={parts}")
+
+
+@pytest.mark.parametrize("dtype,inner", [("bf16", 8), ("f32", 4), ("bf16", 7)])
+def test_long_narrow_full_size(torch_gpu, handle, dtype, inner):
+    """[1, 1000000, inner]: one column group per j-row, so one tile whose 256
+    lanes read 256 steps of j per load, split into about one workgroup per
+    CU; every output against the oracle."""
+    x = make((1, 1_000_000, inner), dtype, seed=inner)
+    ref = oracle_mod.lse_dim(x, dtype, threads=8)
+    note(f"dim long narrow dtype={dtype} inner={inner}")
+    compare(gpu_dim(torch_gpu, handle, x, dtype).ravel(), ref.ravel(), dtype,
+            f"long narrow {dtype} inner={inner}")
 
 
 def test_empty_reduction(torch_gpu, handle):
