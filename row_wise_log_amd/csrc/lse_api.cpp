@@ -662,13 +662,24 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, i
     // least 16 steps of j, at most 1024 (and one tile's pairs must fit the
     // workspace); a forced value from lse_set_tuning's `parts` wins. Split
     // tiles go in batches whose pairs fit the workspace and whose tiles fit
-    // the arrival counters.
+    // the arrival counters. The one-column path, whose 2- and 4-byte loads
+    // keep a quarter to an eighth of the 16-byte path's bytes in flight per
+    // workgroup, aims for two workgroups per CU where that leaves at most 64
+    // parts per tile (more parts make the tile's merge of their pairs wait
+    // longer). Measured as library copies, medians of six alternating blocks,
+    // over the first axis, against one per CU: fp32 [65536, 4097] 334 -> 302
+    // us, bf16 [65536, 4097] 259 -> 221, fp32 [4096, 12001] (unsplit before)
+    // 50.5 -> 45.1, fp32 [4096, 4097] 25.5 -> 22.4, bf16 [20000, 5003] 84.9 ->
+    // 76.2; with up to 512 parts per tile, fp32 [1000000, 7] 16.8 -> 18.5 and
+    // bf16 [1000000, 7] 15.8 -> 18.1, hence the limit. On the 16-byte path two
+    // per CU were 5-15 % slower on every shape timed.
     const int64_t cap_pairs = LSE_DIM_MAX_PAIRS;
     const int64_t tile_pairs = static_cast<int64_t>(a.gw) * cols_per_lane;
     int64_t parts = h->parts;
     if (parts == 0) {
         parts = 1;
-        const int64_t want = h->n_cu;
+        const int64_t want =
+            h->n_cu * (!vec && ceil_div(2 * int64_t{h->n_cu}, tiles) <= 64 ? 2 : 1);
         if (tiles < want)
             parts = std::min<int64_t>({ceil_div(want, tiles), int64_t{1024},
                                        std::max<int64_t>(1, n / (16 * rw))});

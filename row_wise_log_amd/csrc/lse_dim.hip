@@ -559,22 +559,26 @@ __global__ __launch_bounds__(256) void lse_grad_cols(const char* __restrict__ x,
 
 namespace {
 
-// Steps of j per batch: 4 16-byte loads per lane on the vector path; 8 on
-// the one-column path for 16-bit elements, whose 2-byte loads keep few bytes
-// in flight at 4 (measured as library copies, medians of six alternating
-// blocks: bf16 [512, 50257] over its first axis 20.7 -> 15.4 us, [2048,
-// 50257] 71.7 -> 49.4, [4096, 4097] 35.6 -> 23.2, [1000000, 7] 23.3 -> 18.5,
-// [256, 1001] 8.3 -> 7.4; fp32 one-column shapes moved by -18 to +5 %, the
-// vector path by +1 to +6 %, so both keep 4).
+// Steps of j per batch: 4 16-byte loads per lane on the vector path; on the
+// one-column path, whose 2- and 4-byte loads keep few bytes in flight, 8 for
+// 16-bit elements (4 for fp32) when j is not split and twice that when it is
+// (a split launch has about one or two workgroups per CU). Measured as
+// library copies, medians of six alternating blocks, over the first axis:
+// unsplit, 16-bit at 8 against 4: bf16 [512, 50257] 20.7 -> 15.4 us, [2048,
+// 50257] 71.7 -> 49.4 (fp32 moved by -18 to +5 % at 8, the vector path by +1
+// to +6 %); split, 16 and 8 against 8 and 4: bf16 [65536, 4097] 315 -> 259,
+// fp32 [65536, 4097] 378 -> 334, fp32 [4096, 4097] 28.8 -> 25.5, bf16
+// [1000000, 7] 17.1 -> 15.7, bf16 [256, 1001] (one batch per lane) 7.3 -> 7.6.
 template <DType D, bool VEC>
 hipError_t launch_cols_d(const DimArgs& a) {
     constexpr int U = VEC || Elem<D>::kBytes == 4 ? 4 : 8;
+    constexpr int US = VEC ? 4 : 2 * U;  // split launches
     if (a.parts == 1)
         hipLaunchKernelGGL((lse_cols<D, VEC, U, false>), dim3(a.grid), dim3(256), 0, a.stream, a.x,
                            a.n, a.inner, a.ncv, a.gw, a.tile0, a.out, 1, a.ws_pairs, a.counters,
                            a.xcd_runs ? 1 : 0);
     else
-        hipLaunchKernelGGL((lse_cols<D, VEC, U, true>), dim3(a.grid), dim3(256), 0, a.stream, a.x,
+        hipLaunchKernelGGL((lse_cols<D, VEC, US, true>), dim3(a.grid), dim3(256), 0, a.stream, a.x,
                            a.n, a.inner, a.ncv, a.gw, a.tile0, a.out, a.parts, a.ws_pairs,
                            a.counters, a.xcd_runs ? 1 : 0);
     return hipGetLastError();
