@@ -250,8 +250,11 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void *x, lse_dtype_t dtype,
  *              element size; must not overlap x, lse or grad_out.
  * As in lse_backward, the formula is applied as written in fp32 arithmetic
  * (any lse is accepted; IEEE special values). One streaming pass: x read
- * once, grad_x written once, nothing else written; no workspace, no
- * allocation, no synchronisation.
+ * once, grad_x written once, nothing else written; lse and grad_out are read
+ * once per column tile, or, on the flat schedule the planner takes for fp32
+ * and for widths or bases that do not fit 16-byte column groups, once per
+ * element from the caches; no workspace, no allocation, no synchronisation.
+ * The results do not depend on the schedule.
  * Errors: UNSUPPORTED_DTYPE; INVALID_ARG (sizes, NULL or misaligned pointers
  * with work to do, NULL handle); HIP.
  */
@@ -301,7 +304,8 @@ lse_status_t lse_set_schedule(lse_handle_t h, lse_schedule_t s);
  * batch `unroll` (4 or 8), SPLIT_ROW workgroups per row `parts` (1..64;
  * lse_forward uses at most `block` of them, as the last part merges the
  * pairs one per thread; lse_forward_dim takes it as its workgroups per tile
- * along n).
+ * along n, and lse_backward_dim as well, where it also selects the column
+ * tiles over the flat schedule).
  * ROWS_PER_WAVE: at most `waves_per_cu` wavefronts per compute unit in the
  * grid (1..1024; the wavefronts loop over the rest) and `lanes_per_row` lanes
  * sharing a row (a power of two up to 64; ignored where no kernel instance

@@ -27,8 +27,10 @@
 // tile's P workgroups to arrive (an agent-scope counter per tile) merges the
 // tile's pairs in the same launch and resets the counter.
 //
-// The file also holds the backward pass over the same axis (lse_grad_cols,
-// below): the same tiles, one load and one store per step, nothing merged.
+// The file also holds the backward pass over the same axis: lse_grad_cols
+// (the same tiles, one load and one store per step, nothing merged) and
+// lse_grad_flat (lanes own 16-byte vectors of the flat array, for widths that
+// do not fit the tiles' 16-byte column groups, and for fp32).
 #include "lse_device.h"
 #include "lse_launch.h"
 
@@ -557,6 +559,153 @@ __global__ __launch_bounds__(256) void lse_grad_cols(const char* __restrict__ x,
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same backward pass with lanes that own memory instead of columns. For
+// an inner width that is not a multiple of the vector (or a base that is not
+// 16-byte aligned) the column tiles above read and write 2- or 4-byte pieces
+// whose rows start at every phase of the 128-byte lines, and neighbouring
+// tiles write the two halves of a line at different times. Here a workgroup
+// takes 4096 consecutive elements of the flat array as 256 * U 16-byte
+// vectors (x and grad_x share their phase mod 16; the head and tail elements
+// outside whole vectors go one by one), or as single elements where the
+// phases differ, and reads and writes them like a copy. It first stages the
+// lse and grad_out of its 4096 elements in LDS, slot d for element F + d:
+// each slot finds its column i and slice o (exact 32-bit divisions) and
+// reads o * inner + i, so consecutive lanes read consecutive addresses
+// except where a row wraps. Each lane then takes its K pairs from LDS with
+// aligned reads. That is 8 bytes per element read from the caches (lse and
+// grad_out, outer * inner * 8 bytes in all, are read again for every j),
+// against the column kernel's one read per column; the arithmetic per element
+// is the column kernel's, so the results are the same bits. Timed as library
+// copies (medians of six alternating blocks, over the first axis, against
+// the column kernel and a copy kernel moving the same bytes): fp32 [65536,
+// 4097] 1316 -> 364 us (copy 349), fp32 [2048, 30001] 223 -> 85 (81), fp32
+// [8, 25000001] 1211 -> 430 (299), bf16 [65536, 4097] 675 -> 280 (172), bf16
+// [512, 50257] 48.5 -> 28.0 (18.2), bf16 [1000000, 7] 14.3 -> 11.7 (6.4); on
+// aligned widths fp32 [65536, 4096] 417 -> 359 (350), fp32 [16777216, 16]
+// 357 -> 341 (348) and fp32 [2048, 30000] 100 -> 85 (79), but fp32 [16,
+// 4000000] (32 MB of lse and grad_out, read 16 times) 98 -> 135 and 16-bit
+// types, whose elements carry half the bytes, bf16 [512, 128256] 49 -> 69,
+// bf16 [65536, 4096] 235 -> 274. Without the staging (K lookups per lane,
+// each wave instruction spanning K * 256 bytes) the flat kernel took 491, 113,
+// 376 and 41 us on fp32 [65536, 4097], fp32 [2048, 30001], bf16 [65536, 4097]
+// and bf16 [512, 50257].
+
+// Exact floor(a / d) for a, d < 2^32, from m = floor((2^64 - 1) / d) + 1: the
+// high 64 bits of m * a (Lemire, Kaser and Kurz, "Faster Remainder by Direct
+// Computation", 2019). d = 1 would need m = 2^64; callers pass m = 0 for it.
+__device__ __forceinline__ unsigned fastdiv(unsigned a, uint64_t m) {
+    return m ? static_cast<unsigned>(__umul64hi(m, static_cast<uint64_t>(a))) : a;
+}
+
+template <DType D, bool VEC, int U>
+__global__ __launch_bounds__(256) void lse_grad_flat(const char* __restrict__ x,
+                                                     char* __restrict__ gx,
+                                                     const float* __restrict__ lse,
+                                                     const float* __restrict__ gout, int64_t n,
+                                                     int64_t inner, int64_t total, int64_t head,
+                                                     int64_t nvec, uint64_t m_inner,
+                                                     uint64_t m_n) {
+    constexpr int K = VEC ? Elem<D>::kPerVec : 1;
+    constexpr int EB = Elem<D>::kBytes;
+    constexpr int CH = 256 * U * K;  // elements per workgroup
+    __shared__ float sl[CH];
+    __shared__ float sg[CH];
+    const int t = threadIdx.x;
+    const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (256 * U);
+
+    // One element, located with 64-bit divisions: the head and tail.
+    auto one = [&](int64_t f) {
+        const int64_t q = f / inner;
+        const int64_t i = f - q * inner;
+        const int64_t g = (q / n) * inner + i;
+        const float v = load_scalar<D>(x + f * EB);
+        store_elem<D>(gx + f * EB, gout[g] * exp2_hw((v - lse[g]) * kLog2e));
+    };
+    if constexpr (VEC) {
+        const int64_t tail0 = head + nvec * K;
+        if (blockIdx.x == 0 && t < head + (total - tail0))
+            one(t < head ? t : tail0 + (t - head));
+    }
+    if (v0 >= nvec) return;  // uniform: no whole vectors here
+
+    // (o, j, i) of the workgroup's first element, once per workgroup; the
+    // element d places later is in column (iF + d) mod inner, (iF + d) / inner
+    // rows further on, and (jF + rows) / n slices further on. Where inner >
+    // CH there is at most one wrap; else the divisions are 32-bit and exact.
+    const int64_t F = head + v0 * K;
+    const int64_t qF = F / inner;
+    const int64_t iF = F - qF * inner;
+    const int64_t oF = qF / n;
+    const unsigned jF = static_cast<unsigned>(qF - oF * n);
+    auto locate = [&](int d, int64_t& i) -> int64_t {
+        unsigned q;
+        if (inner > CH) {
+            const int64_t a = iF + d;
+            q = a >= inner;
+            i = q ? a - inner : a;
+        } else {
+            const unsigned a = static_cast<unsigned>(iF) + static_cast<unsigned>(d);
+            q = fastdiv(a, m_inner);
+            i = a - q * static_cast<unsigned>(inner);
+        }
+        return (oF + fastdiv(jF + q, m_n)) * inner + i;
+    };
+
+    u32x4 w[VEC ? U : 1];
+    float e[VEC ? 1 : U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + u * 256 + t;
+        const int64_t vv = v < nvec ? v : nvec - 1;  // past the end: reload the last vector
+        const char* p = x + (head + vv * K) * EB;
+        if constexpr (VEC)
+            w[u] = load_vec(reinterpret_cast<const u32x4*>(p));
+        else
+            e[u] = load_scalar<D>(p);
+    }
+    // Stage lse and grad_out of the chunk's elements in LDS, slot d for
+    // element F + d: consecutive lanes take consecutive slots, so each load
+    // instruction reads a contiguous run (broken only where a row wraps).
+    const int64_t left = total - F;
+    constexpr int M = CH / 256;
+    int64_t gs[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int d = m * 256 + t;
+        int64_t i;
+        gs[m] = d < left ? locate(d, i) : 0;
+    }
+    float ls[M], os[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        ls[m] = lse[gs[m]];
+        os[m] = gout[gs[m]];
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        sl[m * 256 + t] = ls[m];
+        sg[m * 256 + t] = os[m];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + u * 256 + t;
+        if (v >= nvec) continue;
+        const int d0 = (u * 256 + t) * K;
+        char* q = gx + (head + v * K) * EB;
+        if constexpr (VEC) {
+            float f[K], r[K];
+            decode<D>(w[u], f);
+#pragma unroll
+            for (int k = 0; k < K; ++k) r[k] = sg[d0 + k] * exp2_hw((f[k] - sl[d0 + k]) * kLog2e);
+            __builtin_nontemporal_store(pack_out<D>(r), reinterpret_cast<u32x4*>(q));
+        } else {
+            store_elem<D>(q, sg[d0] * exp2_hw((e[u] - sl[d0]) * kLog2e));
+        }
+    }
+}
+
 namespace {
 
 // Steps of j per batch: 4 16-byte loads per lane on the vector path; on the
@@ -592,6 +741,33 @@ hipError_t launch_grad_cols_d(const DimGradArgs& a) {
                        a.inner, a.ncv, a.gw, a.tile0, a.parts, a.lse, a.grad_out, a.grad_x,
                        a.xcd_runs ? 1 : 0);
     return hipGetLastError();
+}
+
+template <DType D, bool VEC>
+hipError_t launch_grad_flat_d(const DimFlatArgs& a) {
+    constexpr int U = 16 / (VEC ? Elem<D>::kPerVec : 1);  // 4096 elements per workgroup
+    const int64_t grid = a.nvec > 0 ? (a.nvec + 256 * U - 1) / (256 * U) : 1;
+    if (grid > INT32_MAX) return hipErrorInvalidValue;  // 2^43 elements: beyond any device
+    hipLaunchKernelGGL((lse_grad_flat<D, VEC, U>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                       a.stream, a.x, a.grad_x, a.lse, a.grad_out, a.n, a.inner, a.total, a.head,
+                       a.nvec, a.m_inner, a.m_n);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_flat(const DimFlatArgs& a) {
+    if (a.total <= 0) return hipSuccess;
+    switch (a.dtype) {
+        case LSE_DTYPE_F32:
+            return a.vec ? launch_grad_flat_d<DType::F32, true>(a)
+                         : launch_grad_flat_d<DType::F32, false>(a);
+        case LSE_DTYPE_BF16:
+            return a.vec ? launch_grad_flat_d<DType::BF16, true>(a)
+                         : launch_grad_flat_d<DType::BF16, false>(a);
+        case LSE_DTYPE_F16:
+            return a.vec ? launch_grad_flat_d<DType::F16, true>(a)
+                         : launch_grad_flat_d<DType::F16, false>(a);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_grad_cols(const DimGradArgs& a) {

@@ -146,4 +146,25 @@ struct DimGradArgs {
 
 hipError_t launch_grad_cols(const DimGradArgs& a);
 
+// lse_backward_dim's flat launch: lanes own 16-byte vectors (or single
+// elements) of the flat [outer, n, inner] array and look up each element's
+// lse and grad_out.
+struct DimFlatArgs {
+    int dtype;             // an lse_dtype_t
+    bool vec;              // x and grad_x share their phase mod 16
+    const char* x;
+    char* grad_x;
+    const float* lse;      // [outer, inner] fp32
+    const float* grad_out; // [outer, inner] fp32
+    int64_t n, inner;
+    int64_t total;         // outer * n * inner elements
+    int64_t head;          // elements before x's first 16-byte boundary (0 without vec)
+    int64_t nvec;          // whole 16-byte vectors after the head (elements without vec)
+    uint64_t m_inner;      // floor((2^64 - 1) / inner) + 1 where inner < 2^32, else 0
+    uint64_t m_n;          // the same for n; 0 for n == 1
+    hipStream_t stream;
+};
+
+hipError_t launch_grad_flat(const DimFlatArgs& a);
+
 }  // namespace lse

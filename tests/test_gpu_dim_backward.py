@@ -7,11 +7,14 @@ softmax_grad over the moved axis):
 with lse the oracle's LSE over j rounded to fp32 (never the GPU's) and seeded
 incoming gradients. The bar is the row-wise backward pass's (compare_grad).
 
-* Shapes [outer, n, inner] on the 16-byte path and the element path (odd
-  inner, a misaligned x or grad_x), fp32, bf16 and fp16; nothing outside
+* Shapes [outer, n, inner] on the column tiles (16-bit types at widths that
+  are multiples of the vector) and the flat kernel (fp32; odd inner; a
+  misaligned x, with grad_x at the same phase or not; fewer elements than one
+  vector; n == 1 with several slices), fp32, bf16 and fp16; nothing outside
   grad_x is written.
-* Forced splits of n (parts), special values (NaN, +-inf in x; infinite and
-  NaN lse; zero and huge incoming gradients), inner == 1 (the row path).
+* Forced splits of n (parts: the column tiles, both paths), special values
+  (NaN, +-inf in x; infinite and NaN lse; zero and huge incoming gradients)
+  on both kernels, inner == 1 (the row path).
 * Workload 2 reduced over its first axis at full size, every element.
 * The package's autograd wrapper over every axis of a 4-D tensor against
   torch.logsumexp's float64 autograd, and the plain helper's dispatch to it.
@@ -62,7 +65,7 @@ def lse_and_grads(x3, dtype, seed):
 
 SHAPES = [(1, 8192, 4096), (64, 1000, 32), (3, 5, 7), (2, 30_000, 3), (128, 17, 1024),
           (1, 1, 100), (7, 33, 12), (1, 3, 65), (16, 257, 40), (1, 64, 4 * 64 * 300),
-          (2, 700, 1001)]
+          (2, 700, 1001), (1, 2, 3), (5, 1, 37), (3, 1000, 5001)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -80,13 +83,17 @@ def test_shapes(torch_gpu, handle, dtype, shape):
 
 @pytest.mark.parametrize("parts", [1, 3, 64])
 def test_forced_parts(torch_gpu, handle, parts):
+    """A forced `parts` selects the column tiles: their 16-byte path (inner
+    256) and their one-column path (inner 257, which the planner otherwise
+    gives to the flat kernel)."""
     for dtype in ["f32", "bf16"]:
-        x = make((3, 5000, 256), dtype, seed=parts)
-        lse2, g2 = lse_and_grads(x, dtype, seed=parts + 1)
-        note(f"dim backward forced parts={parts} dtype={dtype}")
-        got, untouched = gpu_dim_grad(torch_gpu, handle, x, lse2, g2, dtype, parts=parts)
-        assert untouched
-        check(got, x, lse2, g2, dtype, f"parts={parts} {dtype}")
+        for inner in (256, 257):
+            x = make((3, 5000, inner), dtype, seed=parts)
+            lse2, g2 = lse_and_grads(x, dtype, seed=parts + 1)
+            note(f"dim backward forced parts={parts} dtype={dtype} inner={inner}")
+            got, untouched = gpu_dim_grad(torch_gpu, handle, x, lse2, g2, dtype, parts=parts)
+            assert untouched
+            check(got, x, lse2, g2, dtype, f"parts={parts} {dtype} inner={inner}")
 
 
 def test_more_parts_than_rows(torch_gpu, handle):
@@ -99,10 +106,13 @@ def test_more_parts_than_rows(torch_gpu, handle):
     check(got, x, lse2, g2, "f32", "parts > n")
 
 
-def test_special_values(torch_gpu, handle):
+@pytest.mark.parametrize("inner", [64, 63])
+def test_special_values(torch_gpu, handle, inner):
+    """Special values on the column tiles and the flat kernel (fp32, and any
+    type at the odd width)."""
     rng = np.random.default_rng(9)
     for dtype in ["f32", "bf16"]:
-        v = rng.normal(0, 2, size=(2, 300, 64)).astype(np.float32)
+        v = rng.normal(0, 2, size=(2, 300, inner)).astype(np.float32)
         v[0, :, 0] = -np.inf          # a column of only -inf (its LSE is -inf)
         v[0, 123, 1] = np.nan         # NaN
         v[0, 299, 2] = np.inf         # +inf (its LSE is +inf)
@@ -115,7 +125,7 @@ def test_special_values(torch_gpu, handle):
         lse2[1, 12] = np.nan          # a NaN lse
         lse2[1, 13] = np.inf          # an infinite lse with finite x: zero gradient
         for parts in (0, 1, 3):
-            note(f"dim backward special values dtype={dtype} parts={parts}")
+            note(f"dim backward special values dtype={dtype} inner={inner} parts={parts}")
             got, untouched = gpu_dim_grad(torch_gpu, handle, x, lse2, g2, dtype, parts=parts)
             assert untouched
             check(got, x, lse2, g2, dtype, f"special {dtype} parts={parts}")

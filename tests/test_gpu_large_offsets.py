@@ -10,9 +10,10 @@ reduction over arrays of 6 to 9 GB (an MI355X holds 288 GB).
   path) and 2^29 + 3 (fp32, element path): all columns zero except 64
   sampled ones, so every untouched output must be ln n; the sampled columns
   against the oracle.
-* lse_backward_dim over [1, 65536, 40000] bf16 (5.2 GB): every gradient of
-  the zero columns must be exactly 2^-16; the sampled columns against the
-  oracle; nothing written past grad_x.
+* lse_backward_dim over [1, 65536, 40000] bf16 (5.2 GB, column tiles) and
+  [1, 40000, 40001] fp32 (6.4 GB, the flat kernel): every gradient of the
+  zero columns must be the same constant g / n; the sampled columns against
+  the oracle; nothing written past grad_x.
 """
 import math
 
@@ -126,45 +127,69 @@ def test_dim_over_large_arrays(torch_gpu, handle, dtype, n, inner):
     del x, out
 
 
-def test_dim_backward_over_a_large_array(torch_gpu, handle):
+@pytest.mark.parametrize("dtype,n,inner", [("bf16", 65536, 40000), ("f32", 40000, 40001)])
+def test_dim_backward_over_a_large_array(torch_gpu, handle, dtype, n, inner):
     """lse_backward_dim over [1, 65536, 40000] bf16 (2.6 G elements, 5.2 GB;
-    byte offsets past 2^32 on the 16-byte path): x = 0 except a few sampled
-    columns, so every other column's gradient is exactly g / n = 2^-16 (for
-    g = 1 and lse = fl(ln 65536)); the sampled columns are checked against
-    the oracle, and the 16 KiB guard after grad_x stays untouched."""
+    the column tiles' 16-byte path) and [1, 40000, 40001] fp32 (1.6 G
+    elements, 6.4 GB; the flat kernel), byte offsets past 2^32: x = 0 except a
+    few sampled columns, so every other column's gradient is exactly g / n
+    for g = 1 and lse = fl(ln n) (2^-16 for n = 65536; for n = 40000 the
+    constant the same formula gives in fp32, computed on the host); the
+    sampled columns are checked against the oracle, and the guard after
+    grad_x stays untouched."""
     torch = torch_gpu
-    n, inner = 65536, 40000
-    note(f"large dim backward bf16 n={n} inner={inner}: {n * inner * 2 / 1e9:.1f} GB")
-    x = torch.zeros((n, inner), dtype=torch.int16, device="cuda")
+    esize = 2 if dtype == "bf16" else 4
+    st = torch.int16 if dtype == "bf16" else torch.int32
+    note(f"large dim backward {dtype} n={n} inner={inner}: {n * inner * esize / 1e9:.1f} GB")
+    x = torch.zeros((n, inner), dtype=st, device="cuda")
     rng = np.random.default_rng(7)
     cols = np.unique(np.concatenate([rng.integers(0, inner, size=20), [0, inner - 1]]))
     vals = rng.normal(0, 3, size=(n, len(cols))).astype(np.float32)
-    hv = workloads.f32_to_bf16_bits(vals)
+    hv = workloads.f32_to_bf16_bits(vals) if dtype == "bf16" else vals
     idx = torch.from_numpy(cols).cuda()
-    x[:, idx] = torch.from_numpy(hv.view(np.int16)).cuda()
+    x[:, idx] = torch.from_numpy(hv.view(np.int16 if dtype == "bf16" else np.int32)).cuda()
     lse = np.full(inner, math.log(n), dtype=np.float32)
-    lse[cols] = oracle_mod.lse(np.ascontiguousarray(hv.T), "bf16").astype(np.float32)
+    lse[cols] = oracle_mod.lse(np.ascontiguousarray(hv.T), dtype).astype(np.float32)
     g = np.ones(inner, dtype=np.float32)
     g[cols] = rng.normal(0, 2, size=len(cols)).astype(np.float32)
     lt, gt = torch.from_numpy(lse).cuda(), torch.from_numpy(g).cuda()
-    guard = 8192
-    grad = torch.full((n * inner + guard,), 0x7F7F, dtype=torch.int16, device="cuda")
-    B.lse_backward_dim(handle, x.data_ptr(), DTYPE_CODE["bf16"], 1, n, inner, lt.data_ptr(),
+    guard = 16384 // esize
+    sentinel = 0x7F7F if dtype == "bf16" else 0x7F7F7F7F
+    grad = torch.full((n * inner + guard,), sentinel, dtype=st, device="cuda")
+    B.lse_backward_dim(handle, x.data_ptr(), DTYPE_CODE[dtype], 1, n, inner, lt.data_ptr(),
                        gt.data_ptr(), grad.data_ptr(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    assert bool((grad[n * inner:] == 0x7F7F).all()), "the guard after grad_x was written"
+    assert bool((grad[n * inner:] == sentinel).all()), "the guard after grad_x was written"
     gv = grad[: n * inner].view(n, inner)
     mask = torch.ones(inner, dtype=torch.bool, device="cuda")
     mask[idx] = False
-    want = np.array([2.0 ** -16], dtype=np.float32)
-    want_bits = int(workloads.f32_to_bf16_bits(want)[0])
-    bad = int((gv[:, mask] != want_bits).sum())
-    assert bad == 0, f"{bad} elements of the constant columns differ from 2^-16"
-    got = gv[:, idx].cpu().numpy().view(np.uint16)
-    got = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    ref = oracle_mod.softmax_grad(np.ascontiguousarray(hv.T), lse[cols], g[cols], "bf16").T
-    rel = 2.0 ** -8 + 1e-6
-    d = np.abs(workloads.bf16_bits_to_f32(hv).astype(np.float64) - lse[cols][None, :])
+    # the zero columns' gradient: 1 * 2^((0 - fl(ln n)) * fl(log2 e)) in fp32,
+    # which is exactly 2^-16 for n = 65536; compared as the stored bits
+    c = np.float32(np.float32(0.0) - np.float32(math.log(n))) * np.float32(math.log2(math.e))
+    want = np.array([np.exp2(np.float64(c))], dtype=np.float32)
+    if n == 65536:
+        assert want[0] == np.float32(2.0 ** -16)
+    if dtype == "bf16":
+        want_bits = int(workloads.f32_to_bf16_bits(want)[0])
+        bad = int((gv[:, mask] != want_bits).sum())
+        assert bad == 0, f"{bad} elements of the constant columns differ from g / n"
+    else:
+        # v_exp_f32 is within 1 ulp of 2^c: the constant columns agree with it
+        # to that and with each other exactly
+        const = gv[:, mask].view(torch.float32)
+        first = const[0, 0].item()
+        assert abs(first - float(want[0])) <= 2.0 ** -23 * float(want[0]) * 2
+        assert bool((const == first).all()), "the constant columns differ from each other"
+    got = gv[:, idx].cpu().numpy()
+    if dtype == "bf16":
+        got = (got.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    else:
+        got = got.view(np.float32)
+    got = got.astype(np.float64)
+    ref = oracle_mod.softmax_grad(np.ascontiguousarray(hv.T), lse[cols], g[cols], dtype).T
+    rel = 2.0 ** -8 + 1e-6 if dtype == "bf16" else 4e-7  # as compare_grad
+    xv = workloads.bf16_bits_to_f32(hv) if dtype == "bf16" else hv
+    d = np.abs(xv.astype(np.float64) - lse[cols][None, :])
     tol = (rel + 2e-7 * d) * np.abs(ref) + 2.0 ** -125 * np.maximum(1.0, np.abs(g[cols]))[None, :]
     assert np.all(np.abs(got - ref) <= tol), "sampled columns differ from the oracle"
     del x, grad, gv
