@@ -8,13 +8,14 @@ the high 64 bits of m * a for every a, d < 2^32 (Lemire, Kaser and Kurz,
 32-bit operands). d = 1 would need m = 2^64, so the host passes m = 0 for it
 and the kernel then returns a itself.
 
-Each workgroup locates its first flat element F with 64-bit divisions, and an
-element d places later (d below the chunk of CH elements) by the column
-(iF + d) mod inner, the rows (iF + d) div inner, and the slices
-(jF + rows) div n: a single compare where inner > CH, exact 32-bit divisions
-otherwise. Written out here as in the kernel and compared with the direct
-index (f div (n * inner)) * inner + f mod inner of every element of random
-chunks.
+Each workgroup locates its first flat element F with 64-bit divisions, and
+the element d places later (d below the chunk of CH elements) by its column
+and the rows and slices it lies past F's: where inner > CH a single compare
+(one wrap at most, to the next row or, from a slice's last row, the next
+slice); else slot m * 256 + t steps column and row by 256 elements from one
+exact division, and the slice is a division unless the array has one slice.
+Written out here as in the kernel and compared with the direct index
+(f div (n * inner)) * inner + f mod inner of every element of random chunks.
 """
 import numpy as np
 import pytest
@@ -54,28 +55,44 @@ def test_fastdiv_random_divisors():
 
 
 def locate_chunk(F: int, CH: int, n: int, inner: int, total: int) -> list:
-    """The kernel's lookup index for elements F .. F + CH - 1 (those < total)."""
+    """The kernel's lookup index for the slots d = m * 256 + t of the chunk at
+    F (elements F + d < total), in its two cases."""
     qF = F // inner
     iF = F - qF * inner
     oF = qF // n
     jF = qF - oF * n
-    m_inner = magic(inner) if inner < (1 << 32) else 0
-    m_n = magic(n)
-    out = []
-    for d in range(min(CH, total - F)):
-        if inner > CH:
-            a = iF + d
-            q = 1 if a >= inner else 0
-            i = a - inner if q else a
-        else:
-            a = iF + d
-            assert a < (1 << 32)
-            q = fastdiv(a, m_inner)
-            i = a - q * inner
-        rows = jF + q
-        assert rows < (1 << 32)
-        out.append((oF + fastdiv(rows, m_n)) * inner + i)
-    return out
+    M = CH // 256
+    out = {}
+    if inner > CH:
+        gF = oF * inner + iF
+        last_row = jF + 1 == n
+        for d in range(CH):
+            if d < total - F:
+                wrap = iF + d >= inner
+                out[d] = gF + d - (inner if wrap and not last_row else 0)
+        return [out[d] for d in sorted(out)]
+    m_inner, m_n = magic(inner), magic(n)
+    one_slice = total == n * inner
+    for t in range(256):
+        a0 = iF + t
+        assert a0 < (1 << 32)
+        q = fastdiv(a0, m_inner)
+        i = a0 - q * inner
+        q256 = fastdiv(256, m_inner)
+        r256 = 256 - q256 * inner
+        for m in range(M):
+            if m > 0:
+                i += r256
+                q += q256
+                if i >= inner:
+                    i -= inner
+                    q += 1
+            assert i < inner and jF + q < (1 << 32)
+            b = 0 if one_slice else fastdiv(jF + q, m_n)
+            d = m * 256 + t
+            if d < total - F:
+                out[d] = (oF + b) * inner + i
+    return [out[d] for d in sorted(out)]
 
 
 @pytest.mark.parametrize("K,U", [(4, 4), (8, 2), (1, 16)])
