@@ -731,15 +731,24 @@ lse_status_t lse_backward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, 
     const bool vec = inner % k == 0 && x_addr % 16 == 0 && g_addr % 16 == 0;
     // The flat kernel (lanes own 16-byte vectors of memory, or elements, and
     // stage their lse and grad_out through LDS) where the column tiles would
-    // take one column per lane, and for fp32 while lse and grad_out fit one
-    // XCD's 4 MiB L2, as it reads them again for every j; the column tiles
-    // otherwise, and whenever lse_set_tuning forces `parts`. Measured as
-    // library copies over the first axis (flat against tiles): fp32 [65536,
-    // 4097] 364 against 1316 us, bf16 [512, 50257] 28.0 against 48.5, fp32
-    // [65536, 4096] 359 against 417; fp32 [16, 4000000] (32 MB of lse and
-    // grad_out) 135 against 98, bf16 [512, 128256] 69 against 49.
+    // take one column per lane; and, while lse and grad_out fit one XCD's
+    // 4 MiB L2 (the flat kernel reads them again for every j), for fp32, and
+    // for 16-bit types whose row pitch is not a multiple of 128 bytes (the
+    // tiles' row pieces then straddle cache lines) unless a tile spans whole
+    // rows (32 column groups or fewer: consecutive rows, contiguous). The
+    // column tiles otherwise, and whenever lse_set_tuning forces `parts`.
+    // Measured as library copies over the first axis (flat against tiles):
+    // fp32 [65536, 4097] 364 against 1316 us, bf16 [512, 50257] 28.0 against
+    // 48.5, fp32 [65536, 4096] 359 against 417; bf16 [65536, 4104] 240
+    // against 318, f16 [16384, 4104] 60.0 against 80.1, bf16 [512, 128264]
+    // 59.7 against 66.8, bf16 [100000, 72] 9.2 against 8.0; fp32 [16, 4000000]
+    // (32 MB of lse and grad_out) 135 against 98, bf16 [512, 128256] 58.7
+    // against 49.3, bf16 [65536, 4096] 261 against 235.
     constexpr int64_t kFlatTableBytes = int64_t{4} << 20;
-    if (h->parts == 0 && (!vec || (dtype == LSE_DTYPE_F32 && nout <= kFlatTableBytes / 8))) {
+    const bool table_cached = nout <= kFlatTableBytes / 8;
+    const bool pitch_off_lines = (inner * esize) % 128 != 0 && inner / k > kDimGroups;
+    if (h->parts == 0 &&
+        (!vec || (table_cached && (dtype == LSE_DTYPE_F32 || pitch_off_lines)))) {
         lse::DimFlatArgs f{};
         f.dtype = dtype;
         f.x = static_cast<const char*>(x);
