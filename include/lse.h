@@ -251,10 +251,12 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void *x, lse_dtype_t dtype,
  * As in lse_backward, the formula is applied as written in fp32 arithmetic
  * (any lse is accepted; IEEE special values). One streaming pass: x read
  * once, grad_x written once, nothing else written; lse and grad_out are read
- * once per column tile, or, on the flat schedule the planner takes for fp32
- * and for widths or bases that do not fit 16-byte column groups, once per
- * element from the caches; no workspace, no allocation, no synchronisation.
- * The results do not depend on the schedule.
+ * once per column tile, or, on the flat schedule (which the planner takes for
+ * widths or bases that do not fit 16-byte column groups, and, while lse and
+ * grad_out total at most 4 MiB, for fp32 and for 16-bit rows whose pitch is
+ * not a multiple of 128 bytes), once per element from the caches; no
+ * workspace, no allocation, no synchronisation. The results do not depend on
+ * the schedule.
  * Errors: UNSUPPORTED_DTYPE; INVALID_ARG (sizes, NULL or misaligned pointers
  * with work to do, NULL handle); HIP.
  */
