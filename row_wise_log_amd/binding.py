@@ -61,8 +61,15 @@ _lib: ctypes.CDLL | None = None
 def load(path: Path | str = LIBRARY) -> ctypes.CDLL:
     """Load the HIP library once; raise if it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
+    if _lib is None:
+        _lib = load_from(path)
+    return _lib
+
+
+def load_from(path: Path | str) -> ctypes.CDLL:
+    """A library build at `path` with the C ABI's signatures set, loaded on its
+    own (not the module's cached library): for timing two builds side by side
+    (`row_wise_log_amd.ab_builds`)."""
     path = Path(path)
     if not path.exists():
         raise RuntimeError(f"{path} is missing: build it with `python -m row_wise_log_amd.build` "
@@ -89,7 +96,6 @@ def load(path: Path | str = LIBRARY) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
     return lib
 
 
