@@ -163,8 +163,14 @@ def test_backward_f16(torch_gpu, handle, oracle, cols, layout):
 
 
 @pytest.mark.parametrize("shape,front", [((1, 8192, 4096), 0), ((64, 1000, 32), 0),
-                                         ((3, 5, 7), 0), ((16, 257, 40), 1), ((2, 100_000, 3), 0)])
+                                         ((3, 5, 7), 0), ((16, 257, 40), 1), ((2, 100_000, 3), 0),
+                                         ((1, 4096, 4097), 0), ((1, 20_000, 1025), 1),
+                                         ((1, 1_000_000, 8), 0)])
 def test_dim_f16(torch_gpu, handle, shape, front):
+    """lse_forward_dim on fp16: the 16-byte path, the one-column path unsplit
+    and split (16-step batches, about two workgroups per CU), a misaligned
+    base, and one column group per row (lanes sharing columns in the end
+    merge)."""
     import oracle as orc
     torch = torch_gpu
     v = np.random.default_rng(sum(shape)).normal(0, 4, size=shape).astype(np.float32)
