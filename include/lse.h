@@ -253,7 +253,7 @@ lse_status_t lse_forward_dim(lse_handle_t h, const void *x, lse_dtype_t dtype,
  * once, grad_x written once, nothing else written; lse and grad_out are read
  * once per column tile, or, on the flat schedule (which the planner takes for
  * widths or bases that do not fit 16-byte column groups, and, while lse and
- * grad_out total at most 4 MiB, for fp32 and for 16-bit rows whose pitch is
+ * grad_out total at most 16 MiB, for fp32 and for 16-bit rows whose pitch is
  * not a multiple of 128 bytes), once per element from the caches; no
  * workspace, no allocation, no synchronisation. The results do not depend on
  * the schedule.

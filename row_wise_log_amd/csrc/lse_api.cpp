@@ -731,8 +731,9 @@ lse_status_t lse_backward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, 
     const bool vec = inner % k == 0 && x_addr % 16 == 0 && g_addr % 16 == 0;
     // The flat kernel (lanes own 16-byte vectors of memory, or elements, and
     // stage their lse and grad_out through LDS) where the column tiles would
-    // take one column per lane; and, while lse and grad_out fit one XCD's
-    // 4 MiB L2 (the flat kernel reads them again for every j), for fp32, and
+    // take one column per lane; and, while lse and grad_out total at most
+    // 16 MiB (the flat kernel reads them again for every j, from L2 or the
+    // Infinity Cache), for fp32, and
     // for 16-bit types whose row pitch is not a multiple of 128 bytes (the
     // tiles' row pieces then straddle cache lines) unless a tile spans whole
     // rows (32 column groups or fewer: consecutive rows, contiguous). The
@@ -741,10 +742,12 @@ lse_status_t lse_backward_dim(lse_handle_t h, const void* x, lse_dtype_t dtype, 
     // fp32 [65536, 4097] 364 against 1316 us, bf16 [512, 50257] 28.0 against
     // 48.5, fp32 [65536, 4096] 359 against 417; bf16 [65536, 4104] 240
     // against 318, f16 [16384, 4104] 60.0 against 80.1, bf16 [512, 128264]
-    // 59.7 against 66.8, bf16 [100000, 72] 9.2 against 8.0; fp32 [16, 4000000]
-    // (32 MB of lse and grad_out) 135 against 98, bf16 [512, 128256] 58.7
-    // against 49.3, bf16 [65536, 4096] 261 against 235.
-    constexpr int64_t kFlatTableBytes = int64_t{4} << 20;
+    // 59.7 against 66.8, bf16 [100000, 72] 9.2 against 8.0; fp32 [512,
+    // 1048576] (8 MiB of lse and grad_out) 729 against 834, fp32 [64, 2000000]
+    // (16 MB) 186 against 189, but fp32 [16, 4000000] and [32, 4000000] (32
+    // MB) 132 against 98 and 263 against 189; bf16 [512, 128256] 58.7 against
+    // 49.3, bf16 [65536, 4096] 261 against 235.
+    constexpr int64_t kFlatTableBytes = int64_t{16} << 20;
     const bool table_cached = nout <= kFlatTableBytes / 8;
     const bool pitch_off_lines = (inner * esize) % 128 != 0 && inner / k > kDimGroups;
     if (h->parts == 0 &&

@@ -9,8 +9,8 @@ incoming gradients. The bar is the row-wise backward pass's (compare_grad).
 
 * Shapes [outer, n, inner] on the column tiles (16-bit types at widths that
   are multiples of the vector, rows on 128-byte lines or spanned by one tile)
-  and the flat kernel (fp32; odd inner; 16-bit rows off the 128-byte lines,
-  inner 1032; a misaligned x, with grad_x at the same phase or not; fewer
+  and the flat kernel (fp32, also with 4.8 MB of lse and grad_out; odd inner;
+  16-bit rows off the 128-byte lines, inner 1032; a misaligned x, with grad_x at the same phase or not; fewer
   elements than one vector; n == 1 with several slices), fp32, bf16 and fp16;
   nothing outside grad_x is written.
 * Forced splits of n (parts: the column tiles, both paths), special values
@@ -66,7 +66,8 @@ def lse_and_grads(x3, dtype, seed):
 
 SHAPES = [(1, 8192, 4096), (64, 1000, 32), (3, 5, 7), (2, 30_000, 3), (128, 17, 1024),
           (1, 1, 100), (7, 33, 12), (1, 3, 65), (16, 257, 40), (1, 64, 4 * 64 * 300),
-          (2, 700, 1001), (1, 2, 3), (5, 1, 37), (3, 1000, 5001), (2, 300, 1032)]
+          (2, 700, 1001), (1, 2, 3), (5, 1, 37), (3, 1000, 5001), (2, 300, 1032),
+          (1, 4, 600_000)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
